@@ -1,0 +1,8 @@
+"""libqmm for MI355X: matrix multiplies whose weights are block-quantized 4/6-bit
+codes dequantized inside hand-written gfx950 HIP kernels against bfloat16
+activations.  The C ABI is include/qmm.h; this package is its ctypes binding.
+"""
+
+from .qmm import (AFFINE4_G64, BF16, F32, FORMATS, MXFP4, NVFP4, Q6_K, PreparedGemv, QmmError,  # noqa: F401
+                  Weight, bench_stream_read, dequant, gemv, gemv_workspace_size, lib_handle, new_workspace,
+                  workspace_init)

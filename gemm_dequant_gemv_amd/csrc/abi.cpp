@@ -1,0 +1,168 @@
+// The C ABI of libqmm: argument validation on the host, workspace sizing, and
+// dispatch to the kernels on the caller's stream.  Nothing here allocates,
+// frees or synchronizes.
+#include <algorithm>
+#include <stdint.h>
+
+#include "qmm.h"
+#include "qmm_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return QMM_OK;
+  g_last_hip_error = (int)e;
+  return QMM_ERR_HIP;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+Range range(const void *p, size_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; }
+
+size_t codes_bytes(const qmm_weight &w) { return (size_t)w.batch * w.n * (size_t)(w.k / 2); }
+size_t hi_bytes(const qmm_weight &w) { return (size_t)w.batch * w.n * (size_t)(w.k / 4); }
+size_t scales_bytes(const qmm_weight &w) {
+  const size_t rows = (size_t)w.batch * w.n;
+  switch (w.format) {
+    case QMM_AFFINE4_G64: return rows * (w.k / 64) * 4;
+    case QMM_MXFP4: return rows * (w.k / 32);
+    case QMM_NVFP4: return rows * (w.k / 16);
+    default: return rows * (w.k / 16);
+  }
+}
+size_t scales2_bytes(const qmm_weight &w) { return (size_t)w.batch * w.n * (size_t)(w.k / 256) * 2; }
+
+// Every byte range the weight occupies (for aliasing checks).
+int weight_ranges(const qmm_weight &w, Range out[5]) {
+  int n = 0;
+  out[n++] = range(w.codes, codes_bytes(w));
+  out[n++] = range(w.scales, scales_bytes(w));
+  if (w.codes_hi) out[n++] = range(w.codes_hi, hi_bytes(w));
+  if (w.scales2) out[n++] = range(w.scales2, scales2_bytes(w));
+  if (w.tensor_scale) out[n++] = range(w.tensor_scale, (size_t)w.batch * 4);
+  return n;
+}
+
+int check_weight(const qmm_weight *w) {
+  if (!w) return QMM_ERR_NULL;
+  if (w->format < QMM_AFFINE4_G64 || w->format > QMM_Q6_K) return QMM_ERR_FORMAT;
+  if (!w->codes || !w->scales) return QMM_ERR_NULL;
+  const bool q6 = w->format == QMM_Q6_K;
+  if (q6 && (!w->codes_hi || !w->scales2)) return QMM_ERR_NULL;
+  if (!q6 && (w->codes_hi || w->scales2)) return QMM_ERR_FORMAT;
+  if (w->tensor_scale && w->format != QMM_NVFP4) return QMM_ERR_FORMAT;
+  if (w->n < 1 || w->k < 32 || w->batch < 1) return QMM_ERR_SHAPE;
+  if (w->k % 32 != 0) return QMM_ERR_SHAPE;
+  // every row of every scale plane starts on a 4-byte boundary
+  if (w->format == QMM_AFFINE4_G64 && w->k % 64 != 0) return QMM_ERR_SHAPE;
+  if (w->format == QMM_NVFP4 && w->k % 64 != 0) return QMM_ERR_SHAPE;
+  if (w->format == QMM_MXFP4 && w->k % 128 != 0) return QMM_ERR_SHAPE;
+  if (q6 && w->k % 256 != 0) return QMM_ERR_SHAPE;
+  // every plane is addressed with 32-bit byte offsets
+  if ((uint64_t)w->batch * (uint64_t)w->n * (uint64_t)(w->k / 2) >= (1ull << 32)) return QMM_ERR_SHAPE;
+  if (!aligned(w->codes, 16) || !aligned(w->scales, 4)) return QMM_ERR_ALIGN;
+  if (q6 && (!aligned(w->codes_hi, 8) || !aligned(w->scales2, 2))) return QMM_ERR_ALIGN;
+  if (w->tensor_scale && !aligned(w->tensor_scale, 4)) return QMM_ERR_ALIGN;
+  return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qstatus_string(int status) {
+  switch (status) {
+    case QMM_OK: return "ok";
+    case QMM_ERR_NULL: return "a required pointer is NULL";
+    case QMM_ERR_FORMAT: return "unknown format, or a plane the format does not have";
+    case QMM_ERR_SHAPE: return "shape out of range, or k not a multiple of 32 and of the format's k granule (64 affine and NVFP4, 128 MXFP4, 256 Q6_K)";
+    case QMM_ERR_ALIGN: return "pointer not aligned as required";
+    case QMM_ERR_M_RANGE: return "m (activation rows) out of range for this call";
+    case QMM_ERR_WORKSPACE: return "workspace missing or too small";
+    case QMM_ERR_ALIAS: return "an output overlaps an input";
+    case QMM_ERR_HIP: return "a HIP runtime call failed";
+    case QMM_ERR_DTYPE: return "unknown output dtype";
+    case QMM_ERR_ARG: return "argument out of range";
+    default: return "unknown status";
+  }
+}
+
+int qlast_hip_error(void) { return g_last_hip_error; }
+
+int qworkspace_init(void *workspace, size_t workspace_bytes, void *stream) {
+  if (workspace_bytes == 0) return QMM_OK;
+  if (!workspace) return QMM_ERR_NULL;
+  if (!aligned(workspace, 4)) return QMM_ERR_ALIGN;
+  return hip_status(qmm::launch_zero(workspace, workspace_bytes, (hipStream_t)stream));
+}
+
+int qdequant(const qmm_weight *w, int32_t out_dtype, void *out, void *stream) {
+  int st = check_weight(w);
+  if (st) return st;
+  if (out_dtype != QMM_F32 && out_dtype != QMM_BF16) return QMM_ERR_DTYPE;
+  if (!out) return QMM_ERR_NULL;
+  if (!aligned(out, 16)) return QMM_ERR_ALIGN;
+  const size_t ob = (size_t)w->batch * w->n * (size_t)w->k * (out_dtype == QMM_F32 ? 4 : 2);
+  Range rs[5];
+  const int nr = weight_ranges(*w, rs);
+  for (int i = 0; i < nr; ++i)
+    if (overlap(range(out, ob), rs[i])) return QMM_ERR_ALIAS;
+  return hip_status(qmm::launch_dequant(*w, out_dtype, out, (hipStream_t)stream));
+}
+
+int qbench_stream_read(const void *buf, size_t bytes, void *sink, int32_t blocks, void *stream) {
+  if (!buf || !sink) return QMM_ERR_NULL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return QMM_ERR_ALIGN;
+  if (bytes == 0 || bytes % 16 != 0) return QMM_ERR_SHAPE;
+  if (blocks < 1 || blocks > (1 << 20)) return QMM_ERR_ARG;
+  if (overlap(range(sink, 4), range(buf, bytes))) return QMM_ERR_ALIAS;
+  return hip_status(
+      qmm::launch_stream_read(buf, bytes, (uint32_t *)sink, blocks, (hipStream_t)stream));
+}
+
+size_t qgemv_workspace_size(const qmm_weight *w, int32_t m) {
+  if (check_weight(w) || m < 1 || m > 4) return 0;
+  return qmm::plan_gemv(w->format, w->n, w->k, m).ws_bytes;
+}
+
+int qgemv(const qmm_weight *w, const void *x, int32_t m, const void *residual, void *y,
+          int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_weight(w);
+  if (st) return st;
+  if (w->batch != 1) return QMM_ERR_SHAPE;
+  if (m < 1 || m > 4) return QMM_ERR_M_RANGE;
+  if (y_dtype != QMM_F32 && y_dtype != QMM_BF16) return QMM_ERR_DTYPE;
+  if (!x || !y) return QMM_ERR_NULL;
+  const size_t esz = y_dtype == QMM_F32 ? 4 : 2;
+  if (!aligned(x, 16) || !aligned(y, esz) || (residual && !aligned(residual, 2)))
+    return QMM_ERR_ALIGN;
+  const qmm::GemvPlan p = qmm::plan_gemv(w->format, w->n, w->k, m);
+  if (p.ws_bytes) {
+    if (!workspace) return QMM_ERR_WORKSPACE;
+    if (workspace_bytes < p.ws_bytes) return QMM_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return QMM_ERR_ALIGN;
+  }
+  const Range ry = range(y, (size_t)m * w->n * esz);
+  Range ins[8];
+  int ni = weight_ranges(*w, ins);
+  ins[ni++] = range(x, (size_t)m * w->k * 2);
+  if (residual) ins[ni++] = range(residual, (size_t)m * w->n * 2);
+  if (p.ws_bytes) ins[ni++] = range(workspace, p.ws_bytes);
+  for (int i = 0; i < ni; ++i)
+    if (overlap(ry, ins[i])) return QMM_ERR_ALIAS;
+  if (p.ws_bytes) {
+    const Range rw = range(workspace, p.ws_bytes);
+    for (int i = 0; i < ni - 1; ++i)
+      if (overlap(rw, ins[i])) return QMM_ERR_ALIAS;
+  }
+  return hip_status(qmm::launch_gemv(*w, x, m, residual, y, y_dtype, workspace, p,
+                                     (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Device-side helpers shared by the libqmm kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmm {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load of data that is read once (weights): non-temporal hint.
+__device__ __forceinline__ uint4 load_stream16(const void *p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// bfloat16 pair (low half, high half) of a 32-bit word, widened to float.
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ __forceinline__ float half_to_float(uint32_t h16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+
+// D = a.lo*b.lo + a.hi*b.hi + c, bfloat16 pairs, float32 accumulate
+// (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Two E2M1 codes (the byte BYTE of w: low nibble first) -> a bfloat16 pair,
+// exactly (v_cvt_scalef32_pk_bf16_fp4 with a unit scale).
+template <int BYTE>
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, BYTE));
+}
+
+// E8M0 power-of-two scale -> float32 (2^(e-127); e = 0 is the subnormal 2^-127;
+// 0xFF is NaN).
+__device__ __forceinline__ float e8m0_to_float(uint32_t e) {
+  e &= 0xFFu;
+  uint32_t bits = e == 0 ? 0x00400000u : (e == 0xFFu ? 0x7FC00000u : e << 23);
+  return __uint_as_float(bits);
+}
+
+// E4M3 (bias 7, subnormals, S.1111.111 = NaN) -> float32, exactly.
+__device__ __forceinline__ float e4m3_to_float(uint32_t b) {
+  b &= 0xFFu;
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  if ((b & 0x7Fu) == 0x7Fu) v = __uint_as_float(0x7FC00000u);
+  return __uint_as_float(__float_as_uint(v) | ((b & 0x80u) << 24));
+}
+
+// float32 -> bfloat16 bits, round to nearest even, NaN kept quiet.
+__device__ __forceinline__ uint32_t float_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Four 4-bit codes at bits 4i (i = p, p+4 within a 32-bit word of eight codes)
+// -> bfloat16 pair (128 + q_p, 128 + q_{p+4}): the nibble lands in the low
+// mantissa bits of 128.0 (0x4300), so no conversion instruction is needed.
+template <int P>
+__device__ __forceinline__ uint32_t nib_pair_128(uint32_t w) {
+  return ((w >> (4 * P)) & 0x000F000Fu) | 0x43004300u;
+}
+
+}  // namespace qmm

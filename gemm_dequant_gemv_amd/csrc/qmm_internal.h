@@ -1,0 +1,45 @@
+// Internal interface between the C-ABI layer (abi.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qmm.h"
+
+namespace qmm {
+
+// Decode-GEMV tiling: a workgroup of 4 waves covers 32 * R rows; inside a
+// wave, 8 lanes share a row (each reading 16 consecutive bytes of codes = 32
+// weights, so the 8 lanes read 128 contiguous bytes) and every lane carries R
+// rows.  One K step is therefore 8 x 32 = 256 weights; D steps are kept in
+// flight.  K is split over `splits` workgroups when the rows alone do not give
+// enough workgroups.
+constexpr int kGemvThreads = 256;
+constexpr int kGemvStep = 256;      // K values per step (8 lanes x 32)
+constexpr int kMaxSplitK = 2048;    // K values one workgroup covers at most
+
+struct GemvPlan {
+  int rows_per_lane;  // R
+  int depth;          // D: steps of weights in flight per lane
+  int lanes_k;        // LK: lanes sharing a row (each reads 16 bytes per step)
+  int steps;      // ceil(k / (32 * LK))
+  int tiles;      // ceil(n / rows per workgroup)
+  int splits;     // K splits (workgroups per row tile)
+  int max_steps;  // steps of the longest split
+  size_t lds_bytes;
+  size_t ws_bytes;        // workspace needed (0 when splits == 1)
+  size_t counters_bytes;  // leading part of the workspace: one u32 per tile
+};
+
+GemvPlan plan_gemv(int format, int n, int k, int m);
+
+hipError_t launch_dequant(const qmm_weight &w, int out_dtype, void *out, hipStream_t s);
+hipError_t launch_gemv(const qmm_weight &w, const void *x, int m, const void *residual,
+                       void *y, int y_dtype, void *workspace, const GemvPlan &p,
+                       hipStream_t s);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+hipError_t launch_stream_read(const void *p, size_t bytes, uint32_t *sink, int blocks,
+                              hipStream_t s);
+
+}  // namespace qmm

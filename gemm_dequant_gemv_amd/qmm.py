@@ -1,0 +1,188 @@
+"""Thin Python binding of libqmm (ctypes): argument marshalling only.
+
+Every step of every call runs in the library's HIP kernels; PyTorch provides
+device memory and the current stream.  If libqmm.so has not been built the
+first call raises; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# QMM_LIB_PATH selects another build of the same library (experiments only)
+LIB_PATH = os.environ.get("QMM_LIB_PATH") or os.path.join(_HERE, "libqmm.so")
+
+AFFINE4_G64, MXFP4, NVFP4, Q6_K = 1, 2, 3, 4
+F32, BF16 = 0, 1
+FORMATS = {"affine4_g64": AFFINE4_G64, "mxfp4": MXFP4, "nvfp4": NVFP4, "q6_k": Q6_K}
+
+ENTRY_POINTS = ("qdequant", "qgemv", "qgemv_workspace_size", "qworkspace_init",
+                "qbench_stream_read", "qstatus_string", "qlast_hip_error")
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib().qstatus_string(status).decode()
+        if status == -8:
+            msg += f" (hipError_t {_lib().qlast_hip_error()})"
+        super().__init__(f"{where}: {msg} [{status}]")
+
+
+class QmmWeightC(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("batch", ctypes.c_int32), ("codes", ctypes.c_void_p),
+                ("codes_hi", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("scales2", ctypes.c_void_p), ("tensor_scale", ctypes.c_void_p)]
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "or python -m gemm_dequant_gemv_amd.build")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ, VP = ctypes.POINTER(QmmWeightC), ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+        lib.qdequant.argtypes = [P, I32, VP, VP]
+        lib.qgemv_workspace_size.argtypes = [P, I32]
+        lib.qgemv_workspace_size.restype = SZ
+        lib.qgemv.argtypes = [P, VP, I32, VP, VP, I32, VP, SZ, VP]
+        lib.qworkspace_init.argtypes = [VP, SZ, VP]
+        lib.qbench_stream_read.argtypes = [VP, SZ, VP, I32, VP]
+        lib.qstatus_string.restype = ctypes.c_char_p
+        lib.qstatus_string.argtypes = [ctypes.c_int]
+        _LIB = lib
+    return _LIB
+
+
+def lib_handle():
+    return _lib()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise QmmError(status, where)
+
+
+class Weight:
+    """A packed weight (or batch of experts) resident on the device.
+
+    Planes follow include/qmm.h: ``codes`` u8 [batch][n][k/2], ``codes_hi``
+    u8 [batch][n][k/4] (Q6_K), ``scales`` (format dependent), ``scales2``
+    f16 [batch][n][k/256] (Q6_K), ``tensor_scale`` f32 [batch] (NVFP4)."""
+
+    def __init__(self, fmt: int, n: int, k: int, batch: int, codes, scales,
+                 codes_hi=None, scales2=None, tensor_scale=None):
+        self.fmt, self.n, self.k, self.batch = int(fmt), int(n), int(k), int(batch)
+        self.codes, self.scales = codes, scales
+        self.codes_hi, self.scales2, self.tensor_scale = codes_hi, scales2, tensor_scale
+        self._c = QmmWeightC(self.fmt, self.n, self.k, self.batch, self.codes.data_ptr(),
+                             None if codes_hi is None else codes_hi.data_ptr(),
+                             self.scales.data_ptr(),
+                             None if scales2 is None else scales2.data_ptr(),
+                             None if tensor_scale is None else tensor_scale.data_ptr())
+
+    @classmethod
+    def from_host(cls, p, device="cuda"):
+        """Upload an object with numpy planes (``fmt, n, k, batch, codes,
+        scales, codes_hi, scales2, tensor_scale``)."""
+        def up(a):
+            if a is None:
+                return None
+            return torch.from_numpy(a.copy()).to(device)
+        return cls(p.fmt, p.n, p.k, p.batch, up(p.codes), up(p.scales), up(p.codes_hi),
+                   up(p.scales2), up(p.tensor_scale))
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in
+                   (self.codes, self.scales, self.codes_hi, self.scales2, self.tensor_scale)
+                   if t is not None)
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def dequant(w: Weight, out_dtype=torch.float32, out=None, stream=None):
+    if out is None:
+        out = torch.empty((w.batch, w.n, w.k), dtype=out_dtype, device=w.codes.device)
+    dt = F32 if out.dtype == torch.float32 else BF16
+    _check(_lib().qdequant(w.c, dt, _ptr(out), _stream(stream)), "qdequant")
+    return out
+
+
+def gemv_workspace_size(w: Weight, m: int) -> int:
+    return int(_lib().qgemv_workspace_size(w.c, m))
+
+
+def new_workspace(nbytes: int, device="cuda"):
+    """A zero-filled workspace (the library leaves it zero-filled after each call)."""
+    if nbytes == 0:
+        return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def gemv(w: Weight, x, residual=None, y_dtype=torch.float32, out=None, workspace=None,
+         stream=None):
+    """y[m][n] = sum_k w[n][k] x[m][k] (+ residual), m = x.shape[0] in 1..4."""
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, w.n), dtype=y_dtype, device=x.device)
+    need = gemv_workspace_size(w, m)
+    if workspace is None and need:
+        workspace = new_workspace(need, x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dt = F32 if out.dtype == torch.float32 else BF16
+    _check(_lib().qgemv(w.c, _ptr(x), m, _ptr(residual), _ptr(out), dt, _ptr(workspace),
+                        ws_bytes, _stream(stream)), "qgemv")
+    return out
+
+
+def workspace_init(ws, stream=None):
+    _check(_lib().qworkspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "qworkspace_init")
+
+
+def bench_stream_read(buf, sink, blocks: int, stream=None):
+    """Stream-read ``buf`` (a device tensor) once; see qbench_stream_read."""
+    _check(_lib().qbench_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                     int(blocks), _stream(stream)), "qbench_stream_read")
+
+
+class PreparedGemv:
+    """A qgemv call with every argument marshalled once, for loops that launch
+    the same call many times (benchmarks, decode loops).  Calling it launches
+    the kernel on the stream given here (the current stream by default)."""
+
+    def __init__(self, w: Weight, x, out, residual=None, workspace=None, stream=None):
+        self.w, self.x, self.out, self.residual, self.workspace = w, x, out, residual, workspace
+        need = gemv_workspace_size(w, x.shape[0])
+        if need and workspace is None:
+            raise ValueError("qgemv needs a workspace of %d bytes" % need)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        dt = F32 if out.dtype == torch.float32 else BF16
+        self._args = (w.c, _ptr(x), x.shape[0], _ptr(residual), _ptr(out), dt, _ptr(workspace),
+                      ws_bytes, _stream(stream))
+        self._fn = _lib().qgemv
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            raise QmmError(st, "qgemv")

@@ -1,0 +1,176 @@
+/*
+ * qmm.h -- C ABI of libqmm: matrix multiplies whose weights are block-quantized
+ * low-bit codes, dequantized inside the kernels against bfloat16 activations
+ * (weights 4 or 6 bits, activations 16 bits), for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one the pages call a W4A16 projection: every weight is
+ * expanded to 16 bits inside the kernel and multiplied at 16-bit precision with
+ * 32-bit accumulation, so that only the weights are approximated ("TurboEXL3",
+ * section 2.2, W4A16 bullet).  Formats ("TurboEXL3", section 2.1; splash PR #19,
+ * "What changed"):
+ *
+ *   QMM_AFFINE4_G64  4-bit unsigned codes q, one float16 scale s and one float16
+ *                    bias b per 64 weights: w = s*q + b           (4.5 bits/weight)
+ *   QMM_MXFP4        E2M1 codes, one E8M0 power-of-two scale E per 32 weights:
+ *                    w = e2m1(c) * 2^(E-127)                      (4.25 bits/weight)
+ *   QMM_NVFP4        E2M1 codes, one E4M3 scale S per 16 weights, one float32
+ *                    multiplier g per tensor: w = e2m1(c)*e4m3(S)*g (4.5 bits/weight)
+ *   QMM_Q6_K         6-bit codes q (4 low bits + 2 high bits), one int8 scale sc
+ *                    per 16 weights, one float16 scale d per 256 weights:
+ *                    w = d*sc*(q-32)                              (6.5625 bits/weight)
+ *
+ * E2M1: sign in bit 3, magnitude index in bits 0-2 into 0, 0.5, 1, 1.5, 2, 3, 4, 6
+ * (code 8 is -0).  E8M0: 2^(e-127), 0xFF is NaN.  E4M3: bias 7 with subnormals,
+ * largest finite 448, S.1111.111 is NaN.
+ *
+ * ----------------------------------------------------------------------------
+ * Conventions for every entry point
+ *
+ * Matrices.  W is N x K (N outputs, K inputs), row-major; quantization blocks run
+ * along K inside a row.  Activations X are M x K bfloat16, row-major; outputs are
+ * M x N, row-major ("y[m][n] = sum_k w[n][k] * x[m][k]").  K must be a multiple
+ * of the format's K granule, so that every row of codes starts on a 16-byte
+ * boundary and every row of scales on a 4-byte boundary: 64 for AFFINE4_G64 and
+ * NVFP4, 128 for MXFP4, 256 for Q6_K.  Each plane of a weight must be smaller
+ * than 4 GiB (32-bit byte offsets).
+ *
+ * Pointers.  Every pointer is a device pointer unless stated otherwise; the
+ * descriptor structs themselves live in host memory and are read before the call
+ * returns.  The caller owns every buffer.  The library never allocates, frees or
+ * synchronizes on a call path.  Codes, x and qdequant's output must be 16-byte
+ * aligned, codes_hi 8-byte, scales 4-byte, scales2 2-byte; y and residual need
+ * their element alignment.  Outputs may not alias any input.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ * Every call is asynchronous on that stream; a kernel fault surfaces at the
+ * caller's next synchronization.
+ *
+ * Errors.  Every entry point returns QMM_OK (0) or a negative QMM_ERR_* code.
+ * Arguments are validated on the host before anything is launched; on an error
+ * nothing is launched and nothing is written.  QMM_ERR_HIP means a HIP runtime
+ * call failed; qlast_hip_error() then returns its hipError_t (thread-local).
+ * Not checked (would need a device synchronization): expert ids in range, finite
+ * scales.  No C++ exception crosses this interface.
+ *
+ * Workspaces.  Calls that split a reduction across workgroups take a caller-
+ * owned workspace of at least *_workspace_size() bytes, 256-byte aligned.  It
+ * must be zero-filled once before its first use (qworkspace_init, hipMemset or
+ * torch.zeros); every call leaves it zero-filled again on the stream.  One
+ * workspace serves one call at a time: calls that may overlap need their own.
+ *
+ * Determinism.  Every sum runs in a fixed order and no floating-point atomics
+ * are used, so the same inputs give bitwise identical outputs on every run
+ * ("TurboEXL3", section 4.4, Numerics).
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum qmm_format { QMM_AFFINE4_G64 = 1, QMM_MXFP4 = 2, QMM_NVFP4 = 3, QMM_Q6_K = 4 };
+enum qmm_dtype { QMM_F32 = 0, QMM_BF16 = 1 };
+
+enum qmm_status {
+  QMM_OK = 0,
+  QMM_ERR_NULL = -1,      /* a required pointer is NULL                        */
+  QMM_ERR_FORMAT = -2,    /* unknown format or a plane that the format lacks    */
+  QMM_ERR_SHAPE = -3,     /* n, k or batch out of range or not block-aligned    */
+  QMM_ERR_ALIGN = -4,     /* a pointer is not aligned as required               */
+  QMM_ERR_M_RANGE = -5,   /* m (rows of x) out of range for the call            */
+  QMM_ERR_WORKSPACE = -6, /* workspace missing or smaller than *_workspace_size */
+  QMM_ERR_ALIAS = -7,     /* an output overlaps an input                        */
+  QMM_ERR_HIP = -8,       /* a HIP runtime call failed (see qlast_hip_error)    */
+  QMM_ERR_DTYPE = -9,     /* unknown output dtype                               */
+  QMM_ERR_ARG = -10       /* another argument out of range (topk, experts ...)  */
+};
+
+/*
+ * One N x K packed weight matrix, or a batch of `batch` of them with the same
+ * shape stored back to back (the experts of an MoE layer).  Planes, for matrix
+ * e of the batch ("[batch]" is the outermost index of every plane):
+ *
+ *   codes     u8 [batch][n][k/2]  4-bit codes; element k = 2j in bits 0-3 of
+ *                                 byte j, element 2j+1 in bits 4-7.  For Q6_K the
+ *                                 low 4 bits of each 6-bit code.
+ *   codes_hi  u8 [batch][n][k/4]  Q6_K only: the 2 high bits; element k = 4j+i in
+ *                                 bits 2i..2i+1 of byte j.  NULL otherwise.
+ *   scales    AFFINE4_G64: f16 [batch][n][k/64][2], pairs (scale s, bias b)
+ *             MXFP4:       u8  [batch][n][k/32], E8M0
+ *             NVFP4:       u8  [batch][n][k/16], E4M3
+ *             Q6_K:        i8  [batch][n][k/16], sub-block scale sc
+ *   scales2   Q6_K: f16 [batch][n][k/256], super-block scale d.  NULL otherwise.
+ *   tensor_scale  NVFP4: f32 [batch] (device), multiplier g of each matrix.
+ *                 NULL otherwise.
+ */
+typedef struct qmm_weight {
+  int32_t format; /* enum qmm_format                        */
+  int32_t n;      /* rows (outputs), >= 1                   */
+  int32_t k;      /* columns (inputs), multiple of the K granule */
+  int32_t batch;  /* matrices stored back to back, >= 1     */
+  const void *codes;
+  const void *codes_hi;
+  const void *scales;
+  const void *scales2;
+  const float *tensor_scale;
+} qmm_weight;
+
+/*
+ * qdequant -- expand every weight of every matrix of `w` to out[batch][n][k].
+ * out_dtype QMM_F32: the exact weight rounded once to nearest float32; for
+ * AFFINE4_G64 that is fma(s, q, b), for NVFP4 (e2m1*e4m3)*g; MXFP4 and Q6_K are
+ * exact.  QMM_BF16: that float32 rounded to nearest-even bfloat16.  Used for
+ * bit-exact checks of the decoders and as a decode-then-multiply building block.
+ */
+int qdequant(const qmm_weight *w, int32_t out_dtype, void *out, void *stream);
+
+/*
+ * qgemv -- decode matrix-vector product for 1 to 4 activation rows
+ * ("TurboEXL3", section 4.3: one GEMV launch for 1 to 4 rows, whose output
+ * blocks are finished by the workgroup that arrives last; section 4.2: split-K
+ * partial sums keep enough workgroups in flight; splash PR #19: lanes 1-4 and
+ * the "+res" projections).
+ *
+ *   y[m][n] = g * sum_k w[n][k] * x[m][k]  (+ residual[m][n])     0 <= m < M
+ *
+ * w         one matrix (batch must be 1)
+ * x         bf16 [m][k]
+ * m         1..4
+ * residual  bf16 [m][n] or NULL (added in float32 after the sum)
+ * y         [m][n], float32 (y_dtype QMM_F32) or bfloat16 rounded to nearest
+ *           even (QMM_BF16)
+ * workspace at least qgemv_workspace_size(w, m) bytes (may be NULL when that is 0)
+ */
+size_t qgemv_workspace_size(const qmm_weight *w, int32_t m);
+int qgemv(const qmm_weight *w, const void *x, int32_t m, const void *residual,
+          void *y, int32_t y_dtype, void *workspace, size_t workspace_bytes,
+          void *stream);
+
+/*
+ * qbench_stream_read -- measurement helper: read `bytes` (multiple of 16) of
+ * `buf` with 16-byte non-temporal loads, the access pattern of the weight
+ * stream, on `blocks` workgroups of 256 threads.  Writes at most 4 bytes to
+ * `sink` (device).  Timing it gives the achievable HBM read bandwidth that the
+ * GEMV figures are compared with (the Conifer note likewise measures its own
+ * peak with a triad microbenchmark instead of trusting the nominal figure).
+ */
+int qbench_stream_read(const void *buf, size_t bytes, void *sink, int32_t blocks, void *stream);
+
+/* Zero-fill a workspace on `stream` (a kernel, not a memset node). */
+int qworkspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *qstatus_string(int status);
+
+/* hipError_t of the last QMM_ERR_HIP returned on this thread (0 if none). */
+int qlast_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

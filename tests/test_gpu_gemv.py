@@ -1,0 +1,244 @@
+"""GPU parity of qdequant and qgemv against the CPU oracle, through the C ABI.
+
+Bars: dequantized weights bit-exact; products |y - y_ref| <= 2e-3 * sum|w||x|
+per output; products of exact-arithmetic inputs bit-exact; repeated calls
+bitwise identical."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import formats as F
+from synth import quant, rng
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [F.AFFINE4_G64, F.MXFP4, F.NVFP4, F.Q6_K]
+TOL = 2e-3
+
+
+def _q():
+    import gemm_dequant_gemv_amd as q
+    return q
+
+
+def _bits_f32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def _randomize_planes(p, seed):
+    """Random bytes in every code and scale plane, so every code and scale
+    value (including -0, NaN scales, subnormal and huge scales) occurs."""
+    p.codes[:] = rng.randint_bytes(seed, "c", p.codes.size).reshape(p.codes.shape)
+    if p.fmt == F.AFFINE4_G64:
+        # random finite float16 scales and biases
+        b = rng.randint_bytes(seed, "s", p.scales.size * 2).view(np.uint16)
+        b = np.where((b & 0x7C00) == 0x7C00, b & 0xBFFF, b).astype(np.uint16)
+        p.scales[:] = b.view(np.float16).reshape(p.scales.shape)
+    elif p.fmt in (F.MXFP4, F.NVFP4):
+        p.scales[:] = rng.randint_bytes(seed, "s", p.scales.size).reshape(p.scales.shape)
+        if p.fmt == F.NVFP4:
+            p.tensor_scale[:] = np.float32(0.37)
+    else:
+        p.codes_hi[:] = rng.randint_bytes(seed, "h", p.codes_hi.size).reshape(p.codes_hi.shape)
+        p.scales[:] = rng.randint_bytes(seed, "s", p.scales.size).view(np.int8).reshape(p.scales.shape)
+        d = rng.randint_bytes(seed, "d", p.scales2.size * 2).view(np.uint16)
+        d = np.where((d & 0x7C00) == 0x7C00, d & 0xBFFF, d).astype(np.uint16)
+        p.scales2[:] = d.view(np.float16).reshape(p.scales2.shape)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dequant_bit_exact_random_planes(fmt):
+    q = _q()
+    k = 1024 if fmt == F.Q6_K else 512
+    p = F.empty(fmt, 96, k, batch=2)
+    _randomize_planes(p, 100 + fmt)
+    w = q.Weight.from_host(p)
+    out32 = q.dequant(w, torch.float32)
+    out16 = q.dequant(w, torch.bfloat16)
+    torch.cuda.synchronize()
+    for e in range(2):
+        with np.errstate(over="ignore", invalid="ignore"):
+            ref32 = oracle.dequant_f32(p, e)
+            ref16 = oracle.dequant_bf16(p, e)
+        got32 = out32[e].cpu().numpy()
+        nan = np.isnan(ref32)
+        assert np.array_equal(np.isnan(got32), nan)
+        assert np.array_equal(got32[~nan].view(np.uint32), ref32[~nan].view(np.uint32))
+        got16 = out16[e].view(torch.int16).cpu().numpy().view(np.uint16)
+        nan16 = (ref16 & 0x7FFF) > 0x7F80
+        assert np.array_equal((got16 & 0x7FFF) > 0x7F80, nan16)
+        assert np.array_equal(got16[~nan16], ref16[~nan16])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dequant_bit_exact_quantized_weights(fmt):
+    q = _q()
+    p = quant.synthetic_weight(fmt, 130, 2048, outlier_rate=0.01, name="dqw")
+    w = q.Weight.from_host(p)
+    got = q.dequant(w, torch.float32)[0].cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), oracle.dequant_f32(p).view(np.uint32))
+
+
+def _case(fmt, n, k, m, tag, outliers=0.0, residual=False):
+    p = quant.synthetic_weight(fmt, n, k, outlier_rate=outliers, name=f"{tag}/W")
+    x = quant.synthetic_bf16(m, k, name=f"{tag}/x")
+    r = quant.synthetic_bf16(m, n, name=f"{tag}/r") if residual else None
+    return p, x, r
+
+
+def _to_dev_bf16(bits):
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+
+def _check_tol(y, yref, mag):
+    ok = oracle.within_tolerance(y, yref, mag, TOL)
+    assert ok.all(), (f"{(~ok).sum()} outputs outside tolerance; worst "
+                      f"{np.max(np.abs(y - yref) / mag):.3e} of mag")
+
+
+# shapes that span several 128-row tiles with a ragged last tile, ragged last
+# K step, K split over several workgroups (k >= 1024) or not (k <= 768)
+SHAPES = [(300, 896), (257, 2304), (128, 256), (1, 512), (515, 4096), (64, 6144), (40, 17408)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_gemv_parity(fmt, m, shape):
+    n, k = shape
+    if fmt == F.Q6_K:
+        k = (k + 255) // 256 * 256
+    q = _q()
+    p, x, r = _case(fmt, n, k, m, f"gv{fmt}{n}{k}", outliers=0.01, residual=(n % 2 == 1))
+    w = q.Weight.from_host(p)
+    y = q.gemv(w, _to_dev_bf16(x), None if r is None else _to_dev_bf16(r))
+    yref, mag = oracle.gemv(p, x, r)
+    _check_tol(y.cpu().numpy().astype(np.float64), yref, mag)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_bf16_output(fmt):
+    q = _q()
+    k = 1024
+    p, x, r = _case(fmt, 200, k, 2, f"gvb{fmt}", residual=True)
+    w = q.Weight.from_host(p)
+    y = q.gemv(w, _to_dev_bf16(x), _to_dev_bf16(r), y_dtype=torch.bfloat16)
+    y32 = q.gemv(w, _to_dev_bf16(x), _to_dev_bf16(r), y_dtype=torch.float32)
+    # the bf16 output is the float32 result rounded to nearest even
+    got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, oracle.bf16_round(y32.cpu().numpy()))
+
+
+def _unit_scale_weight(fmt, n, k, seed):
+    p = F.empty(fmt, n, k)
+    p.codes[:] = rng.randint_bytes(seed, "ec", p.codes.size).reshape(p.codes.shape)
+    if fmt == F.AFFINE4_G64:
+        p.scales[..., 0] = 1.0
+        p.scales[..., 1] = -8.0
+    elif fmt == F.MXFP4:
+        p.scales[:] = 127
+    elif fmt == F.NVFP4:
+        p.scales[:] = 0x38
+        p.tensor_scale[:] = 1.0
+    else:
+        p.codes_hi[:] = rng.randint_bytes(seed, "eh", p.codes_hi.size).reshape(p.codes_hi.shape)
+        p.scales[:] = 1
+        p.scales2[:] = np.float16(2.0 ** -6)
+    return p
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("shape", [(300, 2048), (200, 17408), (129, 512)])
+def test_gemv_exact_arithmetic_bit_exact(fmt, m, shape):
+    """Unit scales and integer activations make every product and partial sum
+    an exact float32, so any summation order must give the oracle's value."""
+    n, k = shape
+    q = _q()
+    p = _unit_scale_weight(fmt, n, k, 40 + fmt)
+    xi = rng.randint_bytes(41, "ex", m * k, 0, 9).astype(np.float64).reshape(m, k) - 4
+    x = quant.bf16_bits(xi)
+    w = q.Weight.from_host(p)
+    y = q.gemv(w, _to_dev_bf16(x)).cpu().numpy()
+    yref, _ = oracle.gemv(p, x)
+    assert np.array_equal(y.astype(np.float64), yref)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_one_hot_blocks(fmt):
+    """Every code zero-valued except one block per row, at a different block
+    position in each row: catches any block/scale addressing slip."""
+    q = _q()
+    n, k = 64, 2048
+    blk = F.BLOCK[fmt]
+    p = F.empty(fmt, n, k)
+    if fmt == F.Q6_K:
+        p.codes_hi[:] = 0xAA            # q = 32 -> zero weight
+        p.scales2[:] = np.float16(1.0)
+    nb = k // blk
+    for row in range(n):
+        b = (row * 7) % nb
+        lo = b * blk
+        vals = (np.arange(blk) * 3 + row) % 8
+        bytes_ = p.codes[0, row]
+        for t in range(blk):
+            kk = lo + t
+            bytes_[kk // 2] |= np.uint8(vals[t] << (4 * (kk % 2)))
+        if fmt == F.AFFINE4_G64:
+            p.scales[0, row, b] = (0.5, 0.25)
+        elif fmt == F.MXFP4:
+            p.scales[0, row, b] = 126
+        elif fmt == F.NVFP4:
+            p.scales[0, row, b] = 0x30
+        else:
+            p.scales[0, row, b * 16:(b + 1) * 16] = 3
+    x = quant.synthetic_bf16(3, k, name="oh")
+    w = q.Weight.from_host(p)
+    y = q.gemv(w, _to_dev_bf16(x)).cpu().numpy().astype(np.float64)
+    yref, mag = oracle.gemv(p, x)
+    _check_tol(y, yref, mag)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_deterministic(fmt):
+    q = _q()
+    p, x, _ = _case(fmt, 1000, 5120, 4, f"det{fmt}")
+    w = q.Weight.from_host(p)
+    xd = _to_dev_bf16(x)
+    ws = q.new_workspace(q.gemv_workspace_size(w, 4))
+    ys = [q.gemv(w, xd, workspace=ws) for _ in range(3)]
+    for y in ys[1:]:
+        assert torch.equal(ys[0].view(torch.int32), y.view(torch.int32))
+
+
+def test_workspace_left_zero_and_reused():
+    q = _q()
+    p, x, _ = _case(F.AFFINE4_G64, 512, 8192, 2, "wsz")
+    w = q.Weight.from_host(p)
+    ws = q.new_workspace(q.gemv_workspace_size(w, 2))
+    assert ws is not None
+    y1 = q.gemv(w, _to_dev_bf16(x), workspace=ws)
+    torch.cuda.synchronize()
+    plan_counters = ws[:256].clone()
+    assert int(plan_counters.sum()) == 0
+    y2 = q.gemv(w, _to_dev_bf16(x), workspace=ws)
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+def test_error_codes_before_launch():
+    q = _q()
+    p, x, _ = _case(F.AFFINE4_G64, 256, 1024, 1, "err")
+    w = q.Weight.from_host(p)
+    xd = _to_dev_bf16(x)
+    with pytest.raises(q.QmmError) as e:
+        q.gemv(w, torch.cat([xd] * 5))           # m = 5
+    assert e.value.status == -5
+    y = torch.empty((1, 256), device="cuda")
+    ws_need = q.gemv_workspace_size(w, 1)
+    if ws_need:
+        small = torch.zeros(ws_need - 4, dtype=torch.uint8, device="cuda")
+        with pytest.raises(q.QmmError) as e:
+            q.gemv(w, xd, out=y, workspace=small)
+        assert e.value.status == -6
