@@ -165,4 +165,32 @@ int qgemv(const qmm_weight *w, const void *x, int32_t m, const void *residual, v
                                      (hipStream_t)stream));
 }
 
+size_t qgemm_workspace_size(const qmm_weight *w, int32_t m) {
+  (void)w;
+  (void)m;
+  return 0;
+}
+
+int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, void *y,
+          void *workspace, size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int st = check_weight(w);
+  if (st) return st;
+  if (w->batch != 1) return QMM_ERR_SHAPE;
+  if (w->k % 64 != 0) return QMM_ERR_SHAPE;
+  if (m < 1) return QMM_ERR_M_RANGE;
+  if (!x || !y) return QMM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16) || (residual && !aligned(residual, 16)))
+    return QMM_ERR_ALIGN;
+  const Range ry = range(y, (size_t)m * w->n * 2);
+  Range ins[8];
+  int ni = weight_ranges(*w, ins);
+  ins[ni++] = range(x, (size_t)m * w->k * 2);
+  if (residual) ins[ni++] = range(residual, (size_t)m * w->n * 2);
+  for (int i = 0; i < ni; ++i)
+    if (overlap(ry, ins[i])) return QMM_ERR_ALIAS;
+  return hip_status(qmm::launch_gemm(*w, x, m, residual, y, (hipStream_t)stream));
+}
+
 }  // extern "C"

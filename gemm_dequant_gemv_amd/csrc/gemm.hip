@@ -1,0 +1,307 @@
+// qgemm: prefill matrix multiply Y[m][n] = g * sum_k x[m][k] w[n][k] (+ r[m][n]),
+// bf16 out, for many activation rows.  "Decode once, multiply many times"
+// ("TurboEXL3" section 4.1): per K-slice of 64, a workgroup decodes its BN x 64
+// tile of weights once into LDS as bfloat16 -- the decoded weights never reach
+// device memory -- and multiplies it against its BM x 64 tile of activations on
+// the matrix cores (v_mfma_f32_16x16x32_bf16, float32 accumulation).
+//
+// Tiles: a workgroup of 4 waves (2 along n x 2 along m) owns BN rows of W and
+// BM rows of X; each wave computes (BN/2) x (BM/2) outputs as 16 x 16 MFMA
+// tiles.  The MFMA's A operand is the weight tile (rows n) and its B operand the
+// activation tile (columns m), so each lane's four accumulators are four
+// consecutive n of one m: one 8-byte store per tile in the epilogue.
+//
+// Pipeline: two LDS stages.  While the MFMAs of slice s run, the global loads of
+// slice s+1 (activations as 16-byte pieces, codes and block scales) are in
+// flight in registers; afterwards the weights are decoded and both tiles are
+// written to the other stage.  One barrier per slice.
+//
+// Decode to bfloat16 per format (the weight is rounded once more, to bf16, as
+// any 16-bit-operand multiply must; E2M1 x E8M0 and E2M1 x E4M3 are exact in
+// bf16, affine and Q6_K values are rounded to nearest even):
+//   affine: fma(s, q, b) in float32 -> bf16
+//   MXFP4:  v_cvt_scalef32_pk_bf16_fp4 with the power-of-two scale (exact)
+//   NVFP4:  E2M1 -> float32, times the E4M3 block scale (exact), -> bf16; the
+//           tensor multiplier g is applied to the float32 sums in the epilogue
+//   Q6_K:   (d * sc) * (q - 32) in float32 (exact) -> bf16
+#include <algorithm>
+#include <atomic>
+
+#include "qmm_device.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+namespace {
+
+constexpr int kBK = 64;          // K values per slice
+constexpr int kLdsPad = 8;       // bf16 of padding per LDS row (keeps MFMA operand reads conflict-free)
+constexpr int kRowH = kBK + kLdsPad;  // bf16 per LDS row
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+struct GemmArgs {
+  const uint8_t *codes;
+  const uint8_t *codes_hi;
+  const uint8_t *scales;
+  const uint8_t *scales2;
+  const float *tensor_scale;
+  const uint16_t *x;
+  const uint16_t *residual;
+  uint16_t *y;
+  int m, n, k;
+};
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
+// Raw bytes of one 32-weight piece of a row (codes and scales).
+struct Piece {
+  uint4 q;
+  uint2 h;
+  uint32_t s, d;
+};
+
+template <int FMT>
+__device__ __forceinline__ Piece load_piece(const GemmArgs &a, int row, int kc) {
+  const size_t k = (size_t)a.k, r = (size_t)row;
+  Piece p;
+  p.q = load_stream16(a.codes + r * (k / 2) + kc / 2);
+  if constexpr (FMT == QMM_AFFINE4_G64) {
+    p.s = *(const uint32_t *)(a.scales + (r * (k / 64) + kc / 64) * 4);
+  } else if constexpr (FMT == QMM_MXFP4) {
+    p.s = a.scales[r * (k / 32) + kc / 32];
+  } else if constexpr (FMT == QMM_NVFP4) {
+    p.s = *(const uint16_t *)(a.scales + r * (k / 16) + kc / 16);
+  } else {
+    p.h = *(const uint2 *)(a.codes_hi + r * (k / 4) + kc / 4);
+    p.s = *(const uint16_t *)(a.scales + r * (k / 16) + kc / 16);
+    p.d = *(const uint16_t *)(a.scales2 + (r * (k / 256) + kc / 256) * 2);
+  }
+  return p;
+}
+
+// The piece's 32 weights as 16 bf16 pairs in natural order.
+template <int FMT>
+__device__ __forceinline__ void decode_piece(const Piece &p, uint32_t (&o)[16]) {
+  const uint32_t w[4] = {p.q.x, p.q.y, p.q.z, p.q.w};
+  if constexpr (FMT == QMM_AFFINE4_G64) {
+    const float s = half_to_float(p.s & 0xFFFFu), b = half_to_float(p.s >> 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = __builtin_fmaf(s, (float)((w[j] >> (8 * i)) & 15u), b);
+        const float hi = __builtin_fmaf(s, (float)((w[j] >> (8 * i + 4)) & 15u), b);
+        o[4 * j + i] = pack_bf16(lo, hi);
+      }
+  } else if constexpr (FMT == QMM_MXFP4) {
+    const float sc = e8m0_to_float(p.s);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[4 * j + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 0));
+      o[4 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 1));
+      o[4 * j + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 2));
+      o[4 * j + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 3));
+    }
+  } else if constexpr (FMT == QMM_NVFP4) {
+    const float s0 = e4m3_to_float(p.s & 0xFFu), s1 = e4m3_to_float(p.s >> 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float sc = j < 2 ? s0 : s1;
+      const uint32_t e[4] = {e2m1x2_to_bf16x2<0>(w[j]), e2m1x2_to_bf16x2<1>(w[j]),
+                             e2m1x2_to_bf16x2<2>(w[j]), e2m1x2_to_bf16x2<3>(w[j])};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[4 * j + i] = pack_bf16(bf_lo(e[i]) * sc, bf_hi(e[i]) * sc);
+    }
+  } else {  // Q6_K
+    const float dd = half_to_float(p.d);
+    const uint32_t hw[2] = {p.h.x, p.h.y};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float dsc = dd * (float)(int8_t)(p.s >> (8 * (j / 2)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v0 = 8 * j + 2 * i;  // value index within the piece (even)
+        const uint32_t q0 = ((w[j] >> (8 * i)) & 15u) | (((hw[v0 / 16] >> (2 * (v0 % 16))) & 3u) << 4);
+        const uint32_t q1 = ((w[j] >> (8 * i + 4)) & 15u) |
+                            (((hw[(v0 + 1) / 16] >> (2 * ((v0 + 1) % 16))) & 3u) << 4);
+        o[4 * j + i] = pack_bf16(dsc * (float)((int)q0 - 32), dsc * (float)((int)q1 - 32));
+      }
+    }
+  }
+}
+
+template <int FMT, int BM, int BN>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+  constexpr int TN = BN / 32, TM = BM / 32;      // 16x16 tiles per wave along n and m
+  constexpr int XP = BM * (kBK / 8) / 256;       // 16-byte activation pieces per thread
+  constexpr int WP = BN * (kBK / 32) / 256;      // 32-weight pieces per thread
+  static_assert(XP >= 1 && WP >= 1, "tile too small for 256 threads");
+  constexpr int STAGE = (BM + BN) * kRowH;       // bf16 per LDS stage
+  extern __shared__ __align__(16) uint16_t lds[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int tiles_m = (a.m + BM - 1) / BM;
+  const int tm_idx = blockIdx.x % tiles_m, tn_idx = blockIdx.x / tiles_m;
+  const int m0 = tm_idx * BM, n0 = tn_idx * BN;
+  const int slices = a.k / kBK;
+
+  // global -> register loads of one slice
+  uint4 xr[XP];
+  Piece wr[WP];
+  auto load_slice = [&](int s) {
+    const int k0 = s * kBK;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int p = tid + 256 * i, row = p / (kBK / 8), col = p % (kBK / 8);
+      const int m = min(m0 + row, a.m - 1);
+      xr[i] = *(const uint4 *)(a.x + (size_t)m * a.k + k0 + col * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < WP; ++i) {
+      const int p = tid + 256 * i, row = p / 2, half = p % 2;
+      const int n = min(n0 + row, a.n - 1);
+      wr[i] = load_piece<FMT>(a, n, k0 + half * 32);
+    }
+  };
+  // decode and write one slice into LDS stage `st`
+  auto store_slice = [&](int st) {
+    uint16_t *xs = lds + st * STAGE;
+    uint16_t *ws = xs + BM * kRowH;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int p = tid + 256 * i, row = p / (kBK / 8), col = p % (kBK / 8);
+      *(uint4 *)(xs + row * kRowH + col * 8) = xr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < WP; ++i) {
+      const int p = tid + 256 * i, row = p / 2, half = p % 2;
+      uint32_t o[16];
+      decode_piece<FMT>(wr[i], o);
+      uint4 *dst = (uint4 *)(ws + row * kRowH + half * 32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    }
+  };
+
+  f32x4_t acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  load_slice(0);
+  store_slice(0);
+  __syncthreads();
+
+  const int lr = lane & 15, lk = (lane >> 4) * 8;  // operand row within a 16-tile, k offset
+  for (int s = 0; s < slices; ++s) {
+    const int st = s & 1;
+    if (s + 1 < slices) load_slice(s + 1);
+    const uint16_t *xs = lds + st * STAGE;
+    const uint16_t *ws = xs + BM * kRowH;
+#pragma unroll
+    for (int kk = 0; kk < kBK; kk += 32) {
+      bf16x8_t af[TN], bfr[TM];
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+        af[i] = *(const bf16x8_t *)(ws + (wn * (BN / 2) + i * 16 + lr) * kRowH + kk + lk);
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        bfr[j] = *(const bf16x8_t *)(xs + (wm * (BM / 2) + j * 16 + lr) * kRowH + kk + lk);
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (s + 1 < slices) store_slice(st ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds D[n = 4*(lane/16) + r][m = lane % 16] of each tile
+  const float g = (FMT == QMM_NVFP4 && a.tensor_scale) ? a.tensor_scale[0] : 1.0f;
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int m = m0 + wm * (BM / 2) + j * 16 + lr;
+      const int nb = n0 + wn * (BN / 2) + i * 16 + (lane >> 4) * 4;
+      if (m >= a.m) continue;
+      float v[4] = {acc[i][j][0] * g, acc[i][j][1] * g, acc[i][j][2] * g, acc[i][j][3] * g};
+      const size_t base = (size_t)m * a.n + nb;
+      if (nb + 3 < a.n && (a.n & 3) == 0) {
+        if (a.residual) {
+          const uint2 r = *(const uint2 *)(a.residual + base);
+          v[0] += bf_lo(r.x);
+          v[1] += bf_hi(r.x);
+          v[2] += bf_lo(r.y);
+          v[3] += bf_hi(r.y);
+        }
+        *(uint2 *)(a.y + base) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (nb + r >= a.n) break;
+          float t = v[r];
+          if (a.residual) t += bf_lo(a.residual[base + r]);
+          a.y[base + r] = __builtin_bit_cast(uint16_t, (__bf16)t);
+        }
+      }
+    }
+}
+
+template <int FMT, int BM, int BN>
+hipError_t launch_tile(const GemmArgs &a, hipStream_t s) {
+  constexpr size_t lds = 2 * (size_t)(BM + BN) * kRowH * 2;
+  // more than 64 KiB of dynamic LDS must be allowed once per device
+  static std::atomic<uint64_t> configured{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(configured.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void *)gemm_kernel<FMT, BM, BN>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    configured.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  const unsigned blocks = (unsigned)(((a.m + BM - 1) / BM) * ((a.n + BN - 1) / BN));
+  hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN>), dim3(blocks), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_f(const GemmArgs &a, hipStream_t s) {
+  return launch_tile<FMT, 128, 128>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
+                       hipStream_t s) {
+  GemmArgs a;
+  a.codes = (const uint8_t *)w.codes;
+  a.codes_hi = (const uint8_t *)w.codes_hi;
+  a.scales = (const uint8_t *)w.scales;
+  a.scales2 = (const uint8_t *)w.scales2;
+  a.tensor_scale = w.tensor_scale;
+  a.x = (const uint16_t *)x;
+  a.residual = (const uint16_t *)residual;
+  a.y = (uint16_t *)y;
+  a.m = m;
+  a.n = w.n;
+  a.k = w.k;
+  switch (w.format) {
+    case QMM_AFFINE4_G64: return launch_f<QMM_AFFINE4_G64>(a, s);
+    case QMM_MXFP4: return launch_f<QMM_MXFP4>(a, s);
+    case QMM_NVFP4: return launch_f<QMM_NVFP4>(a, s);
+    default: return launch_f<QMM_Q6_K>(a, s);
+  }
+}
+
+}  // namespace qmm

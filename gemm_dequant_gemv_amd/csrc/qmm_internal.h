@@ -38,6 +38,8 @@ hipError_t launch_dequant(const qmm_weight &w, int out_dtype, void *out, hipStre
 hipError_t launch_gemv(const qmm_weight &w, const void *x, int m, const void *residual,
                        void *y, int y_dtype, void *workspace, const GemvPlan &p,
                        hipStream_t s);
+hipError_t launch_gemm(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
+                       hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_stream_read(const void *p, size_t bytes, uint32_t *sink, int blocks,
                               hipStream_t s);

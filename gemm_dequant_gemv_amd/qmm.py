@@ -20,8 +20,8 @@ AFFINE4_G64, MXFP4, NVFP4, Q6_K = 1, 2, 3, 4
 F32, BF16 = 0, 1
 FORMATS = {"affine4_g64": AFFINE4_G64, "mxfp4": MXFP4, "nvfp4": NVFP4, "q6_k": Q6_K}
 
-ENTRY_POINTS = ("qdequant", "qgemv", "qgemv_workspace_size", "qworkspace_init",
-                "qbench_stream_read", "qstatus_string", "qlast_hip_error")
+ENTRY_POINTS = ("qdequant", "qgemv", "qgemv_workspace_size", "qgemm", "qgemm_workspace_size",
+                "qworkspace_init", "qbench_stream_read", "qstatus_string", "qlast_hip_error")
 
 
 class QmmError(RuntimeError):
@@ -55,6 +55,9 @@ def _lib():
         lib.qgemv_workspace_size.argtypes = [P, I32]
         lib.qgemv_workspace_size.restype = SZ
         lib.qgemv.argtypes = [P, VP, I32, VP, VP, I32, VP, SZ, VP]
+        lib.qgemm_workspace_size.argtypes = [P, I32]
+        lib.qgemm_workspace_size.restype = SZ
+        lib.qgemm.argtypes = [P, VP, I32, VP, VP, VP, SZ, VP]
         lib.qworkspace_init.argtypes = [VP, SZ, VP]
         lib.qbench_stream_read.argtypes = [VP, SZ, VP, I32, VP]
         lib.qstatus_string.restype = ctypes.c_char_p
@@ -152,6 +155,20 @@ def gemv(w: Weight, x, residual=None, y_dtype=torch.float32, out=None, workspace
     dt = F32 if out.dtype == torch.float32 else BF16
     _check(_lib().qgemv(w.c, _ptr(x), m, _ptr(residual), _ptr(out), dt, _ptr(workspace),
                         ws_bytes, _stream(stream)), "qgemv")
+    return out
+
+
+def gemm(w: Weight, x, residual=None, out=None, workspace=None, stream=None):
+    """y[m][n] = bf16(sum_k w16[n][k] x[m][k] (+ residual)), x bf16 [m][k]."""
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, w.n), dtype=torch.bfloat16, device=x.device)
+    need = int(_lib().qgemm_workspace_size(w.c, m))
+    if workspace is None and need:
+        workspace = new_workspace(need, x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib().qgemm(w.c, _ptr(x), m, _ptr(residual), _ptr(out), _ptr(workspace), ws_bytes,
+                        _stream(stream)), "qgemm")
     return out
 
 

@@ -160,6 +160,30 @@ int qgemv(const qmm_weight *w, const void *x, int32_t m, const void *residual,
  */
 int qbench_stream_read(const void *buf, size_t bytes, void *sink, int32_t blocks, void *stream);
 
+/*
+ * qgemm -- prefill matrix multiply for many activation rows ("TurboEXL3",
+ * section 4.1, decode once, multiply many times: each K-slice of the weights is
+ * decoded once per workgroup into on-chip memory as 16-bit values and multiplied
+ * against a tile of activations with 32-bit accumulation; the decoded weights
+ * never reach device memory).
+ *
+ *   y[m][n] = bf16( g * sum_k w16[n][k] * x[m][k]  (+ residual[m][n]) )
+ *
+ * where w16 is the weight rounded to bfloat16 (exact for MXFP4 and NVFP4;
+ * affine and Q6_K values are rounded to nearest even, a relative error of at
+ * most 2^-9 per weight), summed in float32 on the matrix cores.
+ *
+ * w         one matrix (batch must be 1); k must be a multiple of 64
+ * x         bf16 [m][k], m >= 1 (tuned for m >= 128)
+ * residual  bf16 [m][n] or NULL
+ * y         bf16 [m][n], rounded to nearest even
+ * x, y and residual must be 16-byte aligned.  No workspace is needed today
+ * (qgemm_workspace_size returns 0); the arguments are kept for split variants.
+ */
+size_t qgemm_workspace_size(const qmm_weight *w, int32_t m);
+int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, void *y,
+          void *workspace, size_t workspace_bytes, void *stream);
+
 /* Zero-fill a workspace on `stream` (a kernel, not a memset node). */
 int qworkspace_init(void *workspace, size_t workspace_bytes, void *stream);
 

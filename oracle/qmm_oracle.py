@@ -249,3 +249,16 @@ def moe_gate_up(gate_up, x_bits, e: int, rows_tokens):
 def within_tolerance(y, y_ref, mag, rel: float = 2e-3):
     """Elementwise |y - y_ref| <= rel * mag (the parity rule for products)."""
     return np.abs(np.asarray(y, np.float64) - y_ref) <= rel * mag
+
+
+def bf16_half_ulp(v) -> np.ndarray:
+    """Half a unit in the last place of bfloat16 (8 significant bits) at |v|."""
+    _, e = np.frexp(np.abs(np.asarray(v, np.float64)))
+    return np.ldexp(1.0, e - 9)
+
+
+def within_tolerance_bf16(y, y_ref, mag, rel: float = 2e-3):
+    """The product rule for results stored as bfloat16: the accumulation bound
+    plus the output's own rounding, which the reference applies too ("round
+    where the reference rounds", TurboEXL3 section 4.4)."""
+    return np.abs(np.asarray(y, np.float64) - y_ref) <= rel * mag + bf16_half_ulp(y_ref)

@@ -1,0 +1,114 @@
+"""GPU parity of qgemm (prefill, LDS-staged dequantization + bf16 MFMA) against
+the CPU oracle, through the C ABI.
+
+Bars: |y - y_ref| <= 2e-3 * sum|w||x| + half a bf16 ulp of y_ref per output
+(y is stored as bf16, which the reference rounds too); exact-arithmetic
+inputs give exactly the bf16 rounding of the exact sum; repeated calls are
+bitwise identical."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import formats as F
+from synth import quant, rng
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [F.AFFINE4_G64, F.MXFP4, F.NVFP4, F.Q6_K]
+TOL = 2e-3
+
+
+def _q():
+    import gemm_dequant_gemv_amd as q
+    return q
+
+
+def _dev_bf16(bits):
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+
+def _host_f64(t):
+    return oracle.bf16(t.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def _check(y, yref, mag):
+    ok = oracle.within_tolerance_bf16(y, yref, mag, TOL)
+    assert ok.all(), (f"{(~ok).sum()} of {ok.size} outside tolerance; worst "
+                      f"{np.max(np.abs(y - yref) / mag):.3e} of mag")
+
+
+# several 128 x 128 tiles with ragged m and n, K granules of each format
+SHAPES = [(130, 300, 768), (257, 129, 1024), (1, 64, 512), (128, 256, 256), (200, 1000, 2304)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_gemm_parity(fmt, shape):
+    m, n, k = shape
+    if fmt == F.Q6_K:
+        k = (k + 255) // 256 * 256
+    q = _q()
+    p = quant.synthetic_weight(fmt, n, k, outlier_rate=0.01, name=f"gm{fmt}{n}{k}")
+    x = quant.synthetic_bf16(m, k, name=f"gmx{m}{k}")
+    r = quant.synthetic_bf16(m, n, name=f"gmr{m}{n}") if m % 2 == 0 else None
+    w = q.Weight.from_host(p)
+    y = q.gemm(w, _dev_bf16(x), None if r is None else _dev_bf16(r))
+    yref, mag = oracle.gemm(p, x, r)
+    _check(_host_f64(y), yref, mag)
+
+
+def _unit_scale_weight(fmt, n, k, seed):
+    p = F.empty(fmt, n, k)
+    p.codes[:] = rng.randint_bytes(seed, "gec", p.codes.size).reshape(p.codes.shape)
+    if fmt == F.AFFINE4_G64:
+        p.scales[..., 0] = 1.0
+        p.scales[..., 1] = -8.0
+    elif fmt == F.MXFP4:
+        p.scales[:] = 127
+    elif fmt == F.NVFP4:
+        p.scales[:] = 0x38
+        p.tensor_scale[:] = 1.0
+    else:
+        p.codes_hi[:] = rng.randint_bytes(seed, "geh", p.codes_hi.size).reshape(p.codes_hi.shape)
+        p.scales[:] = 1
+        p.scales2[:] = np.float16(2.0 ** -6)
+    return p
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_exact_arithmetic(fmt):
+    """Unit scales and integer activations: every product and partial sum is an
+    exact float32, so the bf16 output must be the bf16 rounding of the exact
+    sum, whatever the summation order."""
+    q = _q()
+    m, n, k = 150, 260, 5120
+    p = _unit_scale_weight(fmt, n, k, 60 + fmt)
+    xi = rng.randint_bytes(61, "gex", m * k, 0, 9).astype(np.float64).reshape(m, k) - 4
+    x = quant.bf16_bits(xi)
+    w = q.Weight.from_host(p)
+    y = q.gemm(w, _dev_bf16(x)).view(torch.int16).cpu().numpy().view(np.uint16)
+    yref, _ = oracle.gemm(p, x)
+    assert np.array_equal(y, oracle.bf16_round(yref.astype(np.float32)))
+
+
+@pytest.mark.parametrize("fmt", [F.AFFINE4_G64, F.NVFP4])
+def test_gemm_deterministic(fmt):
+    q = _q()
+    p = quant.synthetic_weight(fmt, 1024, 2048, name="gdet")
+    x = _dev_bf16(quant.synthetic_bf16(384, 2048, name="gdetx"))
+    w = q.Weight.from_host(p)
+    ys = [q.gemm(w, x) for _ in range(3)]
+    for y in ys[1:]:
+        assert torch.equal(ys[0].view(torch.int16), y.view(torch.int16))
+
+
+def test_gemm_rejects():
+    q = _q()
+    p = quant.synthetic_weight(F.AFFINE4_G64, 64, 512, name="grej")
+    w = q.Weight.from_host(p)
+    x = _dev_bf16(quant.synthetic_bf16(4, 512, name="grejx"))
+    with pytest.raises(q.QmmError) as e:
+        q.gemm(w, x[:0])                             # m = 0
+    assert e.value.status == -5

@@ -417,3 +417,11 @@ def test_encoder_round_trip_error(fmt):
         amax_blk = np.repeat(np.abs(w.reshape(n, -1, F.BLOCK[fmt])).max(-1), F.BLOCK[fmt], -1)
         assert np.all(err <= amax_blk * (0.25 if fmt == F.NVFP4 else 0.35))
         assert np.median(rel) < 0.2
+
+
+def test_bf16_half_ulp_closed_form():
+    v = np.array([1.0, 1.5, 2.0, 3.99, 0.75, -6.0, 2.0 ** -20])
+    ulp = np.array([2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -6, 2.0 ** -8, 2.0 ** -5, 2.0 ** -27])
+    assert np.array_equal(oracle.bf16_half_ulp(v), ulp / 2)
+    # one ulp step of bf16 around 1.0 is 2^-7
+    assert oracle.bf16(np.uint16(0x3F81)) - 1.0 == 2.0 ** -7
