@@ -193,4 +193,71 @@ int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, v
   return hip_status(qmm::launch_gemm(*w, x, m, residual, y, (hipStream_t)stream));
 }
 
+size_t qmoe_workspace_size(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
+                           int32_t num_shared, int32_t t, int32_t topk) {
+  if (check_weight(gate_up) || check_weight(down) || num_routed < 1 || num_shared < 0 ||
+      t < 1 || topk < 1)
+    return 0;
+  return qmm::moe_layout(num_routed + num_shared, t, topk, num_shared, gate_up->n / 2, down->n)
+      .bytes;
+}
+
+int qmoe_workspace_layout(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
+                          int32_t num_shared, int32_t t, int32_t topk, qmoe_layout *out) {
+  if (!out) return QMM_ERR_NULL;
+  if (check_weight(gate_up) || check_weight(down) || num_routed < 1 || num_shared < 0 ||
+      t < 1 || topk < 1)
+    return QMM_ERR_ARG;
+  const qmm::MoeLayout L = qmm::moe_layout(num_routed + num_shared, t, topk, num_shared,
+                                           gate_up->n / 2, down->n);
+  *out = qmoe_layout{L.counts, L.offsets, L.row_of_slot, L.row_of_shared, L.token_of_row,
+                     L.active, L.scalars, L.tiles, L.h, L.d, L.bytes, L.max_rows, L.max_tiles};
+  return QMM_OK;
+}
+
+int qmoe_grouped(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
+                 int32_t num_shared, const void *x, int32_t t, const int32_t *topk_ids,
+                 const float *topk_w, int32_t topk, const float *shared_w, void *y,
+                 int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_weight(gate_up);
+  if (st) return st;
+  st = check_weight(down);
+  if (st) return st;
+  if (num_routed < 1 || num_shared < 0 || num_routed + num_shared > qmm::kMoeMaxExperts)
+    return QMM_ERR_ARG;
+  if (topk < 1 || topk > 64) return QMM_ERR_ARG;
+  if (t < 1 || (int64_t)t * (topk + num_shared) >= (1ll << 31)) return QMM_ERR_M_RANGE;
+  const int experts = num_routed + num_shared;
+  if (gate_up->batch != experts || down->batch != experts) return QMM_ERR_SHAPE;
+  const int inter = gate_up->n / 2;
+  if (gate_up->n % 128 != 0 || down->k != inter || down->n != gate_up->k) return QMM_ERR_SHAPE;
+  if (gate_up->k % 64 != 0 || down->k % 64 != 0) return QMM_ERR_SHAPE;
+  if (y_dtype != QMM_F32 && y_dtype != QMM_BF16) return QMM_ERR_DTYPE;
+  if (!x || !topk_ids || !topk_w || !y) return QMM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
+      (shared_w && !aligned(shared_w, 4)))
+    return QMM_ERR_ALIGN;
+  const qmm::MoeLayout L = qmm::moe_layout(experts, t, topk, num_shared, inter, down->n);
+  if (!workspace || workspace_bytes < L.bytes) return QMM_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return QMM_ERR_ALIGN;
+  const int hidden = down->n;
+  const Range ry = range(y, (size_t)t * hidden * (y_dtype == QMM_F32 ? 4 : 2));
+  Range ins[16];
+  int ni = weight_ranges(*gate_up, ins);
+  ni += weight_ranges(*down, ins + ni);
+  ins[ni++] = range(x, (size_t)t * gate_up->k * 2);
+  ins[ni++] = range(topk_ids, (size_t)t * topk * 4);
+  ins[ni++] = range(topk_w, (size_t)t * topk * 4);
+  if (shared_w) ins[ni++] = range(shared_w, (size_t)t * 4);
+  ins[ni++] = range(workspace, L.bytes);
+  for (int i = 0; i < ni; ++i)
+    if (overlap(ry, ins[i])) return QMM_ERR_ALIAS;
+  const Range rw = range(workspace, L.bytes);
+  for (int i = 0; i < ni - 1; ++i)
+    if (overlap(rw, ins[i])) return QMM_ERR_ALIAS;
+  return hip_status(qmm::launch_moe(*gate_up, *down, num_routed, num_shared, x, t, topk_ids,
+                                    topk_w, topk, shared_w, y, y_dtype, workspace,
+                                    (hipStream_t)stream));
+}
+
 }  // extern "C"

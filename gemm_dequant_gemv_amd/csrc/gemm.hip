@@ -40,6 +40,14 @@ constexpr int kRowH = kBK + kLdsPad;  // bf16 per LDS row
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
+// What a workgroup's rows are, and where its results go.
+enum GemmMode {
+  kDense = 0,   // y[m][n] = x[m] . w[n]; rows of x are rows of y
+  kMoeGateUp = 1,  // grouped: x rows gathered by token, weight rows interleaved
+                   // (gate i, up i); the epilogue applies SwiGLU and writes bf16 h
+  kMoeDown = 2,    // grouped: rows of h, one expert per tile; writes float32 d
+};
+
 struct GemmArgs {
   const uint8_t *codes;
   const uint8_t *codes_hi;
@@ -50,6 +58,13 @@ struct GemmArgs {
   const uint16_t *residual;
   uint16_t *y;
   int m, n, k;
+  // grouped (MoE) modes
+  const uint32_t *tiles;         // [max_tiles][3] = (expert, first grouped row, rows)
+  const uint32_t *n_tiles;       // device count of valid tiles
+  const uint32_t *token_of_row;  // grouped row -> token (gate/up gather)
+  uint16_t *h;                   // bf16 [rows][inter]   (gate/up output, down input)
+  float *d;                      // float32 [rows][n]    (down output)
+  int inter;                     // I: gate/up rows are 2I
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -134,7 +149,7 @@ __device__ __forceinline__ void decode_piece(const Piece &p, uint32_t (&o)[16]) 
   }
 }
 
-template <int FMT, int BM, int BN>
+template <int FMT, int BM, int BN, int MODE>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   constexpr int TN = BN / 32, TM = BM / 32;      // 16x16 tiles per wave along n and m
   constexpr int XP = BM * (kBK / 8) / 256;       // 16-byte activation pieces per thread
@@ -145,10 +160,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
-  const int tiles_m = (a.m + BM - 1) / BM;
-  const int tm_idx = blockIdx.x % tiles_m, tn_idx = blockIdx.x / tiles_m;
-  const int m0 = tm_idx * BM, n0 = tn_idx * BN;
+  int m0, n0, mrows, wrow0 = 0, expert = 0;
+  if constexpr (MODE == kDense) {
+    const int tiles_m = (a.m + BM - 1) / BM;
+    m0 = (blockIdx.x % tiles_m) * BM;
+    n0 = (blockIdx.x / tiles_m) * BN;
+    mrows = a.m - m0;
+  } else {
+    if (blockIdx.x >= *a.n_tiles) return;            // beyond this call's tiles
+    const uint32_t *t = a.tiles + 3 * blockIdx.x;
+    expert = (int)t[0];
+    m0 = (int)t[1];
+    mrows = (int)t[2];
+    n0 = blockIdx.y * BN;
+    wrow0 = expert * a.n;                              // first row of the expert's matrix
+  }
   const int slices = a.k / kBK;
+  // weight row of tile row j (gate/up interleaved in the gate/up mode)
+  auto wrow = [&](int j) {
+    if constexpr (MODE == kMoeGateUp) {
+      const int i = n0 / 2 + j / 2;
+      return wrow0 + ((j & 1) ? a.inter + i : i);
+    } else {
+      return wrow0 + min(n0 + j, a.n - 1);
+    }
+  };
 
   // global -> register loads of one slice
   uint4 xr[XP];
@@ -158,14 +194,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const int p = tid + 256 * i, row = p / (kBK / 8), col = p % (kBK / 8);
-      const int m = min(m0 + row, a.m - 1);
-      xr[i] = *(const uint4 *)(a.x + (size_t)m * a.k + k0 + col * 8);
+      const int r = m0 + min(row, mrows - 1);
+      const uint16_t *src;
+      if constexpr (MODE == kDense) src = a.x + (size_t)r * a.k;
+      else if constexpr (MODE == kMoeGateUp) src = a.x + (size_t)a.token_of_row[r] * a.k;
+      else src = a.h + (size_t)r * a.k;
+      xr[i] = *(const uint4 *)(src + k0 + col * 8);
     }
 #pragma unroll
     for (int i = 0; i < WP; ++i) {
       const int p = tid + 256 * i, row = p / 2, half = p % 2;
-      const int n = min(n0 + row, a.n - 1);
-      wr[i] = load_piece<FMT>(a, n, k0 + half * 32);
+      wr[i] = load_piece<FMT>(a, wrow(row), k0 + half * 32);
     }
   };
   // decode and write one slice into LDS stage `st`
@@ -224,15 +263,34 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   }
 
   // epilogue: lane holds D[n = 4*(lane/16) + r][m = lane % 16] of each tile
-  const float g = (FMT == QMM_NVFP4 && a.tensor_scale) ? a.tensor_scale[0] : 1.0f;
+  const float g = (FMT == QMM_NVFP4 && a.tensor_scale) ? a.tensor_scale[expert] : 1.0f;
 #pragma unroll
   for (int i = 0; i < TN; ++i)
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-      const int m = m0 + wm * (BM / 2) + j * 16 + lr;
-      const int nb = n0 + wn * (BN / 2) + i * 16 + (lane >> 4) * 4;
-      if (m >= a.m) continue;
+      const int ml = wm * (BM / 2) + j * 16 + lr;
+      const int nl = wn * (BN / 2) + i * 16 + (lane >> 4) * 4;
+      if (ml >= mrows) continue;
+      const int m = m0 + ml;
       float v[4] = {acc[i][j][0] * g, acc[i][j][1] * g, acc[i][j][2] * g, acc[i][j][3] * g};
+      if constexpr (MODE == kMoeGateUp) {
+        // (gate, up, gate, up) of two consecutive intermediate columns; SwiGLU
+        // in float32: h = silu(g) * u, silu(g) = g / (1 + e^-g)
+        const int col = n0 / 2 + nl / 2;
+        const float h0 = v[0] / (1.0f + expf(-v[0])) * v[1];
+        const float h1 = v[2] / (1.0f + expf(-v[2])) * v[3];
+        *(uint32_t *)(a.h + (size_t)m * a.inter + col) = pack_bf16(h0, h1);
+        continue;
+      } else if constexpr (MODE == kMoeDown) {
+        const int nb = n0 + nl;
+        if (nb + 3 < a.n) {
+          *(float4 *)(a.d + (size_t)m * a.n + nb) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          for (int r = 0; r < 4 && nb + r < a.n; ++r) a.d[(size_t)m * a.n + nb + r] = v[r];
+        }
+        continue;
+      }
+      const int nb = n0 + nl;
       const size_t base = (size_t)m * a.n + nb;
       if (nb + 3 < a.n && (a.n & 3) == 0) {
         if (a.residual) {
@@ -255,8 +313,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     }
 }
 
-template <int FMT, int BM, int BN>
-hipError_t launch_tile(const GemmArgs &a, hipStream_t s) {
+template <int FMT, int BM, int BN, int MODE>
+hipError_t launch_tile(const GemmArgs &a, dim3 grid, hipStream_t s) {
   constexpr size_t lds = 2 * (size_t)(BM + BN) * kRowH * 2;
   // more than 64 KiB of dynamic LDS must be allowed once per device
   static std::atomic<uint64_t> configured{0};
@@ -265,43 +323,72 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(configured.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute((const void *)gemm_kernel<FMT, BM, BN>,
+    e = hipFuncSetAttribute((const void *)gemm_kernel<FMT, BM, BN, MODE>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_acq_rel);
   }
-  const unsigned blocks = (unsigned)(((a.m + BM - 1) / BM) * ((a.n + BN - 1) / BN));
-  hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN>), dim3(blocks), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN, MODE>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
-template <int FMT>
-hipError_t launch_f(const GemmArgs &a, hipStream_t s) {
-  return launch_tile<FMT, 128, 128>(a, s);
+template <int MODE>
+hipError_t launch_mode(int format, const GemmArgs &a, dim3 grid, hipStream_t s) {
+  switch (format) {
+    case QMM_AFFINE4_G64: return launch_tile<QMM_AFFINE4_G64, kGemmBM, 128, MODE>(a, grid, s);
+    case QMM_MXFP4: return launch_tile<QMM_MXFP4, kGemmBM, 128, MODE>(a, grid, s);
+    case QMM_NVFP4: return launch_tile<QMM_NVFP4, kGemmBM, 128, MODE>(a, grid, s);
+    default: return launch_tile<QMM_Q6_K, kGemmBM, 128, MODE>(a, grid, s);
+  }
+}
+
+GemmArgs weight_args(const qmm_weight &w) {
+  GemmArgs a{};
+  a.codes = (const uint8_t *)w.codes;
+  a.codes_hi = (const uint8_t *)w.codes_hi;
+  a.scales = (const uint8_t *)w.scales;
+  a.scales2 = (const uint8_t *)w.scales2;
+  a.tensor_scale = w.tensor_scale;
+  a.n = w.n;
+  a.k = w.k;
+  return a;
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
                        hipStream_t s) {
-  GemmArgs a;
-  a.codes = (const uint8_t *)w.codes;
-  a.codes_hi = (const uint8_t *)w.codes_hi;
-  a.scales = (const uint8_t *)w.scales;
-  a.scales2 = (const uint8_t *)w.scales2;
-  a.tensor_scale = w.tensor_scale;
+  GemmArgs a = weight_args(w);
   a.x = (const uint16_t *)x;
   a.residual = (const uint16_t *)residual;
   a.y = (uint16_t *)y;
   a.m = m;
-  a.n = w.n;
-  a.k = w.k;
-  switch (w.format) {
-    case QMM_AFFINE4_G64: return launch_f<QMM_AFFINE4_G64>(a, s);
-    case QMM_MXFP4: return launch_f<QMM_MXFP4>(a, s);
-    case QMM_NVFP4: return launch_f<QMM_NVFP4>(a, s);
-    default: return launch_f<QMM_Q6_K>(a, s);
-  }
+  const unsigned blocks = (unsigned)(((m + kGemmBM - 1) / kGemmBM) * ((w.n + 127) / 128));
+  return launch_mode<kDense>(w.format, a, dim3(blocks), s);
+}
+
+hipError_t launch_moe_gemm_gate_up(const qmm_weight &gu, const void *x, const MoeTables &t,
+                                   int max_tiles, hipStream_t s) {
+  GemmArgs a = weight_args(gu);
+  a.x = (const uint16_t *)x;
+  a.tiles = t.tiles;
+  a.n_tiles = t.n_tiles;
+  a.token_of_row = t.token_of_row;
+  a.h = t.h;
+  a.inter = gu.n / 2;
+  // each workgroup covers 64 intermediate columns (128 interleaved rows)
+  return launch_mode<kMoeGateUp>(gu.format, a, dim3(max_tiles, (gu.n + 127) / 128), s);
+}
+
+hipError_t launch_moe_gemm_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
+                                hipStream_t s) {
+  GemmArgs a = weight_args(dn);
+  a.tiles = t.tiles;
+  a.n_tiles = t.n_tiles;
+  a.h = t.h;
+  a.d = t.d;
+  a.inter = dn.k;
+  return launch_mode<kMoeDown>(dn.format, a, dim3(max_tiles, (dn.n + 127) / 128), s);
 }
 
 }  // namespace qmm

@@ -1,0 +1,238 @@
+// qmoe_grouped: one mixture-of-experts layer (routed experts plus optional
+// shared experts) as grouped per-expert multiplies ("TurboEXL3" section 4.1):
+//   1. route:    one launch counts each expert's tokens, groups the token slots
+//                by expert and builds the table of row tiles (replacing a sort
+//                and a separate table pass);
+//   2. gate/up:  one grouped GEMM over the tile table, activations gathered by
+//                token, weights decoded once per K-slice per workgroup; SwiGLU
+//                in float32 in its epilogue -> bf16 h;
+//   3. down:     one grouped GEMM over the same tiles -> float32 d per slot;
+//   4. combine:  the score-weighted sum of each token's expert outputs, in a
+//                fixed order (routed slots in list order, then shared experts).
+// Grouped rows are the token slots sorted by expert; the order of slots inside
+// one expert's group comes from LDS atomics and is not fixed, but every row is
+// computed independently of its neighbours and the combine reads rows by slot,
+// so the layer's output is the same on every run.
+#include "qmm_device.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+namespace {
+
+constexpr uint32_t kInvalidRow = 0xFFFFFFFFu;
+constexpr int kRouteThreads = 1024;
+
+struct RouteArgs {
+  const int32_t *topk_ids;
+  int t, topk, num_routed, num_shared;
+  MoeTables tb;
+};
+
+// Block-wide exclusive scan of one value per thread (1024 threads); returns the
+// prefix and writes the total to *total.
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *buf, uint32_t *total) {
+  const int tid = threadIdx.x;
+  buf[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kRouteThreads; off <<= 1) {
+    const uint32_t add = tid >= off ? buf[tid - off] : 0u;
+    __syncthreads();
+    buf[tid] += add;
+    __syncthreads();
+  }
+  const uint32_t incl = buf[tid];
+  if (tid == kRouteThreads - 1) *total = incl;
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
+  __shared__ uint32_t s_count[kMoeMaxExperts];
+  __shared__ uint32_t s_off[kMoeMaxExperts];
+  __shared__ uint32_t s_scan[kRouteThreads];
+  __shared__ uint32_t s_total;
+  const int tid = threadIdx.x;
+  const int ne = a.num_routed + a.num_shared;
+  const int slots = a.t * a.topk;
+  const MoeTables &tb = a.tb;
+
+  for (int e = tid; e < ne; e += kRouteThreads) s_count[e] = 0;
+  if (tid == 0) *tb.err = 0;
+  __syncthreads();
+  // 1. position of every routed slot inside its expert's group
+  for (int i = tid; i < slots; i += kRouteThreads) {
+    const int e = a.topk_ids[i];
+    if (e < 0 || e >= a.num_routed) {
+      tb.row_of_slot[i] = kInvalidRow;  // contributes nothing; reported in err
+      atomicOr(tb.err, 1u);
+      continue;
+    }
+    tb.row_of_slot[i] = atomicAdd(&s_count[e], 1u);
+  }
+  // shared experts see every token, in token order
+  for (int e = a.num_routed + tid; e < ne; e += kRouteThreads) s_count[e] = (uint32_t)a.t;
+  __syncthreads();
+
+  // 2. group offsets (exclusive scan over experts, kMoeMaxExperts / 1024 per thread)
+  constexpr int PER = kMoeMaxExperts / kRouteThreads;
+  uint32_t local = 0;
+  for (int j = 0; j < PER; ++j) {
+    const int e = tid * PER + j;
+    local += e < ne ? s_count[e] : 0u;
+  }
+  uint32_t base = block_exclusive_scan(local, s_scan, &s_total);
+  for (int j = 0; j < PER; ++j) {
+    const int e = tid * PER + j;
+    if (e < ne) {
+      s_off[e] = base;
+      tb.counts[e] = s_count[e];
+      tb.offsets[e] = base;
+      base += s_count[e];
+    }
+  }
+  if (tid == 0) tb.offsets[ne] = s_total;
+  __syncthreads();
+
+  // 3. grouped row of every slot, and the token each grouped row reads
+  for (int i = tid; i < slots; i += kRouteThreads) {
+    const uint32_t pos = tb.row_of_slot[i];
+    if (pos == kInvalidRow) continue;
+    const uint32_t row = s_off[a.topk_ids[i]] + pos;
+    tb.row_of_slot[i] = row;
+    tb.token_of_row[row] = (uint32_t)(i / a.topk);
+  }
+  for (int s = 0; s < a.num_shared; ++s)
+    for (int t = tid; t < a.t; t += kRouteThreads) {
+      const uint32_t row = s_off[a.num_routed + s] + t;
+      tb.row_of_shared[(size_t)s * a.t + t] = row;
+      tb.token_of_row[row] = (uint32_t)t;
+    }
+
+  // 4. experts with rows (in expert order) and their tiles of kGemmBM rows
+  uint32_t nact = 0, ntile = 0;
+  for (int j = 0; j < PER; ++j) {
+    const int e = tid * PER + j;
+    if (e < ne && s_count[e]) {
+      nact += 1;
+      ntile += (s_count[e] + kGemmBM - 1) / kGemmBM;
+    }
+  }
+  uint32_t act_base = block_exclusive_scan(nact, s_scan, &s_total);
+  if (tid == 0) *tb.n_active = s_total;
+  uint32_t tile_base = block_exclusive_scan(ntile, s_scan, &s_total);
+  if (tid == 0) *tb.n_tiles = s_total;
+  for (int j = 0; j < PER; ++j) {
+    const int e = tid * PER + j;
+    if (e >= ne || !s_count[e]) continue;
+    tb.active[act_base++] = (uint32_t)e;
+    const uint32_t cnt = s_count[e];
+    for (uint32_t r = 0; r < cnt; r += kGemmBM) {
+      uint32_t *tl = tb.tiles + 3 * (size_t)tile_base++;
+      tl[0] = (uint32_t)e;
+      tl[1] = s_off[e] + r;
+      tl[2] = min(cnt - r, (uint32_t)kGemmBM);
+    }
+  }
+}
+
+struct CombineArgs {
+  const float *topk_w;
+  const float *shared_w;
+  int t, topk, num_shared, h;
+  MoeTables tb;
+  void *y;
+  int y_bf16;
+};
+
+// y[t][n] = sum_j w[t][j] d[row(t, j)][n] + sum_s ws[t] d[row_s(t)][n], fixed order
+__global__ __launch_bounds__(256) void moe_combine_kernel(CombineArgs a) {
+  const int t = blockIdx.x;
+  const int n = blockIdx.y * 256 + threadIdx.x;
+  if (n >= a.h) return;
+  float acc = 0.0f;
+  for (int j = 0; j < a.topk; ++j) {
+    const uint32_t row = a.tb.row_of_slot[(size_t)t * a.topk + j];
+    if (row == kInvalidRow) continue;
+    acc = __builtin_fmaf(a.topk_w[(size_t)t * a.topk + j], a.tb.d[(size_t)row * a.h + n], acc);
+  }
+  for (int s = 0; s < a.num_shared; ++s) {
+    const uint32_t row = a.tb.row_of_shared[(size_t)s * a.t + t];
+    const float ws = a.shared_w ? a.shared_w[t] : 1.0f;
+    acc = __builtin_fmaf(ws, a.tb.d[(size_t)row * a.h + n], acc);
+  }
+  if (a.y_bf16)
+    ((uint16_t *)a.y)[(size_t)t * a.h + n] = (uint16_t)float_to_bf16(acc);
+  else
+    ((float *)a.y)[(size_t)t * a.h + n] = acc;
+}
+
+size_t align_up(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+MoeLayout moe_layout(int num_experts, int t, int topk, int num_shared, int inter, int hidden) {
+  MoeLayout L{};
+  const size_t rows = (size_t)t * topk + (size_t)t * num_shared;
+  L.max_rows = rows;
+  L.max_tiles = (rows + kGemmBM - 1) / kGemmBM + (size_t)num_experts;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.counts = take((size_t)num_experts * 4);
+  L.offsets = take(((size_t)num_experts + 1) * 4);
+  L.row_of_slot = take((size_t)t * topk * 4);
+  L.row_of_shared = take((size_t)t * num_shared * 4 + 4);
+  L.token_of_row = take(rows * 4 + 4);
+  L.active = take((size_t)num_experts * 4);
+  L.scalars = take(16);  // n_active, n_tiles, err
+  L.tiles = take(L.max_tiles * 12);
+  L.h = take(rows * (size_t)inter * 2);
+  L.d = take(rows * (size_t)hidden * 4);
+  L.bytes = o;
+  return L;
+}
+
+MoeTables moe_tables(const MoeLayout &L, void *ws) {
+  char *b = (char *)ws;
+  MoeTables t;
+  t.counts = (uint32_t *)(b + L.counts);
+  t.offsets = (uint32_t *)(b + L.offsets);
+  t.row_of_slot = (uint32_t *)(b + L.row_of_slot);
+  t.row_of_shared = (uint32_t *)(b + L.row_of_shared);
+  t.token_of_row = (uint32_t *)(b + L.token_of_row);
+  t.active = (uint32_t *)(b + L.active);
+  t.n_active = (uint32_t *)(b + L.scalars);
+  t.n_tiles = t.n_active + 1;
+  t.err = t.n_active + 2;
+  t.tiles = (uint32_t *)(b + L.tiles);
+  t.h = (uint16_t *)(b + L.h);
+  t.d = (float *)(b + L.d);
+  return t;
+}
+
+hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed, int num_shared,
+                      const void *x, int t, const int32_t *topk_ids, const float *topk_w,
+                      int topk, const float *shared_w, void *y, int y_dtype, void *workspace,
+                      hipStream_t s) {
+  const MoeLayout L = moe_layout(num_routed + num_shared, t, topk, num_shared, gu.n / 2, dn.n);
+  const MoeTables tb = moe_tables(L, workspace);
+
+  RouteArgs ra{topk_ids, t, topk, num_routed, num_shared, tb};
+  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ra);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  e = launch_moe_gemm_gate_up(gu, x, tb, (int)L.max_tiles, s);
+  if (e != hipSuccess) return e;
+  e = launch_moe_gemm_down(dn, tb, (int)L.max_tiles, s);
+  if (e != hipSuccess) return e;
+
+  CombineArgs ca{topk_w, shared_w, t, topk, num_shared, dn.n, tb, y, y_dtype == QMM_BF16};
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(t, (dn.n + 255) / 256), dim3(256), 0, s, ca);
+  return hipGetLastError();
+}
+
+}  // namespace qmm

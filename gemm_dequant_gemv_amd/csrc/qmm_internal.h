@@ -34,12 +34,47 @@ struct GemvPlan {
 
 GemvPlan plan_gemv(int format, int n, int k, int m);
 
+// Prefill GEMM / grouped MoE tiles: rows of activations per workgroup.
+constexpr int kGemmBM = 128;
+// Experts (routed + shared) one MoE call may have.
+constexpr int kMoeMaxExperts = 4096;
+
+// Device tables of one MoE call, carved from the caller's workspace.
+struct MoeTables {
+  uint32_t *counts;         // [experts] grouped rows per expert
+  uint32_t *offsets;        // [experts + 1] first grouped row of each expert
+  uint32_t *row_of_slot;    // [t][topk] grouped row of each routed slot
+  uint32_t *row_of_shared;  // [shared][t] grouped row of each shared slot
+  uint32_t *token_of_row;   // [rows] token each grouped row reads
+  uint32_t *active;         // [experts] experts with rows, in expert order
+  uint32_t *n_active, *n_tiles, *err;
+  uint32_t *tiles;          // [max_tiles][3] (expert, first row, rows)
+  uint16_t *h;              // bf16 [rows][inter]
+  float *d;                 // float32 [rows][hidden]
+};
+
+struct MoeLayout {
+  size_t counts, offsets, row_of_slot, row_of_shared, token_of_row, active, scalars, tiles, h, d;
+  size_t bytes, max_rows, max_tiles;
+};
+
+MoeLayout moe_layout(int num_experts, int t, int topk, int num_shared, int inter, int hidden);
+MoeTables moe_tables(const MoeLayout &L, void *ws);
+
 hipError_t launch_dequant(const qmm_weight &w, int out_dtype, void *out, hipStream_t s);
 hipError_t launch_gemv(const qmm_weight &w, const void *x, int m, const void *residual,
                        void *y, int y_dtype, void *workspace, const GemvPlan &p,
                        hipStream_t s);
 hipError_t launch_gemm(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
                        hipStream_t s);
+hipError_t launch_moe_gemm_gate_up(const qmm_weight &gu, const void *x, const MoeTables &t,
+                                   int max_tiles, hipStream_t s);
+hipError_t launch_moe_gemm_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
+                                hipStream_t s);
+hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed, int num_shared,
+                      const void *x, int t, const int32_t *topk_ids, const float *topk_w,
+                      int topk, const float *shared_w, void *y, int y_dtype, void *workspace,
+                      hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_stream_read(const void *p, size_t bytes, uint32_t *sink, int blocks,
                               hipStream_t s);

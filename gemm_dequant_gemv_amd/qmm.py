@@ -21,6 +21,7 @@ F32, BF16 = 0, 1
 FORMATS = {"affine4_g64": AFFINE4_G64, "mxfp4": MXFP4, "nvfp4": NVFP4, "q6_k": Q6_K}
 
 ENTRY_POINTS = ("qdequant", "qgemv", "qgemv_workspace_size", "qgemm", "qgemm_workspace_size",
+                "qmoe_grouped", "qmoe_workspace_size", "qmoe_workspace_layout",
                 "qworkspace_init", "qbench_stream_read", "qstatus_string", "qlast_hip_error")
 
 
@@ -38,6 +39,12 @@ class QmmWeightC(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("codes", ctypes.c_void_p),
                 ("codes_hi", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("scales2", ctypes.c_void_p), ("tensor_scale", ctypes.c_void_p)]
+
+
+class QmoeLayoutC(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_size_t) for name in (
+        "counts", "offsets", "row_of_slot", "row_of_shared", "token_of_row", "active",
+        "scalars", "tiles", "h", "d", "bytes", "max_rows", "max_tiles")]
 
 
 _LIB = None
@@ -58,6 +65,10 @@ def _lib():
         lib.qgemm_workspace_size.argtypes = [P, I32]
         lib.qgemm_workspace_size.restype = SZ
         lib.qgemm.argtypes = [P, VP, I32, VP, VP, VP, SZ, VP]
+        lib.qmoe_workspace_size.argtypes = [P, P, I32, I32, I32, I32]
+        lib.qmoe_workspace_size.restype = SZ
+        lib.qmoe_workspace_layout.argtypes = [P, P, I32, I32, I32, I32, ctypes.POINTER(QmoeLayoutC)]
+        lib.qmoe_grouped.argtypes = [P, P, I32, I32, VP, I32, VP, VP, I32, VP, VP, I32, VP, SZ, VP]
         lib.qworkspace_init.argtypes = [VP, SZ, VP]
         lib.qbench_stream_read.argtypes = [VP, SZ, VP, I32, VP]
         lib.qstatus_string.restype = ctypes.c_char_p
@@ -169,6 +180,37 @@ def gemm(w: Weight, x, residual=None, out=None, workspace=None, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib().qgemm(w.c, _ptr(x), m, _ptr(residual), _ptr(out), _ptr(workspace), ws_bytes,
                         _stream(stream)), "qgemm")
+    return out
+
+
+def moe_workspace_size(gate_up: Weight, down: Weight, num_routed: int, num_shared: int,
+                       t: int, topk: int) -> int:
+    return int(_lib().qmoe_workspace_size(gate_up.c, down.c, num_routed, num_shared, t, topk))
+
+
+def moe_workspace_layout(gate_up: Weight, down: Weight, num_routed: int, num_shared: int,
+                         t: int, topk: int) -> dict:
+    """Byte offsets of the intermediates inside a qmoe_grouped workspace, by name."""
+    out = QmoeLayoutC()
+    _check(_lib().qmoe_workspace_layout(gate_up.c, down.c, num_routed, num_shared, t, topk,
+                                        ctypes.byref(out)), "qmoe_workspace_layout")
+    return {name: int(getattr(out, name)) for name, _ in QmoeLayoutC._fields_}
+
+
+def moe(gate_up: Weight, down: Weight, x, topk_ids, topk_w, num_routed: int, num_shared: int,
+        shared_w=None, y_dtype=torch.float32, out=None, workspace=None, stream=None):
+    """One MoE layer; x bf16 [t][H], topk_ids int32 [t][topk], topk_w f32 [t][topk]."""
+    t, topk = topk_ids.shape
+    if out is None:
+        out = torch.empty((t, down.n), dtype=y_dtype, device=x.device)
+    need = moe_workspace_size(gate_up, down, num_routed, num_shared, t, topk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    dt = F32 if out.dtype == torch.float32 else BF16
+    _check(_lib().qmoe_grouped(gate_up.c, down.c, num_routed, num_shared, _ptr(x), t,
+                               _ptr(topk_ids), _ptr(topk_w), topk, _ptr(shared_w), _ptr(out), dt,
+                               _ptr(workspace), ws_bytes, _stream(stream)), "qmoe_grouped")
     return out
 
 

@@ -184,6 +184,68 @@ size_t qgemm_workspace_size(const qmm_weight *w, int32_t m);
 int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, void *y,
           void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * qmoe_grouped -- one mixture-of-experts layer: routed experts chosen per token
+ * plus shared experts that every token visits ("TurboEXL3" section 4.1 and 4.2:
+ * route, gate and up in one multiply, SwiGLU in 32-bit, down, and the
+ * score-weighted sum of each token's expert outputs; tokens that chose the
+ * same expert share one decode of its weights).
+ *
+ *   h_e(x)  = bf16( silu(g) * u ),  [g; u] = W_gu[e] x   (gate rows 0..I-1, up rows I..2I-1)
+ *   d_e(x)  = W_d[e] h_e(x)                                (float32)
+ *   y[t]    = sum_j topk_w[t][j] * d_{topk_ids[t][j]}(x[t])
+ *             + sum_s shared_w[t] * d_{E+s}(x[t])          (fixed order: j, then s)
+ *
+ * gate_up      batch = E + S matrices of 2I x H (routed experts 0..E-1, then the
+ *              S shared experts); 2I a multiple of 128
+ * down         batch = E + S matrices of H x I
+ * num_routed   E >= 1;  num_shared  S >= 0;  E + S <= 4096
+ * x            bf16 [t][H]
+ * topk_ids     int32 [t][topk], each in [0, E); a slot with an id outside that
+ *              range contributes nothing (it is never read out of bounds)
+ * topk_w       float32 [t][topk]
+ * shared_w     float32 [t] or NULL (weight 1 for every shared expert)
+ * y            [t][H], float32 (QMM_F32) or bf16 rounded to nearest even (QMM_BF16)
+ * workspace    at least qmoe_workspace_size(...) bytes, 256-byte aligned; it holds
+ *              the routing tables, h and d.  No zero-fill is needed.
+ * The gate/up and down weights may use different formats.
+ */
+size_t qmoe_workspace_size(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
+                           int32_t num_shared, int32_t t, int32_t topk);
+int qmoe_grouped(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
+                 int32_t num_shared, const void *x, int32_t t, const int32_t *topk_ids,
+                 const float *topk_w, int32_t topk, const float *shared_w, void *y,
+                 int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Where a qmoe_grouped call with these arguments keeps its intermediates inside
+ * the workspace, for inspection after the call.  Byte offsets from the
+ * workspace start; rows = t * (topk + S) grouped rows (slots sorted by expert).
+ */
+typedef struct {
+  size_t counts;        /* uint32 [E+S]     rows of each expert                       */
+  size_t offsets;       /* uint32 [E+S+1]   first grouped row of each expert; last =
+                           number of valid rows                                     */
+  size_t row_of_slot;   /* uint32 [t][topk] grouped row of each routed slot, or
+                           0xFFFFFFFF for an expert id outside [0, E)               */
+  size_t row_of_shared; /* uint32 [S][t]    grouped row of each shared-expert slot   */
+  size_t token_of_row;  /* uint32 [rows]    token each grouped row reads              */
+  size_t active;        /* uint32 [n_active] experts with at least one row, ascending */
+  size_t scalars;       /* uint32 [3]       n_active, n_tiles, err (1 = an id was
+                           outside [0, E) and its slot was dropped)                 */
+  size_t tiles;         /* uint32 [n_tiles][3] expert, first grouped row, rows (<= 128)
+                           of each row tile, experts ascending                      */
+  size_t h;             /* bf16  [rows][I]  SwiGLU outputs                          */
+  size_t d;             /* float [rows][H]  down-projection outputs                  */
+  size_t bytes;         /* = qmoe_workspace_size                                     */
+  size_t max_rows, max_tiles;
+} qmoe_layout;
+
+/* Fill *out for these arguments (host-side arithmetic only, no launch).
+ * QMM_ERR_NULL / QMM_ERR_ARG on bad arguments. */
+int qmoe_workspace_layout(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
+                          int32_t num_shared, int32_t t, int32_t topk, qmoe_layout *out);
+
 /* Zero-fill a workspace on `stream` (a kernel, not a memset node). */
 int qworkspace_init(void *workspace, size_t workspace_bytes, void *stream);
 

@@ -29,6 +29,9 @@ What it computes, and where the pages define it:
   All four products are exact in float64.
 * Products summed in float64 from the exact weights and the bfloat16 inputs
   taken exactly: y[m][n] = sum_k w[n][k] x[m][k] (+ r[m][n]).
+* The MoE route step as plain counting: per-expert row counts, their
+  exclusive prefix sums and the table of 128-row tiles ("TurboEXL3"
+  section 4.1, steps 1 and 6).
 * The MoE layer stage by stage ("TurboEXL3" section 4.1: gate and up in one
   GEMM, SwiGLU in 32-bit between them and the down projection, then the
   score-weighted sum of each token's ten expert outputs), rounding only where
@@ -236,6 +239,42 @@ def moe(gate_up, down, x_bits, topk_ids, topk_w, num_routed: int, num_shared: in
         ys.append(y)
         mags.append(mag)
     return np.array(ys), np.array(mags), hs
+
+
+def moe_grouping(topk_ids, num_routed: int, num_shared: int, tile_rows: int = 128):
+    """The route step ("TurboEXL3" section 4.1, step 1: count each expert's
+    tokens, group the tokens by expert, build the table of row tiles; 128-row
+    tiles per step 6), written as the plain count / exclusive-scan / split.
+
+    An id outside [0, num_routed) names no expert: its slot is dropped.
+    Shared experts follow the routed ones and take every token.
+
+    Returns a dict with the parts of the grouping that are unique:
+      counts [E+S], offsets [E+S+1] (exclusive prefix sums, last = total rows),
+      valid bool [T][k], active (experts with rows, ascending),
+      tiles [(expert, first_row, rows)] in expert order, err (1 if any slot was
+      dropped).  Which row of its expert's group a slot lands on is not unique.
+    """
+    ids = np.asarray(topk_ids).astype(np.int64)
+    T = ids.shape[0]
+    E, S = num_routed, num_shared
+    valid = (ids >= 0) & (ids < E)
+    counts = [0] * (E + S)
+    for e in ids[valid].ravel():
+        counts[int(e)] += 1
+    for s in range(S):
+        counts[E + s] = T
+    offsets = [0]
+    for c in counts:
+        offsets.append(offsets[-1] + c)
+    active = [e for e in range(E + S) if counts[e] > 0]
+    tiles = []
+    for e in active:
+        for r in range(0, counts[e], tile_rows):
+            tiles.append((e, offsets[e] + r, min(tile_rows, counts[e] - r)))
+    return dict(counts=np.array(counts, np.int64), offsets=np.array(offsets, np.int64),
+                valid=valid, active=np.array(active, np.int64),
+                tiles=np.array(tiles, np.int64).reshape(-1, 3), err=int((~valid).any()))
 
 
 def moe_gate_up(gate_up, x_bits, e: int, rows_tokens):

@@ -198,6 +198,18 @@ def synthetic_weight(fmt: int, n: int, k: int, *, seed: int = rng.BASE_SEED,
     jobs = [(e, r0, min(n, r0 + rows_per_chunk)) for e in range(batch)
             for r0 in range(0, n, rows_per_chunk)]
 
+    if fmt == F.NVFP4 and rows_per_chunk >= n:
+        # whole matrices per job: draw once, take the amax, quantize
+        def whole_job(e):
+            w = _weight_rows(seed, f"{name}[{e}]", n, k, std, outlier_rate, outlier_mult, 0, n)
+            ts = nvfp4_tensor_scale(float(np.abs(w).max()))
+            _quantize_rows(p, e, 0, w, ts)
+
+        with ThreadPoolExecutor(_nthreads()) as ex:
+            list(ex.map(whole_job, range(batch)))
+        p.meta = dict(seed=seed, name=name, std=std, outlier_rate=outlier_rate)
+        return p
+
     if fmt == F.NVFP4:
         # the tensor multiplier needs the whole matrix's amax first
         def amax_job(j):

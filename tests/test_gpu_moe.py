@@ -1,0 +1,263 @@
+"""GPU parity of qmoe_grouped (route, grouped gate/up + SwiGLU, grouped down,
+weighted combine) against the CPU oracle, through the C ABI.
+
+Checked stage by stage, as the oracle's contract rounds (h is bf16):
+  * h (SwiGLU output) against the oracle's within the propagated bound
+    |dh| <= |u| silu'max 2e-3 mag_g + |silu(g)| 2e-3 mag_u + half a bf16 ulp;
+  * y against the oracle run on the GPU's own h, within 2e-3 * sum_k |w_k| mag(d_k)
+    (plus half a bf16 ulp when y is bf16)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import formats as F
+from synth import quant, routing
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+SILU_SLOPE_MAX = 1.1  # |d silu / dg| <= 1.0998
+
+
+def _q():
+    import gemm_dequant_gemv_amd as q
+    return q
+
+
+def _dev_bf16(bits):
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+
+def make_case(fmt_gu, fmt_dn, E, S, H, I, T, topk, tag):
+    gu = quant.synthetic_weight(fmt_gu, 2 * I, H, batch=E + S, name=f"{tag}/gu")
+    dn = quant.synthetic_weight(fmt_dn, H, I, batch=E + S, name=f"{tag}/dn")
+    x = quant.synthetic_bf16(T, H, name=f"{tag}/x")
+    ids, w = routing.synthetic_routing(T, E, topk, name=f"{tag}/r")
+    return gu, dn, x, ids, w
+
+
+def _u32(ws, off, count):
+    return ws[off:off + 4 * count].view(torch.int32).cpu().numpy().view(np.uint32).astype(np.int64)
+
+
+def run_gpu(q, gu, dn, x, ids, w, E, S, shared_w=None, y_dtype=torch.float32, wdev=None):
+    """Run the layer; return y (float64) and the workspace's intermediates."""
+    T, topk = ids.shape
+    gud, dnd = wdev if wdev is not None else (q.Weight.from_host(gu), q.Weight.from_host(dn))
+    L = q.moe_workspace_layout(gud, dnd, E, S, T, topk)
+    assert L["bytes"] == q.moe_workspace_size(gud, dnd, E, S, T, topk)
+    ws = torch.empty(L["bytes"], dtype=torch.uint8, device="cuda")
+    sw = None if shared_w is None else torch.from_numpy(shared_w).cuda()
+    y = q.moe(gud, dnd, _dev_bf16(x), torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(),
+              E, S, shared_w=sw, y_dtype=y_dtype, workspace=ws)
+    torch.cuda.synchronize()
+    I = gu.n // 2
+    rows = T * (topk + S)
+    r = {}
+    r["counts"] = _u32(ws, L["counts"], E + S)
+    r["offsets"] = _u32(ws, L["offsets"], E + S + 1)
+    r["row_of_slot"] = _u32(ws, L["row_of_slot"], T * topk).reshape(T, topk)
+    r["row_of_shared"] = _u32(ws, L["row_of_shared"], S * T)
+    r["token_of_row"] = _u32(ws, L["token_of_row"], rows)
+    n_active, n_tiles, err = _u32(ws, L["scalars"], 3)
+    r["active"] = _u32(ws, L["active"], n_active)
+    r["tiles"] = _u32(ws, L["tiles"], 3 * n_tiles).reshape(-1, 3)
+    r["err"] = int(err)
+    r["h"] = ws[L["h"]:L["h"] + rows * I * 2].view(torch.int16).cpu().numpy().view(np.uint16).reshape(rows, I)
+    if y.dtype == torch.bfloat16:
+        yh = oracle.bf16(y.view(torch.int16).cpu().numpy().view(np.uint16))
+    else:
+        yh = y.cpu().numpy().astype(np.float64)
+    return yh, r
+
+
+def check_grouping(r, ids, E, S):
+    """Bit-exact on what the grouping fixes (counts, offsets, active experts,
+    tile table, error flag); valid on what it leaves open (the order of a
+    group's rows): every slot lands inside its expert's rows, once."""
+    g = oracle.moe_grouping(ids, E, S)
+    T, topk = ids.shape
+    assert np.array_equal(r["counts"], g["counts"])
+    assert np.array_equal(r["offsets"], g["offsets"])
+    assert np.array_equal(r["active"], g["active"])
+    assert np.array_equal(r["tiles"], g["tiles"])
+    assert r["err"] == g["err"]
+    ros = r["row_of_slot"]
+    assert (ros[~g["valid"]] == 0xFFFFFFFF).all()
+    e = ids[g["valid"]].astype(np.int64)
+    rv = ros[g["valid"]]
+    assert ((g["offsets"][e] <= rv) & (rv < g["offsets"][e + 1])).all()
+    tok = np.nonzero(g["valid"])[0]
+    assert np.array_equal(r["token_of_row"][rv], tok)
+    rs = r["row_of_shared"].reshape(S, T)
+    for s in range(S):
+        assert ((g["offsets"][E + s] <= rs[s]) & (rs[s] < g["offsets"][E + s + 1])).all()
+        assert np.array_equal(r["token_of_row"][rs[s]], np.arange(T))
+    every = np.concatenate([rv, rs.ravel()])
+    assert len(np.unique(every)) == len(every) == g["offsets"][-1]
+
+
+def gpu_h_dict(r, T, topk, S, tokens):
+    h, ros, rsh = r["h"], r["row_of_slot"], r["row_of_shared"]
+    d = {}
+    for t in tokens:
+        for j in range(topk):
+            if ros[t, j] != 0xFFFFFFFF:
+                d[(t, j)] = h[ros[t, j]]
+        for s in range(S):
+            d[(t, topk + s)] = h[rsh[s * T + t]]
+    return d
+
+
+def check_h(gu, x, ids, E, S, hd, tokens):
+    """GPU h against the oracle's SwiGLU of exact gate/up outputs."""
+    I = gu.n // 2
+    cache = {}
+    for t in tokens:
+        experts = [(int(ids[t, j]), j) for j in range(ids.shape[1])]
+        experts += [(E + s, ids.shape[1] + s) for s in range(S)]
+        xt = oracle.bf16(x[t])
+        for e, slot in experts:
+            if e not in cache:
+                cache[e] = oracle.dequant(gu, e)
+            wgu = cache[e]
+            gu_v = wgu @ xt
+            mag = np.abs(wgu) @ np.abs(xt)
+            g, u, mg, mu = gu_v[:I], gu_v[I:], mag[:I], mag[I:]
+            sg = oracle.silu(g)
+            href = sg * u
+            bound = (np.abs(u) * SILU_SLOPE_MAX * TOL * mg + np.abs(sg) * TOL * mu
+                     + 2 * oracle.bf16_half_ulp(href) + 1e-30)
+            got = oracle.bf16(hd[(t, slot)])
+            bad = np.abs(got - href) > bound
+            assert not bad.any(), f"token {t} expert {e}: {bad.sum()} h values out of bound"
+
+
+def check_y(gu, dn, x, ids, w, E, S, yh, hd, tokens, shared_w=None, bf16_out=False):
+    yref, mag, _ = oracle.moe(gu, dn, x, ids, w, E, S, shared_w=shared_w, tokens=tokens,
+                              h_given=hd)
+    got = yh[np.asarray(tokens)]
+    ok = (oracle.within_tolerance_bf16(got, yref, mag, TOL) if bf16_out
+          else oracle.within_tolerance(got, yref, mag, TOL))
+    assert ok.all(), (f"{(~ok).sum()} of {ok.size} outside; worst "
+                      f"{np.max(np.abs(got - yref) / mag):.3e} of mag")
+
+
+SMALL = dict(E=16, S=1, H=256, I=128, topk=4)
+
+
+@pytest.mark.parametrize("T", [1, 4, 37, 300])
+@pytest.mark.parametrize("fmts", [(F.NVFP4, F.NVFP4), (F.AFFINE4_G64, F.MXFP4), (F.Q6_K, F.AFFINE4_G64)])
+def test_moe_parity_small(T, fmts):
+    q = _q()
+    c = SMALL
+    gu, dn, x, ids, w = make_case(*fmts, c["E"], c["S"], c["H"], c["I"], T, c["topk"],
+                                  f"moe{fmts}{T}")
+    yh, r = run_gpu(q, gu, dn, x, ids, w, c["E"], c["S"])
+    check_grouping(r, ids, c["E"], c["S"])
+    tokens = list(range(T)) if T <= 40 else list(range(0, T, 7))
+    hd = gpu_h_dict(r, T, c["topk"], c["S"], tokens)
+    check_h(gu, x, ids, c["E"], c["S"], hd, tokens)
+    check_y(gu, dn, x, ids, w, c["E"], c["S"], yh, hd, tokens)
+
+
+def test_moe_no_shared_weighted_shared_and_bf16_out():
+    q = _q()
+    E, H, I, T, topk = 8, 256, 128, 50, 2
+    gu, dn, x, ids, w = make_case(F.NVFP4, F.NVFP4, E, 0, H, I, T, topk, "moens")
+    yh, r = run_gpu(q, gu, dn, x, ids, w, E, 0, y_dtype=torch.bfloat16)
+    tokens = list(range(T))
+    hd = gpu_h_dict(r, T, topk, 0, tokens)
+    check_y(gu, dn, x, ids, w, E, 0, yh, hd, tokens, bf16_out=True)
+    # one shared expert with a per-token weight
+    gu, dn, x, ids, w = make_case(F.NVFP4, F.NVFP4, E, 1, H, I, T, topk, "moesw")
+    sw = (np.arange(T, dtype=np.float32) / T - 0.3).astype(np.float32)
+    yh, r = run_gpu(q, gu, dn, x, ids, w, E, 1, shared_w=sw)
+    hd = gpu_h_dict(r, T, topk, 1, tokens)
+    check_y(gu, dn, x, ids, w, E, 1, yh, hd, tokens, shared_w=sw)
+
+
+def test_moe_single_expert_equals_dense_chain():
+    """E = 1, topk = 1, weight 1, no shared expert: the layer is down(SwiGLU(gate_up x))."""
+    q = _q()
+    H, I, T = 512, 256, 130
+    gu, dn, x, _, _ = make_case(F.AFFINE4_G64, F.NVFP4, 1, 0, H, I, T, 1, "moe1")
+    ids = np.zeros((T, 1), np.int32)
+    w = np.ones((T, 1), np.float32)
+    yh, r = run_gpu(q, gu, dn, x, ids, w, 1, 0)
+    tokens = list(range(T))
+    hd = gpu_h_dict(r, T, 1, 0, tokens)
+    # the oracle's down stage on the GPU's h is exactly two dense products
+    hb = np.stack([hd[(t, 0)] for t in tokens])
+    yref, mag = oracle.gemv(dn, hb)
+    assert oracle.within_tolerance(yh, yref, mag, TOL).all()
+    check_h(gu, x, ids, 1, 0, hd, tokens)
+
+
+def test_moe_invalid_expert_ids_contribute_nothing():
+    q = _q()
+    E, H, I, T, topk = 8, 256, 128, 6, 3
+    gu, dn, x, ids, w = make_case(F.NVFP4, F.NVFP4, E, 1, H, I, T, topk, "moebad")
+    ids = ids.copy()
+    ids[0, 1] = E + 5
+    ids[3, 0] = -1
+    yh, r = run_gpu(q, gu, dn, x, ids, w, E, 1)
+    assert r["row_of_slot"][0, 1] == 0xFFFFFFFF and r["row_of_slot"][3, 0] == 0xFFFFFFFF
+    assert r["err"] == 1
+    check_grouping(r, ids, E, 1)
+    w2 = w.copy()
+    w2[0, 1] = 0.0
+    w2[3, 0] = 0.0
+    ids2 = np.where(ids < 0, 0, np.where(ids >= E, 0, ids)).astype(np.int32)
+    tokens = list(range(T))
+    hd = gpu_h_dict(r, T, topk, 1, tokens)
+    # the dropped slots get a placeholder h (their weight is zero in the reference)
+    for (t, j) in [(0, 1), (3, 0)]:
+        hd[(t, j)] = np.zeros(I, np.uint16)
+    check_y(gu, dn, x, ids2, w2, E, 1, yh, hd, tokens)
+
+
+def test_moe_deterministic():
+    q = _q()
+    E, H, I, T, topk = 16, 256, 128, 300, 4
+    gu, dn, x, ids, w = make_case(F.NVFP4, F.NVFP4, E, 1, H, I, T, topk, "moedet")
+    wdev = (q.Weight.from_host(gu), q.Weight.from_host(dn))
+    ys = [run_gpu(q, gu, dn, x, ids, w, E, 1, wdev=wdev)[0] for _ in range(3)]
+    for y in ys[1:]:
+        assert np.array_equal(ys[0], y)
+
+
+# The full layer: 512 routed experts plus one shared expert, hidden 2048,
+# expert intermediate 512, NVFP4, top-10 of softmaxed N(0, 1) logits.
+FULL = dict(E=512, S=1, H=2048, I=512, topk=10)
+
+
+@pytest.fixture(scope="module")
+def full_layer():
+    q = _q()
+    c = FULL
+    gu = quant.synthetic_weight(F.NVFP4, 2 * c["I"], c["H"], batch=c["E"] + c["S"],
+                                name="moe_full/gate_up")
+    dn = quant.synthetic_weight(F.NVFP4, c["H"], c["I"], batch=c["E"] + c["S"],
+                                name="moe_full/down")
+    return gu, dn, (q.Weight.from_host(gu), q.Weight.from_host(dn))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T,y_dtype", [(4, torch.float32), (8192, torch.bfloat16)])
+def test_moe_full_layer(full_layer, T, y_dtype):
+    q = _q()
+    c = FULL
+    gu, dn, wdev = full_layer
+    x = quant.synthetic_bf16(T, c["H"], name=f"moe_full/x{T}")
+    ids, w = routing.synthetic_routing(T, c["E"], c["topk"], name=f"moe_full/r{T}")
+    print(f"moe full layer T={T}", flush=True)
+    yh, r = run_gpu(q, gu, dn, x, ids, w, c["E"], c["S"], y_dtype=y_dtype, wdev=wdev)
+    check_grouping(r, ids, c["E"], c["S"])
+    tokens = list(range(T)) if T <= 4 else [0, 1, 2047, 4096, 6000, T - 1]
+    hd = gpu_h_dict(r, T, c["topk"], c["S"], tokens)
+    check_h(gu, x, ids, c["E"], c["S"], hd, tokens)
+    check_y(gu, dn, x, ids, w, c["E"], c["S"], yh, hd, tokens,
+            bf16_out=y_dtype == torch.bfloat16)
+    assert np.isfinite(yh).all()

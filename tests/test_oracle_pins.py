@@ -425,3 +425,45 @@ def test_bf16_half_ulp_closed_form():
     assert np.array_equal(oracle.bf16_half_ulp(v), ulp / 2)
     # one ulp step of bf16 around 1.0 is 2^-7
     assert oracle.bf16(np.uint16(0x3F81)) - 1.0 == 2.0 ** -7
+
+
+def test_moe_grouping_hand_worked_example():
+    """Three tokens, top-2 of 3 routed experts plus one shared expert; the
+    table is worked by hand: expert 0 gets tokens 0 and 2, expert 1 token 1,
+    expert 2 tokens 0, 1, 2, the shared expert all three."""
+    ids = np.array([[2, 0], [2, 1], [0, 2]])
+    g = oracle.moe_grouping(ids, 3, 1)
+    assert g["counts"].tolist() == [2, 1, 3, 3]
+    assert g["offsets"].tolist() == [0, 2, 3, 6, 9]
+    assert g["active"].tolist() == [0, 1, 2, 3]
+    assert g["tiles"].tolist() == [[0, 0, 2], [1, 2, 1], [2, 3, 3], [3, 6, 3]]
+    assert g["err"] == 0
+    # tiles of 2 rows split expert 2's three rows into 2 + 1
+    g2 = oracle.moe_grouping(ids, 3, 0, tile_rows=2)
+    assert g2["tiles"].tolist() == [[0, 0, 2], [1, 2, 1], [2, 3, 2], [2, 5, 1]]
+    # an id outside [0, E) is dropped and flagged; an unused expert has no tile
+    g3 = oracle.moe_grouping(np.array([[1, 7], [-1, 1]]), 3, 0)
+    assert g3["counts"].tolist() == [0, 2, 0]
+    assert g3["valid"].tolist() == [[True, False], [False, True]]
+    assert g3["active"].tolist() == [1]
+    assert g3["tiles"].tolist() == [[1, 0, 2]]
+    assert g3["err"] == 1
+
+
+def test_moe_grouping_invariants_at_prefill_size():
+    """8192 tokens, top-10 of 512: the counts add to the slot total, the mean
+    is the 160 rows per expert the pages derive ("TurboEXL3" section 3.1),
+    every tile lies inside its expert's rows and the tiles cover them once."""
+    ids, _ = routing.synthetic_routing(8192, 512, 10, name="pin/group")
+    g = oracle.moe_grouping(ids, 512, 1)
+    c = g["counts"]
+    assert c[:512].sum() == 81920 and c[512] == 8192
+    assert c[:512].mean() == 160
+    assert np.array_equal(np.bincount(ids.ravel(), minlength=512), c[:512])
+    covered = np.zeros(g["offsets"][-1], np.int64)
+    for e, r0, rows in g["tiles"]:
+        assert 1 <= rows <= 128
+        assert g["offsets"][e] <= r0 and r0 + rows <= g["offsets"][e + 1]
+        covered[r0:r0 + rows] += 1
+    assert (covered == 1).all()
+    assert len(g["tiles"]) == int(np.sum((c + 127) // 128))
