@@ -38,8 +38,7 @@
 #include <algorithm>
 #include <cstdlib>
 
-#include "qmm_device.h"
-#include "qmm_internal.h"
+#include "gemv_step.h"
 
 namespace qmm {
 namespace {
@@ -62,18 +61,6 @@ struct GemvArgs {
   int n, k, steps, splits, y_bf16;
 };
 
-template <int FMT>
-struct FmtTraits {
-  // sums of x kept per 32-value chunk: affine 1 (per chunk), Q6_K 2 (per
-  // 16-value sub-block), E2M1 formats none.
-  static constexpr int kSums = FMT == QMM_AFFINE4_G64 ? 1 : (FMT == QMM_Q6_K ? 2 : 0);
-  // activations staged in (i, i+4) pair order for the nibble-into-mantissa
-  // unpack, natural pair order for the hardware FP4 conversion.
-  static constexpr bool kPermute = FMT == QMM_AFFINE4_G64 || FMT == QMM_Q6_K;
-  // K values per byte of the `scales` plane
-  static constexpr int kKPerScaleByte = FMT == QMM_MXFP4 ? 32 : 16;
-};
-
 // Row stride (in u32) of the staged scales: room for kMaxSplitK values and a
 // pad that puts the 8 rows one ds_read touches on distinct banks.
 template <int FMT, int R>
@@ -84,111 +71,7 @@ constexpr int scale_stride() {
   return p;
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-// One row's data for one step.
-struct RowData {
-  uint4 q;      // 32 codes (Q6_K: low nibbles)
-  uint2 h;      // Q6_K high bits
-  uint32_t s;   // affine (scale, bias) / E8M0 / two E4M3 / two int8 sc
-  uint32_t d;   // Q6_K super-block scale
-};
-
-// acc[m] += (this row's 32 weights of the chunk) . (x[m] chunk)
-template <int FMT, int M>
-__device__ __forceinline__ void row_step(const RowData &rd, const uint32_t (&X)[M][16],
-                                         const float (&S)[M][2], float (&acc)[M]) {
-  const uint32_t w[4] = {rd.q.x, rd.q.y, rd.q.z, rd.q.w};
-  if constexpr (FMT == QMM_AFFINE4_G64) {
-    const float s = half_to_float(rd.s & 0xFFFFu), b = half_to_float(rd.s >> 16);
-    float d[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) d[m] = -128.0f * S[m][0];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t p0 = nib_pair_128<0>(w[j]), p1 = nib_pair_128<1>(w[j]);
-      const uint32_t p2 = nib_pair_128<2>(w[j]), p3 = nib_pair_128<3>(w[j]);
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        d[m] = dot2(p0, X[m][4 * j + 0], d[m]);
-        d[m] = dot2(p1, X[m][4 * j + 1], d[m]);
-        d[m] = dot2(p2, X[m][4 * j + 2], d[m]);
-        d[m] = dot2(p3, X[m][4 * j + 3], d[m]);
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      acc[m] = __builtin_fmaf(s, d[m], acc[m]);
-      acc[m] = __builtin_fmaf(b, S[m][0], acc[m]);
-    }
-  } else if constexpr (FMT == QMM_MXFP4 || FMT == QMM_NVFP4) {
-    float d0[M], d1[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) d0[m] = d1[m] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t p0 = e2m1x2_to_bf16x2<0>(w[j]), p1 = e2m1x2_to_bf16x2<1>(w[j]);
-      const uint32_t p2 = e2m1x2_to_bf16x2<2>(w[j]), p3 = e2m1x2_to_bf16x2<3>(w[j]);
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float &d = (FMT == QMM_NVFP4 && j >= 2) ? d1[m] : d0[m];
-        d = dot2(p0, X[m][4 * j + 0], d);
-        d = dot2(p1, X[m][4 * j + 1], d);
-        d = dot2(p2, X[m][4 * j + 2], d);
-        d = dot2(p3, X[m][4 * j + 3], d);
-      }
-    }
-    if constexpr (FMT == QMM_MXFP4) {
-      const float sc = e8m0_to_float(rd.s);
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(sc, d0[m], acc[m]);
-    } else {
-      const float s0 = e4m3_to_float(rd.s & 0xFFu), s1 = e4m3_to_float(rd.s >> 8);
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        acc[m] = __builtin_fmaf(s0, d0[m], acc[m]);
-        acc[m] = __builtin_fmaf(s1, d1[m], acc[m]);
-      }
-    }
-  } else {  // Q6_K
-    const float dd = half_to_float(rd.d);
-    const uint32_t hw[2] = {rd.h.x, rd.h.y};
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t A = w[2 * j], B = w[2 * j + 1];
-      // high-bit bytes reordered to (values 0-3, 8-11, 4-7, 12-15) so that one
-      // shift puts the high bits of a (v, v+4) pair at bits 4-5 and 20-21.
-      const uint32_t H = __builtin_amdgcn_perm(hw[j], hw[j], 0x03010200u);
-      const uint32_t a0 = (A & 0x000F000Fu) | ((H << 4) & 0x00300030u) | 0x43004300u;
-      const uint32_t a1 = ((A >> 4) & 0x000F000Fu) | ((H << 2) & 0x00300030u) | 0x43004300u;
-      const uint32_t a2 = ((A >> 8) & 0x000F000Fu) | (H & 0x00300030u) | 0x43004300u;
-      const uint32_t a3 = ((A >> 12) & 0x000F000Fu) | ((H >> 2) & 0x00300030u) | 0x43004300u;
-      const uint32_t b0 = (B & 0x000F000Fu) | ((H >> 4) & 0x00300030u) | 0x43004300u;
-      const uint32_t b1 = ((B >> 4) & 0x000F000Fu) | ((H >> 6) & 0x00300030u) | 0x43004300u;
-      const uint32_t b2 = ((B >> 8) & 0x000F000Fu) | ((H >> 8) & 0x00300030u) | 0x43004300u;
-      const uint32_t b3 = ((B >> 12) & 0x000F000Fu) | ((H >> 10) & 0x00300030u) | 0x43004300u;
-      const float dsc = dd * (float)(int8_t)(rd.s >> (8 * j));
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float d = -160.0f * S[m][j];
-        d = dot2(a0, X[m][8 * j + 0], d);
-        d = dot2(a1, X[m][8 * j + 1], d);
-        d = dot2(a2, X[m][8 * j + 2], d);
-        d = dot2(a3, X[m][8 * j + 3], d);
-        d = dot2(b0, X[m][8 * j + 4], d);
-        d = dot2(b1, X[m][8 * j + 5], d);
-        d = dot2(b2, X[m][8 * j + 6], d);
-        d = dot2(b3, X[m][8 * j + 7], d);
-        acc[m] = __builtin_fmaf(dsc, d, acc[m]);
-      }
-    }
-  }
-}
-
-template <int FMT, int M, int R, int D>
+template <int FMT, int M, int R, int D, bool EARLY>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   using T = FmtTraits<FMT>;
   constexpr int kNS = T::kSums;
@@ -226,6 +109,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales, a.scales_bytes);
   const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(a.scales2, a.scales2_bytes);
 
+  const UnpackK K = unpack_consts();
   float acc[R][M];
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -278,15 +162,17 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     }
   }
 
-  // Wait for the small loads before the code stream starts: issued together,
-  // every workgroup's activations and scales would queue behind the whole
-  // machine's code requests and arrive only after most of the matrix.
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!EARLY) {
+    // Wait for the small loads before the code stream starts.
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // 3. the codes of the first D steps; afterwards every consumed step is
-  //    refilled with the step D ahead, keeping D steps in flight
+  //    refilled with the step D ahead, keeping D steps in flight (when D covers
+  //    a whole split there is nothing to refill)
+  constexpr bool kRefill = D < kMaxSplitK / kGemvStep;
   const int tlast = t1 - 1;
   const int klast = a.k - 32;
   RowData buf[D][R];
@@ -388,15 +274,17 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
             rd.s = *(const uint16_t *)(ssb + (lr * SSTRIDE) * 4 + 2 * lc);
             if constexpr (FMT == QMM_Q6_K) rd.d = sd[lr * (MAXCH / 8) + lc / 8];
           }
-          row_step<FMT, M>(rd, X, S, acc[r]);
+          row_step<FMT, M>(rd, X, S, acc[r], K);
         }
       }
-      const uint32_t kn = (uint32_t)min(min(t + D, tlast) * kGemvStep + c * 32, klast);
+      if constexpr (kRefill) {
+        const uint32_t kn = (uint32_t)min(min(t + D, tlast) * kGemvStep + c * 32, klast);
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        buf[d][r].q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, offc[r] + kn / 2, 0, 2));
-        if constexpr (FMT == QMM_Q6_K)
-          buf[d][r].h = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rh, offh[r] + kn / 4, 0, 2));
+        for (int r = 0; r < R; ++r) {
+          buf[d][r].q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, offc[r] + kn / 2, 0, 2));
+          if constexpr (FMT == QMM_Q6_K)
+            buf[d][r].h = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rh, offh[r] + kn / 4, 0, 2));
+        }
       }
     }
   }
@@ -479,26 +367,27 @@ constexpr size_t lds_bytes_cfg() {
          (FMT == QMM_Q6_K ? (size_t)ROWS * (MAXCH / 8) * 2 : 0);
 }
 
-template <int FMT, int M, int R, int D>
+template <int FMT, int M, int R, int D, bool EARLY>
 hipError_t launch_cfg(const GemvArgs &a, const GemvPlan &p, hipStream_t s) {
   constexpr size_t lds = lds_bytes_cfg<FMT, M, R>();
   static_assert(lds <= 65536, "GEMV LDS budget");
-  hipLaunchKernelGGL((gemv_kernel<FMT, M, R, D>), dim3(p.tiles, p.splits), dim3(kGemvThreads),
+  hipLaunchKernelGGL((gemv_kernel<FMT, M, R, D, EARLY>), dim3(p.tiles, p.splits), dim3(kGemvThreads),
                      lds, s, a);
   return hipGetLastError();
 }
 
 // (rows per lane, steps in flight) configurations compiled in
 #ifdef QMM_TUNE
-#define QMM_GEMV_CONFIGS(X) X(2, 4) X(4, 2) X(2, 2) X(2, 1) X(4, 1) X(1, 4) X(1, 2)
+#define QMM_GEMV_CONFIGS(X) X(1, 2, 0) X(1, 2, 1) X(1, 4, 1) X(1, 8, 1) X(1, 4, 0) X(2, 4, 1) X(2, 2, 1)
 #else
-#define QMM_GEMV_CONFIGS(X) X(1, 2)
+#define QMM_GEMV_CONFIGS(X) X(1, 2, 0)
 #endif
 
 template <int FMT, int M>
 hipError_t launch_fm(const GemvArgs &a, const GemvPlan &p, hipStream_t s) {
-#define QMM_CASE(RR, DD) \
-  if (p.rows_per_lane == RR && p.depth == DD) return launch_cfg<FMT, M, RR, DD>(a, p, s);
+#define QMM_CASE(RR, DD, EE) \
+  if (p.rows_per_lane == RR && p.depth == DD && p.early == EE) \
+    return launch_cfg<FMT, M, RR, DD, EE>(a, p, s);
   QMM_GEMV_CONFIGS(QMM_CASE)
 #undef QMM_CASE
   return hipErrorInvalidConfiguration;
@@ -517,8 +406,14 @@ hipError_t launch_f(const GemvArgs &a, int m, const GemvPlan &p, hipStream_t s) 
 }  // namespace
 
 GemvPlan plan_gemv(int format, int n, int k, int m) {
-  (void)format;
   GemvPlan p{};
+  // the row-streaming kernel whenever the activations fit in LDS
+  bool streaming = true;
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_GEMV_KIND")) streaming = atoi(e) == 1;
+#endif
+  if (streaming && plan_gemv_rows(format, n, k, m, p)) return p;
+  p = GemvPlan{};
   // One row per lane and two steps in flight: measured best on MI355X for the
   // decode shapes.  Deeper prefetch oversubscribes the memory system, and the
   // activation and scale loads of workgroups that start later then queue behind
@@ -529,6 +424,7 @@ GemvPlan plan_gemv(int format, int n, int k, int m) {
 #ifdef QMM_TUNE
   if (const char *e = getenv("QMM_GEMV_R")) p.rows_per_lane = atoi(e);
   if (const char *e = getenv("QMM_GEMV_D")) p.depth = atoi(e);
+  if (const char *e = getenv("QMM_GEMV_EARLY")) p.early = atoi(e);
 #endif
   const int rows = 4 * kGroups * p.rows_per_lane;
   p.steps = (k + kGemvStep - 1) / kGemvStep;
@@ -557,6 +453,7 @@ GemvPlan plan_gemv(int format, int n, int k, int m) {
 hipError_t launch_gemv(const qmm_weight &w, const void *x, int m, const void *residual,
                        void *y, int y_dtype, void *workspace, const GemvPlan &p,
                        hipStream_t s) {
+  if (p.kind == 1) return launch_gemv_rows(w, x, m, residual, y, y_dtype, p, s);
   GemvArgs a;
   a.codes = (const uint8_t *)w.codes;
   a.codes_hi = (const uint8_t *)w.codes_hi;

@@ -1,0 +1,408 @@
+// qgemv, row-streaming form: decode matrix-vector products for 1-4 activation
+// rows, weights dequantized in registers ("TurboEXL3" section 2.2: W4A16, each
+// weight expanded to 16 bits in the kernel, 16-bit products, 32-bit sums).
+//
+// One workgroup of 16 waves per compute unit.  The workgroup first stages the
+// whole activation block x [M][K] in LDS (pair order and per-block sums as in
+// the split-K kernel), then its waves stream weight rows:
+//   * rows go in pairs (2p, 2p+1), one per half-wave; wave w of the grid owns
+//     pairs w, w + W, w + 2W, ... (W = waves in the grid), so at any moment the
+//     grid streams one contiguous band of rows;
+//   * a unit is one step of one pair: 1024 values (512 code bytes) of each
+//     row, one 16-byte load per lane (lane c of a half holds values 32c ..
+//     32c+31), so every load instruction reads whole 128-byte lines of two
+//     rows, and K = 5120 or 17408 is a whole number of steps;
+//   * every load address is a per-lane constant (the lane's half and chunk)
+//     plus a wave-uniform offset (pair and step) passed in the buffer
+//     instruction's scalar offset, so addressing costs no vector ALU work;
+//   * a wave's units form one software pipeline with U units of loads in
+//     flight; each unit brings the codes of two rows, their block scales and
+//     one residual value per output;
+//   * after a pair's last step each half-wave's sums are reduced with DPP row
+//     operations and lanes 0 .. 2M-1 write the pair's 2 x M outputs.
+// Nothing crosses waves, so there is no split-K finish and no workspace, and
+// every sum has a fixed order: the result does not depend on timing.  (Giving
+// each workgroup a contiguous block of pairs split evenly over its waves, with
+// cut pairs finished through LDS, balanced the waves' work but measured
+// slower on the decode shapes.)
+//
+// The activations must fit in LDS (K * M * 2 bytes plus block sums); the host
+// falls back to the split-K kernel otherwise.
+#include <algorithm>
+#include <atomic>
+#include <cstdlib>
+
+#include "gemv_step.h"
+
+namespace qmm {
+namespace {
+
+constexpr int kWaves = 16;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStepK = 1024;       // values of one row per step (32 lanes x 32)
+constexpr int kXPieces = 9;        // 16-byte activation pieces per thread, at most
+constexpr size_t kLdsLimit = 160 * 1024 - 2048;  // dynamic part; the static part is < 1 KB
+
+// Activations of 32-value chunk ch, lane m, as 16-byte pieces p = 4m + part.
+// Pieces are XOR-swizzled inside the chunk so that the 8 lanes of one
+// ds_read_b128 group (consecutive chunks, same piece) hit distinct banks.
+template <int M>
+struct XLayout {
+  static constexpr int kPieces = M == 1 ? 4 : (M == 2 ? 8 : 16);
+  static constexpr int kStride = 4 * kPieces;  // u32 per chunk
+  __device__ static int slot(int ch, int p) {
+    return kPieces == 4 ? (p ^ ((ch >> 1) & 3)) : (p ^ (ch & 7));
+  }
+};
+
+struct RowsArgs {
+  const uint8_t *codes;
+  const uint8_t *codes_hi;
+  const uint8_t *scales;
+  const uint8_t *scales2;
+  const float *tensor_scale;
+  const uint16_t *x;
+  const uint16_t *residual;
+  void *y;
+  uint32_t codes_bytes, hi_bytes, scales_bytes, scales2_bytes, residual_bytes;
+  int n, k, steps, y_bf16;
+};
+
+// v + (v moved by one DPP pattern): quad permutations, half-row and row
+// mirrors, row broadcasts of lane 15 and lane 31 (rows without the mask bit
+// add zero).
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+  int r;
+  switch (ctrl_sel) {
+    case 0: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false); break;
+    case 1: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false); break;
+    case 3: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false); break;
+  }
+  return v + __builtin_bit_cast(float, r);
+}
+
+// Sums over each half-wave (lanes 0-31 and 32-63), returned uniform: DPP
+// quad, half-row and row mirrors give every lane its row's sum, and a row
+// broadcast adds row 0 into row 1 and row 2 into row 3.
+__device__ __forceinline__ void half_sums(float v, float &s0, float &s1) {
+  v = dpp_add(v, 0);  // quad_perm [1,0,3,2]
+  v = dpp_add(v, 1);  // quad_perm [2,3,0,1]
+  v = dpp_add(v, 2);  // row_half_mirror
+  v = dpp_add(v, 3);  // row_mirror
+  v = dpp_add(v, 4);  // row_bcast:15 into rows 1 and 3
+  s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+  s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+template <int FMT, int M, int U>
+__global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
+  using T = FmtTraits<FMT>;
+  using XL = XLayout<M>;
+  constexpr int kNS = T::kSums;
+  constexpr int kChunks = kStepK / 32;  // chunks per step
+  constexpr int kOut = 2 * M;           // outputs of one pair
+  extern __shared__ __align__(16) uint32_t smem[];
+  const int nch = a.k / 32;
+  uint32_t *xs = smem;                                      // [nch][XL::kStride]
+  float *xsum = (float *)(xs + (size_t)nch * XL::kStride);  // [M * kNS][nch]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, hf = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = a.steps;
+  const uint32_t k = (uint32_t)a.k;
+  // this wave's pairs gw, gw + W, ...: units = pairs x steps
+  const int W = gridDim.x * kWaves;
+  const int gw = blockIdx.x * kWaves + wave;
+  const int npairs = (a.n + 1) / 2;
+  const int mypairs = gw < npairs ? (npairs - 1 - gw) / W + 1 : 0;
+  const int units = mypairs * S;
+
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes, a.codes_bytes);
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.codes_hi, a.hi_bytes);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales, a.scales_bytes);
+  const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(a.scales2, a.scales2_bytes);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.residual, a.residual_bytes);
+
+  // per-lane constant parts of the load offsets (row 2p + hf, chunk c)
+  const uint32_t v_code = hf * (k / 2) + 16 * c;
+  const uint32_t v_scale = FMT == QMM_AFFINE4_G64 ? hf * (k / 16) + (c / 2) * 4
+                         : FMT == QMM_MXFP4 ? hf * (k / 32) + c
+                         : hf * (k / 16) + 2 * c;
+  const uint32_t v_hi = hf * (k / 4) + 8 * c;
+  const uint32_t v_d = (hf * (k / 256) + c / 8) * 2;
+  // output lane i = 2m + h writes row 2p + h of activation row m
+  const int o_h = lane & 1, o_m = min(lane >> 1, M - 1);
+  const uint32_t v_res = ((uint32_t)o_m * a.n + o_h) * 2;
+
+  // 1. the activations, first, so that they do not queue behind the codes
+  const int pieces = nch * 4 * M;
+  uint4 xv[kXPieces];
+#pragma unroll
+  for (int j = 0; j < kXPieces; ++j) {
+    const int i = min(j * kThreads + tid, pieces - 1);
+    const int ch = i / (4 * M), m = (i >> 2) % M, part_ = i & 3;
+    xv[j] = *(const uint4 *)(a.x + (size_t)m * a.k + ch * 32 + part_ * 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. the first U units of weights.  Every load is unconditional (a unit
+  //    past the wave's range re-reads its last one; the row past n of an odd
+  //    n and lanes past K read whatever the buffer holds there, or zeros
+  //    beyond its end, and their results are never used), so the compiler can
+  //    count outstanding loads exactly.
+  auto load_unit = [&](int j, int s, RowData &rd, uint32_t &res) {
+    if (j >= mypairs) {  // uniform
+      j = max(mypairs - 1, 0);
+      s = S - 1;
+    }
+    const uint32_t row0 = 2u * (uint32_t)(gw + j * W);
+    rd.q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+        rc, v_code, row0 * (k / 2) + (uint32_t)s * (kStepK / 2), 2));
+    if constexpr (FMT == QMM_AFFINE4_G64) {
+      rd.s = __builtin_amdgcn_raw_buffer_load_b32(
+          rs, v_scale, row0 * (k / 16) + (uint32_t)s * (kStepK / 16), 0);
+    } else if constexpr (FMT == QMM_MXFP4) {
+      rd.s = __builtin_amdgcn_raw_buffer_load_b8(
+          rs, v_scale, row0 * (k / 32) + (uint32_t)s * (kStepK / 32), 0);
+    } else {
+      rd.s = __builtin_amdgcn_raw_buffer_load_b16(
+          rs, v_scale, row0 * (k / 16) + (uint32_t)s * (kStepK / 16), 0);
+    }
+    if constexpr (FMT == QMM_Q6_K) {
+      rd.h = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+          rh, v_hi, row0 * (k / 4) + (uint32_t)s * (kStepK / 4), 2));
+      rd.d = __builtin_amdgcn_raw_buffer_load_b16(
+          rs2, v_d, (row0 * (k / 256) + (uint32_t)s * (kStepK / 256)) * 2, 0);
+    }
+    // a null residual has a zero-sized buffer, whose loads return 0
+    res = __builtin_amdgcn_raw_buffer_load_b16(rr, v_res, row0 * 2u, 0);
+  };
+
+  RowData buf[U];
+  uint32_t res[U];
+  int lj = 0, ls = 0;  // next unit to load: pair index, step
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    load_unit(lj, ls, buf[j], res[j]);
+    if (++ls == S) { ls = 0; ++lj; }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. stage x in LDS: pair order for the nibble-into-mantissa formats, and
+  //    the sums of x per 32 (affine) or 16 (Q6_K) values
+#pragma unroll
+  for (int j = 0; j < kXPieces; ++j) {
+    if (j * kThreads >= pieces) break;  // uniform
+    const int i = j * kThreads + tid;
+    const bool ok = i < pieces;
+    const int ch = i / (4 * M), m = (i >> 2) % M, part_ = i & 3;
+    const uint4 v = xv[j];
+    if constexpr (kNS > 0) {
+      float sm = ((bf_lo(v.x) + bf_hi(v.x)) + (bf_lo(v.y) + bf_hi(v.y))) +
+                 ((bf_lo(v.z) + bf_hi(v.z)) + (bf_lo(v.w) + bf_hi(v.w)));
+      sm += __shfl_xor(sm, 1);
+      if constexpr (kNS == 1) {
+        sm += __shfl_xor(sm, 2);
+        if (ok && part_ == 0) xsum[m * nch + ch] = sm;
+      } else {
+        if (ok && (part_ & 1) == 0) xsum[(m * 2 + (part_ >> 1)) * nch + ch] = sm;
+      }
+    }
+    if (ok) {
+      uint4 o = v;
+      if constexpr (T::kPermute) {
+        o.x = (v.x & 0xFFFFu) | (v.z << 16);
+        o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+        o.z = (v.y & 0xFFFFu) | (v.w << 16);
+        o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+      }
+      *(uint4 *)(xs + ch * XL::kStride + XL::slot(ch, m * 4 + part_) * 4) = o;
+    }
+  }
+  __syncthreads();
+
+  const UnpackK K = unpack_consts();
+  const float gscale = (FMT == QMM_NVFP4 && a.tensor_scale) ? a.tensor_scale[0] : 1.0f;
+  auto store = [&](int row, float v) {
+    if (a.y_bf16)
+      ((uint16_t *)a.y)[(size_t)o_m * a.n + row] = (uint16_t)float_to_bf16(v);
+    else
+      ((float *)a.y)[(size_t)o_m * a.n + row] = v;
+  };
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+
+  int cj = 0, cs = 0;  // unit being computed: pair index, step
+  for (int t0 = 0; t0 < units; t0 += U) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      if (t0 + j < units) {  // uniform
+        const int ch = cs * kChunks + c;
+        if (ch < nch) {
+          uint32_t X[M][16];
+          float Sx[M][2];
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint4 v = *(const uint4 *)(xs + ch * XL::kStride + XL::slot(ch, m * 4 + q) * 4);
+              X[m][4 * q + 0] = v.x;
+              X[m][4 * q + 1] = v.y;
+              X[m][4 * q + 2] = v.z;
+              X[m][4 * q + 3] = v.w;
+            }
+            Sx[m][0] = kNS > 0 ? xsum[(m * (kNS > 0 ? kNS : 1)) * nch + ch] : 0.0f;
+            Sx[m][1] = kNS > 1 ? xsum[(m * 2 + 1) * nch + ch] : 0.0f;
+          }
+          row_step<FMT, M>(buf[j], X, Sx, acc, K);
+        }
+        if (cs == S - 1) {  // the pair is complete
+          float out = 0.0f;
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            float s0, s1;
+            half_sums(acc[m], s0, s1);
+            acc[m] = 0.0f;
+            if (lane == 2 * m) out = s0;
+            if (lane == 2 * m + 1) out = s1;
+          }
+          const int row = 2 * (gw + cj * W) + o_h;
+          if (lane < kOut && row < a.n) store(row, out * gscale + bf_lo(res[j]));
+        }
+        if (++cs == S) { cs = 0; ++cj; }
+      }
+      load_unit(lj, ls, buf[j], res[j]);
+      if (++ls == S) { ls = 0; ++lj; }
+    }
+  }
+}
+
+template <int FMT, int M, int U>
+hipError_t launch_rows_cfg(const RowsArgs &a, size_t lds, int grid, hipStream_t s) {
+  // the dynamic LDS limit is raised once per device for each instantiation
+  static std::atomic<uint64_t> raised{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(raised.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void *)gemv_rows_kernel<FMT, M, U>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
+    if (e != hipSuccess) return e;
+    raised.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  hipLaunchKernelGGL((gemv_rows_kernel<FMT, M, U>), dim3(grid), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+#ifdef QMM_TUNE
+#define QMM_ROWS_CONFIGS(X) X(1) X(2) X(3) X(4) X(6)
+#else
+#define QMM_ROWS_CONFIGS(X) X(2) X(3)
+#endif
+
+template <int FMT, int M>
+hipError_t launch_rows_fm(const RowsArgs &a, const GemvPlan &p, hipStream_t s) {
+#define QMM_CASE(UU) \
+  if (p.depth == UU) return launch_rows_cfg<FMT, M, UU>(a, p.lds_bytes, p.tiles, s);
+  QMM_ROWS_CONFIGS(QMM_CASE)
+#undef QMM_CASE
+  return hipErrorInvalidConfiguration;
+}
+
+template <int FMT>
+hipError_t launch_rows_f(const RowsArgs &a, int m, const GemvPlan &p, hipStream_t s) {
+  switch (m) {
+    case 1: return launch_rows_fm<FMT, 1>(a, p, s);
+    case 2: return launch_rows_fm<FMT, 2>(a, p, s);
+    case 3: return launch_rows_fm<FMT, 3>(a, p, s);
+    default: return launch_rows_fm<FMT, 4>(a, p, s);
+  }
+}
+
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  int v = cached[dev & 63].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    return 0;
+  cached[dev & 63].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+}  // namespace
+
+size_t gemv_rows_lds(int format, int k, int m) {
+  const int pieces = m == 1 ? 4 : (m == 2 ? 8 : 16);
+  const int sums = format == QMM_AFFINE4_G64 ? 1 : (format == QMM_Q6_K ? 2 : 0);
+  const size_t nch = (size_t)k / 32;
+  return nch * pieces * 16 + nch * m * sums * 4;
+}
+
+bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p) {
+  // 3-4 activation rows measured faster with the split-K kernel, whose lanes
+  // reuse each activation load for more weights
+  if (m >= 3) {
+#ifdef QMM_TUNE
+    if (!getenv("QMM_ROWS_ANY_M"))
+#endif
+      return false;
+  }
+  const size_t lds = gemv_rows_lds(format, k, m);
+  if (lds > kLdsLimit || (size_t)k / 32 * 4 * m > (size_t)kXPieces * kThreads) return false;
+  const int cus = cu_count();
+  if (cus <= 0) return false;
+  p = GemvPlan{};
+  p.kind = 1;
+  // units of loads in flight per wave
+  p.rows_per_lane = 1;
+  p.depth = m == 1 ? 3 : 2;
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_ROWS_U")) p.depth = atoi(e);
+#endif
+  p.lanes_k = 32;
+  p.steps = (k + kStepK - 1) / kStepK;
+  p.tiles = cus;  // one workgroup per compute unit
+  p.splits = 1;
+  p.lds_bytes = lds;
+  (void)n;
+  return true;
+}
+
+hipError_t launch_gemv_rows(const qmm_weight &w, const void *x, int m, const void *residual,
+                            void *y, int y_dtype, const GemvPlan &p, hipStream_t s) {
+  RowsArgs a;
+  a.codes = (const uint8_t *)w.codes;
+  a.codes_hi = (const uint8_t *)w.codes_hi;
+  a.scales = (const uint8_t *)w.scales;
+  a.scales2 = (const uint8_t *)w.scales2;
+  a.tensor_scale = w.tensor_scale;
+  const size_t rows = (size_t)w.batch * w.n;
+  a.codes_bytes = (uint32_t)(rows * (size_t)(w.k / 2));
+  a.hi_bytes = w.codes_hi ? (uint32_t)(rows * (size_t)(w.k / 4)) : 0u;
+  a.scales_bytes = (uint32_t)(rows * (size_t)(w.k / (w.format == QMM_MXFP4 ? 32 : 16)));
+  a.scales2_bytes = w.scales2 ? (uint32_t)(rows * (size_t)(w.k / 256) * 2) : 0u;
+  a.residual_bytes = residual ? (uint32_t)((size_t)m * w.n * 2) : 0u;
+  a.x = (const uint16_t *)x;
+  a.residual = (const uint16_t *)residual;
+  a.y = y;
+  a.n = w.n;
+  a.k = w.k;
+  a.steps = p.steps;
+  a.y_bf16 = y_dtype == QMM_BF16;
+  switch (w.format) {
+    case QMM_AFFINE4_G64: return launch_rows_f<QMM_AFFINE4_G64>(a, m, p, s);
+    case QMM_MXFP4: return launch_rows_f<QMM_MXFP4>(a, m, p, s);
+    case QMM_NVFP4: return launch_rows_f<QMM_NVFP4>(a, m, p, s);
+    default: return launch_rows_f<QMM_Q6_K>(a, m, p, s);
+  }
+}
+
+}  // namespace qmm

@@ -1,0 +1,153 @@
+// Per-lane arithmetic shared by the two GEMV kernels: one row's 32 weights
+// (16 code bytes, plus their scales) against the matching 32 activations of
+// each of the M lanes, accumulated in float32.
+#pragma once
+
+#include "qmm_device.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+
+template <int FMT>
+struct FmtTraits {
+  // sums of x kept per 32-value chunk: affine 1 (per chunk), Q6_K 2 (per
+  // 16-value sub-block), E2M1 formats none.
+  static constexpr int kSums = FMT == QMM_AFFINE4_G64 ? 1 : (FMT == QMM_Q6_K ? 2 : 0);
+  // activations staged in (i, i+4) pair order for the nibble-into-mantissa
+  // unpack, natural pair order for the hardware FP4 conversion.
+  static constexpr bool kPermute = FMT == QMM_AFFINE4_G64 || FMT == QMM_Q6_K;
+  // K values per byte of the `scales` plane
+  static constexpr int kKPerScaleByte = FMT == QMM_MXFP4 ? 32 : 16;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// One row's data for one step.
+struct RowData {
+  uint4 q;      // 32 codes (Q6_K: low nibbles)
+  uint2 h;      // Q6_K high bits
+  uint32_t s;   // affine (scale, bias) / E8M0 / two E4M3 / two int8 sc
+  uint32_t d;   // Q6_K super-block scale
+};
+
+// The nibble-into-mantissa unpack: two 4-bit codes at bits 4p and 4p + 16 of
+// a word of eight become the bfloat16 pair (128 + q_p, 128 + q_{p+4}) by
+// landing in the low mantissa bits of 128.0 (0x4300), with no conversion
+// instruction.  Its constants are held in registers: gfx9 VOP3
+// instructions take no literal operand, so with the masks in an SGPR and the
+// bfloat16 128.0 pair in a VGPR each (v, v+4) pair is one v_and_or_b32 (plus
+// a shift) instead of a shift, an and and an or.
+struct UnpackK {
+  uint32_t lo;     // 0x000F000F
+  uint32_t hi;     // 0x00300030
+  uint32_t magic;  // 0x43004300: bfloat16 128.0 in both halves
+};
+
+__device__ __forceinline__ UnpackK unpack_consts() {
+  UnpackK k{0x000F000Fu, 0x00300030u, 0x43004300u};
+  asm volatile("" : "+s"(k.lo));
+  asm volatile("" : "+s"(k.hi));
+  asm volatile("" : "+v"(k.magic));
+  return k;
+}
+
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b) {
+  return (a & mask) | b;
+}
+
+// acc[m] += (this row's 32 weights of the chunk) . (x[m] chunk)
+template <int FMT, int M>
+__device__ __forceinline__ void row_step(const RowData &rd, const uint32_t (&X)[M][16],
+                                         const float (&S)[M][2], float (&acc)[M],
+                                         const UnpackK &K) {
+  const uint32_t w[4] = {rd.q.x, rd.q.y, rd.q.z, rd.q.w};
+  if constexpr (FMT == QMM_AFFINE4_G64) {
+    const float s = half_to_float(rd.s & 0xFFFFu), b = half_to_float(rd.s >> 16);
+    float d[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) d[m] = -128.0f * S[m][0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t p0 = and_or(w[j], K.lo, K.magic), p1 = and_or(w[j] >> 4, K.lo, K.magic);
+      const uint32_t p2 = and_or(w[j] >> 8, K.lo, K.magic), p3 = and_or(w[j] >> 12, K.lo, K.magic);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        d[m] = dot2(p0, X[m][4 * j + 0], d[m]);
+        d[m] = dot2(p1, X[m][4 * j + 1], d[m]);
+        d[m] = dot2(p2, X[m][4 * j + 2], d[m]);
+        d[m] = dot2(p3, X[m][4 * j + 3], d[m]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      acc[m] = __builtin_fmaf(s, d[m], acc[m]);
+      acc[m] = __builtin_fmaf(b, S[m][0], acc[m]);
+    }
+  } else if constexpr (FMT == QMM_MXFP4 || FMT == QMM_NVFP4) {
+    float d0[M], d1[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) d0[m] = d1[m] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t p0 = e2m1x2_to_bf16x2<0>(w[j]), p1 = e2m1x2_to_bf16x2<1>(w[j]);
+      const uint32_t p2 = e2m1x2_to_bf16x2<2>(w[j]), p3 = e2m1x2_to_bf16x2<3>(w[j]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float &d = (FMT == QMM_NVFP4 && j >= 2) ? d1[m] : d0[m];
+        d = dot2(p0, X[m][4 * j + 0], d);
+        d = dot2(p1, X[m][4 * j + 1], d);
+        d = dot2(p2, X[m][4 * j + 2], d);
+        d = dot2(p3, X[m][4 * j + 3], d);
+      }
+    }
+    if constexpr (FMT == QMM_MXFP4) {
+      const float sc = e8m0_to_float(rd.s);
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(sc, d0[m], acc[m]);
+    } else {
+      const float s0 = e4m3_to_float(rd.s & 0xFFu), s1 = e4m3_to_float(rd.s >> 8);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        acc[m] = __builtin_fmaf(s0, d0[m], acc[m]);
+        acc[m] = __builtin_fmaf(s1, d1[m], acc[m]);
+      }
+    }
+  } else {  // Q6_K
+    const float dd = half_to_float(rd.d);
+    const uint32_t hw[2] = {rd.h.x, rd.h.y};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t A = w[2 * j], B = w[2 * j + 1];
+      // high-bit bytes reordered to (values 0-3, 8-11, 4-7, 12-15) so that one
+      // shift puts the high bits of a (v, v+4) pair at bits 4-5 and 20-21.
+      const uint32_t H = __builtin_amdgcn_perm(hw[j], hw[j], 0x03010200u);
+      const uint32_t a0 = and_or(H << 4, K.hi, and_or(A, K.lo, K.magic));
+      const uint32_t a1 = and_or(H << 2, K.hi, and_or(A >> 4, K.lo, K.magic));
+      const uint32_t a2 = and_or(H, K.hi, and_or(A >> 8, K.lo, K.magic));
+      const uint32_t a3 = and_or(H >> 2, K.hi, and_or(A >> 12, K.lo, K.magic));
+      const uint32_t b0 = and_or(H >> 4, K.hi, and_or(B, K.lo, K.magic));
+      const uint32_t b1 = and_or(H >> 6, K.hi, and_or(B >> 4, K.lo, K.magic));
+      const uint32_t b2 = and_or(H >> 8, K.hi, and_or(B >> 8, K.lo, K.magic));
+      const uint32_t b3 = and_or(H >> 10, K.hi, and_or(B >> 12, K.lo, K.magic));
+      const float dsc = dd * (float)(int8_t)(rd.s >> (8 * j));
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float d = -160.0f * S[m][j];
+        d = dot2(a0, X[m][8 * j + 0], d);
+        d = dot2(a1, X[m][8 * j + 1], d);
+        d = dot2(a2, X[m][8 * j + 2], d);
+        d = dot2(a3, X[m][8 * j + 3], d);
+        d = dot2(b0, X[m][8 * j + 4], d);
+        d = dot2(b1, X[m][8 * j + 5], d);
+        d = dot2(b2, X[m][8 * j + 6], d);
+        d = dot2(b3, X[m][8 * j + 7], d);
+        acc[m] = __builtin_fmaf(dsc, d, acc[m]);
+      }
+    }
+  }
+}
+
+}  // namespace qmm

@@ -62,12 +62,4 @@ __device__ __forceinline__ uint32_t float_to_bf16(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Four 4-bit codes at bits 4i (i = p, p+4 within a 32-bit word of eight codes)
-// -> bfloat16 pair (128 + q_p, 128 + q_{p+4}): the nibble lands in the low
-// mantissa bits of 128.0 (0x4300), so no conversion instruction is needed.
-template <int P>
-__device__ __forceinline__ uint32_t nib_pair_128(uint32_t w) {
-  return ((w >> (4 * P)) & 0x000F000Fu) | 0x43004300u;
-}
-
 }  // namespace qmm

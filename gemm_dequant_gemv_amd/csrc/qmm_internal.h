@@ -20,11 +20,13 @@ constexpr int kGemvStep = 256;      // K values per step (8 lanes x 32)
 constexpr int kMaxSplitK = 2048;    // K values one workgroup covers at most
 
 struct GemvPlan {
-  int rows_per_lane;  // R
-  int depth;          // D: steps of weights in flight per lane
-  int lanes_k;        // LK: lanes sharing a row (each reads 16 bytes per step)
-  int steps;      // ceil(k / (32 * LK))
-  int tiles;      // ceil(n / rows per workgroup)
+  int kind;           // 0: split-K kernel, 1: row-streaming kernel
+  int rows_per_lane;  // R (row-streaming: rows per batch)
+  int depth;          // D: steps (row-streaming: units) of weights in flight per lane
+  int early;          // split-K: code loads issued before waiting for activations and scales
+  int lanes_k;        // lanes sharing a row (each reads 16 bytes per step)
+  int steps;      // steps per row
+  int tiles;      // split-K: ceil(n / rows per workgroup); row-streaming: workgroups
   int splits;     // K splits (workgroups per row tile)
   int max_steps;  // steps of the longest split
   size_t lds_bytes;
@@ -33,6 +35,8 @@ struct GemvPlan {
 };
 
 GemvPlan plan_gemv(int format, int n, int k, int m);
+bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p);
+size_t gemv_rows_lds(int format, int k, int m);
 
 // Prefill GEMM / grouped MoE tiles: rows of activations per workgroup.
 constexpr int kGemmBM = 128;
@@ -62,6 +66,8 @@ MoeLayout moe_layout(int num_experts, int t, int topk, int num_shared, int inter
 MoeTables moe_tables(const MoeLayout &L, void *ws);
 
 hipError_t launch_dequant(const qmm_weight &w, int out_dtype, void *out, hipStream_t s);
+hipError_t launch_gemv_rows(const qmm_weight &w, const void *x, int m, const void *residual,
+                            void *y, int y_dtype, const GemvPlan &p, hipStream_t s);
 hipError_t launch_gemv(const qmm_weight &w, const void *x, int m, const void *residual,
                        void *y, int y_dtype, void *workspace, const GemvPlan &p,
                        hipStream_t s);

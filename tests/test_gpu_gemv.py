@@ -98,9 +98,13 @@ def _check_tol(y, yref, mag):
                       f"{np.max(np.abs(y - yref) / mag):.3e} of mag")
 
 
-# shapes that span several 128-row tiles with a ragged last tile, ragged last
-# K step, K split over several workgroups (k >= 1024) or not (k <= 768)
-SHAPES = [(300, 896), (257, 2304), (128, 256), (1, 512), (515, 4096), (64, 6144), (40, 17408)]
+# Shapes with ragged row counts and ragged last K steps.  Up to K = 17408 the
+# activations fit in LDS and the row-streaming kernel runs for 1-2 rows (no
+# workspace); K = 81920 exceeds that at every M and takes the split-K kernel,
+# whose workgroups finish split rows through the workspace, as do 3-4 rows.
+SHAPES = [(300, 896), (257, 2304), (128, 256), (1, 512), (515, 4096), (64, 6144), (40, 17408),
+          (40, 81920)]
+SPLIT_K = 81920
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -113,6 +117,12 @@ def test_gemv_parity(fmt, m, shape):
     q = _q()
     p, x, r = _case(fmt, n, k, m, f"gv{fmt}{n}{k}", outliers=0.01, residual=(n % 2 == 1))
     w = q.Weight.from_host(p)
+    # the kernel choice shows in the workspace it asks for: split-K whenever
+    # the activations do not fit in LDS, row-streaming at least for 1-2 rows
+    if k == SPLIT_K:
+        assert q.gemv_workspace_size(w, m) > 0
+    elif m <= 2:
+        assert q.gemv_workspace_size(w, m) == 0
     y = q.gemv(w, _to_dev_bf16(x), None if r is None else _to_dev_bf16(r))
     yref, mag = oracle.gemv(p, x, r)
     _check_tol(y.cpu().numpy().astype(np.float64), yref, mag)
@@ -151,7 +161,7 @@ def _unit_scale_weight(fmt, n, k, seed):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m", [1, 4])
-@pytest.mark.parametrize("shape", [(300, 2048), (200, 17408), (129, 512)])
+@pytest.mark.parametrize("shape", [(300, 2048), (200, 17408), (129, 512), (40, SPLIT_K)])
 def test_gemv_exact_arithmetic_bit_exact(fmt, m, shape):
     """Unit scales and integer activations make every product and partial sum
     an exact float32, so any summation order must give the oracle's value."""
@@ -215,7 +225,7 @@ def test_gemv_deterministic(fmt):
 
 def test_workspace_left_zero_and_reused():
     q = _q()
-    p, x, _ = _case(F.AFFINE4_G64, 512, 8192, 2, "wsz")
+    p, x, _ = _case(F.AFFINE4_G64, 512, SPLIT_K, 2, "wsz")
     w = q.Weight.from_host(p)
     ws = q.new_workspace(q.gemv_workspace_size(w, 2))
     assert ws is not None
@@ -242,3 +252,40 @@ def test_error_codes_before_launch():
         with pytest.raises(q.QmmError) as e:
             q.gemv(w, xd, out=y, workspace=small)
         assert e.value.status == -6
+
+
+# The decode matvecs at full size, as the benchmark launches them: every
+# output is computed on the GPU, a sample of rows (spread over the matrix,
+# including both ends) is checked against the oracle.
+DECODE = [(F.AFFINE4_G64, 17408, 5120, False), (F.AFFINE4_G64, 5120, 17408, True),
+          (F.Q6_K, 17408, 5120, False), (F.Q6_K, 5120, 17408, True),
+          (F.MXFP4, 5120, 6144, False), (F.NVFP4, 5120, 5120, False)]
+
+
+@pytest.fixture(scope="module")
+def decode_weights():
+    cache = {}
+
+    def get(fmt, n, k):
+        if (fmt, n, k) not in cache:
+            cache[(fmt, n, k)] = quant.synthetic_weight(fmt, n, k, outlier_rate=0.01,
+                                                        name=f"full{fmt}/{n}x{k}")
+        return cache[(fmt, n, k)]
+    return get
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("case", DECODE)
+def test_gemv_decode_full_size_sampled(decode_weights, case, m):
+    fmt, n, k, res = case
+    q = _q()
+    p = decode_weights(fmt, n, k)
+    x = quant.synthetic_bf16(m, k, name=f"fullx{m}/{k}")
+    r = quant.synthetic_bf16(m, n, name=f"fullr{m}/{n}") if res else None
+    w = q.Weight.from_host(p)
+    y = q.gemv(w, _to_dev_bf16(x), None if r is None else _to_dev_bf16(r)).cpu().numpy()
+    rows = np.unique(np.concatenate([[0, 1, n - 2, n - 1],
+                                     rng.randint_bytes(7, f"rows{n}", 60, 0, 256).astype(np.int64)
+                                     * (n // 256) + 3]))
+    yref, mag = oracle.gemv(p, x, r, rows=rows)
+    _check_tol(y[:, rows].astype(np.float64), yref, mag)
