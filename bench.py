@@ -1,6 +1,7 @@
-"""Benchmark of the dequantizing GEMV hot path on one MI355X.
+"""Benchmark of the dequantizing matmul hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--sections decode,prefill,moe,fp4]
+    python bench.py --record-traffic FETCH.csv WRITE.csv   (no GPU work; see below)
 
 One step = one pass of the decode workload: every (format, shape, lanes)
 matvec of the decode configuration, each reading its own copy of the weights
@@ -12,13 +13,32 @@ so that no call finds its weights in the 256 MB Infinity Cache:
     inputs   weights N(0, 0.02) quantized, activations/residual N(0, 1) bf16
 
 value = weight bytes (codes + scales) read per step / step time, in GB/s.
+
+After the timed steps the other rows of the hot path are measured on their
+own configurations and reported under "sections" (each with its own unit):
+
+    prefill  X [M][5120] x W 17408 x 5120, affine4_g64 and nvfp4,
+             M in 128, 512, 2048, 8192 -> TFLOP/s (2 M N K per launch)
+    moe      512 routed + 1 shared expert, hidden 2048, intermediate 512,
+             nvfp4, top-10 of softmaxed N(0, 1) logits, T = 4 and 8192
+    fp4      mxfp4 and nvfp4 matvecs (1% outliers at 8x), 5120 x 5120,
+             5120 x 6144 and 248320 x 5120, M = 1..4 -> weight GB/s
+
 Prints one JSON line.  The oracle (CPU, float64) is timed on a bounded sample
-of the same workload for the cpu_baseline field.
+of the decode workload for the cpu_baseline field.
+
+--record-traffic turns two rocprofv3 counter CSVs (FETCH_SIZE, then
+WRITE_SIZE, each from `rocprofv3 --pmc <counter> --output-format csv -- python3
+bench.py --steps 2 --warmup 1 --no-cpu --sections decode`) into
+profiles/gemv_decode_traffic.json: HBM bytes per GEMV launch, calibrated by
+the same counters on the benchmark's own 1 GiB read and torch's 1 GiB fill.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -30,7 +50,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "dequant-GEMV weight GB/s (% of HBM peak) at M=1..4; prefill TFLOP/s"
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemv_decode_traffic.json")
+GEMV_SOURCES = ("gemv.hip", "gemv_rows.hip", "gemv_step.h", "qmm_device.h")
 
 
 def parse():
@@ -38,10 +61,19 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--sections", default="decode,prefill,moe,fp4")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     return ap.parse_args()
+
+
+def gemv_sources_sha():
+    h = hashlib.sha256()
+    for name in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "gemm_dequant_gemv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def decode_cases():
@@ -62,22 +94,36 @@ def algorithmic_bytes(w_bytes, c):
     return b
 
 
+def dev_bf16(torch, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def timed(torch, fn, reps, warm=2):
+    """Median and mean milliseconds of `fn` over `reps` launches, HIP events on
+    the current stream around each launch."""
+    for _ in range(warm):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    ts = [e0.elapsed_time(e1) for e0, e1 in ev]
+    return float(np.median(ts)), float(np.mean(ts))
+
+
 def measured_read_peak(q, torch, dev, gib=1.0, reps=10):
     """Achievable HBM read bandwidth: qbench_stream_read over a buffer far
-    larger than the caches, median of `reps` launches."""
+    larger than the caches, median of `reps` launches; then torch fills the
+    same buffer once (the write calibration of the traffic counters)."""
     buf = torch.empty(int(gib * 2**30) // 4, dtype=torch.int32, device=dev).fill_(1)
     sink = torch.zeros(64, dtype=torch.int32, device=dev)
     best = None
     for blocks in (256, 512):
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            q.bench_stream_read(buf, sink, blocks)
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        gbs = buf.numel() * 4 / (float(np.median(ts)) * 1e-3) / 1e9
+        med, _ = timed(torch, lambda: q.bench_stream_read(buf, sink, blocks), reps, warm=1)
+        gbs = buf.numel() * 4 / (med * 1e-3) / 1e9
         if best is None or gbs > best[0]:
             best = (gbs, blocks)
     del buf
@@ -88,20 +134,62 @@ def measured_read_peak(q, torch, dev, gib=1.0, reps=10):
 
 def traffic_from_profile():
     """HBM bytes per GEMV launch measured with rocprofv3 counters, if the
-    committed measurement was taken on the current kernel source."""
-    import hashlib
-    src = os.path.join(ROOT, "gemm_dequant_gemv_amd", "csrc", "gemv.hip")
-    prof = os.path.join(ROOT, "profiles", "gemv_decode_traffic.json")
-    if not os.path.exists(prof):
+    committed measurement was taken on the current kernel sources."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
-    with open(prof) as f:
+    with open(TRAFFIC_JSON) as f:
         rec = json.load(f)
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    return rec.get("hbm_bytes_per_launch") if rec.get("gemv_source_sha256") == sha else None
+    if rec.get("gemv_sources_sha256") != gemv_sources_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def record_traffic(fetch_csv, write_csv):
+    """Parse two rocprofv3 --pmc CSVs (KiB per dispatch) into the traffic record."""
+    def per_kernel(path, counter):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "")
+            name = name.split("(")[0].replace("qmm::", "")
+            out.setdefault(name, []).append(float(r["Counter_Value"]))
+        return {k: float(np.mean(v)) for k, v in out.items()}
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    gib_kib = 2**30 / 1024
+    read_k = [v for k, v in fetch.items() if k.startswith("stream_read_kernel")]
+    fill_k = [v for k, v in write.items() if "FillFunctor" in k or "fill" in k.lower()]
+    f_factor = gib_kib / max(read_k) if read_k else None
+    w_factor = gib_kib / max(fill_k) if fill_k else None
+    gemv = sorted(k for k in fetch if k.startswith("gemv"))
+    per = {k: {"FETCH_SIZE_KiB": round(fetch[k], 1), "WRITE_SIZE_KiB": round(write.get(k, 0.0), 1)}
+           for k in gemv}
+    tot = [fetch[k] * f_factor + write.get(k, 0.0) * w_factor for k in gemv]
+    rec = {
+        "gemv_sources_sha256": gemv_sources_sha(),
+        "hbm_bytes_per_launch": int(np.mean(tot) * 1024) if tot else None,
+        "fetch_factor": round(f_factor, 3) if f_factor else None,
+        "write_factor": round(w_factor, 3) if w_factor else None,
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o run -- python3 bench.py "
+            "--steps 2 --warmup 1 --no-cpu --sections decode",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out> -o run -- python3 bench.py "
+            "--steps 2 --warmup 1 --no-cpu --sections decode",
+            "python3 bench.py --record-traffic <fetch csv> <write csv>"],
+        "calibration": "FETCH_SIZE of stream_read_kernel over the bench's 1 GiB buffer and "
+                       "WRITE_SIZE of torch's fill of that buffer",
+        "per_kernel": per,
+    }
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def cpu_baseline(cases, seconds):
-    """The oracle as it stands, on sampled rows of the same matrices."""
+    """The oracle as it stands, on sampled rows of the same matrices: passes
+    over the decode cases, 1024 rows of each matrix per pass (a new row block
+    each pass), until `seconds` of oracle time have been spent."""
     import oracle
     from synth import quant
     try:
@@ -109,39 +197,133 @@ def cpu_baseline(cases, seconds):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = 1
-    t_total, bytes_total, rows_done = 0.0, 0, 0
-    rows = 256
-    t_start = time.perf_counter()
-    for c in cases:
-        if time.perf_counter() - t_start > seconds:
-            break
-        name = f"bench/{c['tag']}/{c['fmt']}"
-        p = quant.synthetic_weight(c["fmt"], rows, c["k"], name=name + "/cpu")
-        x = quant.synthetic_bf16(c["m"], c["k"], name=name + "/x")
-        r = quant.synthetic_bf16(c["m"], rows, name=name + "/r") if c["residual"] else None
-        t0 = time.perf_counter()
-        oracle.gemv(p, x, r)
-        t_total += time.perf_counter() - t0
-        bytes_total += p.nbytes()
-        rows_done += rows
+    t_total, bytes_total, rows_done, calls = 0.0, 0, 0, 0
+    rows = 1024
+    p_idx = 0
+    while t_total < seconds:
+        for c in cases:
+            name = f"bench/{c['tag']}/{c['fmt']}"
+            p = quant.synthetic_weight(c["fmt"], rows, c["k"], name=f"{name}/cpu{p_idx}")
+            x = quant.synthetic_bf16(c["m"], c["k"], name=name + "/x")
+            r = quant.synthetic_bf16(c["m"], rows, name=name + "/r") if c["residual"] else None
+            t0 = time.perf_counter()
+            oracle.gemv(p, x, r)
+            t_total += time.perf_counter() - t0
+            bytes_total += p.nbytes()
+            rows_done += rows
+            calls += 1
+            if t_total >= seconds:
+                break
+        p_idx += 1
     gbs = bytes_total / t_total / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{rows} rows of each decode matrix ({rows_done} rows, "
-                      f"{bytes_total / 1e6:.1f} MB of packed weights), float64 numpy oracle, "
-                      f"{t_total:.1f} s"}
+            "sample": f"{rows}-row blocks of the decode matrices ({calls} oracle calls, "
+                      f"{rows_done} rows, {bytes_total / 1e6:.1f} MB of packed weights), "
+                      f"float64 numpy oracle, {t_total:.1f} s of oracle time"}
+
+
+FMT_NAME = {1: "affine4_g64", 2: "mxfp4", 3: "nvfp4", 4: "q6_k"}
+
+
+def prefill_section(q, torch, dev):
+    from synth import formats as F
+    from synth import quant
+    out = []
+    n, k = 17408, 5120
+    for fmt in (F.AFFINE4_G64, F.NVFP4):
+        w = q.Weight.from_host(quant.synthetic_weight(fmt, n, k, name=f"bench/prefill/{fmt}"), dev)
+        for m in (128, 512, 2048, 8192):
+            x = dev_bf16(torch, quant.synthetic_bf16(m, k, name=f"bench/prefill/x{m}"), dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            call = q.prepare_gemm(w, x, y)
+            reps = 20 if m <= 512 else 8
+            med, _ = timed(torch, call, reps)
+            tf = 2.0 * m * n * k / (med * 1e-3) / 1e12
+            out.append({"format": FMT_NAME[fmt], "m": m, "shape": f"{n}x{k}", "ms": round(med, 4),
+                        "TFLOPs": round(tf, 1),
+                        "frac_bf16_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)})
+            del x, y, call
+        del w
+        torch.cuda.empty_cache()
+    big = [c for c in out if c["m"] >= 2048]
+    best = max(big, key=lambda c: c["TFLOPs"])
+    return {"unit": "TFLOP/s", "kernel": "gemm_kernel (LDS-staged dequant, bf16 MFMA)",
+            "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS, "best_at_M_ge_2048": best, "cases": out}
+
+
+def moe_section(q, torch, dev):
+    from synth import formats as F
+    from synth import quant, routing
+    E, S, H, I, topk = 512, 1, 2048, 512, 10
+    gu_p = quant.synthetic_weight(F.NVFP4, 2 * I, H, batch=E + S, name="bench/moe/gate_up")
+    dn_p = quant.synthetic_weight(F.NVFP4, H, I, batch=E + S, name="bench/moe/down")
+    gu, dn = q.Weight.from_host(gu_p, dev), q.Weight.from_host(dn_p, dev)
+    per_expert = (gu.nbytes() + dn.nbytes()) / (E + S)
+    out = []
+    for T, ydt in ((4, torch.float32), (8192, torch.bfloat16)):
+        x = dev_bf16(torch, quant.synthetic_bf16(T, H, name=f"bench/moe/x{T}"), dev)
+        ids, wts = routing.synthetic_routing(T, E, topk, name=f"bench/moe/r{T}")
+        y = torch.empty((T, H), dtype=ydt, device=dev)
+        call = q.prepare_moe(gu, dn, x, torch.from_numpy(ids).to(dev),
+                             torch.from_numpy(wts).to(dev), E, S, y)
+        med, _ = timed(torch, call, 20 if T == 4 else 8)
+        rows = T * (topk + S)
+        flops = 2.0 * rows * (2 * I * H + H * I)
+        active = len(np.unique(ids)) + S
+        c = {"tokens": T, "ms": round(med, 4), "rows": rows, "active_experts": int(active),
+             "TFLOPs": round(flops / (med * 1e-3) / 1e12, 2),
+             "active_weight_GBps": round(active * per_expert / (med * 1e-3) / 1e9, 1),
+             "y_dtype": "bf16" if ydt == torch.bfloat16 else "f32"}
+        out.append(c)
+        del x, y, call
+    return {"unit": "ms per layer", "launches_per_layer": 4,
+            "config": "512 routed + 1 shared experts, hidden 2048, intermediate 512, nvfp4, top-10",
+            "cases": out}
+
+
+def fp4_section(q, torch, dev):
+    from synth import formats as F
+    from synth import quant
+    out = []
+    for fmt in (F.MXFP4, F.NVFP4):
+        for n, k in ((5120, 5120), (5120, 6144), (248320, 5120)):
+            p = quant.synthetic_weight(fmt, n, k, outlier_rate=0.01, name=f"bench/fp4/{fmt}/{n}x{k}")
+            w0 = q.Weight.from_host(p, dev)
+            copies = max(2, int(np.ceil(1.0e9 / w0.nbytes())))
+            ws_ = [w0] + [q.Weight.from_host(p, dev) for _ in range(copies - 1)]
+            del p
+            for m in (1, 2, 3, 4):
+                x = dev_bf16(torch, quant.synthetic_bf16(m, k, name=f"bench/fp4/x{m}/{k}"), dev)
+                y = torch.empty((m, n), dtype=torch.float32, device=dev)
+                need = q.gemv_workspace_size(w0, m)
+                wsp = q.new_workspace(need, dev) if need else None
+                calls = [q.PreparedGemv(w, x, y, None, wsp) for w in ws_]
+                it = iter(range(1 << 30))
+                med, _ = timed(torch, lambda: calls[next(it) % copies](), 4 * copies if copies > 2 else 10)
+                gbs = w0.nbytes() / (med * 1e-3) / 1e9
+                out.append({"format": FMT_NAME[fmt], "shape": f"{n}x{k}", "m": m,
+                            "us": round(med * 1e3, 2), "weight_GBps": round(gbs, 1),
+                            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
+            del ws_, w0
+            torch.cuda.empty_cache()
+    return {"unit": "GB/s", "cases": out}
 
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); the sharded path "
-              "is described in DESIGN.md and not launched.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); how the path would "
+              "shard is described in DESIGN.md, and no multi-GPU run is made.", file=sys.stderr)
         sys.exit(2)
     import torch
 
     import gemm_dequant_gemv_amd as q
     from synth import quant
 
+    sections = set(s for s in args.sections.split(",") if s)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     cases = decode_cases()
@@ -151,16 +333,14 @@ def main():
         name = f"bench/{c['tag']}/{c['fmt']}"
         p = quant.synthetic_weight(c["fmt"], c["n"], c["k"], name=f"{name}/W{c['m']}")
         w = q.Weight.from_host(p, dev)
-        x = torch.from_numpy(quant.synthetic_bf16(c["m"], c["k"], name=name + "/x").view(np.int16)
-                             ).view(torch.bfloat16).to(dev)
-        r = None
-        if c["residual"]:
-            r = torch.from_numpy(quant.synthetic_bf16(c["m"], c["n"], name=name + "/r")
-                                 .view(np.int16)).view(torch.bfloat16).to(dev)
+        x = dev_bf16(torch, quant.synthetic_bf16(c["m"], c["k"], name=name + "/x"), dev)
+        r = dev_bf16(torch, quant.synthetic_bf16(c["m"], c["n"], name=name + "/r"), dev) \
+            if c["residual"] else None
         y = torch.empty((c["m"], c["n"]), dtype=torch.float32, device=dev)
-        ws = q.new_workspace(q.gemv_workspace_size(w, c["m"]), dev)
+        need = q.gemv_workspace_size(w, c["m"])
+        ws = q.new_workspace(need, dev) if need else None
         call = q.PreparedGemv(w, x, y, r, ws)
-        setup.append((c, w, x, r, y, ws, w.nbytes(), call))
+        setup.append((c, w, w.nbytes(), call))
     torch.cuda.synchronize()
 
     def step(events=None):
@@ -169,7 +349,7 @@ def main():
         for i, item in enumerate(setup):
             if events is not None:
                 events[i][0].record()
-            item[7]()
+            item[3]()
             if events is not None:
                 events[i][1].record()
 
@@ -190,22 +370,30 @@ def main():
 
     per_case = []
     tot_w, tot_alg, tot_kt = 0, 0, 0.0
-    for i, (c, w, x, r, y, ws, wb, _) in enumerate(setup):
+    for i, (c, w, wb, _) in enumerate(setup):
         ts = [evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]
         med = float(np.median(ts))
-        mean = float(np.mean(ts))
         alg = algorithmic_bytes(wb, c)
         tot_w += wb * args.steps
         tot_alg += alg * args.steps
         tot_kt += sum(ts)
-        per_case.append({"format": {1: "affine4_g64", 4: "q6_k"}[c["fmt"]],
-                         "shape": f"{c['n']}x{c['k']}", "m": c["m"], "residual": c["residual"],
-                         "us_median": round(med * 1e3, 2),
+        per_case.append({"format": FMT_NAME[c["fmt"]], "shape": f"{c['n']}x{c['k']}", "m": c["m"],
+                         "residual": c["residual"], "us_median": round(med * 1e3, 2),
                          "weight_GBps": round(wb / (med * 1e-3) / 1e9, 1),
                          "pct_hbm_peak": round(100 * wb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)})
     step_s = wall / args.steps
     value = tot_w / args.steps / step_s / 1e9
     achieved = tot_alg / (tot_kt * 1e-3) / 1e9
+    del setup
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if "prefill" in sections:
+        extra["prefill"] = prefill_section(q, torch, dev)
+    if "moe" in sections:
+        extra["moe"] = moe_section(q, torch, dev)
+    if "fp4" in sections:
+        extra["fp4"] = fp4_section(q, torch, dev)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -214,17 +402,18 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "decode matvecs, affine4_g64 and q6_k, 17408x5120 and "
                                "5120x17408 (+bf16 residual), M=1,2,4, cold weights",
-                   "calls_per_step": len(setup),
+                   "calls_per_step": len(cases),
                    "weight_bytes_per_step": tot_w // args.steps},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(),
-                     "kernel": "gemv_kernel (all instances of the step)",
-                     "algorithmic_bytes_per_launch": int(tot_alg / (args.steps * len(setup))),
-                     "mean_launch_us": round(tot_kt / (args.steps * len(setup)) * 1e3, 2),
+                     "kernel": "qgemv kernels (gemv_rows_kernel for M=1,2; gemv_kernel for M=4)",
+                     "algorithmic_bytes_per_launch": int(tot_alg / (args.steps * len(cases))),
+                     "mean_launch_us": round(tot_kt / (args.steps * len(cases)) * 1e3, 2),
                      "measured_read_peak": read_peak,
                      "frac_of_measured_read_peak": round(achieved / read_peak["GBps"], 4)},
         "detail": per_case,
+        "sections": extra,
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds)

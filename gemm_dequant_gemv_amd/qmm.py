@@ -245,3 +245,41 @@ class PreparedGemv:
         st = self._fn(*self._args)
         if st:
             raise QmmError(st, "qgemv")
+
+
+class _Prepared:
+    """A library call with every argument marshalled once (benchmarks, decode
+    loops); calling it launches on the stream given at construction."""
+
+    def __init__(self, name, args, keep):
+        self._fn = getattr(_lib(), name)
+        self._name = name
+        self._args = args
+        self._keep = keep  # tensors the raw pointers refer to
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            raise QmmError(st, self._name)
+
+
+def prepare_gemm(w: Weight, x, out, residual=None, stream=None):
+    m = x.shape[0]
+    need = int(_lib().qgemm_workspace_size(w.c, m))
+    ws = new_workspace(need, x.device) if need else None
+    ws_bytes = 0 if ws is None else ws.numel()
+    return _Prepared("qgemm", (w.c, _ptr(x), m, _ptr(residual), _ptr(out), _ptr(ws), ws_bytes,
+                               _stream(stream)), (w, x, out, residual, ws))
+
+
+def prepare_moe(gate_up: Weight, down: Weight, x, topk_ids, topk_w, num_routed: int,
+                num_shared: int, out, shared_w=None, stream=None):
+    t, topk = topk_ids.shape
+    need = moe_workspace_size(gate_up, down, num_routed, num_shared, t, topk)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    dt = F32 if out.dtype == torch.float32 else BF16
+    return _Prepared("qmoe_grouped",
+                     (gate_up.c, down.c, num_routed, num_shared, _ptr(x), t, _ptr(topk_ids),
+                      _ptr(topk_w), topk, _ptr(shared_w), _ptr(out), dt, _ptr(ws), ws.numel(),
+                      _stream(stream)),
+                     (gate_up, down, x, topk_ids, topk_w, out, shared_w, ws))
