@@ -150,4 +150,45 @@ __device__ __forceinline__ void row_step(const RowData &rd, const uint32_t (&X)[
   }
 }
 
+// v + (v moved by one DPP pattern): quad permutations, half-row and row
+// mirrors, row broadcasts of lane 15 and lane 31 (rows without the mask bit
+// add zero).
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+  int r;
+  switch (ctrl_sel) {
+    case 0: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false); break;
+    case 1: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false); break;
+    case 3: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false); break;
+  }
+  return v + __builtin_bit_cast(float, r);
+}
+
+// Sums over each quarter-wave (16-lane DPP row), returned uniform: the quad,
+// half-row and row mirrors give every lane its row's sum.
+__device__ __forceinline__ void quarter_sums(float v, float (&s)[4]) {
+  v = dpp_add(v, 0);  // quad_perm [1,0,3,2]
+  v = dpp_add(v, 1);  // quad_perm [2,3,0,1]
+  v = dpp_add(v, 2);  // row_half_mirror
+  v = dpp_add(v, 3);  // row_mirror
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    s[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16 * r + 15));
+}
+
+// Sums over each half-wave (lanes 0-31 and 32-63), returned uniform: DPP
+// quad, half-row and row mirrors give every lane its row's sum, and a row
+// broadcast adds row 0 into row 1 and row 2 into row 3.
+__device__ __forceinline__ void half_sums(float v, float &s0, float &s1) {
+  v = dpp_add(v, 0);  // quad_perm [1,0,3,2]
+  v = dpp_add(v, 1);  // quad_perm [2,3,0,1]
+  v = dpp_add(v, 2);  // row_half_mirror
+  v = dpp_add(v, 3);  // row_mirror
+  v = dpp_add(v, 4);  // row_bcast:15 into rows 1 and 3
+  s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+  s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 }  // namespace qmm

@@ -1,5 +1,7 @@
 // qmoe_grouped: one mixture-of-experts layer (routed experts plus optional
-// shared experts) as grouped per-expert multiplies ("TurboEXL3" section 4.1):
+// shared experts).  Up to 4 tokens take the decode form (grouped GEMV over the
+// token slots, moe_gemv.hip, then the combine below); more tokens take the
+// grouped-GEMM form ("TurboEXL3" section 4.1):
 //   1. route:    one launch counts each expert's tokens, groups the token slots
 //                by expert and builds the table of row tiles (replacing a sort
 //                and a separate table pass);
@@ -13,6 +15,8 @@
 // one expert's group comes from LDS atomics and is not fixed, but every row is
 // computed independently of its neighbours and the combine reads rows by slot,
 // so the layer's output is the same on every run.
+#include <cstdlib>
+
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
@@ -138,28 +142,74 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
 struct CombineArgs {
   const float *topk_w;
   const float *shared_w;
-  int t, topk, num_shared, h;
+  const int32_t *topk_ids;  // slot-order rows only
+  int t, topk, num_routed, num_shared, h;
+  int slot_rows;            // 1: d row = slot (decode form), 0: the grouping tables
   MoeTables tb;
   void *y;
   int y_bf16;
 };
 
-// y[t][n] = sum_j w[t][j] d[row(t, j)][n] + sum_s ws[t] d[row_s(t)][n], fixed order
+// y[t][n] = sum_j w[t][j] d[row(t, j)][n] + sum_s ws[t] d[row_s(t)][n], fixed order.
+// A block serves one token: the token's rows and weights go to LDS in chunks
+// of 64 slots, then each thread issues its d loads 8 at a time before adding
+// them, so that no load waits for the previous one.
 __global__ __launch_bounds__(256) void moe_combine_kernel(CombineArgs a) {
+  constexpr int kChunk = 64, kBatch = 8;
+  __shared__ uint32_t s_row[kChunk];
+  __shared__ float s_w[kChunk];
   const int t = blockIdx.x;
   const int n = blockIdx.y * 256 + threadIdx.x;
-  if (n >= a.h) return;
+  if (a.slot_rows && t == 0 && blockIdx.y == 0) {
+    // the decode form has no routing pass: report dropped ids here
+    int bad = 0;
+    for (int i = threadIdx.x; i < a.t * a.topk; i += 256)
+      bad |= (a.topk_ids[i] < 0 || a.topk_ids[i] >= a.num_routed) ? 1 : 0;
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) *a.tb.err = bad ? 1u : 0u;
+  }
+  const int total = a.topk + a.num_shared;
+  const int nn = min(n, a.h - 1);
   float acc = 0.0f;
-  for (int j = 0; j < a.topk; ++j) {
-    const uint32_t row = a.tb.row_of_slot[(size_t)t * a.topk + j];
-    if (row == kInvalidRow) continue;
-    acc = __builtin_fmaf(a.topk_w[(size_t)t * a.topk + j], a.tb.d[(size_t)row * a.h + n], acc);
+  for (int c0 = 0; c0 < total; c0 += kChunk) {
+    const int cnt = min(kChunk, total - c0);
+    __syncthreads();  // the previous chunk is consumed
+    if ((int)threadIdx.x < cnt) {
+      const int j = c0 + threadIdx.x;
+      uint32_t row;
+      float w;
+      if (j < a.topk) {
+        const int slot = t * a.topk + j;
+        if (a.slot_rows) {
+          const int e = a.topk_ids[slot];
+          row = (e < 0 || e >= a.num_routed) ? kInvalidRow : (uint32_t)slot;
+        } else {
+          row = a.tb.row_of_slot[slot];
+        }
+        w = a.topk_w[slot];
+      } else {
+        const int sh = j - a.topk;
+        row = a.slot_rows ? (uint32_t)(a.t * a.topk + sh * a.t + t)
+                          : a.tb.row_of_shared[(size_t)sh * a.t + t];
+        w = a.shared_w ? a.shared_w[t] : 1.0f;
+      }
+      s_row[threadIdx.x] = row;
+      s_w[threadIdx.x] = w;
+    }
+    __syncthreads();
+    for (int j0 = 0; j0 < cnt; j0 += kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t r = j0 + u < cnt ? s_row[j0 + u] : kInvalidRow;
+        v[u] = a.tb.d[(size_t)(r == kInvalidRow ? 0u : r) * a.h + nn];
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (j0 + u < cnt && s_row[j0 + u] != kInvalidRow) acc = __builtin_fmaf(s_w[j0 + u], v[u], acc);
+    }
   }
-  for (int s = 0; s < a.num_shared; ++s) {
-    const uint32_t row = a.tb.row_of_shared[(size_t)s * a.t + t];
-    const float ws = a.shared_w ? a.shared_w[t] : 1.0f;
-    acc = __builtin_fmaf(ws, a.tb.d[(size_t)row * a.h + n], acc);
-  }
+  if (n >= a.h) return;
   if (a.y_bf16)
     ((uint16_t *)a.y)[(size_t)t * a.h + n] = (uint16_t)float_to_bf16(acc);
   else
@@ -213,24 +263,37 @@ MoeTables moe_tables(const MoeLayout &L, void *ws) {
   return t;
 }
 
+bool moe_uses_gemv(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_shared) {
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_MOE_GEMV")) return atoi(e) != 0 && moe_gemv_fits(gu, dn, t, topk, num_shared);
+#endif
+  return moe_gemv_fits(gu, dn, t, topk, num_shared);
+}
+
 hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed, int num_shared,
                       const void *x, int t, const int32_t *topk_ids, const float *topk_w,
                       int topk, const float *shared_w, void *y, int y_dtype, void *workspace,
                       hipStream_t s) {
   const MoeLayout L = moe_layout(num_routed + num_shared, t, topk, num_shared, gu.n / 2, dn.n);
   const MoeTables tb = moe_tables(L, workspace);
+  const bool slot_rows = moe_uses_gemv(gu, dn, t, topk, num_shared);
+  hipError_t e;
+  if (slot_rows) {
+    e = launch_moe_gemv(gu, dn, num_routed, num_shared, x, t, topk_ids, topk, tb, s);
+    if (e != hipSuccess) return e;
+  } else {
+    RouteArgs ra{topk_ids, t, topk, num_routed, num_shared, tb};
+    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ra);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_moe_gemm_gate_up(gu, x, tb, (int)L.max_tiles, s);
+    if (e != hipSuccess) return e;
+    e = launch_moe_gemm_down(dn, tb, (int)L.max_tiles, s);
+    if (e != hipSuccess) return e;
+  }
 
-  RouteArgs ra{topk_ids, t, topk, num_routed, num_shared, tb};
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ra);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  e = launch_moe_gemm_gate_up(gu, x, tb, (int)L.max_tiles, s);
-  if (e != hipSuccess) return e;
-  e = launch_moe_gemm_down(dn, tb, (int)L.max_tiles, s);
-  if (e != hipSuccess) return e;
-
-  CombineArgs ca{topk_w, shared_w, t, topk, num_shared, dn.n, tb, y, y_dtype == QMM_BF16};
+  CombineArgs ca{topk_w, shared_w, topk_ids, t, topk, num_routed, num_shared, dn.n,
+                 slot_rows ? 1 : 0, tb, y, y_dtype == QMM_BF16};
   hipLaunchKernelGGL(moe_combine_kernel, dim3(t, (dn.n + 255) / 256), dim3(256), 0, s, ca);
   return hipGetLastError();
 }

@@ -1,0 +1,408 @@
+// qmoe_grouped for decode (1-4 tokens): the expert multiplies as one grouped
+// GEMV launch per projection ("TurboEXL3" section 3.1: decode passes 1 to 4
+// tokens, and a layer's work must not split into many small dependent
+// launches; section 4.3: few rows take the GEMV form).
+//
+// With so few tokens nearly every active expert serves one row, so row tiles
+// of an MFMA GEMM would be almost empty.  Instead every token slot (routed
+// slots in list order, then the shared experts' slots) is its own matrix-
+// vector product, streamed like the row-streaming qgemv kernel:
+//   * gate/up: a unit is one 1024-value step of the row pair (gate i, up I+i)
+//     of the slot's expert, one row per half-wave, against the slot's token;
+//     after the pair's last step the two half-wave sums are g and u, and one
+//     lane writes h = silu(g) * u (float32, then bfloat16);
+//   * down: a unit is the row quad (4p .. 4p+3) of the slot's down matrix,
+//     one row per quarter-wave (a quarter-wave covers 512 values, the whole
+//     intermediate width at I = 512), against the slot's h; the four sums go
+//     to d [slot][H] in float32.
+// The grouped rows are the slots themselves (no routing pass): h and d row s
+// belong to slot s, a shared expert's rows follow all routed slots.  The
+// combine launch then adds each token's rows in a fixed order.  Slots whose
+// expert id is outside [0, E) are skipped (their rows are never read).
+#include <algorithm>
+#include <atomic>
+#include <cstdlib>
+
+#include "gemv_step.h"
+
+namespace qmm {
+namespace {
+
+constexpr size_t kLdsLimit = 160 * 1024 - 6144;  // dynamic part; the static tables take 4 KB
+
+struct MoeGemvArgs {
+  const uint8_t *codes, *codes_hi, *scales, *scales2;
+  const float *tensor_scale;
+  uint32_t codes_bytes, hi_bytes, scales_bytes, scales2_bytes;
+  int k;            // reduction length: H (gate/up) or I (down)
+  int rows;         // rows of one expert's matrix: 2I or H
+  int pairs;        // row groups per slot: I (gate/up pairs) or H / 4 (down quads)
+  int half_rows;    // rows between the lane groups of a row group: I or 1
+  int pair_step;    // rows between consecutive row groups: 1 or 4
+  int steps;        // ceil(k / step values)
+  const int32_t *topk_ids;
+  int t, topk, num_routed, num_shared;
+  const uint16_t *src;  // vectors staged in LDS: x [t][H] or h [slots][I]
+  int nsrc;
+  uint16_t *h;      // gate/up output [slots][I]
+  float *d;         // down output [slots][H]
+};
+
+// LDS layout of the staged vectors: chunk ch (32 values) of vector l at u32
+// offset ch * stride + 16 l, stride = 16 nsrc + 4 (the pad spreads the chunks
+// of one ds_read over the banks); then the sums of x per chunk (affine) or
+// per 16 values (Q6_K), [l][sub][nch].
+__host__ __device__ inline size_t moe_gemv_stride(int nsrc) { return 16 * (size_t)nsrc + 4; }
+
+template <bool DOWN>
+struct MoeShape {
+  static constexpr int kGroups = DOWN ? 4 : 2;      // rows per unit, one per lane group
+  static constexpr int kLanes = 64 / kGroups;       // lanes per row
+  static constexpr int kStepK = 32 * kLanes;        // values per row per step
+};
+
+template <int FMT, bool DOWN, int U, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
+  constexpr int kThreads = 64 * WAVES;
+  using SH = MoeShape<DOWN>;
+  constexpr int kStepK = SH::kStepK;
+  using T = FmtTraits<FMT>;
+  constexpr int kNS = T::kSums;
+  extern __shared__ __align__(16) uint32_t smem[];
+  __shared__ int s_expert[kMoeGemvMaxSlots];  // expert of each slot, -1 if dropped
+  __shared__ int s_vec[kMoeGemvMaxSlots];     // staged vector of each slot
+  const int nch = a.k / 32;
+  const int stride = (int)moe_gemv_stride(a.nsrc);
+  uint32_t *xs = smem;
+  float *xsum = (float *)(xs + (size_t)nch * stride);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, hf = lane / SH::kLanes, c = lane % SH::kLanes;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = a.steps;
+  const uint32_t k = (uint32_t)a.k;
+  const int routed = a.t * a.topk;
+  const int slots = routed + a.t * a.num_shared;
+  const int items = slots * a.pairs;
+  const int W = gridDim.x * WAVES;
+  const int gw = blockIdx.x * WAVES + wave;
+  const int myitems = gw < items ? (items - 1 - gw) / W + 1 : 0;
+  const int units = myitems * S;
+  const int last_item = myitems > 0 ? gw + (myitems - 1) * W : gw;
+  const int s_last = last_item / a.pairs, p_last = last_item - (last_item / a.pairs) * a.pairs;
+
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes, a.codes_bytes);
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.codes_hi, a.hi_bytes);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales, a.scales_bytes);
+  const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(a.scales2, a.scales2_bytes);
+  const uint32_t hr = (uint32_t)(hf * a.half_rows);
+  const uint32_t v_code = hr * (k / 2) + 16 * c;
+  const uint32_t v_scale = FMT == QMM_AFFINE4_G64 ? hr * (k / 16) + (c / 2) * 4
+                         : FMT == QMM_MXFP4 ? hr * (k / 32) + c
+                         : hr * (k / 16) + 2 * c;
+  const uint32_t v_hi = hr * (k / 4) + 8 * c;
+  const uint32_t v_d = (hr * (k / 256) + c / 8) * 2;
+
+  // slot -> expert (-1 for an id outside [0, E)) and staged vector
+  auto slot_expert = [&](int s) {
+    if (s < routed) {
+      const int e = a.topk_ids[s];
+      return (e < 0 || e >= a.num_routed) ? -1 : e;
+    }
+    return a.num_routed + (s - routed) / a.t;
+  };
+  auto slot_vector = [&](int s) {
+    return DOWN ? s : (s < routed ? s / a.topk : (s - routed) % a.t);
+  };
+
+  // 1. the first units' weights, then the staged vectors.  The expert of a
+  //    unit comes from global memory for these first units and from the LDS
+  //    table afterwards, so that no later weight load waits for a scalar
+  //    load of the routing ids.
+  // Items advance by W: (slot, pair) moves by (W / pairs, W % pairs), so the
+  //    walk needs no division per unit.
+  const int sW = W / a.pairs, pW = W - (W / a.pairs) * a.pairs;
+  const int s_first = gw / a.pairs, p_first = gw - (gw / a.pairs) * a.pairs;
+  auto advance = [&](int &s, int &p) {
+    s += sW;
+    p += pW;
+    if (p >= a.pairs) { p -= a.pairs; ++s; }
+  };
+  auto load_unit = [&](int j, int s, int p, int s_step, RowData &rd, bool from_lds) {
+    if (j >= myitems) {  // uniform: re-read the wave's last unit (or its first item)
+      s = s_last;
+      p = p_last;
+      s_step = S - 1;
+    }
+    s = min(s, slots - 1);
+    const int e = max(from_lds ? s_expert[s] : slot_expert(s), 0);
+    const uint32_t row0 = (uint32_t)(e * a.rows + p * a.pair_step);
+    rd.q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+        rc, v_code, row0 * (k / 2) + (uint32_t)s_step * (kStepK / 2), 2));
+    if constexpr (FMT == QMM_AFFINE4_G64) {
+      rd.s = __builtin_amdgcn_raw_buffer_load_b32(
+          rs, v_scale, row0 * (k / 16) + (uint32_t)s_step * (kStepK / 16), 0);
+    } else if constexpr (FMT == QMM_MXFP4) {
+      rd.s = __builtin_amdgcn_raw_buffer_load_b8(
+          rs, v_scale, row0 * (k / 32) + (uint32_t)s_step * (kStepK / 32), 0);
+    } else {
+      rd.s = __builtin_amdgcn_raw_buffer_load_b16(
+          rs, v_scale, row0 * (k / 16) + (uint32_t)s_step * (kStepK / 16), 0);
+    }
+    if constexpr (FMT == QMM_Q6_K) {
+      rd.h = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+          rh, v_hi, row0 * (k / 4) + (uint32_t)s_step * (kStepK / 4), 2));
+      rd.d = __builtin_amdgcn_raw_buffer_load_b16(
+          rs2, v_d, (row0 * (k / 256) + (uint32_t)s_step * (kStepK / 256)) * 2, 0);
+    }
+  };
+  RowData buf[U];
+  int lj = 0, ls = 0, l_s = s_first, l_p = p_first;  // next unit to load
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    load_unit(lj, l_s, l_p, ls, buf[j], false);
+    if (++ls == S) { ls = 0; ++lj; advance(l_s, l_p); }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  for (int i = tid; i < slots; i += kThreads) {
+    s_expert[i] = slot_expert(i);
+    s_vec[i] = slot_vector(i);
+  }
+
+  const int pieces = a.nsrc * nch * 4;  // 16-byte pieces, [vector][chunk][part]
+  constexpr int XP = 4;                  // pieces per thread in flight
+  for (int i0 = 0; i0 < pieces; i0 += XP * kThreads) {  // uniform trip count
+    uint4 xv[XP];
+#pragma unroll
+    for (int u = 0; u < XP; ++u) {
+      const int i = min(i0 + u * kThreads + tid, pieces - 1);
+      const int l = i / (nch * 4), ch = (i / 4) % nch, part = i & 3;
+      xv[u] = *(const uint4 *)(a.src + (size_t)l * a.k + ch * 32 + part * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < XP; ++u) {
+      const bool ok = i0 + u * kThreads + tid < pieces;
+      const int i = min(i0 + u * kThreads + tid, pieces - 1);
+      const int l = i / (nch * 4), ch = (i / 4) % nch, part = i & 3;
+      const uint4 v = xv[u];
+      if constexpr (kNS > 0) {
+        float sm = ((bf_lo(v.x) + bf_hi(v.x)) + (bf_lo(v.y) + bf_hi(v.y))) +
+                   ((bf_lo(v.z) + bf_hi(v.z)) + (bf_lo(v.w) + bf_hi(v.w)));
+        sm += __shfl_xor(sm, 1);
+        if constexpr (kNS == 1) {
+          sm += __shfl_xor(sm, 2);
+          if (ok && part == 0) xsum[l * nch + ch] = sm;
+        } else {
+          if (ok && (part & 1) == 0) xsum[(l * 2 + (part >> 1)) * nch + ch] = sm;
+        }
+      }
+      if (ok) {
+        uint4 o = v;
+        if constexpr (T::kPermute) {
+          o.x = (v.x & 0xFFFFu) | (v.z << 16);
+          o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+          o.z = (v.y & 0xFFFFu) | (v.w << 16);
+          o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+        }
+        *(uint4 *)(xs + ch * stride + l * 16 + part * 4) = o;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. the units: unit (item j, step) of this wave
+  const UnpackK K = unpack_consts();
+  float acc[1] = {0.0f};
+  int cs = 0, c_s = s_first, c_p = p_first;  // unit being computed
+  for (int t0 = 0; t0 < units; t0 += U) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      if (t0 + j < units) {  // uniform
+        const int s = c_s, p = c_p;
+        const int e = s_expert[s], l = s_vec[s];
+        const int ch = cs * SH::kLanes + c;
+        if (ch < nch) {
+          uint32_t X[1][16];
+          float Sx[1][2];
+          const uint4 *src = (const uint4 *)(xs + ch * stride + l * 16);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 v = src[q];
+            X[0][4 * q + 0] = v.x;
+            X[0][4 * q + 1] = v.y;
+            X[0][4 * q + 2] = v.z;
+            X[0][4 * q + 3] = v.w;
+          }
+          Sx[0][0] = kNS > 0 ? xsum[(l * (kNS > 0 ? kNS : 1)) * nch + ch] : 0.0f;
+          Sx[0][1] = kNS > 1 ? xsum[(l * 2 + 1) * nch + ch] : 0.0f;
+          row_step<FMT, 1>(buf[j], X, Sx, acc, K);
+        }
+        if (cs == S - 1) {  // the item's rows are complete
+          const float g = (FMT == QMM_NVFP4 && a.tensor_scale && e >= 0) ? a.tensor_scale[e] : 1.0f;
+          if constexpr (!DOWN) {
+            float s0, s1;
+            half_sums(acc[0], s0, s1);
+            if (e >= 0 && lane == 0) {
+              const float gv = s0 * g, uv = s1 * g;
+              const float hv = gv / (1.0f + expf(-gv)) * uv;
+              a.h[(size_t)s * a.pairs + p] = (uint16_t)float_to_bf16(hv);
+            }
+          } else {
+            float q4[4];
+            quarter_sums(acc[0], q4);
+            const float v = lane == 0 ? q4[0] : lane == 1 ? q4[1] : lane == 2 ? q4[2] : q4[3];
+            if (e >= 0 && lane < 4) a.d[(size_t)s * a.rows + 4 * p + lane] = v * g;
+          }
+          acc[0] = 0.0f;
+        }
+        if (++cs == S) { cs = 0; advance(c_s, c_p); }
+      }
+      load_unit(lj, l_s, l_p, ls, buf[j], true);
+      if (++ls == S) { ls = 0; ++lj; advance(l_s, l_p); }
+    }
+  }
+}
+
+int cu_count_moe() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  int v = cached[dev & 63].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    return 0;
+  cached[dev & 63].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// (units in flight, waves per workgroup, workgroups per compute unit)
+struct MoeGemvCfg {
+  int u, waves, wpc;
+};
+
+MoeGemvCfg moe_gemv_cfg() {
+  MoeGemvCfg c{2, 16, 1};  // measured best on the 512-expert decode layer
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_MOE_U")) c.u = atoi(e);
+  if (const char *e = getenv("QMM_MOE_WAVES")) c.waves = atoi(e);
+  if (const char *e = getenv("QMM_MOE_WPC")) c.wpc = atoi(e);
+#endif
+  return c;
+}
+
+template <int FMT, bool DOWN, int U, int WAVES>
+hipError_t launch_one(const MoeGemvArgs &a, size_t lds, int grid, hipStream_t s) {
+  static std::atomic<uint64_t> raised{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(raised.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void *)moe_gemv_kernel<FMT, DOWN, U, WAVES>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
+    if (e != hipSuccess) return e;
+    raised.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  hipLaunchKernelGGL((moe_gemv_kernel<FMT, DOWN, U, WAVES>), dim3(grid), dim3(64 * WAVES), lds, s, a);
+  return hipGetLastError();
+}
+
+#ifdef QMM_TUNE
+#define QMM_MOE_GEMV_CONFIGS(X) X(2, 16) X(4, 16) X(2, 8) X(4, 8) X(8, 8) X(4, 4) X(8, 4)
+#else
+#define QMM_MOE_GEMV_CONFIGS(X) X(2, 16)
+#endif
+
+template <int FMT, bool DOWN>
+hipError_t launch_cfg(const MoeGemvCfg &c, const MoeGemvArgs &a, size_t lds, int grid, hipStream_t s) {
+#define QMM_CASE(UU, WW) \
+  if (c.u == UU && c.waves == WW) return launch_one<FMT, DOWN, UU, WW>(a, lds, grid, s);
+  QMM_MOE_GEMV_CONFIGS(QMM_CASE)
+#undef QMM_CASE
+  return hipErrorInvalidConfiguration;
+}
+
+template <bool DOWN>
+hipError_t launch_fmt(int format, const MoeGemvArgs &a, size_t lds, hipStream_t s) {
+  const MoeGemvCfg c = moe_gemv_cfg();
+  const int grid = cu_count_moe() * c.wpc;
+  switch (format) {
+    case QMM_AFFINE4_G64: return launch_cfg<QMM_AFFINE4_G64, DOWN>(c, a, lds, grid, s);
+    case QMM_MXFP4: return launch_cfg<QMM_MXFP4, DOWN>(c, a, lds, grid, s);
+    case QMM_NVFP4: return launch_cfg<QMM_NVFP4, DOWN>(c, a, lds, grid, s);
+    default: return launch_cfg<QMM_Q6_K, DOWN>(c, a, lds, grid, s);
+  }
+}
+
+size_t stage_lds(int format, int k, int nsrc) {
+  const int sums = format == QMM_AFFINE4_G64 ? 1 : (format == QMM_Q6_K ? 2 : 0);
+  const size_t nch = (size_t)k / 32;
+  return nch * moe_gemv_stride(nsrc) * 4 + (size_t)nsrc * sums * nch * 4;
+}
+
+MoeGemvArgs weight_args(const qmm_weight &w) {
+  MoeGemvArgs a{};
+  a.codes = (const uint8_t *)w.codes;
+  a.codes_hi = (const uint8_t *)w.codes_hi;
+  a.scales = (const uint8_t *)w.scales;
+  a.scales2 = (const uint8_t *)w.scales2;
+  a.tensor_scale = w.tensor_scale;
+  const size_t rows = (size_t)w.batch * w.n;
+  a.codes_bytes = (uint32_t)(rows * (size_t)(w.k / 2));
+  a.hi_bytes = w.codes_hi ? (uint32_t)(rows * (size_t)(w.k / 4)) : 0u;
+  a.scales_bytes = (uint32_t)(rows * (size_t)(w.k / (w.format == QMM_MXFP4 ? 32 : 16)));
+  a.scales2_bytes = w.scales2 ? (uint32_t)(rows * (size_t)(w.k / 256) * 2) : 0u;
+  a.k = w.k;
+  a.rows = w.n;
+  return a;
+}
+
+}  // namespace
+
+bool moe_gemv_fits(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_shared) {
+  if (t > kMoeGemvMaxTokens) return false;
+  const int slots = t * (topk + num_shared);
+  if (slots > kMoeGemvMaxSlots || dn.n % 4 != 0) return false;
+  return stage_lds(gu.format, gu.k, t) <= kLdsLimit &&
+         stage_lds(dn.format, dn.k, slots) <= kLdsLimit && cu_count_moe() > 0;
+}
+
+hipError_t launch_moe_gemv(const qmm_weight &gu, const qmm_weight &dn, int num_routed,
+                           int num_shared, const void *x, int t, const int32_t *topk_ids,
+                           int topk, const MoeTables &tb, hipStream_t s) {
+  const int slots = t * (topk + num_shared);
+  const int inter = gu.n / 2;
+
+  MoeGemvArgs g = weight_args(gu);
+  g.steps = (gu.k + MoeShape<false>::kStepK - 1) / MoeShape<false>::kStepK;
+  g.pairs = inter;
+  g.half_rows = inter;
+  g.pair_step = 1;
+  g.topk_ids = topk_ids;
+  g.t = t;
+  g.topk = topk;
+  g.num_routed = num_routed;
+  g.num_shared = num_shared;
+  g.src = (const uint16_t *)x;
+  g.nsrc = t;
+  g.h = tb.h;
+  hipError_t e = launch_fmt<false>(gu.format, g, stage_lds(gu.format, gu.k, t), s);
+  if (e != hipSuccess) return e;
+
+  MoeGemvArgs d = weight_args(dn);
+  d.steps = (dn.k + MoeShape<true>::kStepK - 1) / MoeShape<true>::kStepK;
+  d.pairs = dn.n / 4;
+  d.half_rows = 1;
+  d.pair_step = 4;
+  d.topk_ids = topk_ids;
+  d.t = t;
+  d.topk = topk;
+  d.num_routed = num_routed;
+  d.num_shared = num_shared;
+  d.src = tb.h;
+  d.nsrc = slots;
+  d.d = tb.d;
+  return launch_fmt<true>(dn.format, d, stage_lds(dn.format, dn.k, slots), s);
+}
+
+}  // namespace qmm

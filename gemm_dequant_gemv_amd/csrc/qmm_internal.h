@@ -77,6 +77,14 @@ hipError_t launch_moe_gemm_gate_up(const qmm_weight &gu, const void *x, const Mo
                                    int max_tiles, hipStream_t s);
 hipError_t launch_moe_gemm_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
                                 hipStream_t s);
+// decode form of qmoe_grouped: grouped GEMV over token slots (t <= 4)
+constexpr int kMoeGemvMaxTokens = 4;
+constexpr int kMoeGemvMaxSlots = 512;
+bool moe_gemv_fits(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_shared);
+bool moe_uses_gemv(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_shared);
+hipError_t launch_moe_gemv(const qmm_weight &gu, const qmm_weight &dn, int num_routed,
+                           int num_shared, const void *x, int t, const int32_t *topk_ids,
+                           int topk, const MoeTables &tb, hipStream_t s);
 hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed, int num_shared,
                       const void *x, int t, const int32_t *topk_ids, const float *topk_w,
                       int topk, const float *shared_w, void *y, int y_dtype, void *workspace,

@@ -209,6 +209,13 @@ int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, v
  * workspace    at least qmoe_workspace_size(...) bytes, 256-byte aligned; it holds
  *              the routing tables, h and d.  No zero-fill is needed.
  * The gate/up and down weights may use different formats.
+ *
+ * Two forms, the same result contract: up to 4 tokens (when the activations
+ * fit in LDS) take the decode form, one grouped matrix-vector launch per
+ * projection over the token slots plus the combine ("TurboEXL3" section 3.1:
+ * decode verifies 1 to 4 tokens); more tokens take the grouped-GEMM form
+ * (route, gate/up, down, combine; section 4.1).  qmoe_workspace_layout says
+ * which form a call takes.
  */
 size_t qmoe_workspace_size(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
                            int32_t num_shared, int32_t t, int32_t topk);
@@ -239,6 +246,12 @@ typedef struct {
   size_t d;             /* float [rows][H]  down-projection outputs                  */
   size_t bytes;         /* = qmoe_workspace_size                                     */
   size_t max_rows, max_tiles;
+  size_t slot_rows;     /* 1: the call takes the decode form (t <= 4 and the
+                           vectors fit in LDS): no routing pass; h and d row s is
+                           token slot s (routed slots in list order, then shared
+                           expert j's slot of token i at t*topk + j*t + i); of the
+                           tables only scalars[2] (err) is written.
+                           0: the grouped form; every table above is written.   */
 } qmoe_layout;
 
 /* Fill *out for these arguments (host-side arithmetic only, no launch).

@@ -54,16 +54,23 @@ def run_gpu(q, gu, dn, x, ids, w, E, S, shared_w=None, y_dtype=torch.float32, wd
     torch.cuda.synchronize()
     I = gu.n // 2
     rows = T * (topk + S)
-    r = {}
-    r["counts"] = _u32(ws, L["counts"], E + S)
-    r["offsets"] = _u32(ws, L["offsets"], E + S + 1)
-    r["row_of_slot"] = _u32(ws, L["row_of_slot"], T * topk).reshape(T, topk)
-    r["row_of_shared"] = _u32(ws, L["row_of_shared"], S * T)
-    r["token_of_row"] = _u32(ws, L["token_of_row"], rows)
-    n_active, n_tiles, err = _u32(ws, L["scalars"], 3)
-    r["active"] = _u32(ws, L["active"], n_active)
-    r["tiles"] = _u32(ws, L["tiles"], 3 * n_tiles).reshape(-1, 3)
-    r["err"] = int(err)
+    r = {"slot_rows": bool(L["slot_rows"])}
+    r["err"] = int(_u32(ws, L["scalars"], 3)[2])
+    if r["slot_rows"]:
+        # decode form: h / d row s is token slot s, shared slots after the routed
+        routed = T * topk
+        valid = (ids >= 0) & (ids < E)
+        r["row_of_slot"] = np.where(valid, np.arange(routed).reshape(T, topk), 0xFFFFFFFF)
+        r["row_of_shared"] = routed + np.arange(S * T)
+    else:
+        r["counts"] = _u32(ws, L["counts"], E + S)
+        r["offsets"] = _u32(ws, L["offsets"], E + S + 1)
+        r["row_of_slot"] = _u32(ws, L["row_of_slot"], T * topk).reshape(T, topk)
+        r["row_of_shared"] = _u32(ws, L["row_of_shared"], S * T)
+        r["token_of_row"] = _u32(ws, L["token_of_row"], rows)
+        n_active, n_tiles, _ = _u32(ws, L["scalars"], 3)
+        r["active"] = _u32(ws, L["active"], n_active)
+        r["tiles"] = _u32(ws, L["tiles"], 3 * n_tiles).reshape(-1, 3)
     r["h"] = ws[L["h"]:L["h"] + rows * I * 2].view(torch.int16).cpu().numpy().view(np.uint16).reshape(rows, I)
     if y.dtype == torch.bfloat16:
         yh = oracle.bf16(y.view(torch.int16).cpu().numpy().view(np.uint16))
@@ -78,6 +85,9 @@ def check_grouping(r, ids, E, S):
     group's rows): every slot lands inside its expert's rows, once."""
     g = oracle.moe_grouping(ids, E, S)
     T, topk = ids.shape
+    assert r["err"] == g["err"]
+    if r["slot_rows"]:  # the decode form builds no grouping tables
+        return
     assert np.array_equal(r["counts"], g["counts"])
     assert np.array_equal(r["offsets"], g["offsets"])
     assert np.array_equal(r["active"], g["active"])
@@ -155,6 +165,7 @@ def test_moe_parity_small(T, fmts):
     gu, dn, x, ids, w = make_case(*fmts, c["E"], c["S"], c["H"], c["I"], T, c["topk"],
                                   f"moe{fmts}{T}")
     yh, r = run_gpu(q, gu, dn, x, ids, w, c["E"], c["S"])
+    assert r["slot_rows"] == (T <= 4)
     check_grouping(r, ids, c["E"], c["S"])
     tokens = list(range(T)) if T <= 40 else list(range(0, T, 7))
     hd = gpu_h_dict(r, T, c["topk"], c["S"], tokens)
@@ -195,33 +206,36 @@ def test_moe_single_expert_equals_dense_chain():
     check_h(gu, x, ids, 1, 0, hd, tokens)
 
 
-def test_moe_invalid_expert_ids_contribute_nothing():
+@pytest.mark.parametrize("T", [3, 6])
+def test_moe_invalid_expert_ids_contribute_nothing(T):
     q = _q()
-    E, H, I, T, topk = 8, 256, 128, 6, 3
-    gu, dn, x, ids, w = make_case(F.NVFP4, F.NVFP4, E, 1, H, I, T, topk, "moebad")
+    E, H, I, topk = 8, 256, 128, 3
+    gu, dn, x, ids, w = make_case(F.NVFP4, F.NVFP4, E, 1, H, I, T, topk, f"moebad{T}")
     ids = ids.copy()
-    ids[0, 1] = E + 5
-    ids[3, 0] = -1
+    bad = [(0, 1), (T - 1, 0)]
+    ids[bad[0]] = E + 5
+    ids[bad[1]] = -1
     yh, r = run_gpu(q, gu, dn, x, ids, w, E, 1)
-    assert r["row_of_slot"][0, 1] == 0xFFFFFFFF and r["row_of_slot"][3, 0] == 0xFFFFFFFF
+    assert all(r["row_of_slot"][b] == 0xFFFFFFFF for b in bad)
     assert r["err"] == 1
     check_grouping(r, ids, E, 1)
     w2 = w.copy()
-    w2[0, 1] = 0.0
-    w2[3, 0] = 0.0
+    for b in bad:
+        w2[b] = 0.0
     ids2 = np.where(ids < 0, 0, np.where(ids >= E, 0, ids)).astype(np.int32)
     tokens = list(range(T))
     hd = gpu_h_dict(r, T, topk, 1, tokens)
     # the dropped slots get a placeholder h (their weight is zero in the reference)
-    for (t, j) in [(0, 1), (3, 0)]:
-        hd[(t, j)] = np.zeros(I, np.uint16)
+    for b in bad:
+        hd[b] = np.zeros(I, np.uint16)
     check_y(gu, dn, x, ids2, w2, E, 1, yh, hd, tokens)
 
 
-def test_moe_deterministic():
+@pytest.mark.parametrize("T", [4, 300])
+def test_moe_deterministic(T):
     q = _q()
-    E, H, I, T, topk = 16, 256, 128, 300, 4
-    gu, dn, x, ids, w = make_case(F.NVFP4, F.NVFP4, E, 1, H, I, T, topk, "moedet")
+    E, H, I, topk = 16, 256, 128, 4
+    gu, dn, x, ids, w = make_case(F.NVFP4, F.NVFP4, E, 1, H, I, T, topk, f"moedet{T}")
     wdev = (q.Weight.from_host(gu), q.Weight.from_host(dn))
     ys = [run_gpu(q, gu, dn, x, ids, w, E, 1, wdev=wdev)[0] for _ in range(3)]
     for y in ys[1:]:
@@ -254,6 +268,7 @@ def test_moe_full_layer(full_layer, T, y_dtype):
     ids, w = routing.synthetic_routing(T, c["E"], c["topk"], name=f"moe_full/r{T}")
     print(f"moe full layer T={T}", flush=True)
     yh, r = run_gpu(q, gu, dn, x, ids, w, c["E"], c["S"], y_dtype=y_dtype, wdev=wdev)
+    assert r["slot_rows"] == (T <= 4)
     check_grouping(r, ids, c["E"], c["S"])
     tokens = list(range(T)) if T <= 4 else [0, 1, 2047, 4096, 6000, T - 1]
     hd = gpu_h_dict(r, T, c["topk"], c["S"], tokens)
