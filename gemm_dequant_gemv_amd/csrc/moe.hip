@@ -3,8 +3,8 @@
 // token slots, moe_gemv.hip, then the combine below); more tokens take the
 // grouped-GEMM form ("TurboEXL3" section 4.1):
 //   1. route:    one launch counts each expert's tokens, groups the token slots
-//                by expert and builds the table of row tiles (replacing a sort
-//                and a separate table pass);
+//                by expert and builds the table of row tiles, all in one
+//                pass instead of sorting first and tabulating afterwards;
 //   2. gate/up:  one grouped GEMM over the tile table, activations gathered by
 //                token, weights decoded once per K-slice per workgroup; SwiGLU
 //                in float32 in its epilogue -> bf16 h;

@@ -18,7 +18,8 @@ What it computes, and where the pages define it:
   - float16 and bfloat16 by their IEEE-style bit fields.
 * Dequantization of each weight to its exact real value:
   - affine4_g64 (section 2.1, MLX affine bullet: 16-bit scale and 16-bit bias
-    per 64 weights; section 3.1 "a shift, a mask and a multiply-add"):
+    per 64 weights; section 3.1: each weight costs a shift, a mask and one
+    multiply-add):
     w = s * q + b.
   - mxfp4 (section 2.1): w = e2m1(c) * 2^(E - 127), one E per 32 weights.
   - nvfp4 (section 2.1: E4M3 scale per 16 weights plus one 32-bit scale per
@@ -298,6 +299,7 @@ def bf16_half_ulp(v) -> np.ndarray:
 
 def within_tolerance_bf16(y, y_ref, mag, rel: float = 2e-3):
     """The product rule for results stored as bfloat16: the accumulation bound
-    plus the output's own rounding, which the reference applies too ("round
-    where the reference rounds", TurboEXL3 section 4.4)."""
+    plus the output's own rounding, which the reference applies at the same
+    point (TurboEXL3 section 4.4: tolerance kernels keep the reference's
+    rounding points and differ only in summation order)."""
     return np.abs(np.asarray(y, np.float64) - y_ref) <= rel * mag + bf16_half_ulp(y_ref)
