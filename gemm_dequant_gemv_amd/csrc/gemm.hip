@@ -26,128 +26,14 @@
 //   Q6_K:   (d * sc) * (q - 32) in float32 (exact) -> bf16
 #include <algorithm>
 #include <atomic>
+#include <cstdlib>
 
-#include "qmm_device.h"
-#include "qmm_internal.h"
+#include "gemm_common.h"
 
 namespace qmm {
 namespace {
 
-constexpr int kBK = 64;          // K values per slice
-constexpr int kLdsPad = 8;       // bf16 of padding per LDS row (keeps MFMA operand reads conflict-free)
-constexpr int kRowH = kBK + kLdsPad;  // bf16 per LDS row
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-
-// What a workgroup's rows are, and where its results go.
-enum GemmMode {
-  kDense = 0,   // y[m][n] = x[m] . w[n]; rows of x are rows of y
-  kMoeGateUp = 1,  // grouped: x rows gathered by token, weight rows interleaved
-                   // (gate i, up i); the epilogue applies SwiGLU and writes bf16 h
-  kMoeDown = 2,    // grouped: rows of h, one expert per tile; writes float32 d
-};
-
-struct GemmArgs {
-  const uint8_t *codes;
-  const uint8_t *codes_hi;
-  const uint8_t *scales;
-  const uint8_t *scales2;
-  const float *tensor_scale;
-  const uint16_t *x;
-  const uint16_t *residual;
-  uint16_t *y;
-  int m, n, k;
-  // grouped (MoE) modes
-  const uint32_t *tiles;         // [max_tiles][3] = (expert, first grouped row, rows)
-  const uint32_t *n_tiles;       // device count of valid tiles
-  const uint32_t *token_of_row;  // grouped row -> token (gate/up gather)
-  uint16_t *h;                   // bf16 [rows][inter]   (gate/up output, down input)
-  float *d;                      // float32 [rows][n]    (down output)
-  int inter;                     // I: gate/up rows are 2I
-};
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
-}
-
-// Raw bytes of one 32-weight piece of a row (codes and scales).
-struct Piece {
-  uint4 q;
-  uint2 h;
-  uint32_t s, d;
-};
-
-template <int FMT>
-__device__ __forceinline__ Piece load_piece(const GemmArgs &a, int row, int kc) {
-  const size_t k = (size_t)a.k, r = (size_t)row;
-  Piece p;
-  p.q = load_stream16(a.codes + r * (k / 2) + kc / 2);
-  if constexpr (FMT == QMM_AFFINE4_G64) {
-    p.s = *(const uint32_t *)(a.scales + (r * (k / 64) + kc / 64) * 4);
-  } else if constexpr (FMT == QMM_MXFP4) {
-    p.s = a.scales[r * (k / 32) + kc / 32];
-  } else if constexpr (FMT == QMM_NVFP4) {
-    p.s = *(const uint16_t *)(a.scales + r * (k / 16) + kc / 16);
-  } else {
-    p.h = *(const uint2 *)(a.codes_hi + r * (k / 4) + kc / 4);
-    p.s = *(const uint16_t *)(a.scales + r * (k / 16) + kc / 16);
-    p.d = *(const uint16_t *)(a.scales2 + (r * (k / 256) + kc / 256) * 2);
-  }
-  return p;
-}
-
-// The piece's 32 weights as 16 bf16 pairs in natural order.
-template <int FMT>
-__device__ __forceinline__ void decode_piece(const Piece &p, uint32_t (&o)[16]) {
-  const uint32_t w[4] = {p.q.x, p.q.y, p.q.z, p.q.w};
-  if constexpr (FMT == QMM_AFFINE4_G64) {
-    const float s = half_to_float(p.s & 0xFFFFu), b = half_to_float(p.s >> 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float lo = __builtin_fmaf(s, (float)((w[j] >> (8 * i)) & 15u), b);
-        const float hi = __builtin_fmaf(s, (float)((w[j] >> (8 * i + 4)) & 15u), b);
-        o[4 * j + i] = pack_bf16(lo, hi);
-      }
-  } else if constexpr (FMT == QMM_MXFP4) {
-    const float sc = e8m0_to_float(p.s);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      o[4 * j + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 0));
-      o[4 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 1));
-      o[4 * j + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 2));
-      o[4 * j + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 3));
-    }
-  } else if constexpr (FMT == QMM_NVFP4) {
-    const float s0 = e4m3_to_float(p.s & 0xFFu), s1 = e4m3_to_float(p.s >> 8);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float sc = j < 2 ? s0 : s1;
-      const uint32_t e[4] = {e2m1x2_to_bf16x2<0>(w[j]), e2m1x2_to_bf16x2<1>(w[j]),
-                             e2m1x2_to_bf16x2<2>(w[j]), e2m1x2_to_bf16x2<3>(w[j])};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[4 * j + i] = pack_bf16(bf_lo(e[i]) * sc, bf_hi(e[i]) * sc);
-    }
-  } else {  // Q6_K
-    const float dd = half_to_float(p.d);
-    const uint32_t hw[2] = {p.h.x, p.h.y};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float dsc = dd * (float)(int8_t)(p.s >> (8 * (j / 2)));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v0 = 8 * j + 2 * i;  // value index within the piece (even)
-        const uint32_t q0 = ((w[j] >> (8 * i)) & 15u) | (((hw[v0 / 16] >> (2 * (v0 % 16))) & 3u) << 4);
-        const uint32_t q1 = ((w[j] >> (8 * i + 4)) & 15u) |
-                            (((hw[(v0 + 1) / 16] >> (2 * ((v0 + 1) % 16))) & 3u) << 4);
-        o[4 * j + i] = pack_bf16(dsc * (float)((int)q0 - 32), dsc * (float)((int)q1 - 32));
-      }
-    }
-  }
-}
+using namespace gemm;
 
 template <int FMT, int BM, int BN, int MODE>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
@@ -177,7 +63,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   }
   const int slices = a.k / kBK;
   // weight row of tile row j (gate/up interleaved in the gate/up mode)
-  auto wrow = [&](int j) {
+  auto wrow = [&](int j) __attribute__((always_inline)) {
     if constexpr (MODE == kMoeGateUp) {
       const int i = n0 / 2 + j / 2;
       return wrow0 + ((j & 1) ? a.inter + i : i);
@@ -187,9 +73,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   };
 
   // global -> register loads of one slice
-  uint4 xr[XP];
+  u32x4_t xr[XP];
   Piece wr[WP];
-  auto load_slice = [&](int s) {
+  auto load_slice = [&](int s) __attribute__((always_inline)) {
     const int k0 = s * kBK;
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
@@ -199,7 +85,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       if constexpr (MODE == kDense) src = a.x + (size_t)r * a.k;
       else if constexpr (MODE == kMoeGateUp) src = a.x + (size_t)a.token_of_row[r] * a.k;
       else src = a.h + (size_t)r * a.k;
-      xr[i] = *(const uint4 *)(src + k0 + col * 8);
+      xr[i] = *(const u32x4_t *)(src + k0 + col * 8);
     }
 #pragma unroll
     for (int i = 0; i < WP; ++i) {
@@ -208,22 +94,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     }
   };
   // decode and write one slice into LDS stage `st`
-  auto store_slice = [&](int st) {
+  auto store_slice = [&](int st) __attribute__((always_inline)) {
     uint16_t *xs = lds + st * STAGE;
     uint16_t *ws = xs + BM * kRowH;
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const int p = tid + 256 * i, row = p / (kBK / 8), col = p % (kBK / 8);
-      *(uint4 *)(xs + row * kRowH + col * 8) = xr[i];
+      *(u32x4_t *)(xs + row * kRowH + col * 8) = xr[i];
     }
 #pragma unroll
     for (int i = 0; i < WP; ++i) {
       const int p = tid + 256 * i, row = p / 2, half = p % 2;
       uint32_t o[16];
       decode_piece<FMT>(wr[i], o);
-      uint4 *dst = (uint4 *)(ws + row * kRowH + half * 32);
+      u32x4_t *dst = (u32x4_t *)(ws + row * kRowH + half * 32);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+      for (int q = 0; q < 4; ++q) dst[q] = u32x4_t{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
     }
   };
 
@@ -358,6 +244,13 @@ GemmArgs weight_args(const qmm_weight &w) {
 
 hipError_t launch_gemm(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
                        hipStream_t s) {
+  // many rows: 256 x 256 tiles (gemm_wide.hip); fewer: 128 x 128 tiles, which
+  // keep more workgroups in flight
+  bool wide = false;
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_GEMM_WIDE")) wide = atoi(e) != 0;
+#endif
+  if (wide) return launch_gemm_wide(w, x, m, residual, y, s);
   GemmArgs a = weight_args(w);
   a.x = (const uint16_t *)x;
   a.residual = (const uint16_t *)residual;
