@@ -35,7 +35,7 @@ namespace {
 
 using namespace gemm;
 
-template <int FMT, int BM, int BN, int MODE>
+template <int FMT, int BM, int BN, int MODE, int PD>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   constexpr int TN = BN / 32, TM = BM / 32;      // 16x16 tiles per wave along n and m
   constexpr int XP = BM * (kBK / 8) / 256;       // 16-byte activation pieces per thread
@@ -72,41 +72,41 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     }
   };
 
-  // global -> register loads of one slice
-  u32x4_t xr[XP];
-  Piece wr[WP];
-  auto load_slice = [&](int s) __attribute__((always_inline)) {
+  // global -> register loads of one slice, into register stage `r`
+  u32x4_t xr[PD][XP];
+  Piece wr[PD][WP];
+  auto load_slice = [&](int s, int r) __attribute__((always_inline)) {
     const int k0 = s * kBK;
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const int p = tid + 256 * i, row = p / (kBK / 8), col = p % (kBK / 8);
-      const int r = m0 + min(row, mrows - 1);
+      const int rr = m0 + min(row, mrows - 1);
       const uint16_t *src;
-      if constexpr (MODE == kDense) src = a.x + (size_t)r * a.k;
-      else if constexpr (MODE == kMoeGateUp) src = a.x + (size_t)a.token_of_row[r] * a.k;
-      else src = a.h + (size_t)r * a.k;
-      xr[i] = *(const u32x4_t *)(src + k0 + col * 8);
+      if constexpr (MODE == kDense) src = a.x + (size_t)rr * a.k;
+      else if constexpr (MODE == kMoeGateUp) src = a.x + (size_t)a.token_of_row[rr] * a.k;
+      else src = a.h + (size_t)rr * a.k;
+      xr[r][i] = *(const u32x4_t *)(src + k0 + col * 8);
     }
 #pragma unroll
     for (int i = 0; i < WP; ++i) {
       const int p = tid + 256 * i, row = p / 2, half = p % 2;
-      wr[i] = load_piece<FMT>(a, wrow(row), k0 + half * 32);
+      wr[r][i] = load_piece<FMT>(a, wrow(row), k0 + half * 32);
     }
   };
-  // decode and write one slice into LDS stage `st`
-  auto store_slice = [&](int st) __attribute__((always_inline)) {
+  // decode register stage `r` and write it into LDS stage `st`
+  auto store_slice = [&](int r, int st) __attribute__((always_inline)) {
     uint16_t *xs = lds + st * STAGE;
     uint16_t *ws = xs + BM * kRowH;
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const int p = tid + 256 * i, row = p / (kBK / 8), col = p % (kBK / 8);
-      *(u32x4_t *)(xs + row * kRowH + col * 8) = xr[i];
+      *(u32x4_t *)(xs + row * kRowH + col * 8) = xr[r][i];
     }
 #pragma unroll
     for (int i = 0; i < WP; ++i) {
       const int p = tid + 256 * i, row = p / 2, half = p % 2;
       uint32_t o[16];
-      decode_piece<FMT>(wr[i], o);
+      decode_piece<FMT>(wr[r][i], o);
       u32x4_t *dst = (u32x4_t *)(ws + row * kRowH + half * 32);
 #pragma unroll
       for (int q = 0; q < 4; ++q) dst[q] = u32x4_t{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
@@ -119,33 +119,44 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  load_slice(0);
-  store_slice(0);
+  // slices 0 .. PD-1 in flight, slice 0 decoded into LDS stage 0
+#pragma unroll
+  for (int r = 0; r < PD; ++r)
+    if (r < slices) load_slice(r, r);
+  store_slice(0, 0);
   __syncthreads();
 
+  // Slice q lives in register stage q % PD and LDS stage q % 2.  Iteration q:
+  // the loads of slice q + PD go to register stage q % PD (slice q is already
+  // in LDS), the MFMAs run on LDS stage q % 2, then slice q + 1 is decoded
+  // into the other LDS stage; one barrier per slice.
   const int lr = lane & 15, lk = (lane >> 4) * 8;  // operand row within a 16-tile, k offset
-  for (int s = 0; s < slices; ++s) {
-    const int st = s & 1;
-    if (s + 1 < slices) load_slice(s + 1);
-    const uint16_t *xs = lds + st * STAGE;
-    const uint16_t *ws = xs + BM * kRowH;
+  for (int s0 = 0; s0 < slices; s0 += PD) {
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 32) {
-      bf16x8_t af[TN], bfr[TM];
+    for (int u = 0; u < PD; ++u) {
+      const int s = s0 + u;
+      if (s >= slices) break;  // uniform
+      if (s + PD < slices) load_slice(s + PD, u);
+      const uint16_t *xs = lds + (s & 1) * STAGE;
+      const uint16_t *ws = xs + BM * kRowH;
 #pragma unroll
-      for (int i = 0; i < TN; ++i)
-        af[i] = *(const bf16x8_t *)(ws + (wn * (BN / 2) + i * 16 + lr) * kRowH + kk + lk);
+      for (int kk = 0; kk < kBK; kk += 32) {
+        bf16x8_t af[TN], bfr[TM];
 #pragma unroll
-      for (int j = 0; j < TM; ++j)
-        bfr[j] = *(const bf16x8_t *)(xs + (wm * (BM / 2) + j * 16 + lr) * kRowH + kk + lk);
-#pragma unroll
-      for (int i = 0; i < TN; ++i)
+        for (int i = 0; i < TN; ++i)
+          af[i] = *(const bf16x8_t *)(ws + (wn * (BN / 2) + i * 16 + lr) * kRowH + kk + lk);
 #pragma unroll
         for (int j = 0; j < TM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          bfr[j] = *(const bf16x8_t *)(xs + (wm * (BM / 2) + j * 16 + lr) * kRowH + kk + lk);
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int j = 0; j < TM; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+      if (s + 1 < slices) store_slice((u + 1) % PD, (s + 1) & 1);
+      __syncthreads();
     }
-    if (s + 1 < slices) store_slice(st ^ 1);
-    __syncthreads();
   }
 
   // epilogue: lane holds D[n = 4*(lane/16) + r][m = lane % 16] of each tile
@@ -199,7 +210,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     }
 }
 
-template <int FMT, int BM, int BN, int MODE>
+template <int FMT, int BM, int BN, int MODE, int PD>
 hipError_t launch_tile(const GemmArgs &a, dim3 grid, hipStream_t s) {
   constexpr size_t lds = 2 * (size_t)(BM + BN) * kRowH * 2;
   // more than 64 KiB of dynamic LDS must be allowed once per device
@@ -209,22 +220,42 @@ hipError_t launch_tile(const GemmArgs &a, dim3 grid, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(configured.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute((const void *)gemm_kernel<FMT, BM, BN, MODE>,
+    e = hipFuncSetAttribute((const void *)gemm_kernel<FMT, BM, BN, MODE, PD>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN, MODE>), grid, dim3(256), lds, s, a);
+  hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN, MODE, PD>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
+}
+
+// slices of global loads in flight (register stages)
+int gemm_depth() {
+  int pd = 1;  // deeper register prefetch measured slower (it costs occupancy)
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_GEMM_PD")) pd = atoi(e);
+#endif
+  return pd;
+}
+
+template <int FMT, int MODE>
+hipError_t launch_fd(const GemmArgs &a, dim3 grid, hipStream_t s) {
+  switch (gemm_depth()) {
+#ifdef QMM_TUNE
+    case 2: return launch_tile<FMT, kGemmBM, 128, MODE, 2>(a, grid, s);
+    case 3: return launch_tile<FMT, kGemmBM, 128, MODE, 3>(a, grid, s);
+#endif
+    default: return launch_tile<FMT, kGemmBM, 128, MODE, 1>(a, grid, s);
+  }
 }
 
 template <int MODE>
 hipError_t launch_mode(int format, const GemmArgs &a, dim3 grid, hipStream_t s) {
   switch (format) {
-    case QMM_AFFINE4_G64: return launch_tile<QMM_AFFINE4_G64, kGemmBM, 128, MODE>(a, grid, s);
-    case QMM_MXFP4: return launch_tile<QMM_MXFP4, kGemmBM, 128, MODE>(a, grid, s);
-    case QMM_NVFP4: return launch_tile<QMM_NVFP4, kGemmBM, 128, MODE>(a, grid, s);
-    default: return launch_tile<QMM_Q6_K, kGemmBM, 128, MODE>(a, grid, s);
+    case QMM_AFFINE4_G64: return launch_fd<QMM_AFFINE4_G64, MODE>(a, grid, s);
+    case QMM_MXFP4: return launch_fd<QMM_MXFP4, MODE>(a, grid, s);
+    case QMM_NVFP4: return launch_fd<QMM_NVFP4, MODE>(a, grid, s);
+    default: return launch_fd<QMM_Q6_K, MODE>(a, grid, s);
   }
 }
 

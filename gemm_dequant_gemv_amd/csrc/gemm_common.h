@@ -42,9 +42,12 @@ struct GemmArgs {
   int inter;                     // I: gate/up rows are 2I
 };
 
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v_t;
+
+// Two floats -> a bfloat16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2v_t));
 }
 
 // Raw bytes of one 32-weight piece of a row (codes and scales).
@@ -82,8 +85,12 @@ __device__ __forceinline__ void decode_piece(const Piece &p, uint32_t (&o)[16]) 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // even codes to the bytes of one word, odd codes to the bytes of another,
-      // so that each code becomes a float with one v_cvt_f32_ubyteN
-      const uint32_t ev = w[j] & 0x0F0F0F0Fu, od = (w[j] >> 4) & 0x0F0F0F0Fu;
+      // so that each code becomes a float with one v_cvt_f32_ubyteN (the
+      // empty asm keeps the compiler from folding the mask into a bit-field
+      // extract per code)
+      uint32_t ev = w[j] & 0x0F0F0F0Fu, od = (w[j] >> 4) & 0x0F0F0F0Fu;
+      asm volatile("" : "+v"(ev));
+      asm volatile("" : "+v"(od));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float lo = __builtin_fmaf(s, (float)((ev >> (8 * i)) & 0xFFu), b);
@@ -105,10 +112,14 @@ __device__ __forceinline__ void decode_piece(const Piece &p, uint32_t (&o)[16]) 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float sc = j < 2 ? s0 : s1;
-      const uint32_t e[4] = {e2m1x2_to_bf16x2<0>(w[j]), e2m1x2_to_bf16x2<1>(w[j]),
-                             e2m1x2_to_bf16x2<2>(w[j]), e2m1x2_to_bf16x2<3>(w[j])};
+      // E2M1 pair -> two float32 (hardware conversion, unit scale), times the
+      // E4M3 block scale (exact), -> bfloat16 pair (exact)
+      const f32x2_t e[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 0),
+                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 1),
+                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 2),
+                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 3)};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[4 * j + i] = pack_bf16(bf_lo(e[i]) * sc, bf_hi(e[i]) * sc);
+      for (int i = 0; i < 4; ++i) o[4 * j + i] = pack_bf16(e[i][0] * sc, e[i][1] * sc);
     }
   } else {  // Q6_K
     const float dd = half_to_float(p.d);
