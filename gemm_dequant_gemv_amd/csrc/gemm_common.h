@@ -108,7 +108,8 @@ __device__ __forceinline__ void decode_piece(const Piece &p, uint32_t (&o)[16]) 
       o[4 * j + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 3));
     }
   } else if constexpr (FMT == QMM_NVFP4) {
-    const float s0 = e4m3_to_float(p.s & 0xFFu), s1 = e4m3_to_float(p.s >> 8);
+    float s0, s1;
+    e4m3x2_to_float(p.s, s0, s1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float sc = j < 2 ? s0 : s1;

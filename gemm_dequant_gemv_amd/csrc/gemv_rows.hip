@@ -43,17 +43,24 @@ constexpr int kStepK = 1024;       // values of one row per step (32 lanes x 32)
 constexpr int kXPieces = 9;        // 16-byte activation pieces per thread, at most
 constexpr size_t kLdsLimit = 160 * 1024 - 2048;  // dynamic part; the static part is < 1 KB
 
-// Activations of 32-value chunk ch, lane m, as 16-byte pieces p = 4m + part.
-// Pieces are XOR-swizzled inside the chunk so that the 8 lanes of one
-// ds_read_b128 group (consecutive chunks, same piece) hit distinct banks.
-template <int M>
+// LDS image of the activations, one record per 32-value chunk ch: M x 64
+// bytes of x (16-byte pieces p = 4m + part, in pair order for the
+// nibble-into-mantissa formats), then the chunk's block sums of x (M x NS
+// floats), padded so that the record stride is an odd multiple of 16 bytes.
+// The 8 lanes of one ds_read_b128 group read consecutive records at the same
+// offset, and an odd multiple of 16 bytes sends them to 8 distinct groups of
+// 4 banks; every read of a unit is one lane base plus an immediate offset.
+template <int M, int NS>
 struct XLayout {
-  static constexpr int kPieces = M == 1 ? 4 : (M == 2 ? 8 : 16);
-  static constexpr int kStride = 4 * kPieces;  // u32 per chunk
-  __device__ static int slot(int ch, int p) {
-    return kPieces == 4 ? (p ^ ((ch >> 1) & 3)) : (p ^ (ch & 7));
-  }
+  static constexpr int kSumOff = 64 * M;                   // bytes
+  static constexpr int kPad = M * NS * 4 <= 16 ? 16 : 48;  // sums fit, stride/16 odd
+  static constexpr int kStride = 64 * M + kPad;            // bytes per record
+  static_assert(M * NS * 4 <= kPad && (kStride / 16) % 2 == 1, "record layout");
 };
+
+constexpr int sums_per_chunk(int format) {
+  return format == QMM_AFFINE4_G64 ? 1 : (format == QMM_Q6_K ? 2 : 0);
+}
 
 struct RowsArgs {
   const uint8_t *codes;
@@ -71,14 +78,14 @@ struct RowsArgs {
 template <int FMT, int M, int U>
 __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
   using T = FmtTraits<FMT>;
-  using XL = XLayout<M>;
   constexpr int kNS = T::kSums;
+  using XL = XLayout<M, kNS>;
+  static_assert(kNS == sums_per_chunk(FMT), "sums per chunk");
   constexpr int kChunks = kStepK / 32;  // chunks per step
   constexpr int kOut = 2 * M;           // outputs of one pair
   extern __shared__ __align__(16) uint32_t smem[];
   const int nch = a.k / 32;
-  uint32_t *xs = smem;                                      // [nch][XL::kStride]
-  float *xsum = (float *)(xs + (size_t)nch * XL::kStride);  // [M * kNS][nch]
+  char *xs = (char *)smem;  // [nch] records of XL::kStride bytes
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, hf = lane >> 5, c = lane & 31;
@@ -172,15 +179,17 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
     const bool ok = i < pieces;
     const int ch = i / (4 * M), m = (i >> 2) % M, part_ = i & 3;
     const uint4 v = xv[j];
+    char *rec = xs + ch * XL::kStride;
     if constexpr (kNS > 0) {
       float sm = ((bf_lo(v.x) + bf_hi(v.x)) + (bf_lo(v.y) + bf_hi(v.y))) +
                  ((bf_lo(v.z) + bf_hi(v.z)) + (bf_lo(v.w) + bf_hi(v.w)));
       sm += __shfl_xor(sm, 1);
+      float *sums = (float *)(rec + XL::kSumOff);
       if constexpr (kNS == 1) {
         sm += __shfl_xor(sm, 2);
-        if (ok && part_ == 0) xsum[m * nch + ch] = sm;
+        if (ok && part_ == 0) sums[m] = sm;
       } else {
-        if (ok && (part_ & 1) == 0) xsum[(m * 2 + (part_ >> 1)) * nch + ch] = sm;
+        if (ok && (part_ & 1) == 0) sums[m * 2 + (part_ >> 1)] = sm;
       }
     }
     if (ok) {
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
         o.z = (v.y & 0xFFFFu) | (v.w << 16);
         o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
       }
-      *(uint4 *)(xs + ch * XL::kStride + XL::slot(ch, m * 4 + part_) * 4) = o;
+      *(uint4 *)(rec + (m * 4 + part_) * 16) = o;
     }
   }
   __syncthreads();
@@ -207,28 +216,31 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
   float acc[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+  const char *xs_lane = xs + c * XL::kStride;
 
   int cj = 0, cs = 0;  // unit being computed: pair index, step
   for (int t0 = 0; t0 < units; t0 += U) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       if (t0 + j < units) {  // uniform
-        const int ch = cs * kChunks + c;
-        if (ch < nch) {
+        if (cs * kChunks + c < nch) {
+          // this lane's record of step cs: lane base + a wave-uniform offset
+          const char *rec = xs_lane + cs * (kChunks * XL::kStride);
           uint32_t X[M][16];
           float Sx[M][2];
 #pragma unroll
           for (int m = 0; m < M; ++m) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const uint4 v = *(const uint4 *)(xs + ch * XL::kStride + XL::slot(ch, m * 4 + q) * 4);
+              const uint4 v = *(const uint4 *)(rec + (m * 4 + q) * 16);
               X[m][4 * q + 0] = v.x;
               X[m][4 * q + 1] = v.y;
               X[m][4 * q + 2] = v.z;
               X[m][4 * q + 3] = v.w;
             }
-            Sx[m][0] = kNS > 0 ? xsum[(m * (kNS > 0 ? kNS : 1)) * nch + ch] : 0.0f;
-            Sx[m][1] = kNS > 1 ? xsum[(m * 2 + 1) * nch + ch] : 0.0f;
+            const float *sums = (const float *)(rec + XL::kSumOff);
+            Sx[m][0] = kNS > 0 ? sums[m * (kNS > 0 ? kNS : 1)] : 0.0f;
+            Sx[m][1] = kNS > 1 ? sums[m * 2 + 1] : 0.0f;
           }
           row_step<FMT, M>(buf[j], X, Sx, acc, K);
         }
@@ -311,10 +323,9 @@ int cu_count() {
 }  // namespace
 
 size_t gemv_rows_lds(int format, int k, int m) {
-  const int pieces = m == 1 ? 4 : (m == 2 ? 8 : 16);
-  const int sums = format == QMM_AFFINE4_G64 ? 1 : (format == QMM_Q6_K ? 2 : 0);
-  const size_t nch = (size_t)k / 32;
-  return nch * pieces * 16 + nch * m * sums * 4;
+  const int ns = sums_per_chunk(format);
+  const int pad = m * ns * 4 <= 16 ? 16 : 48;
+  return (size_t)(k / 32) * (size_t)(64 * m + pad);
 }
 
 bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p) {

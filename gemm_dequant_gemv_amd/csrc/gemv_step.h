@@ -54,8 +54,12 @@ __device__ __forceinline__ UnpackK unpack_consts() {
   return k;
 }
 
+// (a & mask) | b as one v_and_or_b32 (left to itself the compiler turns the
+// nested Q6_K form into two ands and an or3)
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b) {
-  return (a & mask) | b;
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(b));
+  return r;
 }
 
 // acc[m] += (this row's 32 weights of the chunk) . (x[m] chunk)
@@ -108,7 +112,8 @@ __device__ __forceinline__ void row_step(const RowData &rd, const uint32_t (&X)[
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(sc, d0[m], acc[m]);
     } else {
-      const float s0 = e4m3_to_float(rd.s & 0xFFu), s1 = e4m3_to_float(rd.s >> 8);
+      float s0, s1;
+      e4m3x2_to_float(rd.s, s0, s1);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         acc[m] = __builtin_fmaf(s0, d0[m], acc[m]);

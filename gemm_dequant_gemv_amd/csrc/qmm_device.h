@@ -55,6 +55,16 @@ __device__ __forceinline__ float e4m3_to_float(uint32_t b) {
   return __uint_as_float(__float_as_uint(v) | ((b & 0x80u) << 24));
 }
 
+// The two E4M3 scales in the low 16 bits of w -> float32, with the gfx950
+// FP8 conversion (OCP E4M3: bias 7, subnormals, S.1111.111 = NaN; a unit
+// scale makes it exact).  It agrees with e4m3_to_float on all 256 codes.
+__device__ __forceinline__ void e4m3x2_to_float(uint32_t w, float &s0, float &s1) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+  s0 = v.x;
+  s1 = v.y;
+}
+
 // float32 -> bfloat16 bits, round to nearest even, NaN kept quiet.
 __device__ __forceinline__ uint32_t float_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
