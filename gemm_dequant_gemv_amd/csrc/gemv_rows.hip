@@ -3,8 +3,9 @@
 // weight expanded to 16 bits in the kernel, 16-bit products, 32-bit sums).
 //
 // One workgroup of 16 waves per compute unit.  The workgroup first stages the
-// whole activation block x [M][K] in LDS (pair order and per-block sums as in
-// the split-K kernel), then its waves stream weight rows:
+// whole activation block x [M][K] in LDS (one padded record per 32-value
+// chunk: its x in pair order, then its block sums), then its waves stream
+// weight rows:
 //   * rows go in pairs (2p, 2p+1), one per half-wave; wave w of the grid owns
 //     pairs w, w + W, w + 2W, ... (W = waves in the grid), so at any moment the
 //     grid streams one contiguous band of rows;
@@ -19,12 +20,14 @@
 //     flight; each unit brings the codes of two rows, their block scales and
 //     one residual value per output;
 //   * after a pair's last step each half-wave's sums are reduced with DPP row
-//     operations and lanes 0 .. 2M-1 write the pair's 2 x M outputs.
+//     operations and lanes 0 .. 2M-1 write the pair's 2 x M outputs;
+//   * a wave lowers its issue priority at each quarter of its units, so that
+//     the waves sharing a SIMD progress together instead of oldest first.
 // Nothing crosses waves, so there is no split-K finish and no workspace, and
 // every sum has a fixed order: the result does not depend on timing.  (Giving
 // each workgroup a contiguous block of pairs split evenly over its waves, with
-// cut pairs finished through LDS, balanced the waves' work but measured
-// slower on the decode shapes.)
+// cut pairs finished through LDS, balanced the waves' work but its longer
+// per-unit bookkeeping measured slower on the decode shapes.)
 //
 // The activations must fit in LDS (K * M * 2 bytes plus block sums); the host
 // falls back to the split-K kernel otherwise.
@@ -219,7 +222,17 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
   const char *xs_lane = xs + c * XL::kStride;
 
   int cj = 0, cs = 0;  // unit being computed: pair index, step
+  // Issue priority falls as the wave gets through its units.  The arbiter of
+  // a SIMD favours its oldest wave; left alone, the four waves of a SIMD
+  // finish one after another and the last ones run with little memory in
+  // flight.  Lowering the priority of waves that are ahead lets the ones
+  // behind catch up, so that the waves of a SIMD end close together.
+  __builtin_amdgcn_s_setprio(3);
+  const int q1 = units / 4, q2 = units / 2, q3 = (3 * units) / 4;
   for (int t0 = 0; t0 < units; t0 += U) {
+    if (t0 >= q1 && t0 - U < q1) __builtin_amdgcn_s_setprio(2);
+    if (t0 >= q2 && t0 - U < q2) __builtin_amdgcn_s_setprio(1);
+    if (t0 >= q3 && t0 - U < q3) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       if (t0 + j < units) {  // uniform
@@ -329,14 +342,6 @@ size_t gemv_rows_lds(int format, int k, int m) {
 }
 
 bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p) {
-  // 3-4 activation rows measured faster with the split-K kernel, whose lanes
-  // reuse each activation load for more weights
-  if (m >= 3) {
-#ifdef QMM_TUNE
-    if (!getenv("QMM_ROWS_ANY_M"))
-#endif
-      return false;
-  }
   const size_t lds = gemv_rows_lds(format, k, m);
   if (lds > kLdsLimit || (size_t)k / 32 * 4 * m > (size_t)kXPieces * kThreads) return false;
   const int cus = cu_count();
