@@ -275,13 +275,15 @@ GemmArgs weight_args(const qmm_weight &w) {
 
 hipError_t launch_gemm(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
                        hipStream_t s) {
-  // many rows: 256 x 256 tiles (gemm_wide.hip); fewer: 128 x 128 tiles, which
-  // keep more workgroups in flight
-  bool wide = false;
+  // from a few hundred rows on, 256-row weight tiles with the activations
+  // streamed straight into LDS (gemm_big.hip) move half the bytes per flop
+  bool big = m >= 256;
 #ifdef QMM_TUNE
-  if (const char *e = getenv("QMM_GEMM_WIDE")) wide = atoi(e) != 0;
+  if (const char *e = getenv("QMM_GEMM_BIG")) big = atoi(e) != 0;
 #endif
-  if (wide) return launch_gemm_wide(w, x, m, residual, y, s);
+  // the big-tile kernel addresses X and the weight planes with 32-bit offsets
+  if (big && (size_t)m * w.k * 2 < (1ull << 32) && (size_t)w.n * w.k < (1ull << 32))
+    return launch_gemm_big(w, x, m, residual, y, s);
   GemmArgs a = weight_args(w);
   a.x = (const uint16_t *)x;
   a.residual = (const uint16_t *)residual;

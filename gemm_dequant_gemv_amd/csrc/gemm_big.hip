@@ -1,0 +1,339 @@
+// qgemm with 256-row weight tiles, for prefill with many activation rows
+// (dense mode).  Same arithmetic as gemm.hip -- each weight decoded once per
+// tile into bfloat16 ("TurboEXL3" section 4.1: decode once, multiply many
+// times), v_mfma_f32_16x16x32_bf16, float32 sums over K in slice order -- on
+// a different data path:
+//
+//   * the activation tile (TM x 16 rows) goes from memory straight into LDS
+//     (buffer_load_dwordx4 ... lds), three 64-wide K slices in flight, with no
+//     register staging; its 16-byte chunks are XOR-swizzled by row so that the
+//     MFMA operand reads of 16 lanes cover all 64 banks once;
+//   * the weights never pass through LDS: each of the 4 waves owns 64 rows of
+//     the tile, loads their codes and scales itself (registers, three slices
+//     ahead) and decodes them straight into its MFMA A operands.  The K order
+//     inside a slice is permuted (lane group g of a 16-lane row holds K values
+//     16g .. 16g+15, the first 8 for the slice's first MFMA, the rest for the
+//     second) and the activation operand is read in the same order, so each
+//     lane decodes one contiguous 16-weight run of one row;
+//   * a wave computes 64 rows of W x 16 TM rows of X as 4 x TM MFMA tiles.
+//     TM = 8 (128 activation rows, 128 accumulators per lane) keeps two
+//     waves per SIMD; TM = 16 measured slower (its 256 accumulators leave one
+//     wave per SIMD and spill).
+//
+// Per slice and wave (TM = 8): 64 MFMAs, 64 decoded weights per lane, 16 KB
+// of LDS operand reads; per workgroup 16 KB of activations and 9-14 KB of
+// weight codes from memory, about 60% of what the 128 x 128 tiles of gemm.hip
+// move per flop.
+#include <atomic>
+#include <cstdlib>
+
+#include "gemm_common.h"
+
+namespace qmm {
+namespace {
+
+using namespace gemm;
+
+constexpr int kBN = 256;        // rows of W per workgroup (64 per wave)
+constexpr int kStages = 3;      // LDS stages of X = slices in flight
+constexpr int kXRow = kBK * 2;  // bytes of one X row in a slice
+constexpr int kTN = 4;          // 16-row W tiles per wave
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from buffer `r` (lane's byte offset voff + soff) to LDS at
+// dst + 16 * lane (an ordinary function, so that host passes over the kernel
+// templates never see the LDS address space)
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void *dst, uint32_t voff,
+                                                  uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, voff, soff, 0, 0);
+}
+
+// A 16-weight run of one row: codes and what scales them.
+struct Run {
+  uint2 q;     // 16 codes (Q6_K: low nibbles), value 2i in the low nibble of byte i
+  uint32_t h;  // Q6_K: 2 high bits per value
+  uint32_t s;  // affine (scale, bias) / E8M0 / E4M3 / Q6_K int8 sub-block scale
+  uint32_t d;  // Q6_K super-block scale
+};
+
+// Buffer descriptors and the per-lane constant parts of the weight offsets
+// (the lane's row and run); the slice's part goes in the scalar offset.
+struct WSrc {
+  __amdgpu_buffer_rsrc_t rc, rh, rs, rs2;
+  uint32_t v_code[kTN], v_hi[kTN], v_s[kTN], v_d[kTN];
+};
+
+template <int FMT>
+__device__ __forceinline__ Run load_run(const WSrc &w, int i, int s) {
+  Run p;
+  p.q = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(w.rc, w.v_code[i], s * (kBK / 2), 0));
+  if constexpr (FMT == QMM_AFFINE4_G64) {
+    p.s = __builtin_amdgcn_raw_buffer_load_b32(w.rs, w.v_s[i], s * 4, 0);
+  } else if constexpr (FMT == QMM_MXFP4) {
+    p.s = __builtin_amdgcn_raw_buffer_load_b8(w.rs, w.v_s[i], s * 2, 0);
+  } else if constexpr (FMT == QMM_NVFP4) {
+    p.s = __builtin_amdgcn_raw_buffer_load_b8(w.rs, w.v_s[i], s * 4, 0);
+  } else {
+    p.h = __builtin_amdgcn_raw_buffer_load_b32(w.rh, w.v_hi[i], s * (kBK / 4), 0);
+    p.s = __builtin_amdgcn_raw_buffer_load_b8(w.rs, w.v_s[i], s * 4, 0);
+    p.d = __builtin_amdgcn_raw_buffer_load_b16(w.rs2, w.v_d[i], (s / 4) * 2, 0);
+  }
+  return p;
+}
+
+// The run's 16 weights as bfloat16: values 0-7 -> lo, 8-15 -> hi.
+template <int FMT>
+__device__ __forceinline__ void decode_run(const Run &p, bf16x8_t &lo, bf16x8_t &hi) {
+  const uint32_t w[2] = {p.q.x, p.q.y};
+  uint32_t o[8];
+  if constexpr (FMT == QMM_AFFINE4_G64) {
+    const float s = half_to_float(p.s & 0xFFFFu), b = half_to_float(p.s >> 16);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      // even codes to the bytes of one word, odd codes to another, so that
+      // each code becomes a float with one v_cvt_f32_ubyteN
+      uint32_t ev = w[j] & 0x0F0F0F0Fu, od = (w[j] >> 4) & 0x0F0F0F0Fu;
+      asm volatile("" : "+v"(ev));
+      asm volatile("" : "+v"(od));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[4 * j + i] = pack_bf16(__builtin_fmaf(s, (float)((ev >> (8 * i)) & 0xFFu), b),
+                                 __builtin_fmaf(s, (float)((od >> (8 * i)) & 0xFFu), b));
+    }
+  } else if constexpr (FMT == QMM_MXFP4) {
+    const float sc = e8m0_to_float(p.s);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      o[4 * j + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 0));
+      o[4 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 1));
+      o[4 * j + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 2));
+      o[4 * j + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 3));
+    }
+  } else if constexpr (FMT == QMM_NVFP4) {
+    float sc, unused;
+    e4m3x2_to_float(p.s, sc, unused);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      // E2M1 pair -> two float32 (unit scale), times the E4M3 block scale
+      // (exact), -> bfloat16 pair (exact)
+      const f32x2_t e[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 0),
+                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 1),
+                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 2),
+                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 3)};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[4 * j + i] = pack_bf16(e[i][0] * sc, e[i][1] * sc);
+    }
+  } else {  // Q6_K: (d * sc) * (q - 32), exact in float32
+    const float dsc = half_to_float(p.d) * (float)(int8_t)(p.s & 0xFFu);
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      const uint32_t q0 = ((w[v / 8] >> (4 * (v % 8))) & 15u) | (((p.h >> (2 * v)) & 3u) << 4);
+      const uint32_t q1 = ((w[v / 8] >> (4 * (v % 8) + 4)) & 15u) | (((p.h >> (2 * v + 2)) & 3u) << 4);
+      o[v / 2] = pack_bf16(dsc * (float)((int)q0 - 32), dsc * (float)((int)q1 - 32));
+    }
+  }
+  lo = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
+  hi = __builtin_bit_cast(bf16x8_t, u32x4_t{o[4], o[5], o[6], o[7]});
+}
+
+// s_waitcnt with vmcnt <= n and the other counters left free (gfx9 encoding)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int FMT>
+constexpr int w_loads_per_run() { return FMT == QMM_Q6_K ? 4 : 2; }
+
+// TM 16-row X tiles per wave: BM = 16 TM rows of X per workgroup
+template <int FMT, int TM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM >= 16 ? 1 : 2)))
+void gemm_big_kernel(GemmArgs a) {
+  constexpr int BM = 16 * TM;
+  constexpr int kXStage = BM * kXRow;  // bytes per LDS stage
+  constexpr int XI = BM / 32;          // X load instructions per wave and slice (8 rows each)
+  extern __shared__ __align__(16) uint8_t lds[];  // kStages x [BM rows][128 bytes]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles_m = (a.m + BM - 1) / BM;
+  const int m0 = (blockIdx.x % tiles_m) * BM, n0 = (blockIdx.x / tiles_m) * kBN;
+  const int mrows = a.m - m0;
+  const int slices = a.k / kBK;
+  const uint32_t k = (uint32_t)a.k;
+  const int lr = lane & 15, g = lane >> 4;
+
+  // activations: wave w fills rows (BM/4) w .. of a stage, 8 rows per
+  // instruction; lane l of instruction i writes LDS chunk l % 8 of row
+  // (BM/4) w + 8i + l / 8, which holds the row's logical chunk (l % 8) ^ swz(row)
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(a.x, (uint32_t)((size_t)a.m * a.k * 2));
+  uint32_t v_x[XI];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int row = (BM / 4) * wave + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    v_x[i] = ((uint32_t)(m0 + min(row, mrows - 1)) * k + (uint32_t)c * 8) * 2;
+  }
+  auto load_x = [&](int s) __attribute__((always_inline)) {
+    uint8_t *st = lds + (s % kStages) * kXStage + wave * (BM / 4) * kXRow;
+#pragma unroll
+    for (int i = 0; i < XI; ++i)
+      buffer_load_lds16(rx, st + i * 8 * kXRow, v_x[i], s * kXRow);
+  };
+
+  // weights: lane (lr, g) of tile i holds row n0 + 64w + 16i + lr, run g
+  WSrc ws;
+  {
+    const size_t rows = (size_t)a.n;
+    ws.rc = make_rsrc(a.codes, (uint32_t)(rows * (k / 2)));
+    ws.rh = make_rsrc(a.codes_hi, a.codes_hi ? (uint32_t)(rows * (k / 4)) : 0u);
+    ws.rs = make_rsrc(a.scales, (uint32_t)(rows * (k / (FMT == QMM_AFFINE4_G64 ? 16 : (FMT == QMM_MXFP4 ? 32 : 16)))));
+    ws.rs2 = make_rsrc(a.scales2, a.scales2 ? (uint32_t)(rows * (k / 256) * 2) : 0u);
+#pragma unroll
+    for (int i = 0; i < kTN; ++i) {
+      const uint32_t r = (uint32_t)min(n0 + 64 * wave + 16 * i + lr, a.n - 1);
+      ws.v_code[i] = r * (k / 2) + 8 * g;
+      ws.v_hi[i] = r * (k / 4) + 4 * g;
+      ws.v_s[i] = FMT == QMM_AFFINE4_G64 ? r * (k / 64) * 4
+                : FMT == QMM_MXFP4       ? r * (k / 32) + (g >> 1)
+                                         : r * (k / 16) + g;
+      ws.v_d[i] = r * (k / 256) * 2;
+    }
+  }
+  Run wr[kStages][kTN];
+  auto load_w = [&](int s, int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kTN; ++i) wr[st][i] = load_run<FMT>(ws, i, s);
+  };
+
+  f32x4_t acc[kTN][TM];
+#pragma unroll
+  for (int i = 0; i < kTN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // operand reads of the activation tile: row 16j + lr, logical chunk 2g + kk
+  // at physical chunk (2g + kk) ^ swz(lr) (swz of 16j + lr is swz(lr))
+  const uint32_t xo0 = (uint32_t)lr * kXRow + (uint32_t)(((2 * g) ^ ((lr >> 1) & 7)) * 16);
+  const uint32_t xo1 = (uint32_t)lr * kXRow + (uint32_t)(((2 * g + 1) ^ ((lr >> 1) & 7)) * 16);
+
+  // slices 0 .. kStages-2 in flight; every iteration then issues one more
+  // (the last slice again past the end, so that every wave issues the same
+  // loads and the counts below hold)
+  constexpr int kLoadsPerSlice = XI + kTN * w_loads_per_run<FMT>();
+#pragma unroll
+  for (int p = 0; p < kStages - 1; ++p) {
+    const int sp = min(p, slices - 1);
+    load_x(sp);
+    load_w(sp, p);
+  }
+
+  for (int s0 = 0; s0 < slices; s0 += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+      const int s = s0 + u;
+      if (s >= slices) break;  // uniform
+      // this wave's share of slice s is in LDS once at most the loads issued
+      // after it (kStages - 2 slices) are outstanding; the barrier then makes
+      // every wave's share visible and frees the stage read in iteration s - 1
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kLoadsPerSlice));
+      __syncthreads();
+      const int sn = min(s + kStages - 1, slices - 1);
+      load_x(sn);
+      load_w(sn, (u + kStages - 1) % kStages);
+
+      bf16x8_t af[kTN][2];
+#pragma unroll
+      for (int i = 0; i < kTN; ++i) decode_run<FMT>(wr[u][i], af[i][0], af[i][1]);
+
+      const uint8_t *st = lds + (s % kStages) * kXStage;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          const bf16x8_t bfr = *(const bf16x8_t *)(st + j * 16 * kXRow + (kk ? xo1 : xo0));
+#pragma unroll
+          for (int i = 0; i < kTN; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i][kk], bfr, acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // epilogue: lane holds D[n = 4*(lane/16) + r][m = lane % 16] of each tile
+  const float gs = (FMT == QMM_NVFP4 && a.tensor_scale) ? a.tensor_scale[0] : 1.0f;
+#pragma unroll
+  for (int i = 0; i < kTN; ++i) {
+    const int nb = n0 + 64 * wave + 16 * i + 4 * g;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int ml = 16 * j + lr;
+      if (ml >= mrows) continue;
+      const int m = m0 + ml;
+      float v[4] = {acc[i][j][0] * gs, acc[i][j][1] * gs, acc[i][j][2] * gs, acc[i][j][3] * gs};
+      const size_t base = (size_t)m * a.n + nb;
+      if (nb + 3 < a.n && (a.n & 3) == 0) {
+        if (a.residual) {
+          const uint2 r = *(const uint2 *)(a.residual + base);
+          v[0] += bf_lo(r.x);
+          v[1] += bf_hi(r.x);
+          v[2] += bf_lo(r.y);
+          v[3] += bf_hi(r.y);
+        }
+        *(uint2 *)(a.y + base) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (nb + r >= a.n) break;
+          float t = v[r];
+          if (a.residual) t += bf_lo(a.residual[base + r]);
+          a.y[base + r] = __builtin_bit_cast(uint16_t, (__bf16)t);
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, int TM>
+hipError_t launch_big(const GemmArgs &a, hipStream_t s) {
+  constexpr int BM = 16 * TM;
+  constexpr size_t lds = (size_t)kStages * BM * kXRow;
+  static std::atomic<uint64_t> configured{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(configured.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void *)gemm_big_kernel<FMT, TM>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    configured.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  const unsigned blocks = (unsigned)(((a.m + BM - 1) / BM) * ((a.n + kBN - 1) / kBN));
+  hipLaunchKernelGGL((gemm_big_kernel<FMT, TM>), dim3(blocks), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
+                           hipStream_t s) {
+  GemmArgs a{};
+  a.codes = (const uint8_t *)w.codes;
+  a.codes_hi = (const uint8_t *)w.codes_hi;
+  a.scales = (const uint8_t *)w.scales;
+  a.scales2 = (const uint8_t *)w.scales2;
+  a.tensor_scale = w.tensor_scale;
+  a.x = (const uint16_t *)x;
+  a.residual = (const uint16_t *)residual;
+  a.y = (uint16_t *)y;
+  a.m = m;
+  a.n = w.n;
+  a.k = w.k;
+  switch (w.format) {
+    case QMM_AFFINE4_G64: return launch_big<QMM_AFFINE4_G64, 8>(a, s);
+    case QMM_MXFP4: return launch_big<QMM_MXFP4, 8>(a, s);
+    case QMM_NVFP4: return launch_big<QMM_NVFP4, 8>(a, s);
+    default: return launch_big<QMM_Q6_K, 8>(a, s);
+  }
+}
+
+}  // namespace qmm

@@ -20,10 +20,6 @@ struct FmtTraits {
   static constexpr int kKPerScaleByte = FMT == QMM_MXFP4 ? 32 : 16;
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
 
 // One row's data for one step.
 struct RowData {

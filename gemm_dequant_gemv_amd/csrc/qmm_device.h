@@ -65,6 +65,13 @@ __device__ __forceinline__ void e4m3x2_to_float(uint32_t w, float &s0, float &s1
   s1 = v.y;
 }
 
+// Buffer resource for raw buffer loads of `bytes` bytes at `base`; loads past
+// the end return zeros (a null base with 0 bytes is a buffer that reads 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 // float32 -> bfloat16 bits, round to nearest even, NaN kept quiet.
 __device__ __forceinline__ uint32_t float_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);

@@ -71,8 +71,8 @@ hipError_t launch_gemv_rows(const qmm_weight &w, const void *x, int m, const voi
 hipError_t launch_gemv(const qmm_weight &w, const void *x, int m, const void *residual,
                        void *y, int y_dtype, void *workspace, const GemvPlan &p,
                        hipStream_t s);
-hipError_t launch_gemm_wide(const qmm_weight &w, const void *x, int m, const void *residual,
-                            void *y, hipStream_t s);
+hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void *residual,
+                           void *y, hipStream_t s);
 hipError_t launch_gemm(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
                        hipStream_t s);
 hipError_t launch_moe_gemm_gate_up(const qmm_weight &gu, const void *x, const MoeTables &t,
