@@ -268,6 +268,7 @@ GemmArgs weight_args(const qmm_weight &w) {
   a.tensor_scale = w.tensor_scale;
   a.n = w.n;
   a.k = w.k;
+  a.wrows = w.batch * w.n;
   return a;
 }
 
@@ -281,9 +282,7 @@ hipError_t launch_gemm(const qmm_weight &w, const void *x, int m, const void *re
 #ifdef QMM_TUNE
   if (const char *e = getenv("QMM_GEMM_BIG")) big = atoi(e) != 0;
 #endif
-  // the big-tile kernel addresses X and the weight planes with 32-bit offsets
-  if (big && (size_t)m * w.k * 2 < (1ull << 32) && (size_t)w.n * w.k < (1ull << 32))
-    return launch_gemm_big(w, x, m, residual, y, s);
+  if (big && gemm_big_fits(w, (size_t)m)) return launch_gemm_big(w, x, m, residual, y, s);
   GemmArgs a = weight_args(w);
   a.x = (const uint16_t *)x;
   a.residual = (const uint16_t *)residual;

@@ -143,8 +143,11 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 template <int FMT>
 constexpr int w_loads_per_run() { return FMT == QMM_Q6_K ? 4 : 2; }
 
-// TM 16-row X tiles per wave: BM = 16 TM rows of X per workgroup
-template <int FMT, int TM>
+// TM 16-row X tiles per wave: BM = 16 TM rows of X per workgroup.  MODE as
+// in gemm.hip: dense, or the grouped MoE gate/up (rows of x gathered by token,
+// gate and up weight rows interleaved, SwiGLU epilogue) and down products
+// over the routing tile table (tiles of BM grouped rows, one expert each).
+template <int FMT, int TM, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM >= 16 ? 1 : 2)))
 void gemm_big_kernel(GemmArgs a) {
   constexpr int BM = 16 * TM;
@@ -153,9 +156,21 @@ void gemm_big_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];  // kStages x [BM rows][128 bytes]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tiles_m = (a.m + BM - 1) / BM;
-  const int m0 = (blockIdx.x % tiles_m) * BM, n0 = (blockIdx.x / tiles_m) * kBN;
-  const int mrows = a.m - m0;
+  int m0, n0, mrows, wrow0 = 0, expert = 0;
+  if constexpr (MODE == kDense) {
+    const int tiles_m = (a.m + BM - 1) / BM;
+    m0 = (blockIdx.x % tiles_m) * BM;
+    n0 = (blockIdx.x / tiles_m) * kBN;
+    mrows = a.m - m0;
+  } else {
+    if (blockIdx.x >= *a.n_tiles) return;  // beyond this call's tiles (whole workgroup)
+    const uint32_t *t = a.tiles + 3 * blockIdx.x;
+    expert = (int)t[0];
+    m0 = (int)t[1];
+    mrows = (int)t[2];
+    n0 = blockIdx.y * kBN;
+    wrow0 = expert * a.n;  // first row of the expert's matrix
+  }
   const int slices = a.k / kBK;
   const uint32_t k = (uint32_t)a.k;
   const int lr = lane & 15, g = lane >> 4;
@@ -163,14 +178,19 @@ void gemm_big_kernel(GemmArgs a) {
   // activations: wave w fills rows (BM/4) w .. of a stage, 8 rows per
   // instruction; lane l of instruction i writes LDS chunk l % 8 of row
   // (BM/4) w + 8i + l / 8, which holds the row's logical chunk (l % 8) ^ swz(row)
+  // (grouped modes: the routing tables index valid rows of x or h, whose
+  // extent the call does not pass; their descriptor spans the 32-bit range)
   const __amdgpu_buffer_rsrc_t rx =
-      make_rsrc(a.x, (uint32_t)((size_t)a.m * a.k * 2));
+      MODE == kDense ? make_rsrc(a.x, (uint32_t)((size_t)a.m * a.k * 2))
+                     : make_rsrc(MODE == kMoeGateUp ? (const void *)a.x : (const void *)a.h, 0xFFFFFFFFu);
   uint32_t v_x[XI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
     const int row = (BM / 4) * wave + 8 * i + (lane >> 3);
     const int c = (lane & 7) ^ ((row >> 1) & 7);
-    v_x[i] = ((uint32_t)(m0 + min(row, mrows - 1)) * k + (uint32_t)c * 8) * 2;
+    const int rr = m0 + min(row, mrows - 1);
+    const uint32_t src = MODE == kMoeGateUp ? a.token_of_row[rr] : (uint32_t)rr;
+    v_x[i] = (src * k + (uint32_t)c * 8) * 2;
   }
   auto load_x = [&](int s) __attribute__((always_inline)) {
     uint8_t *st = lds + (s % kStages) * kXStage + wave * (BM / 4) * kXRow;
@@ -179,17 +199,24 @@ void gemm_big_kernel(GemmArgs a) {
       buffer_load_lds16(rx, st + i * 8 * kXRow, v_x[i], s * kXRow);
   };
 
-  // weights: lane (lr, g) of tile i holds row n0 + 64w + 16i + lr, run g
+  // weights: lane (lr, g) of tile i holds tile row j = 64w + 16i + lr, run g;
+  // tile row j is weight row n0 + j, or in the gate/up mode gate or up row
+  // n0/2 + j/2 of the expert (even j gate, odd j up)
   WSrc ws;
   {
-    const size_t rows = (size_t)a.n;
+    const size_t rows = (size_t)a.wrows;
     ws.rc = make_rsrc(a.codes, (uint32_t)(rows * (k / 2)));
     ws.rh = make_rsrc(a.codes_hi, a.codes_hi ? (uint32_t)(rows * (k / 4)) : 0u);
     ws.rs = make_rsrc(a.scales, (uint32_t)(rows * (k / (FMT == QMM_AFFINE4_G64 ? 16 : (FMT == QMM_MXFP4 ? 32 : 16)))));
     ws.rs2 = make_rsrc(a.scales2, a.scales2 ? (uint32_t)(rows * (k / 256) * 2) : 0u);
 #pragma unroll
     for (int i = 0; i < kTN; ++i) {
-      const uint32_t r = (uint32_t)min(n0 + 64 * wave + 16 * i + lr, a.n - 1);
+      const int j = 64 * wave + 16 * i + lr;
+      uint32_t r;
+      if constexpr (MODE == kMoeGateUp)
+        r = (uint32_t)(wrow0 + ((j & 1) ? a.inter : 0) + min(n0 / 2 + j / 2, a.inter - 1));
+      else
+        r = (uint32_t)(wrow0 + min(n0 + j, a.n - 1));
       ws.v_code[i] = r * (k / 2) + 8 * g;
       ws.v_hi[i] = r * (k / 4) + 4 * g;
       ws.v_s[i] = FMT == QMM_AFFINE4_G64 ? r * (k / 64) * 4
@@ -247,28 +274,53 @@ void gemm_big_kernel(GemmArgs a) {
       const uint8_t *st = lds + (s % kStages) * kXStage;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
+        // all of this half-slice's activation operands first, so that the
+        // MFMAs below do not wait on LDS after every four
+        bf16x8_t bfr[TM];
 #pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          const bf16x8_t bfr = *(const bf16x8_t *)(st + j * 16 * kXRow + (kk ? xo1 : xo0));
+        for (int j = 0; j < TM; ++j) bfr[j] = *(const bf16x8_t *)(st + j * 16 * kXRow + (kk ? xo1 : xo0));
+        // (Q6_K's longer decode leaves no registers for that)
+        if constexpr (FMT != QMM_Q6_K) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
 #pragma unroll
           for (int i = 0; i < kTN; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i][kk], bfr, acc[i][j], 0, 0, 0);
-        }
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i][kk], bfr[j], acc[i][j], 0, 0, 0);
       }
     }
   }
 
   // epilogue: lane holds D[n = 4*(lane/16) + r][m = lane % 16] of each tile
-  const float gs = (FMT == QMM_NVFP4 && a.tensor_scale) ? a.tensor_scale[0] : 1.0f;
+  const float gs = (FMT == QMM_NVFP4 && a.tensor_scale) ? a.tensor_scale[expert] : 1.0f;
 #pragma unroll
   for (int i = 0; i < kTN; ++i) {
-    const int nb = n0 + 64 * wave + 16 * i + 4 * g;
+    const int nl = 64 * wave + 16 * i + 4 * g;  // tile row of v[0]
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       const int ml = 16 * j + lr;
       if (ml >= mrows) continue;
       const int m = m0 + ml;
       float v[4] = {acc[i][j][0] * gs, acc[i][j][1] * gs, acc[i][j][2] * gs, acc[i][j][3] * gs};
+      if constexpr (MODE == kMoeGateUp) {
+        // (gate, up, gate, up) of two consecutive intermediate columns; SwiGLU
+        // in float32: h = silu(g) * u, silu(g) = g / (1 + e^-g)
+        const int col = n0 / 2 + nl / 2;  // even, and I is even
+        if (col < a.inter) {
+          const float h0 = v[0] / (1.0f + expf(-v[0])) * v[1];
+          const float h1 = v[2] / (1.0f + expf(-v[2])) * v[3];
+          *(uint32_t *)(a.h + (size_t)m * a.inter + col) = pack_bf16(h0, h1);
+        }
+        continue;
+      } else if constexpr (MODE == kMoeDown) {
+        const int nb = n0 + nl;
+        if (nb + 3 < a.n) {
+          *(float4 *)(a.d + (size_t)m * a.n + nb) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          for (int r = 0; r < 4 && nb + r < a.n; ++r) a.d[(size_t)m * a.n + nb + r] = v[r];
+        }
+        continue;
+      }
+      const int nb = n0 + nl;
       const size_t base = (size_t)m * a.n + nb;
       if (nb + 3 < a.n && (a.n & 3) == 0) {
         if (a.residual) {
@@ -292,48 +344,90 @@ void gemm_big_kernel(GemmArgs a) {
   }
 }
 
-template <int FMT, int TM>
-hipError_t launch_big(const GemmArgs &a, hipStream_t s) {
-  constexpr int BM = 16 * TM;
-  constexpr size_t lds = (size_t)kStages * BM * kXRow;
+template <int FMT, int MODE>
+hipError_t launch_big(const GemmArgs &a, dim3 grid, hipStream_t s) {
+  constexpr int TM = 8;
+  static_assert(16 * TM == kGemmBM, "X tiles are the routing table's tiles of kGemmBM rows");
+  constexpr size_t lds = (size_t)kStages * 16 * TM * kXRow;
+  // more than 64 KiB of dynamic LDS must be allowed once per device
   static std::atomic<uint64_t> configured{0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(configured.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute((const void *)gemm_big_kernel<FMT, TM>,
+    e = hipFuncSetAttribute((const void *)gemm_big_kernel<FMT, TM, MODE>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_acq_rel);
   }
-  const unsigned blocks = (unsigned)(((a.m + BM - 1) / BM) * ((a.n + kBN - 1) / kBN));
-  hipLaunchKernelGGL((gemm_big_kernel<FMT, TM>), dim3(blocks), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((gemm_big_kernel<FMT, TM, MODE>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
-}  // namespace
+template <int MODE>
+hipError_t launch_big_mode(int format, const GemmArgs &a, dim3 grid, hipStream_t s) {
+  switch (format) {
+    case QMM_AFFINE4_G64: return launch_big<QMM_AFFINE4_G64, MODE>(a, grid, s);
+    case QMM_MXFP4: return launch_big<QMM_MXFP4, MODE>(a, grid, s);
+    case QMM_NVFP4: return launch_big<QMM_NVFP4, MODE>(a, grid, s);
+    default: return launch_big<QMM_Q6_K, MODE>(a, grid, s);
+  }
+}
 
-hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
-                           hipStream_t s) {
+GemmArgs big_args(const qmm_weight &w) {
   GemmArgs a{};
   a.codes = (const uint8_t *)w.codes;
   a.codes_hi = (const uint8_t *)w.codes_hi;
   a.scales = (const uint8_t *)w.scales;
   a.scales2 = (const uint8_t *)w.scales2;
   a.tensor_scale = w.tensor_scale;
+  a.n = w.n;
+  a.k = w.k;
+  a.wrows = w.batch * w.n;
+  return a;
+}
+
+}  // namespace
+
+bool gemm_big_fits(const qmm_weight &w, size_t x_rows) {
+  // 32-bit buffer offsets for X and every weight plane
+  return x_rows * (size_t)w.k * 2 < (1ull << 32) && (size_t)w.batch * w.n * w.k < (1ull << 32);
+}
+
+hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
+                           hipStream_t s) {
+  GemmArgs a = big_args(w);
   a.x = (const uint16_t *)x;
   a.residual = (const uint16_t *)residual;
   a.y = (uint16_t *)y;
   a.m = m;
-  a.n = w.n;
-  a.k = w.k;
-  switch (w.format) {
-    case QMM_AFFINE4_G64: return launch_big<QMM_AFFINE4_G64, 8>(a, s);
-    case QMM_MXFP4: return launch_big<QMM_MXFP4, 8>(a, s);
-    case QMM_NVFP4: return launch_big<QMM_NVFP4, 8>(a, s);
-    default: return launch_big<QMM_Q6_K, 8>(a, s);
-  }
+  const unsigned blocks = (unsigned)(((m + kGemmBM - 1) / kGemmBM) * ((w.n + kBN - 1) / kBN));
+  return launch_big_mode<kDense>(w.format, a, dim3(blocks), s);
+}
+
+hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const MoeTables &t,
+                                  int max_tiles, hipStream_t s) {
+  GemmArgs a = big_args(gu);
+  a.x = (const uint16_t *)x;
+  a.tiles = t.tiles;
+  a.n_tiles = t.n_tiles;
+  a.token_of_row = t.token_of_row;
+  a.h = t.h;
+  a.inter = gu.n / 2;
+  // each workgroup covers 128 intermediate columns (256 interleaved rows)
+  return launch_big_mode<kMoeGateUp>(gu.format, a, dim3(max_tiles, (gu.n + kBN - 1) / kBN), s);
+}
+
+hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
+                               hipStream_t s) {
+  GemmArgs a = big_args(dn);
+  a.tiles = t.tiles;
+  a.n_tiles = t.n_tiles;
+  a.h = t.h;
+  a.d = t.d;
+  a.inter = dn.k;
+  return launch_big_mode<kMoeDown>(dn.format, a, dim3(max_tiles, (dn.n + kBN - 1) / kBN), s);
 }
 
 }  // namespace qmm

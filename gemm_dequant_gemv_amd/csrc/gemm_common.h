@@ -33,6 +33,7 @@ struct GemmArgs {
   const uint16_t *residual;
   uint16_t *y;
   int m, n, k;
+  int wrows;                     // rows of the weight planes (all experts)
   // grouped (MoE) modes
   const uint32_t *tiles;         // [max_tiles][3] = (expert, first grouped row, rows)
   const uint32_t *n_tiles;       // device count of valid tiles

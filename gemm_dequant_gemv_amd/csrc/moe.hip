@@ -286,9 +286,17 @@ hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ra);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_moe_gemm_gate_up(gu, x, tb, (int)L.max_tiles, s);
+    // 256-row weight tiles decoded straight into MFMA operands (gemm_big.hip)
+    // where their 32-bit offsets reach; the LDS-staged 128 x 128 tiles else
+    bool big = gemm_big_fits(gu, (size_t)t) && gemm_big_fits(dn, L.max_rows) && (gu.n / 2) % 2 == 0;
+#ifdef QMM_TUNE
+    if (const char *ev = getenv("QMM_MOE_BIG")) big = big && atoi(ev) != 0;
+#endif
+    e = big ? launch_moe_big_gate_up(gu, x, tb, (int)L.max_tiles, s)
+            : launch_moe_gemm_gate_up(gu, x, tb, (int)L.max_tiles, s);
     if (e != hipSuccess) return e;
-    e = launch_moe_gemm_down(dn, tb, (int)L.max_tiles, s);
+    e = big ? launch_moe_big_down(dn, tb, (int)L.max_tiles, s)
+            : launch_moe_gemm_down(dn, tb, (int)L.max_tiles, s);
     if (e != hipSuccess) return e;
   }
 

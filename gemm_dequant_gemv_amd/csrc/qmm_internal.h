@@ -73,6 +73,13 @@ hipError_t launch_gemv(const qmm_weight &w, const void *x, int m, const void *re
                        hipStream_t s);
 hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void *residual,
                            void *y, hipStream_t s);
+// the 256-row-tile kernels (gemm_big.hip) address X (x_rows rows) and the
+// weight planes with 32-bit offsets
+bool gemm_big_fits(const qmm_weight &w, size_t x_rows);
+hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const MoeTables &t,
+                                  int max_tiles, hipStream_t s);
+hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
+                               hipStream_t s);
 hipError_t launch_gemm(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
                        hipStream_t s);
 hipError_t launch_moe_gemm_gate_up(const qmm_weight &gu, const void *x, const MoeTables &t,
