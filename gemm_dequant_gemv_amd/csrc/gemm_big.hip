@@ -8,21 +8,23 @@
 //     (buffer_load_dwordx4 ... lds), three 64-wide K slices in flight, with no
 //     register staging; its 16-byte chunks are XOR-swizzled by row so that the
 //     MFMA operand reads of a lane group fall on distinct LDS bank groups;
-//   * the weights never pass through LDS: each of the 4 waves owns 64 rows of
-//     the tile, loads their codes and scales itself (registers, three slices
+//   * the weights never pass through LDS: each wave owns 16 TN rows of the
+//     tile, loads their codes and scales itself (registers, three slices
 //     ahead) and decodes them straight into its MFMA A operands.  The K order
 //     inside a slice is permuted (lane group g of a 16-lane row holds K values
 //     16g .. 16g+15, the first 8 for the slice's first MFMA, the rest for the
 //     second) and the activation operand is read in the same order, so each
 //     lane decodes one contiguous 16-weight run of one row;
-//   * a wave computes 64 rows of W x 16 TM rows of X as 4 x TM MFMA tiles.
-//     TM = 8 (128 activation rows, 128 accumulators per lane) keeps two
-//     waves per SIMD; TM = 16 measured slower (its 256 accumulators leave one
-//     wave per SIMD and spill).
+//   * a wave computes TN x TM MFMA tiles (16 TN rows of W x 16 TM rows of X).
+//     Dense: 8 waves of 32 W rows x 256 X rows (TN = 2, TM = 16), so that
+//     each decoded weight feeds 32 MFMAs of its slice; the grouped MoE modes
+//     keep 4 waves of 64 x 128, the routing table's tile height.  Either way
+//     a wave holds 128 float32 accumulators and two waves share a SIMD.
+//     (One wave of 64 x 256, with 256 accumulators, spilled.)
 //
-// Per slice and wave (TM = 8): 64 MFMAs, 64 decoded weights per lane, 16 KB
-// of LDS operand reads; per workgroup 16 KB of activations and 9-14 KB of
-// weight codes from memory, about 60% of what the 128 x 128 tiles of gemm.hip
+// Per slice and wave (dense): 64 MFMAs, 32 decoded weights per lane, 32 KB of
+// LDS operand reads; per workgroup 32 KB of activations and 9-14 KB of
+// weight codes from memory, about half of what the 128 x 128 tiles of gemm.hip
 // move per flop.
 #include <atomic>
 #include <cstdlib>
@@ -37,7 +39,6 @@ using namespace gemm;
 constexpr int kBN = 256;        // rows of W per workgroup (64 per wave)
 constexpr int kStages = 3;      // LDS stages of X = slices in flight
 constexpr int kXRow = kBK * 2;  // bytes of one X row in a slice
-constexpr int kTN = 4;          // 16-row W tiles per wave
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -61,7 +62,7 @@ struct Run {
 // (the lane's row and run); the slice's part goes in the scalar offset.
 struct WSrc {
   __amdgpu_buffer_rsrc_t rc, rh, rs, rs2;
-  uint32_t v_code[kTN], v_hi[kTN], v_s[kTN], v_d[kTN];
+  uint32_t v_code[4], v_hi[4], v_s[4], v_d[4];  // per W tile (TN <= 4)
 };
 
 template <int FMT>
@@ -149,16 +150,21 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 template <int FMT>
 constexpr int w_loads_per_run() { return FMT == QMM_Q6_K ? 4 : 2; }
 
-// TM 16-row X tiles per wave: BM = 16 TM rows of X per workgroup.  MODE as
-// in gemm.hip: dense, or the grouped MoE gate/up (rows of x gathered by token,
-// gate and up weight rows interleaved, SwiGLU epilogue) and down products
-// over the routing tile table (tiles of BM grouped rows, one expert each).
-template <int FMT, int TM, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM >= 16 ? 1 : 2)))
+// A wave computes TN x TM MFMA tiles: 16 TN rows of W x 16 TM rows of X;
+// the workgroup's 16 / TN waves cover the 256 rows of W, all sharing the
+// BM = 16 TM rows of X.  MODE as in gemm.hip: dense, or the grouped MoE
+// gate/up (rows of x gathered by token, gate and up weight rows interleaved,
+// SwiGLU epilogue) and down products over the routing tile table (tiles of BM
+// grouped rows, one expert each).
+template <int FMT, int TN, int TM, int MODE>
+__global__ __launch_bounds__(64 * (16 / TN)) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_big_kernel(GemmArgs a) {
+  constexpr int kTN = TN;
+  constexpr int WAVES = 16 / TN;
+  constexpr int WROWS = 16 * TN;  // W rows per wave
   constexpr int BM = 16 * TM;
   constexpr int kXStage = BM * kXRow;  // bytes per LDS stage
-  constexpr int XI = BM / 32;          // X load instructions per wave and slice (8 rows each)
+  constexpr int XI = BM / (8 * WAVES);  // X load instructions per wave and slice (8 rows each)
   extern __shared__ __align__(16) uint8_t lds[];  // kStages x [BM rows][128 bytes]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -192,14 +198,14 @@ void gemm_big_kernel(GemmArgs a) {
   uint32_t v_x[XI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
-    const int row = (BM / 4) * wave + 8 * i + (lane >> 3);
+    const int row = (BM / WAVES) * wave + 8 * i + (lane >> 3);
     const int c = (lane & 7) ^ swz(row);
     const int rr = m0 + min(row, mrows - 1);
     const uint32_t src = MODE == kMoeGateUp ? a.token_of_row[rr] : (uint32_t)rr;
     v_x[i] = (src * k + (uint32_t)c * 8) * 2;
   }
   auto load_x = [&](int s) __attribute__((always_inline)) {
-    uint8_t *st = lds + (s % kStages) * kXStage + wave * (BM / 4) * kXRow;
+    uint8_t *st = lds + (s % kStages) * kXStage + wave * (BM / WAVES) * kXRow;
 #pragma unroll
     for (int i = 0; i < XI; ++i)
       buffer_load_lds16(rx, st + i * 8 * kXRow, v_x[i], s * kXRow);
@@ -217,7 +223,7 @@ void gemm_big_kernel(GemmArgs a) {
     ws.rs2 = make_rsrc(a.scales2, a.scales2 ? (uint32_t)(rows * (k / 256) * 2) : 0u);
 #pragma unroll
     for (int i = 0; i < kTN; ++i) {
-      const int j = 64 * wave + 16 * i + lr;
+      const int j = WROWS * wave + 16 * i + lr;
       uint32_t r;
       if constexpr (MODE == kMoeGateUp)
         r = (uint32_t)(wrow0 + ((j & 1) ? a.inter : 0) + min(n0 / 2 + j / 2, a.inter - 1));
@@ -300,7 +306,7 @@ void gemm_big_kernel(GemmArgs a) {
   const float gs = (FMT == QMM_NVFP4 && a.tensor_scale) ? a.tensor_scale[expert] : 1.0f;
 #pragma unroll
   for (int i = 0; i < kTN; ++i) {
-    const int nl = 64 * wave + 16 * i + 4 * g;  // tile row of v[0]
+    const int nl = WROWS * wave + 16 * i + 4 * g;  // tile row of v[0]
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       const int ml = 16 * j + lr;
@@ -350,10 +356,10 @@ void gemm_big_kernel(GemmArgs a) {
   }
 }
 
-template <int FMT, int MODE>
+template <int FMT, int TN, int TM, int MODE>
 hipError_t launch_big(const GemmArgs &a, dim3 grid, hipStream_t s) {
-  constexpr int TM = 8;
-  static_assert(16 * TM == kGemmBM, "X tiles are the routing table's tiles of kGemmBM rows");
+  static_assert(MODE == kDense || 16 * TM == kGemmBM,
+                "X tiles are the routing table's tiles of kGemmBM rows");
   constexpr size_t lds = (size_t)kStages * 16 * TM * kXRow;
   // more than 64 KiB of dynamic LDS must be allowed once per device
   static std::atomic<uint64_t> configured{0};
@@ -362,22 +368,22 @@ hipError_t launch_big(const GemmArgs &a, dim3 grid, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(configured.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute((const void *)gemm_big_kernel<FMT, TM, MODE>,
+    e = hipFuncSetAttribute((const void *)gemm_big_kernel<FMT, TN, TM, MODE>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((gemm_big_kernel<FMT, TM, MODE>), grid, dim3(256), lds, s, a);
+  hipLaunchKernelGGL((gemm_big_kernel<FMT, TN, TM, MODE>), grid, dim3(64 * (16 / TN)), lds, s, a);
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int TN, int TM, int MODE>
 hipError_t launch_big_mode(int format, const GemmArgs &a, dim3 grid, hipStream_t s) {
   switch (format) {
-    case QMM_AFFINE4_G64: return launch_big<QMM_AFFINE4_G64, MODE>(a, grid, s);
-    case QMM_MXFP4: return launch_big<QMM_MXFP4, MODE>(a, grid, s);
-    case QMM_NVFP4: return launch_big<QMM_NVFP4, MODE>(a, grid, s);
-    default: return launch_big<QMM_Q6_K, MODE>(a, grid, s);
+    case QMM_AFFINE4_G64: return launch_big<QMM_AFFINE4_G64, TN, TM, MODE>(a, grid, s);
+    case QMM_MXFP4: return launch_big<QMM_MXFP4, TN, TM, MODE>(a, grid, s);
+    case QMM_NVFP4: return launch_big<QMM_NVFP4, TN, TM, MODE>(a, grid, s);
+    default: return launch_big<QMM_Q6_K, TN, TM, MODE>(a, grid, s);
   }
 }
 
@@ -408,8 +414,15 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
   a.residual = (const uint16_t *)residual;
   a.y = (uint16_t *)y;
   a.m = m;
-  const unsigned blocks = (unsigned)(((m + kGemmBM - 1) / kGemmBM) * ((w.n + kBN - 1) / kBN));
-  return launch_big_mode<kDense>(w.format, a, dim3(blocks), s);
+  const unsigned nt = (unsigned)((w.n + kBN - 1) / kBN);
+  // 8 waves of 32 W rows x 256 X rows: each decoded weight feeds twice the
+  // MFMAs of the 4-wave form (measured 1.3x faster from M = 512 on)
+  bool wide = true;
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_BIG_WIDE")) wide = atoi(e) != 0;
+#endif
+  if (wide) return launch_big_mode<2, 16, kDense>(w.format, a, dim3(((m + 255) / 256) * nt), s);
+  return launch_big_mode<4, 8, kDense>(w.format, a, dim3(((m + 127) / 128) * nt), s);
 }
 
 hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const MoeTables &t,
@@ -422,7 +435,7 @@ hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const Moe
   a.h = t.h;
   a.inter = gu.n / 2;
   // each workgroup covers 128 intermediate columns (256 interleaved rows)
-  return launch_big_mode<kMoeGateUp>(gu.format, a, dim3(max_tiles, (gu.n + kBN - 1) / kBN), s);
+  return launch_big_mode<4, 8, kMoeGateUp>(gu.format, a, dim3(max_tiles, (gu.n + kBN - 1) / kBN), s);
 }
 
 hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
@@ -433,7 +446,7 @@ hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max
   a.h = t.h;
   a.d = t.d;
   a.inter = dn.k;
-  return launch_big_mode<kMoeDown>(dn.format, a, dim3(max_tiles, (dn.n + kBN - 1) / kBN), s);
+  return launch_big_mode<4, 8, kMoeDown>(dn.format, a, dim3(max_tiles, (dn.n + kBN - 1) / kBN), s);
 }
 
 }  // namespace qmm
