@@ -238,14 +238,18 @@ int gemm_depth() {
   return pd;
 }
 
+// activation rows per tile: kGemmBM dense, the routing table's tiles grouped
+template <int MODE>
+constexpr int kTileM = MODE == kDense ? kGemmBM : kMoeTileRows;
+
 template <int FMT, int MODE>
 hipError_t launch_fd(const GemmArgs &a, dim3 grid, hipStream_t s) {
   switch (gemm_depth()) {
 #ifdef QMM_TUNE
-    case 2: return launch_tile<FMT, kGemmBM, 128, MODE, 2>(a, grid, s);
-    case 3: return launch_tile<FMT, kGemmBM, 128, MODE, 3>(a, grid, s);
+    case 2: return launch_tile<FMT, kTileM<MODE>, 128, MODE, 2>(a, grid, s);
+    case 3: return launch_tile<FMT, kTileM<MODE>, 128, MODE, 3>(a, grid, s);
 #endif
-    default: return launch_tile<FMT, kGemmBM, 128, MODE, 1>(a, grid, s);
+    default: return launch_tile<FMT, kTileM<MODE>, 128, MODE, 1>(a, grid, s);
   }
 }
 

@@ -17,9 +17,10 @@
 //     lane decodes one contiguous 16-weight run of one row;
 //   * a wave computes TN x TM MFMA tiles (16 TN rows of W x 16 TM rows of X).
 //     Dense: 8 waves of 32 W rows x 256 X rows (TN = 2, TM = 16), so that
-//     each decoded weight feeds 32 MFMAs of its slice; the grouped MoE modes
-//     keep 4 waves of 64 x 128, the routing table's tile height.  Either way
-//     a wave holds 128 float32 accumulators and two waves share a SIMD.
+//     each decoded weight feeds 32 MFMAs of its slice, as do the grouped MoE
+//     modes (256 rows is the routing table's tile height); 4 waves of 64 x 128
+//     (TN = 4, TM = 8) remain for comparison.  Either way a wave holds 128
+//     float32 accumulators and two waves share a SIMD.
 //     (One wave of 64 x 256, with 256 accumulators, spilled.)
 //
 // Per slice and wave (dense): 64 MFMAs, 32 decoded weights per lane, 32 KB of
@@ -358,8 +359,8 @@ void gemm_big_kernel(GemmArgs a) {
 
 template <int FMT, int TN, int TM, int MODE>
 hipError_t launch_big(const GemmArgs &a, dim3 grid, hipStream_t s) {
-  static_assert(MODE == kDense || 16 * TM == kGemmBM,
-                "X tiles are the routing table's tiles of kGemmBM rows");
+  static_assert(MODE == kDense || 16 * TM == kMoeTileRows,
+                "X tiles are the routing table's tiles of kMoeTileRows rows");
   constexpr size_t lds = (size_t)kStages * 16 * TM * kXRow;
   // more than 64 KiB of dynamic LDS must be allowed once per device
   static std::atomic<uint64_t> configured{0};
@@ -435,7 +436,7 @@ hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const Moe
   a.h = t.h;
   a.inter = gu.n / 2;
   // each workgroup covers 128 intermediate columns (256 interleaved rows)
-  return launch_big_mode<4, 8, kMoeGateUp>(gu.format, a, dim3(max_tiles, (gu.n + kBN - 1) / kBN), s);
+  return launch_big_mode<2, 16, kMoeGateUp>(gu.format, a, dim3(max_tiles, (gu.n + kBN - 1) / kBN), s);
 }
 
 hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
@@ -446,7 +447,7 @@ hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max
   a.h = t.h;
   a.d = t.d;
   a.inter = dn.k;
-  return launch_big_mode<4, 8, kMoeDown>(dn.format, a, dim3(max_tiles, (dn.n + kBN - 1) / kBN), s);
+  return launch_big_mode<2, 16, kMoeDown>(dn.format, a, dim3(max_tiles, (dn.n + kBN - 1) / kBN), s);
 }
 
 }  // namespace qmm

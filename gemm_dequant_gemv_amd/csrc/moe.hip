@@ -112,13 +112,13 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
       tb.token_of_row[row] = (uint32_t)t;
     }
 
-  // 4. experts with rows (in expert order) and their tiles of kGemmBM rows
+  // 4. experts with rows (in expert order) and their tiles of kMoeTileRows rows
   uint32_t nact = 0, ntile = 0;
   for (int j = 0; j < PER; ++j) {
     const int e = tid * PER + j;
     if (e < ne && s_count[e]) {
       nact += 1;
-      ntile += (s_count[e] + kGemmBM - 1) / kGemmBM;
+      ntile += (s_count[e] + kMoeTileRows - 1) / kMoeTileRows;
     }
   }
   uint32_t act_base = block_exclusive_scan(nact, s_scan, &s_total);
@@ -130,11 +130,11 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
     if (e >= ne || !s_count[e]) continue;
     tb.active[act_base++] = (uint32_t)e;
     const uint32_t cnt = s_count[e];
-    for (uint32_t r = 0; r < cnt; r += kGemmBM) {
+    for (uint32_t r = 0; r < cnt; r += kMoeTileRows) {
       uint32_t *tl = tb.tiles + 3 * (size_t)tile_base++;
       tl[0] = (uint32_t)e;
       tl[1] = s_off[e] + r;
-      tl[2] = min(cnt - r, (uint32_t)kGemmBM);
+      tl[2] = min(cnt - r, (uint32_t)kMoeTileRows);
     }
   }
 }
@@ -224,7 +224,7 @@ MoeLayout moe_layout(int num_experts, int t, int topk, int num_shared, int inter
   MoeLayout L{};
   const size_t rows = (size_t)t * topk + (size_t)t * num_shared;
   L.max_rows = rows;
-  L.max_tiles = (rows + kGemmBM - 1) / kGemmBM + (size_t)num_experts;
+  L.max_tiles = (rows + kMoeTileRows - 1) / kMoeTileRows + (size_t)num_experts;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;

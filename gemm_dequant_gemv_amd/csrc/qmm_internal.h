@@ -40,6 +40,8 @@ size_t gemv_rows_lds(int format, int k, int m);
 
 // Prefill GEMM / grouped MoE tiles: rows of activations per workgroup.
 constexpr int kGemmBM = 128;
+// rows per tile of the MoE routing table (the grouped GEMMs' activation tiles)
+constexpr int kMoeTileRows = 256;
 // Experts (routed + shared) one MoE call may have.
 constexpr int kMoeMaxExperts = 4096;
 

@@ -240,7 +240,7 @@ typedef struct {
   size_t active;        /* uint32 [n_active] experts with at least one row, ascending */
   size_t scalars;       /* uint32 [3]       n_active, n_tiles, err (1 = an id was
                            outside [0, E) and its slot was dropped)                 */
-  size_t tiles;         /* uint32 [n_tiles][3] expert, first grouped row, rows (<= 128)
+  size_t tiles;         /* uint32 [n_tiles][3] expert, first grouped row, rows (<= 256)
                            of each row tile, experts ascending                      */
   size_t h;             /* bf16  [rows][I]  SwiGLU outputs                          */
   size_t d;             /* float [rows][H]  down-projection outputs                  */

@@ -79,11 +79,15 @@ def run_gpu(q, gu, dn, x, ids, w, E, S, shared_w=None, y_dtype=torch.float32, wd
     return yh, r
 
 
+# rows per tile of the library's routing table (its grouped GEMMs' tile height)
+TILE_ROWS = 256
+
+
 def check_grouping(r, ids, E, S):
     """Bit-exact on what the grouping fixes (counts, offsets, active experts,
     tile table, error flag); valid on what it leaves open (the order of a
     group's rows): every slot lands inside its expert's rows, once."""
-    g = oracle.moe_grouping(ids, E, S)
+    g = oracle.moe_grouping(ids, E, S, tile_rows=TILE_ROWS)
     T, topk = ids.shape
     assert r["err"] == g["err"]
     if r["slot_rows"]:  # the decode form builds no grouping tables
