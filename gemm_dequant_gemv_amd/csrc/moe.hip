@@ -25,6 +25,7 @@ namespace {
 
 constexpr uint32_t kInvalidRow = 0xFFFFFFFFu;
 constexpr int kRouteThreads = 1024;
+constexpr int kRun = 16;  // slots per thread and pass in the route kernel
 
 struct RouteArgs {
   const int32_t *topk_ids;
@@ -63,15 +64,32 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
   for (int e = tid; e < ne; e += kRouteThreads) s_count[e] = 0;
   if (tid == 0) *tb.err = 0;
   __syncthreads();
-  // 1. position of every routed slot inside its expert's group
-  for (int i = tid; i < slots; i += kRouteThreads) {
-    const int e = a.topk_ids[i];
-    if (e < 0 || e >= a.num_routed) {
-      tb.row_of_slot[i] = kInvalidRow;  // contributes nothing; reported in err
-      atomicOr(tb.err, 1u);
-      continue;
+  // 1. position of every routed slot inside its expert's group.  A pass
+  //    covers kRun x 1024 slots (slot b + 1024 j for thread j-th of the pass;
+  //    consecutive threads, consecutive slots); a thread loads all its ids of
+  //    the pass before its atomics, so that it waits on memory once per pass
+  //    rather than once per slot.
+  constexpr int kStride = kRouteThreads;
+  for (int b0 = 0; b0 < slots; b0 += kRouteThreads * kRun) {
+    const int b = b0 + tid;
+    int32_t id[kRun];
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) id[j] = b + kStride * j < slots ? a.topk_ids[b + kStride * j] : 0;
+    uint32_t pos[kRun];
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      const int e = id[j];
+      pos[j] = kInvalidRow;
+      if (b + kStride * j >= slots) continue;
+      if (e < 0 || e >= a.num_routed) {
+        atomicOr(tb.err, 1u);  // contributes nothing; reported in err
+        continue;
+      }
+      pos[j] = atomicAdd(&s_count[e], 1u);
     }
-    tb.row_of_slot[i] = atomicAdd(&s_count[e], 1u);
+#pragma unroll
+    for (int j = 0; j < kRun; ++j)
+      if (b + kStride * j < slots) tb.row_of_slot[b + kStride * j] = pos[j];
   }
   // shared experts see every token, in token order
   for (int e = a.num_routed + tid; e < ne; e += kRouteThreads) s_count[e] = (uint32_t)a.t;
@@ -97,13 +115,26 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
   if (tid == 0) tb.offsets[ne] = s_total;
   __syncthreads();
 
-  // 3. grouped row of every slot, and the token each grouped row reads
-  for (int i = tid; i < slots; i += kRouteThreads) {
-    const uint32_t pos = tb.row_of_slot[i];
-    if (pos == kInvalidRow) continue;
-    const uint32_t row = s_off[a.topk_ids[i]] + pos;
-    tb.row_of_slot[i] = row;
-    tb.token_of_row[row] = (uint32_t)(i / a.topk);
+  // 3. grouped row of every slot, and the token each grouped row reads (the
+  //    same passes as in 1: this thread wrote these slots' positions)
+  for (int b0 = 0; b0 < slots; b0 += kRouteThreads * kRun) {
+    const int b = b0 + tid;
+    uint32_t pos[kRun];
+    int32_t id[kRun];
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      const int i = b + kStride * j;
+      pos[j] = i < slots ? tb.row_of_slot[i] : kInvalidRow;
+      id[j] = i < slots ? a.topk_ids[i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      if (pos[j] == kInvalidRow) continue;
+      const int i = b + kStride * j;
+      const uint32_t row = s_off[id[j]] + pos[j];
+      tb.row_of_slot[i] = row;
+      tb.token_of_row[row] = (uint32_t)(i / a.topk);
+    }
   }
   for (int s = 0; s < a.num_shared; ++s)
     for (int t = tid; t < a.t; t += kRouteThreads) {
