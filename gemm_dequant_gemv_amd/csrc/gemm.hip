@@ -280,9 +280,9 @@ GemmArgs weight_args(const qmm_weight &w) {
 
 hipError_t launch_gemm(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
                        hipStream_t s) {
-  // from a few hundred rows on, 256-row weight tiles with the activations
-  // streamed straight into LDS (gemm_big.hip) move half the bytes per flop
-  bool big = m >= 256;
+  // weights decoded straight into MFMA operands (gemm_big.hip) wherever its
+  // 32-bit offsets reach; this LDS-staged kernel otherwise
+  bool big = true;
 #ifdef QMM_TUNE
   if (const char *e = getenv("QMM_GEMM_BIG")) big = atoi(e) != 0;
 #endif

@@ -16,11 +16,11 @@
 //     second) and the activation operand is read in the same order, so each
 //     lane decodes one contiguous 16-weight run of one row;
 //   * a wave computes TN x TM MFMA tiles (16 TN rows of W x 16 TM rows of X).
-//     Dense: 8 waves of 32 W rows x 256 X rows (TN = 2, TM = 16), so that
-//     each decoded weight feeds 32 MFMAs of its slice, as do the grouped MoE
-//     modes (256 rows is the routing table's tile height); 4 waves of 64 x 128
-//     (TN = 4, TM = 8) remain for comparison.  Either way a wave holds 128
-//     float32 accumulators and two waves share a SIMD.
+//     From 257 rows of X on: 8 waves of 32 W rows x 256 X rows (TN = 2,
+//     TM = 16), so that each decoded weight feeds 32 MFMAs of its slice, as
+//     do the grouped MoE modes (256 rows is the routing table's tile height).
+//     Up to 256 rows: 4 waves of 32 x 128 (more workgroups for small calls).
+//     A wave holds at most 128 float32 accumulators; two waves share a SIMD.
 //     (One wave of 64 x 256, with 256 accumulators, spilled.)
 //
 // Per slice and wave (dense): 64 MFMAs, 32 decoded weights per lane, 32 KB of
@@ -37,7 +37,6 @@ namespace {
 
 using namespace gemm;
 
-constexpr int kBN = 256;        // rows of W per workgroup (64 per wave)
 constexpr int kStages = 3;      // LDS stages of X = slices in flight
 constexpr int kXRow = kBK * 2;  // bytes of one X row in a slice
 
@@ -152,17 +151,17 @@ template <int FMT>
 constexpr int w_loads_per_run() { return FMT == QMM_Q6_K ? 4 : 2; }
 
 // A wave computes TN x TM MFMA tiles: 16 TN rows of W x 16 TM rows of X;
-// the workgroup's 16 / TN waves cover the 256 rows of W, all sharing the
-// BM = 16 TM rows of X.  MODE as in gemm.hip: dense, or the grouped MoE
+// the workgroup's WAVES waves cover BN = 16 TN WAVES rows of W, all sharing
+// the BM = 16 TM rows of X.  MODE as in gemm.hip: dense, or the grouped MoE
 // gate/up (rows of x gathered by token, gate and up weight rows interleaved,
 // SwiGLU epilogue) and down products over the routing tile table (tiles of BM
 // grouped rows, one expert each).
-template <int FMT, int TN, int TM, int MODE>
-__global__ __launch_bounds__(64 * (16 / TN)) __attribute__((amdgpu_waves_per_eu(2)))
+template <int FMT, int TN, int TM, int WAVES, int MODE>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_big_kernel(GemmArgs a) {
   constexpr int kTN = TN;
-  constexpr int WAVES = 16 / TN;
   constexpr int WROWS = 16 * TN;  // W rows per wave
+  constexpr int kBN = WROWS * WAVES;
   constexpr int BM = 16 * TM;
   constexpr int kXStage = BM * kXRow;  // bytes per LDS stage
   constexpr int XI = BM / (8 * WAVES);  // X load instructions per wave and slice (8 rows each)
@@ -357,7 +356,7 @@ void gemm_big_kernel(GemmArgs a) {
   }
 }
 
-template <int FMT, int TN, int TM, int MODE>
+template <int FMT, int TN, int TM, int WAVES, int MODE>
 hipError_t launch_big(const GemmArgs &a, dim3 grid, hipStream_t s) {
   static_assert(MODE == kDense || 16 * TM == kMoeTileRows,
                 "X tiles are the routing table's tiles of kMoeTileRows rows");
@@ -369,24 +368,27 @@ hipError_t launch_big(const GemmArgs &a, dim3 grid, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(configured.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute((const void *)gemm_big_kernel<FMT, TN, TM, MODE>,
+    e = hipFuncSetAttribute((const void *)gemm_big_kernel<FMT, TN, TM, WAVES, MODE>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((gemm_big_kernel<FMT, TN, TM, MODE>), grid, dim3(64 * (16 / TN)), lds, s, a);
+  hipLaunchKernelGGL((gemm_big_kernel<FMT, TN, TM, WAVES, MODE>), grid, dim3(64 * WAVES), lds, s, a);
   return hipGetLastError();
 }
 
-template <int TN, int TM, int MODE>
+template <int TN, int TM, int WAVES, int MODE>
 hipError_t launch_big_mode(int format, const GemmArgs &a, dim3 grid, hipStream_t s) {
   switch (format) {
-    case QMM_AFFINE4_G64: return launch_big<QMM_AFFINE4_G64, TN, TM, MODE>(a, grid, s);
-    case QMM_MXFP4: return launch_big<QMM_MXFP4, TN, TM, MODE>(a, grid, s);
-    case QMM_NVFP4: return launch_big<QMM_NVFP4, TN, TM, MODE>(a, grid, s);
-    default: return launch_big<QMM_Q6_K, TN, TM, MODE>(a, grid, s);
+    case QMM_AFFINE4_G64: return launch_big<QMM_AFFINE4_G64, TN, TM, WAVES, MODE>(a, grid, s);
+    case QMM_MXFP4: return launch_big<QMM_MXFP4, TN, TM, WAVES, MODE>(a, grid, s);
+    case QMM_NVFP4: return launch_big<QMM_NVFP4, TN, TM, WAVES, MODE>(a, grid, s);
+    default: return launch_big<QMM_Q6_K, TN, TM, WAVES, MODE>(a, grid, s);
   }
 }
+
+// workgroups' rows of W for a TN x WAVES configuration
+constexpr int bn_of(int tn, int waves) { return 16 * tn * waves; }
 
 GemmArgs big_args(const qmm_weight &w) {
   GemmArgs a{};
@@ -415,15 +417,21 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
   a.residual = (const uint16_t *)residual;
   a.y = (uint16_t *)y;
   a.m = m;
-  const unsigned nt = (unsigned)((w.n + kBN - 1) / kBN);
+  auto grid = [&](int bm, int bn) {
+    return dim3((unsigned)(((m + bm - 1) / bm) * ((w.n + bn - 1) / bn)));
+  };
   // 8 waves of 32 W rows x 256 X rows: each decoded weight feeds twice the
-  // MFMAs of the 4-wave form (measured 1.3x faster from M = 512 on)
-  bool wide = true;
+  // MFMAs of the 4-wave 64 x 128 form (measured 1.3x faster from M = 512 on).
+  // Up to 256 rows of X: 4 waves of 32 x 128, whose 128-row W tiles give a
+  // 128-row call 136 workgroups (measured 1.9x faster than the LDS-staged
+  // kernel at M = 128, 1.4x at M = 256).
+  int cfg = m > 256 ? 0 : 1;
 #ifdef QMM_TUNE
-  if (const char *e = getenv("QMM_BIG_WIDE")) wide = atoi(e) != 0;
+  if (const char *e = getenv("QMM_BIG_CFG")) cfg = atoi(e);
+  if (cfg == 2) return launch_big_mode<4, 8, 4, kDense>(w.format, a, grid(128, bn_of(4, 4)), s);
 #endif
-  if (wide) return launch_big_mode<2, 16, kDense>(w.format, a, dim3(((m + 255) / 256) * nt), s);
-  return launch_big_mode<4, 8, kDense>(w.format, a, dim3(((m + 127) / 128) * nt), s);
+  if (cfg == 0) return launch_big_mode<2, 16, 8, kDense>(w.format, a, grid(256, bn_of(2, 8)), s);
+  return launch_big_mode<2, 8, 4, kDense>(w.format, a, grid(128, bn_of(2, 4)), s);
 }
 
 hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const MoeTables &t,
@@ -436,7 +444,8 @@ hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const Moe
   a.h = t.h;
   a.inter = gu.n / 2;
   // each workgroup covers 128 intermediate columns (256 interleaved rows)
-  return launch_big_mode<2, 16, kMoeGateUp>(gu.format, a, dim3(max_tiles, (gu.n + kBN - 1) / kBN), s);
+  constexpr int bn = bn_of(2, 8);
+  return launch_big_mode<2, 16, 8, kMoeGateUp>(gu.format, a, dim3(max_tiles, (gu.n + bn - 1) / bn), s);
 }
 
 hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
@@ -447,7 +456,8 @@ hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max
   a.h = t.h;
   a.d = t.d;
   a.inter = dn.k;
-  return launch_big_mode<2, 16, kMoeDown>(dn.format, a, dim3(max_tiles, (dn.n + kBN - 1) / kBN), s);
+  constexpr int bn = bn_of(2, 8);
+  return launch_big_mode<2, 16, 8, kMoeDown>(dn.format, a, dim3(max_tiles, (dn.n + bn - 1) / bn), s);
 }
 
 }  // namespace qmm
