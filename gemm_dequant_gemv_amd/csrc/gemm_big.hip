@@ -390,6 +390,19 @@ hipError_t launch_big_mode(int format, const GemmArgs &a, dim3 grid, hipStream_t
 // workgroups' rows of W for a TN x WAVES configuration
 constexpr int bn_of(int tn, int waves) { return 16 * tn * waves; }
 
+// compute units of the current device (cached per device)
+long compute_units() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  int v = cached[dev & 63].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    return 256;
+  cached[dev & 63].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 GemmArgs big_args(const qmm_weight &w) {
   GemmArgs a{};
   a.codes = (const uint8_t *)w.codes;
@@ -421,16 +434,26 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
     return dim3((unsigned)(((m + bm - 1) / bm) * ((w.n + bn - 1) / bn)));
   };
   // 8 waves of 32 W rows x 256 X rows: each decoded weight feeds twice the
-  // MFMAs of the 4-wave 64 x 128 form (measured 1.3x faster from M = 512 on).
-  // Up to 256 rows of X: 4 waves of 32 x 128, whose 128-row W tiles give a
-  // 128-row call 136 workgroups (measured 1.9x faster than the LDS-staged
-  // kernel at M = 128, 1.4x at M = 256).
-  int cfg = m > 256 ? 0 : 1;
+  // MFMAs of the 4-wave 64 x 128 form (measured 1.3x faster from M = 512 on);
+  // or 8 waves of 32 x 192 where that leaves fewer idle compute units in the
+  // last round of workgroups (one workgroup per compute unit; a 192-row round
+  // takes about 0.85 of a 256-row one): M = 2048 at 17408 rows is 544
+  // workgroups of 256 (2.1 rounds) or 748 of 192 (2.9 rounds), measured 1.14x
+  // faster; M = 300 and 512 1.2x, M >= 3072 no gain.  Up to 256 rows of X: 4 waves of 32 x 128, whose 128-row W tiles
+  // give a 128-row call 136 workgroups (1.9x faster than the LDS-staged kernel
+  // at M = 128, 1.4x at M = 256).
+  int cfg = 1;
+  if (m > 256) {
+    const long nt = (w.n + bn_of(2, 8) - 1) / bn_of(2, 8), cus = compute_units();
+    auto rounds = [&](int bm) { return ((m + bm - 1) / bm * nt + cus - 1) / cus; };
+    cfg = 17 * rounds(192) < 20 * rounds(256) ? 4 : 0;
+  }
 #ifdef QMM_TUNE
   if (const char *e = getenv("QMM_BIG_CFG")) cfg = atoi(e);
   if (cfg == 2) return launch_big_mode<4, 8, 4, kDense>(w.format, a, grid(128, bn_of(4, 4)), s);
 #endif
   if (cfg == 0) return launch_big_mode<2, 16, 8, kDense>(w.format, a, grid(256, bn_of(2, 8)), s);
+  if (cfg == 4) return launch_big_mode<2, 12, 8, kDense>(w.format, a, grid(192, bn_of(2, 8)), s);
   return launch_big_mode<2, 8, 4, kDense>(w.format, a, grid(128, bn_of(2, 4)), s);
 }
 
