@@ -1,5 +1,7 @@
-"""GPU parity of qgemm (prefill, LDS-staged dequantization + bf16 MFMA) against
-the CPU oracle, through the C ABI.
+"""GPU parity of qgemm (prefill: weights dequantized to bf16 inside the kernel,
+bf16 MFMA) against the CPU oracle, through the C ABI.  The small shapes run
+the 128- and 192-row tile configurations; the sampled full-size cases run
+the prefill workload's own configurations.
 
 Bars: |y - y_ref| <= 2e-3 * sum|w||x| + half a bf16 ulp of y_ref per output
 (y is stored as bf16, which the reference rounds too); exact-arithmetic
@@ -112,3 +114,24 @@ def test_gemm_rejects():
     with pytest.raises(q.QmmError) as e:
         q.gemm(w, x[:0])                             # m = 0
     assert e.value.status == -5
+
+
+# The prefill workload's own sizes, in the tile configurations the library
+# picks for them (256-row activation tiles at M = 8192, 192-row at 2048): the
+# GPU computes the whole product; the oracle checks sampled activation rows
+# (every output column of each), including both edges of the tiles.
+FULL_N, FULL_K = 17408, 5120
+
+
+@pytest.mark.parametrize("fmt,m", [(F.AFFINE4_G64, 8192), (F.NVFP4, 2048)])
+def test_gemm_prefill_full_size_sampled(fmt, m):
+    q = _q()
+    p = quant.synthetic_weight(fmt, FULL_N, FULL_K, name=f"gfull{fmt}")
+    x = quant.synthetic_bf16(m, FULL_K, name=f"gfullx{m}")
+    w = q.Weight.from_host(p)
+    y = _host_f64(q.gemm(w, _dev_bf16(x)))
+    edges = [0, 1, 127, 128, 191, 192, 255, 256, m // 2, m - 2, m - 1]
+    rows = np.unique(np.concatenate([edges, rng.randint_bytes(71, f"gfr{m}", 21, 0, 256).astype(np.int64) * (m // 256)]))
+    rows = rows[rows < m]
+    yref, mag = oracle.gemm(p, x[rows])
+    _check(y[rows], yref, mag)
