@@ -254,7 +254,7 @@ def prefill_section(q, torch, dev):
         torch.cuda.empty_cache()
     big = [c for c in out if c["m"] >= 2048]
     best = max(big, key=lambda c: c["TFLOPs"])
-    return {"unit": "TFLOP/s", "kernel": "gemm_kernel (LDS-staged dequant, bf16 MFMA)",
+    return {"unit": "TFLOP/s", "kernel": "gemm_big_kernel (dequant in registers, bf16 MFMA)",
             "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS, "best_at_M_ge_2048": best, "cases": out}
 
 
