@@ -6,9 +6,12 @@
 // whole activation block x [M][K] in LDS (one padded record per 32-value
 // chunk: its x in pair order, then its block sums), then its waves stream
 // weight rows:
-//   * rows go in pairs (2p, 2p+1), one per half-wave; wave w of the grid owns
-//     pairs w, w + W, w + 2W, ... (W = waves in the grid), so at any moment the
-//     grid streams one contiguous band of rows;
+//   * rows go in pairs (2p, 2p+1), one per half-wave, dealt out in one of two
+//     ways: round-robin, where wave w of the grid owns pairs w, w + W, w + 2W,
+//     ... (W = waves in the grid), so at any moment the grid streams one
+//     contiguous band of rows; or balanced, where workgroup g owns the
+//     contiguous pairs [g P / G, (g+1) P / G) (P pairs, G workgroups) and
+//     splits their units (below), pair-major, evenly over its 16 waves;
 //   * a unit is one step of one pair: 1024 values (512 code bytes) of each
 //     row, one 16-byte load per lane (lane c of a half holds values 32c ..
 //     32c+31), so every load instruction reads whole 128-byte lines of two
@@ -19,15 +22,23 @@
 //   * a wave's units form one software pipeline with U units of loads in
 //     flight; each unit brings the codes of two rows, their block scales and
 //     one residual value per output;
-//   * after a pair's last step each half-wave's sums are reduced with DPP row
-//     operations and lanes 0 .. 2M-1 write the pair's 2 x M outputs;
+//   * when a wave is done with a pair, each half-wave's sums are reduced with
+//     DPP row operations and lanes 0 .. 2M-1 write the pair's 2 x M outputs;
+//     in the balanced form a pair cut by a wave boundary leaves its sums in an
+//     LDS slot instead, and after the last barrier the wave that did the
+//     pair's last step adds the slots in wave order and writes the outputs;
 //   * a wave lowers its issue priority at each quarter of its units, so that
 //     the waves sharing a SIMD progress together instead of oldest first.
-// Nothing crosses waves, so there is no split-K finish and no workspace, and
-// every sum has a fixed order: the result does not depend on timing.  (Giving
-// each workgroup a contiguous block of pairs split evenly over its waves, with
-// cut pairs finished through LDS, balanced the waves' work but its longer
-// per-unit bookkeeping measured slower on the decode shapes.)
+// Nothing crosses workgroups, so there is no split-K finish and no workspace,
+// and every sum has a fixed order: the result does not depend on timing.
+//
+// Round-robin pairs leave the waves uneven work: on 17408 rows an eighth of
+// the waves take half as many units again as the rest, on 5120 rows 40% of
+// the waves have none.  Where the per-unit vector work is heavy (Q6_K, and
+// the affine format at M >= 2) those waves set the kernel's time, and the
+// balanced form measured 4-15% faster; where it is light (the E2M1 formats,
+// affine at M = 1) the kernel waits on memory either way, and the balanced
+// form's final barrier and cut-pair finish made it 2-4% slower.
 //
 // The activations must fit in LDS (K * M * 2 bytes plus block sums); the host
 // falls back to the split-K kernel otherwise.
@@ -44,7 +55,7 @@ constexpr int kWaves = 16;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStepK = 1024;       // values of one row per step (32 lanes x 32)
 constexpr int kXPieces = 9;        // 16-byte activation pieces per thread, at most
-constexpr size_t kLdsLimit = 160 * 1024 - 2048;  // dynamic part; the static part is < 1 KB
+constexpr size_t kLdsLimit = 160 * 1024 - 2048;  // dynamic part; the static part is <= 1 KB
 
 // LDS image of the activations, one record per 32-value chunk ch: M x 64
 // bytes of x (16-byte pieces p = 4m + part, in pair order for the
@@ -60,6 +71,11 @@ struct XLayout {
   static constexpr int kStride = 64 * M + kPad;            // bytes per record
   static_assert(M * NS * 4 <= kPad && (kStride / 16) % 2 == 1, "record layout");
 };
+
+// The balanced split where the per-unit vector work is heavy.
+constexpr bool use_balanced(int format, int m) {
+  return format == QMM_Q6_K || (format == QMM_AFFINE4_G64 && m >= 2);
+}
 
 constexpr int sums_per_chunk(int format) {
   return format == QMM_AFFINE4_G64 ? 1 : (format == QMM_Q6_K ? 2 : 0);
@@ -78,7 +94,7 @@ struct RowsArgs {
   int n, k, steps, y_bf16;
 };
 
-template <int FMT, int M, int U>
+template <int FMT, int M, int U, bool BAL>
 __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
   using T = FmtTraits<FMT>;
   constexpr int kNS = T::kSums;
@@ -95,12 +111,32 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = a.steps;
   const uint32_t k = (uint32_t)a.k;
-  // this wave's pairs gw, gw + W, ...: units = pairs x steps
-  const int W = gridDim.x * kWaves;
-  const int gw = blockIdx.x * kWaves + wave;
+  // The wave walks pairs pbase + j * pstride from j = j0, step st0, for
+  // `units` units; (jl, sl) is its last unit, re-read by the loads past the end.
   const int npairs = (a.n + 1) / 2;
-  const int mypairs = gw < npairs ? (npairs - 1 - gw) / W + 1 : 0;
-  const int units = mypairs * S;
+  int pbase, pstride, units, j0 = 0, st0 = 0, jl, sl, L = 0;
+  if constexpr (BAL) {
+    // the workgroup's pairs [pbase, pbase + L / S) and their L units
+    pbase = (int)((long long)blockIdx.x * npairs / gridDim.x);
+    L = ((int)((long long)(blockIdx.x + 1) * npairs / gridDim.x) - pbase) * S;
+    pstride = 1;
+    const int u0 = wave * L / kWaves;
+    units = (wave + 1) * L / kWaves - u0;
+    j0 = u0 / S;
+    st0 = u0 - j0 * S;
+    const int ulast = u0 + max(units, 1) - 1;
+    jl = ulast / S;
+    sl = ulast - jl * S;
+  } else {
+    // pairs gw, gw + W, ... of the grid's W waves
+    pbase = blockIdx.x * kWaves + wave;
+    pstride = gridDim.x * kWaves;
+    const int mypairs = pbase < npairs ? (npairs - 1 - pbase) / pstride + 1 : 0;
+    units = mypairs * S;
+    jl = max(mypairs - 1, 0);
+    sl = S - 1;
+  }
+  __shared__ float part[BAL ? kWaves : 1][2][kOut];  // sums of pairs cut by wave boundaries
 
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes, a.codes_bytes);
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.codes_hi, a.hi_bytes);
@@ -135,12 +171,12 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
   //    n and lanes past K read whatever the buffer holds there, or zeros
   //    beyond its end, and their results are never used), so the compiler can
   //    count outstanding loads exactly.
-  auto load_unit = [&](int j, int s, RowData &rd, uint32_t &res) {
-    if (j >= mypairs) {  // uniform
-      j = max(mypairs - 1, 0);
-      s = S - 1;
+  auto load_unit = [&](int t, int j, int s, RowData &rd, uint32_t &res) {
+    if (t >= units) {  // uniform
+      j = jl;
+      s = sl;
     }
-    const uint32_t row0 = 2u * (uint32_t)(gw + j * W);
+    const uint32_t row0 = 2u * (uint32_t)(pbase + j * pstride);
     rd.q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
         rc, v_code, row0 * (k / 2) + (uint32_t)s * (kStepK / 2), 2));
     if constexpr (FMT == QMM_AFFINE4_G64) {
@@ -165,10 +201,10 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
 
   RowData buf[U];
   uint32_t res[U];
-  int lj = 0, ls = 0;  // next unit to load: pair index, step
+  int lj = j0, ls = st0;  // next unit to load: pair index, step
 #pragma unroll
   for (int j = 0; j < U; ++j) {
-    load_unit(lj, ls, buf[j], res[j]);
+    load_unit(j, lj, ls, buf[j], res[j]);
     if (++ls == S) { ls = 0; ++lj; }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -221,7 +257,8 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
   const char *xs_lane = xs + c * XL::kStride;
 
-  int cj = 0, cs = 0;  // unit being computed: pair index, step
+  int cj = j0, cs = st0;  // unit being computed: pair index, step
+  float fin_res = 0.0f;    // balanced: residual of the cut pair this wave finishes
   // Issue priority falls as the wave gets through its units.  The arbiter of
   // a SIMD favours its oldest wave; left alone, the four waves of a SIMD
   // finish one after another and the last ones run with little memory in
@@ -257,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
           }
           row_step<FMT, M>(buf[j], X, Sx, acc, K);
         }
-        if (cs == S - 1) {  // the pair is complete
+        if (cs == S - 1 || (BAL && t0 + j == units - 1)) {  // the wave is done with the pair
           float out = 0.0f;
 #pragma unroll
           for (int m = 0; m < M; ++m) {
@@ -267,18 +304,41 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
             if (lane == 2 * m) out = s0;
             if (lane == 2 * m + 1) out = s1;
           }
-          const int row = 2 * (gw + cj * W) + o_h;
-          if (lane < kOut && row < a.n) store(row, out * gscale + bf_lo(res[j]));
+          if (cs == S - 1 && (!BAL || cj != j0 || st0 == 0)) {  // the whole pair
+            const int row = 2 * (pbase + cj * pstride) + o_h;
+            if (lane < kOut && row < a.n) store(row, out * gscale + bf_lo(res[j]));
+          } else {  // a cut pair, the wave's first (slot 0) or last (slot 1)
+            if (lane < kOut) part[BAL ? wave : 0][cj == j0 ? 0 : 1][lane] = out;
+            if (cs == S - 1) fin_res = bf_lo(res[j]);
+          }
         }
         if (++cs == S) { cs = 0; ++cj; }
       }
-      load_unit(lj, ls, buf[j], res[j]);
+      load_unit(t0 + j + U, lj, ls, buf[j], res[j]);
       if (++ls == S) { ls = 0; ++lj; }
+    }
+  }
+
+  if constexpr (BAL) {
+    // A wave that starts inside a pair and does that pair's last step adds
+    // the parts of every wave that shared the pair, in wave order.
+    __syncthreads();
+    const int u0 = wave * L / kWaves;
+    if (st0 != 0 && units > 0 && u0 + units >= (j0 + 1) * S && lane < kOut) {
+      int wa = wave - 1;  // the wave holding the pair's first unit
+      while (wa * L / kWaves > j0 * S) --wa;
+      float sum = 0.0f;
+      for (int w = wa; w <= wave; ++w) {
+        const int b0 = w * L / kWaves;
+        if ((w + 1) * L / kWaves > b0) sum += part[w][b0 / S == j0 ? 0 : 1][lane];
+      }
+      const int row = 2 * (pbase + j0) + o_h;
+      if (row < a.n) store(row, sum * gscale + fin_res);
     }
   }
 }
 
-template <int FMT, int M, int U>
+template <int FMT, int M, int U, bool BAL>
 hipError_t launch_rows_cfg(const RowsArgs &a, size_t lds, int grid, hipStream_t s) {
   // the dynamic LDS limit is raised once per device for each instantiation
   static std::atomic<uint64_t> raised{0};
@@ -287,12 +347,12 @@ hipError_t launch_rows_cfg(const RowsArgs &a, size_t lds, int grid, hipStream_t 
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(raised.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute((const void *)gemv_rows_kernel<FMT, M, U>,
+    e = hipFuncSetAttribute((const void *)gemv_rows_kernel<FMT, M, U, BAL>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     if (e != hipSuccess) return e;
     raised.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((gemv_rows_kernel<FMT, M, U>), dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((gemv_rows_kernel<FMT, M, U, BAL>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -304,8 +364,9 @@ hipError_t launch_rows_cfg(const RowsArgs &a, size_t lds, int grid, hipStream_t 
 
 template <int FMT, int M>
 hipError_t launch_rows_fm(const RowsArgs &a, const GemvPlan &p, hipStream_t s) {
+  constexpr bool kBal = use_balanced(FMT, M);
 #define QMM_CASE(UU) \
-  if (p.depth == UU) return launch_rows_cfg<FMT, M, UU>(a, p.lds_bytes, p.tiles, s);
+  if (p.depth == UU) return launch_rows_cfg<FMT, M, UU, kBal>(a, p.lds_bytes, p.tiles, s);
   QMM_ROWS_CONFIGS(QMM_CASE)
 #undef QMM_CASE
   return hipErrorInvalidConfiguration;
@@ -351,6 +412,7 @@ bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p) {
   // units of loads in flight per wave
   p.rows_per_lane = 1;
   p.depth = m == 1 ? 3 : 2;
+  p.balanced = use_balanced(format, m);
 #ifdef QMM_TUNE
   if (const char *e = getenv("QMM_ROWS_U")) p.depth = atoi(e);
 #endif
