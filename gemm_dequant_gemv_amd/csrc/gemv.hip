@@ -125,12 +125,19 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   constexpr int XP = (MAXCH * M * 4 + kGemvThreads - 1) / kGemvThreads;
   const int valid_ch = krange / 32;
   const int items = valid_ch * M * 4;
+  // (a load with no piece to fetch points past the end of the buffer and
+  // returns zeros without a memory access: clamped copies of the last piece
+  // from every workgroup of a split would queue on one L2 channel)
+  const uint32_t x_bytes = (uint32_t)(M * a.k * 2);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, x_bytes);
   uint4 xv[XP];
 #pragma unroll
   for (int j = 0; j < XP; ++j) {
-    const int i = min(j * kGemvThreads + tid, items - 1);
+    const int i = j * kGemvThreads + tid;
     const int ch = i / (4 * M), m = (i >> 2) % M, part = i & 3;
-    xv[j] = *(const uint4 *)(a.x + (size_t)m * a.k + kbase + ch * 32 + part * 8);
+    const uint32_t off =
+        i < items ? ((uint32_t)m * a.k + kbase + ch * 32 + part * 8) * 2u : x_bytes;
+    xv[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
   }
 
   // 2. block scales of the workgroup's rows and K range, as 32-bit words (the

@@ -155,14 +155,22 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
   const int o_h = lane & 1, o_m = min(lane >> 1, M - 1);
   const uint32_t v_res = ((uint32_t)o_m * a.n + o_h) * 2;
 
-  // 1. the activations, first, so that they do not queue behind the codes
+  // 1. the activations, first, so that they do not queue behind the codes.
+  //    Every thread issues kXPieces loads (so the compiler counts outstanding
+  //    loads exactly); a load with no piece to fetch points past the end of
+  //    the buffer and returns zeros without a memory access (clamping it to
+  //    the last piece instead queued copies from every wave of the grid on
+  //    the one L2 channel holding that piece).
   const int pieces = nch * 4 * M;
+  const uint32_t x_bytes = (uint32_t)pieces * 16u;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, x_bytes);
   uint4 xv[kXPieces];
 #pragma unroll
   for (int j = 0; j < kXPieces; ++j) {
-    const int i = min(j * kThreads + tid, pieces - 1);
+    const int i = j * kThreads + tid;
     const int ch = i / (4 * M), m = (i >> 2) % M, part_ = i & 3;
-    xv[j] = *(const uint4 *)(a.x + (size_t)m * a.k + ch * 32 + part_ * 8);
+    const uint32_t off = i < pieces ? ((uint32_t)m * k + ch * 32 + part_ * 8) * 2u : x_bytes;
+    xv[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
   }
   __builtin_amdgcn_sched_barrier(0);
 

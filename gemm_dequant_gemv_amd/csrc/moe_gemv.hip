@@ -171,13 +171,19 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
 
   const int pieces = a.nsrc * nch * 4;  // 16-byte pieces, [vector][chunk][part]
   constexpr int XP = 4;                  // pieces per thread in flight
+  // a load with no piece to fetch points past the end of the buffer and
+  // returns zeros without a memory access (clamped copies of the last piece
+  // from every wave would all queue on the one L2 channel holding it)
+  const uint32_t src_bytes = (uint32_t)pieces * 16u;
+  const __amdgpu_buffer_rsrc_t rsrc_x = make_rsrc(a.src, src_bytes);
   for (int i0 = 0; i0 < pieces; i0 += XP * kThreads) {  // uniform trip count
     uint4 xv[XP];
 #pragma unroll
     for (int u = 0; u < XP; ++u) {
-      const int i = min(i0 + u * kThreads + tid, pieces - 1);
+      const int i = i0 + u * kThreads + tid;
       const int l = i / (nch * 4), ch = (i / 4) % nch, part = i & 3;
-      xv[u] = *(const uint4 *)(a.src + (size_t)l * a.k + ch * 32 + part * 8);
+      const uint32_t off = i < pieces ? ((uint32_t)l * a.k + ch * 32 + part * 8) * 2u : src_bytes;
+      xv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_x, off, 0, 0));
     }
 #pragma unroll
     for (int u = 0; u < XP; ++u) {
