@@ -126,6 +126,14 @@ int qbench_stream_read(const void *buf, size_t bytes, void *sink, int32_t blocks
       qmm::launch_stream_read(buf, bytes, (uint32_t *)sink, blocks, (hipStream_t)stream));
 }
 
+int qbench_mfma_peak(int32_t iters, int32_t blocks, void *sink, double *flops, void *stream) {
+  if (!sink) return QMM_ERR_NULL;
+  if (!aligned(sink, 4)) return QMM_ERR_ALIGN;
+  if (iters < 1 || iters > (1 << 24) || blocks < 1 || blocks > (1 << 20)) return QMM_ERR_ARG;
+  if (flops) *flops = qmm::mfma_peak_flops(iters, blocks);
+  return hip_status(qmm::launch_mfma_peak(iters, (float *)sink, blocks, (hipStream_t)stream));
+}
+
 size_t qgemv_workspace_size(const qmm_weight *w, int32_t m) {
   if (check_weight(w) || m < 1 || m > 4) return 0;
   return qmm::plan_gemv(w->format, w->n, w->k, m).ws_bytes;

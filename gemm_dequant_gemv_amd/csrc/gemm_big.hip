@@ -1,32 +1,36 @@
 // qgemm with 256-row weight tiles, for prefill with many activation rows
 // (dense mode).  Same arithmetic as gemm.hip -- each weight decoded once per
 // tile into bfloat16 ("TurboEXL3" section 4.1: decode once, multiply many
-// times), v_mfma_f32_16x16x32_bf16, float32 sums over K in slice order -- on
-// a different data path:
+// times), bf16 MFMA with float32 sums over K in slice order -- on a different
+// data path:
 //
-//   * the activation tile (TM x 16 rows) goes from memory straight into LDS
+//   * the activation tile (32 TM rows) goes from memory straight into LDS
 //     (buffer_load_dwordx4 ... lds), three 64-wide K slices in flight, with no
 //     register staging; its 16-byte chunks are XOR-swizzled by row so that the
 //     MFMA operand reads of a lane group fall on distinct LDS bank groups;
-//   * the weights never pass through LDS: each wave owns 16 TN rows of the
-//     tile, loads their codes and scales itself (registers, three slices
-//     ahead) and decodes them straight into its MFMA A operands.  The K order
-//     inside a slice is permuted (lane group g of a 16-lane row holds K values
-//     16g .. 16g+15, the first 8 for the slice's first MFMA, the rest for the
-//     second) and the activation operand is read in the same order, so each
-//     lane decodes one contiguous 16-weight run of one row;
-//   * a wave computes TN x TM MFMA tiles (16 TN rows of W x 16 TM rows of X).
-//     From 257 rows of X on: 8 waves of 32 W rows x 256 X rows (TN = 2,
-//     TM = 16), so that each decoded weight feeds 32 MFMAs of its slice, as
-//     do the grouped MoE modes (256 rows is the routing table's tile height).
-//     Up to 256 rows: 4 waves of 32 x 128 (more workgroups for small calls).
-//     A wave holds at most 128 float32 accumulators; two waves share a SIMD.
-//     (One wave of 64 x 256, with 256 accumulators, spilled.)
+//   * the weights never pass through LDS: each wave owns 32 rows of the tile,
+//     loads their codes and scales itself (registers, three slices ahead) and
+//     decodes them straight into its MFMA A operands.  The K order inside a
+//     slice is permuted (lane half h of a 32-lane row holds K values 32h ..
+//     32h+31, 8 of them for each of the slice's four k-steps) and the
+//     activation operand is read in the same order, so each lane decodes one
+//     contiguous 32-weight run of one row with one 16-byte code load;
+//   * a wave computes TM v_mfma_f32_32x32x16_bf16 tiles (its 32 W rows x 32 TM
+//     rows of X).  From 257 rows of X on: 8 waves of 32 W rows x 256 X rows
+//     (TM = 8), so that each decoded weight feeds 8 MFMAs per k-step, as do
+//     the grouped MoE modes (256 rows is the routing table's tile height), or
+//     x 192 rows (TM = 6) where that fills the last round of workgroups
+//     better; up to 256 rows: 4 waves of 32 x 128 (more workgroups for small
+//     calls).  A wave holds at most 128 float32 accumulators; two waves share
+//     a SIMD.
 //
-// Per slice and wave (dense): 64 MFMAs, 32 decoded weights per lane, 32 KB of
-// LDS operand reads; per workgroup 32 KB of activations and 9-14 KB of
-// weight codes from memory, about half of what the 128 x 128 tiles of gemm.hip
-// move per flop.
+// Per slice and wave (dense, TM = 8): 32 MFMAs, 32 decoded weights per lane,
+// 32 KB of LDS operand reads; per workgroup 32 KB of activations and 9-14 KB
+// of weight codes from memory, about half of what the 128 x 128 tiles of
+// gemm.hip move per flop.  (The 32 x 32 x 16 form against the 16 x 16 x 32
+// one, same tiles: 3-15% faster up to 512 rows, the same from 2048 on, where
+// the matrix cores' clock sets the pace: with random operands a bare MFMA
+// loop runs both at ~1.75 PFLOP/s on MI355X, the clock falling to ~1.8 GHz.)
 #include <atomic>
 #include <cstdlib>
 
@@ -50,92 +54,31 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, voff, soff, 0, 0);
 }
 
-// A 16-weight run of one row: codes and what scales them.
-struct Run {
-  uint2 q;     // 16 codes (Q6_K: low nibbles), value 2i in the low nibble of byte i
-  uint32_t h;  // Q6_K: 2 high bits per value
-  uint32_t s;  // affine (scale, bias) / E8M0 / E4M3 / Q6_K int8 sub-block scale
-  uint32_t d;  // Q6_K super-block scale
-};
-
-// Buffer descriptors and the per-lane constant parts of the weight offsets
-// (the lane's row and run); the slice's part goes in the scalar offset.
+// Buffer descriptors and the per-lane constant parts of a lane's weight
+// offsets (its row and half); the slice's part goes in the scalar offset.
 struct WSrc {
   __amdgpu_buffer_rsrc_t rc, rh, rs, rs2;
-  uint32_t v_code[4], v_hi[4], v_s[4], v_d[4];  // per W tile (TN <= 4)
+  uint32_t v_code, v_hi, v_s, v_d;
 };
 
+// The lane's 32-weight run of slice s: values 32h .. 32h+31 of the slice
+// (h = lane / 32), codes and what scales them.
 template <int FMT>
-__device__ __forceinline__ Run load_run(const WSrc &w, int i, int s) {
-  Run p;
-  p.q = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(w.rc, w.v_code[i], s * (kBK / 2), 0));
+__device__ __forceinline__ Piece load_run(const WSrc &w, int s) {
+  Piece p;
+  p.q = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w.rc, w.v_code, s * (kBK / 2), 0));
   if constexpr (FMT == QMM_AFFINE4_G64) {
-    p.s = __builtin_amdgcn_raw_buffer_load_b32(w.rs, w.v_s[i], s * 4, 0);
+    p.s = __builtin_amdgcn_raw_buffer_load_b32(w.rs, w.v_s, s * 4, 0);
   } else if constexpr (FMT == QMM_MXFP4) {
-    p.s = __builtin_amdgcn_raw_buffer_load_b8(w.rs, w.v_s[i], s * 2, 0);
+    p.s = __builtin_amdgcn_raw_buffer_load_b8(w.rs, w.v_s, s * 2, 0);
   } else if constexpr (FMT == QMM_NVFP4) {
-    p.s = __builtin_amdgcn_raw_buffer_load_b8(w.rs, w.v_s[i], s * 4, 0);
+    p.s = __builtin_amdgcn_raw_buffer_load_b16(w.rs, w.v_s, s * 4, 0);
   } else {
-    p.h = __builtin_amdgcn_raw_buffer_load_b32(w.rh, w.v_hi[i], s * (kBK / 4), 0);
-    p.s = __builtin_amdgcn_raw_buffer_load_b8(w.rs, w.v_s[i], s * 4, 0);
-    p.d = __builtin_amdgcn_raw_buffer_load_b16(w.rs2, w.v_d[i], (s / 4) * 2, 0);
+    p.h = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(w.rh, w.v_hi, s * (kBK / 4), 0));
+    p.s = __builtin_amdgcn_raw_buffer_load_b16(w.rs, w.v_s, s * 4, 0);
+    p.d = __builtin_amdgcn_raw_buffer_load_b16(w.rs2, w.v_d, (s / 4) * 2, 0);
   }
   return p;
-}
-
-// The run's 16 weights as bfloat16: values 0-7 -> lo, 8-15 -> hi.
-template <int FMT>
-__device__ __forceinline__ void decode_run(const Run &p, bf16x8_t &lo, bf16x8_t &hi) {
-  const uint32_t w[2] = {p.q.x, p.q.y};
-  uint32_t o[8];
-  if constexpr (FMT == QMM_AFFINE4_G64) {
-    const float s = half_to_float(p.s & 0xFFFFu), b = half_to_float(p.s >> 16);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      // even codes to the bytes of one word, odd codes to another, so that
-      // each code becomes a float with one v_cvt_f32_ubyteN
-      uint32_t ev = w[j] & 0x0F0F0F0Fu, od = (w[j] >> 4) & 0x0F0F0F0Fu;
-      asm volatile("" : "+v"(ev));
-      asm volatile("" : "+v"(od));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[4 * j + i] = pack_bf16(__builtin_fmaf(s, (float)((ev >> (8 * i)) & 0xFFu), b),
-                                 __builtin_fmaf(s, (float)((od >> (8 * i)) & 0xFFu), b));
-    }
-  } else if constexpr (FMT == QMM_MXFP4) {
-    const float sc = e8m0_to_float(p.s);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      o[4 * j + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 0));
-      o[4 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 1));
-      o[4 * j + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 2));
-      o[4 * j + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 3));
-    }
-  } else if constexpr (FMT == QMM_NVFP4) {
-    float sc, unused;
-    e4m3x2_to_float(p.s, sc, unused);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      // E2M1 pair -> two float32 (unit scale), times the E4M3 block scale
-      // (exact), -> bfloat16 pair (exact)
-      const f32x2_t e[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 0),
-                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 1),
-                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 2),
-                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 3)};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[4 * j + i] = pack_bf16(e[i][0] * sc, e[i][1] * sc);
-    }
-  } else {  // Q6_K: (d * sc) * (q - 32), exact in float32
-    const float dsc = half_to_float(p.d) * (float)(int8_t)(p.s & 0xFFu);
-#pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      const uint32_t q0 = ((w[v / 8] >> (4 * (v % 8))) & 15u) | (((p.h >> (2 * v)) & 3u) << 4);
-      const uint32_t q1 = ((w[v / 8] >> (4 * (v % 8) + 4)) & 15u) | (((p.h >> (2 * v + 2)) & 3u) << 4);
-      o[v / 2] = pack_bf16(dsc * (float)((int)q0 - 32), dsc * (float)((int)q1 - 32));
-    }
-  }
-  lo = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
-  hi = __builtin_bit_cast(bf16x8_t, u32x4_t{o[4], o[5], o[6], o[7]});
 }
 
 // Physical 16-byte chunk offset of X row `row` in LDS: logical chunk c sits at
@@ -150,20 +93,18 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 template <int FMT>
 constexpr int w_loads_per_run() { return FMT == QMM_Q6_K ? 4 : 2; }
 
-// A wave computes TN x TM MFMA tiles: 16 TN rows of W x 16 TM rows of X;
-// the workgroup's WAVES waves cover BN = 16 TN WAVES rows of W, all sharing
-// the BM = 16 TM rows of X.  MODE as in gemm.hip: dense, or the grouped MoE
+// A wave owns 32 rows of W and computes them against the workgroup's BM =
+// 32 TM rows of X as TM v_mfma_f32_32x32x16_bf16 tiles; the WAVES waves cover
+// BN = 32 WAVES rows of W.  MODE as in gemm.hip: dense, or the grouped MoE
 // gate/up (rows of x gathered by token, gate and up weight rows interleaved,
 // SwiGLU epilogue) and down products over the routing tile table (tiles of BM
 // grouped rows, one expert each).
-template <int FMT, int TN, int TM, int WAVES, int MODE>
+template <int FMT, int TM, int WAVES, int MODE>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_big_kernel(GemmArgs a) {
-  constexpr int kTN = TN;
-  constexpr int WROWS = 16 * TN;  // W rows per wave
-  constexpr int kBN = WROWS * WAVES;
-  constexpr int BM = 16 * TM;
-  constexpr int kXStage = BM * kXRow;  // bytes per LDS stage
+  constexpr int kBN = 32 * WAVES;
+  constexpr int BM = 32 * TM;
+  constexpr int kXStage = BM * kXRow;   // bytes per LDS stage
   constexpr int XI = BM / (8 * WAVES);  // X load instructions per wave and slice (8 rows each)
   extern __shared__ __align__(16) uint8_t lds[];  // kStages x [BM rows][128 bytes]
   const int tid = threadIdx.x, lane = tid & 63;
@@ -185,13 +126,14 @@ void gemm_big_kernel(GemmArgs a) {
   }
   const int slices = a.k / kBK;
   const uint32_t k = (uint32_t)a.k;
-  const int lr = lane & 15, g = lane >> 4;
+  const int lr = lane & 31, h = lane >> 5;
 
-  // activations: wave w fills rows (BM/4) w .. of a stage, 8 rows per
+  // activations: wave w fills rows (BM/WAVES) w .. of a stage, 8 rows per
   // instruction; lane l of instruction i writes LDS chunk l % 8 of row
-  // (BM/4) w + 8i + l / 8, which holds the row's logical chunk (l % 8) ^ swz(row)
-  // (grouped modes: the routing tables index valid rows of x or h, whose
-  // extent the call does not pass; their descriptor spans the 32-bit range)
+  // (BM/WAVES) w + 8i + l / 8, which holds the row's logical chunk
+  // (l % 8) ^ swz(row) (grouped modes: the routing tables index valid rows
+  // of x or h, whose extent the call does not pass; their descriptor spans
+  // the 32-bit range)
   const __amdgpu_buffer_rsrc_t rx =
       MODE == kDense ? make_rsrc(a.x, (uint32_t)((size_t)a.m * a.k * 2))
                      : make_rsrc(MODE == kMoeGateUp ? (const void *)a.x : (const void *)a.h, 0xFFFFFFFFu);
@@ -211,9 +153,9 @@ void gemm_big_kernel(GemmArgs a) {
       buffer_load_lds16(rx, st + i * 8 * kXRow, v_x[i], s * kXRow);
   };
 
-  // weights: lane (lr, g) of tile i holds tile row j = 64w + 16i + lr, run g;
-  // tile row j is weight row n0 + j, or in the gate/up mode gate or up row
-  // n0/2 + j/2 of the expert (even j gate, odd j up)
+  // weights: lane (lr, h) holds tile row j = 32 w + lr, values 32h .. 32h+31
+  // of each slice; tile row j is weight row n0 + j, or in the gate/up mode
+  // gate or up row n0/2 + j/2 of the expert (even j gate, odd j up)
   WSrc ws;
   {
     const size_t rows = (size_t)a.wrows;
@@ -221,48 +163,43 @@ void gemm_big_kernel(GemmArgs a) {
     ws.rh = make_rsrc(a.codes_hi, a.codes_hi ? (uint32_t)(rows * (k / 4)) : 0u);
     ws.rs = make_rsrc(a.scales, (uint32_t)(rows * (k / (FMT == QMM_AFFINE4_G64 ? 16 : (FMT == QMM_MXFP4 ? 32 : 16)))));
     ws.rs2 = make_rsrc(a.scales2, a.scales2 ? (uint32_t)(rows * (k / 256) * 2) : 0u);
-#pragma unroll
-    for (int i = 0; i < kTN; ++i) {
-      const int j = WROWS * wave + 16 * i + lr;
-      uint32_t r;
-      if constexpr (MODE == kMoeGateUp)
-        r = (uint32_t)(wrow0 + ((j & 1) ? a.inter : 0) + min(n0 / 2 + j / 2, a.inter - 1));
-      else
-        r = (uint32_t)(wrow0 + min(n0 + j, a.n - 1));
-      ws.v_code[i] = r * (k / 2) + 8 * g;
-      ws.v_hi[i] = r * (k / 4) + 4 * g;
-      ws.v_s[i] = FMT == QMM_AFFINE4_G64 ? r * (k / 64) * 4
-                : FMT == QMM_MXFP4       ? r * (k / 32) + (g >> 1)
-                                         : r * (k / 16) + g;
-      ws.v_d[i] = r * (k / 256) * 2;
-    }
+    const int j = 32 * wave + lr;
+    uint32_t r;
+    if constexpr (MODE == kMoeGateUp)
+      r = (uint32_t)(wrow0 + ((j & 1) ? a.inter : 0) + min(n0 / 2 + j / 2, a.inter - 1));
+    else
+      r = (uint32_t)(wrow0 + min(n0 + j, a.n - 1));
+    ws.v_code = r * (k / 2) + 16 * h;
+    ws.v_hi = r * (k / 4) + 8 * h;
+    ws.v_s = FMT == QMM_AFFINE4_G64 ? r * (k / 64) * 4
+           : FMT == QMM_MXFP4       ? r * (k / 32) + h
+                                    : r * (k / 16) + 2 * h;
+    ws.v_d = r * (k / 256) * 2;
   }
-  Run wr[kStages][kTN];
-  auto load_w = [&](int s, int st) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kTN; ++i) wr[st][i] = load_run<FMT>(ws, i, s);
-  };
+  Piece wr[kStages];
 
-  f32x4_t acc[kTN][TM];
+  f32x16_t acc[TM];
 #pragma unroll
-  for (int i = 0; i < kTN; ++i)
+  for (int t = 0; t < TM; ++t)
 #pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
 
-  // operand reads of the activation tile: row 16j + lr, logical chunk 2g + kk
-  // at physical chunk (2g + kk) ^ swz(lr) (swz of 16j + lr is swz(lr))
-  const uint32_t xo0 = (uint32_t)lr * kXRow + (uint32_t)(((2 * g) ^ swz(lr)) * 16);
-  const uint32_t xo1 = (uint32_t)lr * kXRow + (uint32_t)(((2 * g + 1) ^ swz(lr)) * 16);
+  // operand reads of the activation tile for k-step st: row 32t + lr,
+  // logical chunk 4h + st at physical chunk (4h + st) ^ swz(lr) (swz of
+  // 32t + lr is swz(lr))
+  uint32_t xo[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) xo[st] = (uint32_t)lr * kXRow + (uint32_t)(((4 * h + st) ^ swz(lr)) * 16);
 
   // slices 0 .. kStages-2 in flight; every iteration then issues one more
   // (the last slice again past the end, so that every wave issues the same
   // loads and the counts below hold)
-  constexpr int kLoadsPerSlice = XI + kTN * w_loads_per_run<FMT>();
+  constexpr int kLoadsPerSlice = XI + w_loads_per_run<FMT>();
 #pragma unroll
   for (int p = 0; p < kStages - 1; ++p) {
     const int sp = min(p, slices - 1);
     load_x(sp);
-    load_w(sp, p);
+    wr[p] = load_run<FMT>(ws, sp);
   }
 
   for (int s0 = 0; s0 < slices; s0 += kStages) {
@@ -277,42 +214,45 @@ void gemm_big_kernel(GemmArgs a) {
       __syncthreads();
       const int sn = min(s + kStages - 1, slices - 1);
       load_x(sn);
-      load_w(sn, (u + kStages - 1) % kStages);
+      wr[(u + kStages - 1) % kStages] = load_run<FMT>(ws, sn);
 
-      bf16x8_t af[kTN][2];
+      // the run's 32 weights: k-step st takes values 8 st .. 8 st + 7
+      uint32_t o[16];
+      decode_piece<FMT>(wr[u], o);
+      bf16x8_t af[4];
 #pragma unroll
-      for (int i = 0; i < kTN; ++i) decode_run<FMT>(wr[u][i], af[i][0], af[i][1]);
+      for (int st = 0; st < 4; ++st)
+        af[st] = __builtin_bit_cast(bf16x8_t, u32x4_t{o[4 * st], o[4 * st + 1], o[4 * st + 2], o[4 * st + 3]});
 
-      const uint8_t *st = lds + (s % kStages) * kXStage;
+      const uint8_t *stg = lds + (s % kStages) * kXStage;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        // all of this half-slice's activation operands first, so that the
-        // MFMAs below do not wait on LDS after every four
+      for (int st = 0; st < 4; ++st) {
+        // all of this k-step's activation operands first, so that the MFMAs
+        // below do not wait on LDS after each one
         bf16x8_t bfr[TM];
 #pragma unroll
-        for (int j = 0; j < TM; ++j) bfr[j] = *(const bf16x8_t *)(st + j * 16 * kXRow + (kk ? xo1 : xo0));
-        // (Q6_K's longer decode leaves no registers for that)
+        for (int t = 0; t < TM; ++t) bfr[t] = *(const bf16x8_t *)(stg + t * 32 * kXRow + xo[st]);
         if constexpr (FMT != QMM_Q6_K) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < TM; ++j)
-#pragma unroll
-          for (int i = 0; i < kTN; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i][kk], bfr[j], acc[i][j], 0, 0, 0);
+        for (int t = 0; t < TM; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[st], bfr[t], acc[t], 0, 0, 0);
       }
     }
   }
 
-  // epilogue: lane holds D[n = 4*(lane/16) + r][m = lane % 16] of each tile
+  // epilogue: lane (lr, h) holds D[n = 8b + 4h + r][m = lr] of each tile as
+  // value 4b + r: four consecutive W rows per b
   const float gs = (FMT == QMM_NVFP4 && a.tensor_scale) ? a.tensor_scale[expert] : 1.0f;
 #pragma unroll
-  for (int i = 0; i < kTN; ++i) {
-    const int nl = WROWS * wave + 16 * i + 4 * g;  // tile row of v[0]
+  for (int t = 0; t < TM; ++t) {
+    const int ml = 32 * t + lr;
+    if (ml >= mrows) continue;
+    const int m = m0 + ml;
 #pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int ml = 16 * j + lr;
-      if (ml >= mrows) continue;
-      const int m = m0 + ml;
-      float v[4] = {acc[i][j][0] * gs, acc[i][j][1] * gs, acc[i][j][2] * gs, acc[i][j][3] * gs};
+    for (int b = 0; b < 4; ++b) {
+      const int nl = 32 * wave + 8 * b + 4 * h;  // tile row of v[0]
+      float v[4] = {acc[t][4 * b] * gs, acc[t][4 * b + 1] * gs, acc[t][4 * b + 2] * gs,
+                    acc[t][4 * b + 3] * gs};
       if constexpr (MODE == kMoeGateUp) {
         // (gate, up, gate, up) of two consecutive intermediate columns; SwiGLU
         // in float32: h = silu(g) * u, silu(g) = g / (1 + e^-g)
@@ -347,20 +287,20 @@ void gemm_big_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (nb + r >= a.n) break;
-          float t = v[r];
-          if (a.residual) t += bf_lo(a.residual[base + r]);
-          a.y[base + r] = __builtin_bit_cast(uint16_t, (__bf16)t);
+          float t2 = v[r];
+          if (a.residual) t2 += bf_lo(a.residual[base + r]);
+          a.y[base + r] = __builtin_bit_cast(uint16_t, (__bf16)t2);
         }
       }
     }
   }
 }
 
-template <int FMT, int TN, int TM, int WAVES, int MODE>
+template <int FMT, int TM, int WAVES, int MODE>
 hipError_t launch_big(const GemmArgs &a, dim3 grid, hipStream_t s) {
-  static_assert(MODE == kDense || 16 * TM == kMoeTileRows,
+  static_assert(MODE == kDense || 32 * TM == kMoeTileRows,
                 "X tiles are the routing table's tiles of kMoeTileRows rows");
-  constexpr size_t lds = (size_t)kStages * 16 * TM * kXRow;
+  constexpr size_t lds = (size_t)kStages * 32 * TM * kXRow;
   // more than 64 KiB of dynamic LDS must be allowed once per device
   static std::atomic<uint64_t> configured{0};
   int dev = 0;
@@ -368,27 +308,27 @@ hipError_t launch_big(const GemmArgs &a, dim3 grid, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(configured.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute((const void *)gemm_big_kernel<FMT, TN, TM, WAVES, MODE>,
+    e = hipFuncSetAttribute((const void *)gemm_big_kernel<FMT, TM, WAVES, MODE>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((gemm_big_kernel<FMT, TN, TM, WAVES, MODE>), grid, dim3(64 * WAVES), lds, s, a);
+  hipLaunchKernelGGL((gemm_big_kernel<FMT, TM, WAVES, MODE>), grid, dim3(64 * WAVES), lds, s, a);
   return hipGetLastError();
 }
 
-template <int TN, int TM, int WAVES, int MODE>
+template <int TM, int WAVES, int MODE>
 hipError_t launch_big_mode(int format, const GemmArgs &a, dim3 grid, hipStream_t s) {
   switch (format) {
-    case QMM_AFFINE4_G64: return launch_big<QMM_AFFINE4_G64, TN, TM, WAVES, MODE>(a, grid, s);
-    case QMM_MXFP4: return launch_big<QMM_MXFP4, TN, TM, WAVES, MODE>(a, grid, s);
-    case QMM_NVFP4: return launch_big<QMM_NVFP4, TN, TM, WAVES, MODE>(a, grid, s);
-    default: return launch_big<QMM_Q6_K, TN, TM, WAVES, MODE>(a, grid, s);
+    case QMM_AFFINE4_G64: return launch_big<QMM_AFFINE4_G64, TM, WAVES, MODE>(a, grid, s);
+    case QMM_MXFP4: return launch_big<QMM_MXFP4, TM, WAVES, MODE>(a, grid, s);
+    case QMM_NVFP4: return launch_big<QMM_NVFP4, TM, WAVES, MODE>(a, grid, s);
+    default: return launch_big<QMM_Q6_K, TM, WAVES, MODE>(a, grid, s);
   }
 }
 
-// workgroups' rows of W for a TN x WAVES configuration
-constexpr int bn_of(int tn, int waves) { return 16 * tn * waves; }
+// workgroups' rows of W for a configuration of `waves` waves
+constexpr int bn_of(int waves) { return 32 * waves; }
 
 // compute units of the current device (cached per device)
 long compute_units() {
@@ -444,17 +384,16 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
   // at M = 128, 1.4x at M = 256).
   int cfg = 1;
   if (m > 256) {
-    const long nt = (w.n + bn_of(2, 8) - 1) / bn_of(2, 8), cus = compute_units();
+    const long nt = (w.n + bn_of(8) - 1) / bn_of(8), cus = compute_units();
     auto rounds = [&](int bm) { return ((m + bm - 1) / bm * nt + cus - 1) / cus; };
     cfg = 17 * rounds(192) < 20 * rounds(256) ? 4 : 0;
   }
 #ifdef QMM_TUNE
   if (const char *e = getenv("QMM_BIG_CFG")) cfg = atoi(e);
-  if (cfg == 2) return launch_big_mode<4, 8, 4, kDense>(w.format, a, grid(128, bn_of(4, 4)), s);
 #endif
-  if (cfg == 0) return launch_big_mode<2, 16, 8, kDense>(w.format, a, grid(256, bn_of(2, 8)), s);
-  if (cfg == 4) return launch_big_mode<2, 12, 8, kDense>(w.format, a, grid(192, bn_of(2, 8)), s);
-  return launch_big_mode<2, 8, 4, kDense>(w.format, a, grid(128, bn_of(2, 4)), s);
+  if (cfg == 0) return launch_big_mode<8, 8, kDense>(w.format, a, grid(256, bn_of(8)), s);
+  if (cfg == 4) return launch_big_mode<6, 8, kDense>(w.format, a, grid(192, bn_of(8)), s);
+  return launch_big_mode<4, 4, kDense>(w.format, a, grid(128, bn_of(4)), s);
 }
 
 hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const MoeTables &t,
@@ -467,8 +406,8 @@ hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const Moe
   a.h = t.h;
   a.inter = gu.n / 2;
   // each workgroup covers 128 intermediate columns (256 interleaved rows)
-  constexpr int bn = bn_of(2, 8);
-  return launch_big_mode<2, 16, 8, kMoeGateUp>(gu.format, a, dim3(max_tiles, (gu.n + bn - 1) / bn), s);
+  constexpr int bn = bn_of(8);
+  return launch_big_mode<8, 8, kMoeGateUp>(gu.format, a, dim3(max_tiles, (gu.n + bn - 1) / bn), s);
 }
 
 hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
@@ -479,8 +418,8 @@ hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max
   a.h = t.h;
   a.d = t.d;
   a.inter = dn.k;
-  constexpr int bn = bn_of(2, 8);
-  return launch_big_mode<2, 16, 8, kMoeDown>(dn.format, a, dim3(max_tiles, (dn.n + bn - 1) / bn), s);
+  constexpr int bn = bn_of(8);
+  return launch_big_mode<8, 8, kMoeDown>(dn.format, a, dim3(max_tiles, (dn.n + bn - 1) / bn), s);
 }
 
 }  // namespace qmm

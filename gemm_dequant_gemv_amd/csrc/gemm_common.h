@@ -14,6 +14,7 @@ constexpr int kRowH = kBK + kLdsPad;  // bf16 per LDS row
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 // What a workgroup's rows are, and where its results go.
 enum GemmMode {

@@ -1,7 +1,8 @@
-// Achievable HBM read bandwidth: a streaming read of a device buffer with
-// 16-byte non-temporal loads, the same access the GEMV kernels make for their
-// weights.  The GEMV numbers are reported against both this measured figure
-// and the nominal 8 TB/s (the Conifer note measures its own peak with a triad
+// Achievable peaks: a streaming read of a device buffer with 16-byte
+// non-temporal loads, the same access the GEMV kernels make for their weights,
+// and a loop of the bfloat16 MFMA the GEMM uses.  The GEMV and GEMM numbers are
+// reported against both these measured figures and the nominal ones (8 TB/s,
+// 2.5 PFLOP/s; the Conifer note measures its own peak with a triad
 // microbenchmark for the same reason, "How the numbers were taken").
 #include "qmm_device.h"
 #include "qmm_internal.h"
@@ -31,7 +32,48 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restric
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_m;
+typedef __attribute__((ext_vector_type(4))) float f32x4_m;
+
+constexpr int kMfmaChains = 8;  // independent accumulators per wave
+
+// Achievable dense bfloat16 MFMA rate: every wave issues `iters` rounds of
+// kMfmaChains independent v_mfma_f32_16x16x32_bf16 (the instruction the
+// prefill GEMM uses) on operands held in registers, so nothing but the matrix
+// cores and the clock they run at sets the time.
+__global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float *sink) {
+  const uint32_t t = threadIdx.x;
+  bf16x8_m a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(float)((t + i) & 7);
+    b[i] = (__bf16)(float)((t * 3 + i) & 7);
+  }
+  f32x4_m acc[kMfmaChains];
+#pragma unroll
+  for (int j = 0; j < kMfmaChains; ++j) acc[j] = f32x4_m{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < kMfmaChains; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMfmaChains; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  // never true for the operands above; keeps the products alive
+  if (s == -1.0f) sink[0] = s;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_peak(int iters, float *sink, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3(blocks), dim3(256), 0, s, iters, sink);
+  return hipGetLastError();
+}
+
+double mfma_peak_flops(int iters, int blocks) {
+  return 2.0 * 16 * 16 * 32 * (double)kMfmaChains * iters * 4.0 * blocks;
+}
 
 hipError_t launch_stream_read(const void *p, size_t bytes, uint32_t *sink, int blocks,
                               hipStream_t s) {

@@ -22,7 +22,8 @@ FORMATS = {"affine4_g64": AFFINE4_G64, "mxfp4": MXFP4, "nvfp4": NVFP4, "q6_k": Q
 
 ENTRY_POINTS = ("qdequant", "qgemv", "qgemv_workspace_size", "qgemm", "qgemm_workspace_size",
                 "qmoe_grouped", "qmoe_workspace_size", "qmoe_workspace_layout",
-                "qworkspace_init", "qbench_stream_read", "qstatus_string", "qlast_hip_error")
+                "qworkspace_init", "qbench_stream_read", "qbench_mfma_peak", "qstatus_string",
+                "qlast_hip_error")
 
 
 class QmmError(RuntimeError):
@@ -71,6 +72,7 @@ def _lib():
         lib.qmoe_grouped.argtypes = [P, P, I32, I32, VP, I32, VP, VP, I32, VP, VP, I32, VP, SZ, VP]
         lib.qworkspace_init.argtypes = [VP, SZ, VP]
         lib.qbench_stream_read.argtypes = [VP, SZ, VP, I32, VP]
+        lib.qbench_mfma_peak.argtypes = [I32, I32, VP, ctypes.POINTER(ctypes.c_double), VP]
         lib.qstatus_string.restype = ctypes.c_char_p
         lib.qstatus_string.argtypes = [ctypes.c_int]
         _LIB = lib
@@ -223,6 +225,15 @@ def bench_stream_read(buf, sink, blocks: int, stream=None):
     """Stream-read ``buf`` (a device tensor) once; see qbench_stream_read."""
     _check(_lib().qbench_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                      int(blocks), _stream(stream)), "qbench_stream_read")
+
+
+def bench_mfma_peak(iters: int, blocks: int, sink, stream=None) -> float:
+    """Launch the MFMA loop once; returns its operation count.  See
+    qbench_mfma_peak."""
+    flops = ctypes.c_double(0.0)
+    _check(_lib().qbench_mfma_peak(int(iters), int(blocks), _ptr(sink), ctypes.byref(flops),
+                                   _stream(stream)), "qbench_mfma_peak")
+    return flops.value
 
 
 class PreparedGemv:

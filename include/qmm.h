@@ -161,6 +161,17 @@ int qgemv(const qmm_weight *w, const void *x, int32_t m, const void *residual,
 int qbench_stream_read(const void *buf, size_t bytes, void *sink, int32_t blocks, void *stream);
 
 /*
+ * qbench_mfma_peak -- measurement helper: `blocks` workgroups of 4 waves, each
+ * wave issuing `iters` (1 .. 2^24) rounds of 8 independent
+ * v_mfma_f32_16x16x32_bf16 on register operands, the instruction of the
+ * prefill GEMM.  Stores the launch's floating-point operation count in *flops
+ * (host, may be NULL) and writes at most 4 bytes to `sink` (device).  Timing it
+ * gives the achievable dense bf16 matrix rate that the GEMM figures are
+ * compared with, beside the nominal 2.5 PFLOP/s.
+ */
+int qbench_mfma_peak(int32_t iters, int32_t blocks, void *sink, double *flops, void *stream);
+
+/*
  * qgemm -- prefill matrix multiply for many activation rows ("TurboEXL3",
  * section 4.1, decode once, multiply many times: each K-slice of the weights is
  * decoded once per workgroup into on-chip memory as 16-bit values and multiplied
