@@ -140,13 +140,13 @@ def measured_read_peak(q, torch, dev, gib=1.0, reps=10):
 
 
 def measured_mfma_peak(q, torch, dev, reps=10):
-    """Achievable dense bf16 MFMA rate: qbench_mfma_peak (register operands,
-    8 independent accumulators per wave), median of `reps` launches, best of
-    2 and 4 waves per SIMD."""
+    """Achievable dense bf16 MFMA rate: qbench_mfma_peak (random register
+    operands, 4 independent accumulators per wave), median of `reps` launches,
+    best of 2, 4 and 8 waves per SIMD."""
     sink = torch.zeros(64, dtype=torch.int32, device=dev)
-    iters = 4000
+    iters = 2000
     best = None
-    for blocks in (512, 1024):
+    for blocks in (512, 1024, 2048):
         flops = [0.0]
 
         def launch():
@@ -157,7 +157,7 @@ def measured_mfma_peak(q, torch, dev, reps=10):
         if best is None or tf > best[0]:
             best = (tf, blocks)
     return {"TFLOPs": round(best[0], 1), "blocks": best[1], "waves_per_block": 4, "iters": iters,
-            "kernel": "mfma_peak_kernel (v_mfma_f32_16x16x32_bf16, register operands)"}
+            "kernel": "mfma_peak_kernel (v_mfma_f32_32x32x16_bf16, random register operands)"}
 
 
 def traffic_from_profile():

@@ -33,34 +33,55 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restric
 }
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_m;
-typedef __attribute__((ext_vector_type(4))) float f32x4_m;
+typedef __attribute__((ext_vector_type(16))) float f32x16_m;
 
-constexpr int kMfmaChains = 8;  // independent accumulators per wave
+constexpr int kMfmaChains = 4;  // independent accumulators per wave (and operand sets)
+
+// A bfloat16 operand in [-2, 2) with a full random mantissa, from an integer
+// hash of its position (operands that toggle like real data draw the power
+// that real data does, and the matrix cores' clock follows it).
+__device__ __forceinline__ __bf16 operand(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return (__bf16)((float)(int)(x & 0xFFFFu) / 16384.0f - 2.0f);
+}
 
 // Achievable dense bfloat16 MFMA rate: every wave issues `iters` rounds of
-// kMfmaChains independent v_mfma_f32_16x16x32_bf16 (the instruction the
-// prefill GEMM uses) on operands held in registers, so nothing but the matrix
-// cores and the clock they run at sets the time.
+// kMfmaChains independent v_mfma_f32_32x32x16_bf16 (the instruction the
+// prefill GEMM uses) on random operands held in registers, rotating the B
+// operand among kMfmaChains sets, so nothing but the matrix cores and the
+// clock they run at sets the time.
 __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float *sink) {
-  const uint32_t t = threadIdx.x;
-  bf16x8_m a, b;
+  const uint32_t t = threadIdx.x + 256u * blockIdx.x;
+  bf16x8_m a[kMfmaChains], b[kMfmaChains];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(float)((t + i) & 7);
-    b[i] = (__bf16)(float)((t * 3 + i) & 7);
-  }
-  f32x4_m acc[kMfmaChains];
+  for (int c = 0; c < kMfmaChains; ++c)
 #pragma unroll
-  for (int j = 0; j < kMfmaChains; ++j) acc[j] = f32x4_m{0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < iters; ++i) {
+    for (int i = 0; i < 8; ++i) {
+      a[c][i] = operand(t * 64u + c * 8u + i);
+      b[c][i] = operand(t * 64u + 32u + c * 8u + i + 0x9E3779B9u);
+    }
+  f32x16_m acc[kMfmaChains];
 #pragma unroll
-    for (int j = 0; j < kMfmaChains; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+  for (int j = 0; j < kMfmaChains; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+  for (int i = 0; i < iters; i += kMfmaChains) {
+#pragma unroll
+    for (int r = 0; r < kMfmaChains; ++r)
+#pragma unroll
+      for (int j = 0; j < kMfmaChains; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[(j + r) % kMfmaChains], acc[j], 0, 0, 0);
   }
   float s = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kMfmaChains; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
-  // never true for the operands above; keeps the products alive
+  for (int j = 0; j < kMfmaChains; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[j][e];
+  // never true in practice; keeps the products alive
   if (s == -1.0f) sink[0] = s;
 }
 
@@ -72,7 +93,9 @@ hipError_t launch_mfma_peak(int iters, float *sink, int blocks, hipStream_t s) {
 }
 
 double mfma_peak_flops(int iters, int blocks) {
-  return 2.0 * 16 * 16 * 32 * (double)kMfmaChains * iters * 4.0 * blocks;
+  // iterations run in whole rounds of kMfmaChains
+  const double rounds = (double)((iters + kMfmaChains - 1) / kMfmaChains) * kMfmaChains;
+  return 2.0 * 32 * 32 * 16 * (double)kMfmaChains * rounds * 4.0 * blocks;
 }
 
 hipError_t launch_stream_read(const void *p, size_t bytes, uint32_t *sink, int blocks,

@@ -162,9 +162,9 @@ int qbench_stream_read(const void *buf, size_t bytes, void *sink, int32_t blocks
 
 /*
  * qbench_mfma_peak -- measurement helper: `blocks` workgroups of 4 waves, each
- * wave issuing `iters` (1 .. 2^24) rounds of 8 independent
- * v_mfma_f32_16x16x32_bf16 on register operands, the instruction of the
- * prefill GEMM.  Stores the launch's floating-point operation count in *flops
+ * wave issuing `iters` (1 .. 2^24, rounded up to a multiple of 4) rounds of 4
+ * independent v_mfma_f32_32x32x16_bf16 on random register operands, the
+ * instruction of the prefill GEMM.  Stores the launch's floating-point operation count in *flops
  * (host, may be NULL) and writes at most 4 bytes to `sink` (device).  Timing it
  * gives the achievable dense bf16 matrix rate that the GEMM figures are
  * compared with, beside the nominal 2.5 PFLOP/s.
