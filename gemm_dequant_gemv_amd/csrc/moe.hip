@@ -1,7 +1,7 @@
 // qmoe_grouped: one mixture-of-experts layer (routed experts plus optional
-// shared experts).  Up to 4 tokens take the decode form (grouped GEMV over the
-// token slots, moe_gemv.hip, then the combine below); more tokens take the
-// grouped-GEMM form ("TurboEXL3" section 4.1):
+// shared experts).  Up to 4 tokens take the decode form (two grouped GEMV
+// launches over the token slots, moe_gemv.hip, the second also running the
+// combine); more tokens take the grouped-GEMM form ("TurboEXL3" section 4.1):
 //   1. route:    one launch counts each expert's tokens, groups the token slots
 //                by expert and builds the table of row tiles, all in one
 //                pass instead of sorting first and tabulating afterwards;
@@ -173,15 +173,14 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
 struct CombineArgs {
   const float *topk_w;
   const float *shared_w;
-  const int32_t *topk_ids;  // slot-order rows only
   int t, topk, num_routed, num_shared, h;
-  int slot_rows;            // 1: d row = slot (decode form), 0: the grouping tables
   MoeTables tb;
   void *y;
   int y_bf16;
 };
 
-// y[t][n] = sum_j w[t][j] d[row(t, j)][n] + sum_s ws[t] d[row_s(t)][n], fixed order.
+// y[t][n] = sum_j w[t][j] d[row(t, j)][n] + sum_s ws[t] d[row_s(t)][n], fixed order
+// (one fma per term; the decode form runs the same chain in its down launch).
 // A block serves one token: the token's rows and weights go to LDS in chunks
 // of 64 slots, then each thread issues its d loads 8 at a time before adding
 // them, so that no load waits for the previous one.
@@ -191,14 +190,6 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(CombineArgs a) {
   __shared__ float s_w[kChunk];
   const int t = blockIdx.x;
   const int n = blockIdx.y * 256 + threadIdx.x;
-  if (a.slot_rows && t == 0 && blockIdx.y == 0) {
-    // the decode form has no routing pass: report dropped ids here
-    int bad = 0;
-    for (int i = threadIdx.x; i < a.t * a.topk; i += 256)
-      bad |= (a.topk_ids[i] < 0 || a.topk_ids[i] >= a.num_routed) ? 1 : 0;
-    bad = __syncthreads_or(bad);
-    if (threadIdx.x == 0) *a.tb.err = bad ? 1u : 0u;
-  }
   const int total = a.topk + a.num_shared;
   const int nn = min(n, a.h - 1);
   float acc = 0.0f;
@@ -211,17 +202,11 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(CombineArgs a) {
       float w;
       if (j < a.topk) {
         const int slot = t * a.topk + j;
-        if (a.slot_rows) {
-          const int e = a.topk_ids[slot];
-          row = (e < 0 || e >= a.num_routed) ? kInvalidRow : (uint32_t)slot;
-        } else {
-          row = a.tb.row_of_slot[slot];
-        }
+        row = a.tb.row_of_slot[slot];
         w = a.topk_w[slot];
       } else {
         const int sh = j - a.topk;
-        row = a.slot_rows ? (uint32_t)(a.t * a.topk + sh * a.t + t)
-                          : a.tb.row_of_shared[(size_t)sh * a.t + t];
+        row = a.tb.row_of_shared[(size_t)sh * a.t + t];
         w = a.shared_w ? a.shared_w[t] : 1.0f;
       }
       s_row[threadIdx.x] = row;
@@ -307,11 +292,11 @@ hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed
                       hipStream_t s) {
   const MoeLayout L = moe_layout(num_routed + num_shared, t, topk, num_shared, gu.n / 2, dn.n);
   const MoeTables tb = moe_tables(L, workspace);
-  const bool slot_rows = moe_uses_gemv(gu, dn, t, topk, num_shared);
   hipError_t e;
-  if (slot_rows) {
-    e = launch_moe_gemv(gu, dn, num_routed, num_shared, x, t, topk_ids, topk, tb, s);
-    if (e != hipSuccess) return e;
+  if (moe_uses_gemv(gu, dn, t, topk, num_shared)) {
+    // the decode form's down launch also runs the combine
+    return launch_moe_gemv(gu, dn, num_routed, num_shared, x, t, topk_ids, topk_w, topk, shared_w,
+                           y, y_dtype == QMM_BF16, tb, s);
   } else {
     RouteArgs ra{topk_ids, t, topk, num_routed, num_shared, tb};
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ra);
@@ -331,8 +316,8 @@ hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed
     if (e != hipSuccess) return e;
   }
 
-  CombineArgs ca{topk_w, shared_w, topk_ids, t, topk, num_routed, num_shared, dn.n,
-                 slot_rows ? 1 : 0, tb, y, y_dtype == QMM_BF16};
+  CombineArgs ca{topk_w, shared_w, t, topk, num_routed, num_shared, dn.n, tb, y,
+                 y_dtype == QMM_BF16};
   hipLaunchKernelGGL(moe_combine_kernel, dim3(t, (dn.n + 255) / 256), dim3(256), 0, s, ca);
   return hipGetLastError();
 }

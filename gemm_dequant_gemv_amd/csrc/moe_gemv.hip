@@ -11,14 +11,22 @@
 //     of the slot's expert, one row per half-wave, against the slot's token;
 //     after the pair's last step the two half-wave sums are g and u, and one
 //     lane writes h = silu(g) * u (float32, then bfloat16);
-//   * down: a unit is the row quad (4p .. 4p+3) of the slot's down matrix,
+//   * down and combine, one launch: an item is (token t, output quad 4p ..
+//     4p+3) and a job is one of the item's terms j: the token's slots in
+//     combine order (routed slots in list order, then the shared experts).
+//     Workgroup g owns a contiguous block of items and splits its jobs evenly
+//     over its waves (at 4 tokens there are half as many items as waves).  A
+//     unit is one step of a job: the quad's rows of the slot's down matrix,
 //     one row per quarter-wave (a quarter-wave covers 512 values, the whole
-//     intermediate width at I = 512), against the slot's h; the four sums go
-//     to d [slot][H] in float32.
+//     intermediate width at I = 512), against the slot's h; after the job's
+//     last step the four sums are d, written to d [slot][H] in float32 and to
+//     an LDS slot of the item.  After a barrier one wave per item runs, in
+//     lanes 0-3, the chain y = fma(w_j, d_j, y) over the item's terms in
+//     order from 0, the chain the grouped form's combine kernel runs.
 // The grouped rows are the slots themselves (no routing pass): h and d row s
-// belong to slot s, a shared expert's rows follow all routed slots.  The
-// combine launch then adds each token's rows in a fixed order.  Slots whose
-// expert id is outside [0, E) are skipped (their rows are never read).
+// belong to slot s, a shared expert's rows follow all routed slots.  Slots
+// whose expert id is outside [0, E) are skipped (their rows are never read
+// and they add nothing).
 #include <algorithm>
 #include <atomic>
 #include <cstdlib>
@@ -28,7 +36,7 @@
 namespace qmm {
 namespace {
 
-constexpr size_t kLdsLimit = 160 * 1024 - 6144;  // dynamic part; the static tables take 4 KB
+constexpr size_t kLdsLimit = 160 * 1024 - 8192;  // dynamic part; the static tables take <= 6.5 KB
 
 struct MoeGemvArgs {
   const uint8_t *codes, *codes_hi, *scales, *scales2;
@@ -46,6 +54,12 @@ struct MoeGemvArgs {
   int nsrc;
   uint16_t *h;      // gate/up output [slots][I]
   float *d;         // down output [slots][H]
+  // down and combine
+  const float *topk_w;    // [t][topk]
+  const float *shared_w;  // [t] or null (weight 1)
+  void *y;                // [t][H] float32, or bfloat16 when y_bf16
+  int y_bf16;
+  uint32_t *err;          // 1 when an id was outside [0, E)
 };
 
 // LDS layout of the staged vectors: chunk ch (32 values) of vector l at u32
@@ -71,6 +85,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
   extern __shared__ __align__(16) uint32_t smem[];
   __shared__ int s_expert[kMoeGemvMaxSlots];  // expert of each slot, -1 if dropped
   __shared__ int s_vec[kMoeGemvMaxSlots];     // staged vector of each slot
+  __shared__ float s_w[DOWN ? kMoeGemvMaxSlots : 1];  // combine weight of each slot
   const int nch = a.k / 32;
   const int stride = (int)moe_gemv_stride(a.nsrc);
   uint32_t *xs = smem;
@@ -83,13 +98,46 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
   const uint32_t k = (uint32_t)a.k;
   const int routed = a.t * a.topk;
   const int slots = routed + a.t * a.num_shared;
-  const int items = slots * a.pairs;
+  // gate/up: items (slot, pair), one pass of S steps each; down: items
+  // (token, quad), one pass of S steps for each of the token's J slots
+  const int J = DOWN ? a.topk + a.num_shared : 1;
+  const int items = (DOWN ? a.t : slots) * a.pairs;
   const int W = gridDim.x * WAVES;
   const int gw = blockIdx.x * WAVES + wave;
-  const int myitems = gw < items ? (items - 1 - gw) / W + 1 : 0;
-  const int units = myitems * S;
-  const int last_item = myitems > 0 ? gw + (myitems - 1) * W : gw;
-  const int s_last = last_item / a.pairs, p_last = last_item - (last_item / a.pairs) * a.pairs;
+  // the wave's jobs: gate/up items gw, gw + W, ...; down jobs [q0, q1) of the
+  // workgroup's items [ib0, ib1), item-major
+  int ib0 = 0, ib1 = 0, q0 = 0, myjobs;
+  if constexpr (DOWN) {
+    ib0 = (int)((long long)blockIdx.x * items / gridDim.x);
+    ib1 = (int)((long long)(blockIdx.x + 1) * items / gridDim.x);
+    const int nq = (ib1 - ib0) * J;
+    q0 = wave * nq / WAVES;
+    myjobs = (wave + 1) * nq / WAVES - q0;
+  } else {
+    myjobs = gw < items ? (items - 1 - gw) / W + 1 : 0;
+  }
+  const int units = myjobs * S;
+  // the wave's first and last job: (slot or token, pair or quad, term)
+  int s_first, p_first, term_first, s_last, p_last, term_last;
+  {
+    int i0, i1;
+    if constexpr (DOWN) {
+      const int qa = q0, qb = q0 + max(myjobs, 1) - 1;
+      i0 = ib0 + qa / J;
+      term_first = qa % J;
+      i1 = ib0 + qb / J;
+      term_last = qb % J;
+    } else {
+      i0 = gw;
+      i1 = myjobs > 0 ? gw + (myjobs - 1) * W : gw;
+      term_first = term_last = 0;
+    }
+    s_first = i0 / a.pairs;
+    p_first = i0 - s_first * a.pairs;
+    s_last = i1 / a.pairs;
+    p_last = i1 - s_last * a.pairs;
+  }
+  float *dq = (float *)(xs + (size_t)nch * stride) + (size_t)a.nsrc * kNS * nch;  // down: [items][J][4]
 
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes, a.codes_bytes);
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.codes_hi, a.hi_bytes);
@@ -114,26 +162,37 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
   auto slot_vector = [&](int s) {
     return DOWN ? s : (s < routed ? s / a.topk : (s - routed) % a.t);
   };
+  // down: slot of the token's j-th term (routed slots in list order, then the
+  // shared experts), and its combine weight
+  auto slot_of = [&](int t, int j) {
+    return j < a.topk ? t * a.topk + j : routed + (j - a.topk) * a.t + t;
+  };
+  auto slot_weight = [&](int sl) {
+    if (sl < routed) return a.topk_w[sl];
+    return a.shared_w ? a.shared_w[(sl - routed) % a.t] : 1.0f;
+  };
 
   // 1. the first units' weights, then the staged vectors.  The expert of a
   //    unit comes from global memory for these first units and from the LDS
   //    table afterwards, so that no later weight load waits for a scalar
   //    load of the routing ids.
-  // Items advance by W: (slot, pair) moves by (W / pairs, W % pairs), so the
-  //    walk needs no division per unit.
-  const int sW = W / a.pairs, pW = W - (W / a.pairs) * a.pairs;
-  const int s_first = gw / a.pairs, p_first = gw - (gw / a.pairs) * a.pairs;
+  // Gate/up items advance by W: (slot, pair) moves by (W / pairs, W %
+  //    pairs), so the walk needs no division per unit; down items advance by
+  //    one (token, quad).
+  const int sW = DOWN ? 0 : W / a.pairs, pW = DOWN ? 1 : W - (W / a.pairs) * a.pairs;
   auto advance = [&](int &s, int &p) {
     s += sW;
     p += pW;
     if (p >= a.pairs) { p -= a.pairs; ++s; }
   };
-  auto load_unit = [&](int j, int s, int p, int s_step, RowData &rd, bool from_lds) {
-    if (j >= myitems) {  // uniform: re-read the wave's last unit (or its first item)
+  auto load_unit = [&](int u, int s, int p, int term, int s_step, RowData &rd, bool from_lds) {
+    if (u >= units) {  // uniform: re-read the wave's last unit (or its first job)
       s = s_last;
       p = p_last;
+      term = term_last;
       s_step = S - 1;
     }
+    if constexpr (DOWN) s = slot_of(min(s, a.t - 1), term);
     s = min(s, slots - 1);
     const int e = max(from_lds ? s_expert[s] : slot_expert(s), 0);
     const uint32_t row0 = (uint32_t)(e * a.rows + p * a.pair_step);
@@ -157,16 +216,33 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
     }
   };
   RowData buf[U];
-  int lj = 0, ls = 0, l_s = s_first, l_p = p_first;  // next unit to load
+  int ls = 0, lt = term_first, l_s = s_first, l_p = p_first;  // next unit to load
+  auto advance_unit = [&](int &st, int &term, int &s, int &p) {
+    if (++st == S) {
+      st = 0;
+      if (++term == J) { term = 0; advance(s, p); }
+    }
+  };
 #pragma unroll
   for (int j = 0; j < U; ++j) {
-    load_unit(lj, l_s, l_p, ls, buf[j], false);
-    if (++ls == S) { ls = 0; ++lj; advance(l_s, l_p); }
+    load_unit(j, l_s, l_p, lt, ls, buf[j], false);
+    advance_unit(ls, lt, l_s, l_p);
   }
   __builtin_amdgcn_sched_barrier(0);
   for (int i = tid; i < slots; i += kThreads) {
     s_expert[i] = slot_expert(i);
     s_vec[i] = slot_vector(i);
+    if constexpr (DOWN) s_w[i] = slot_weight(i);
+  }
+  if constexpr (DOWN) {
+    // the decode form has no routing pass: report dropped ids here
+    if (blockIdx.x == 0) {
+      int bad = 0;
+      for (int i = tid; i < routed; i += kThreads)
+        bad |= (a.topk_ids[i] < 0 || a.topk_ids[i] >= a.num_routed) ? 1 : 0;
+      bad = __syncthreads_or(bad);
+      if (tid == 0) *a.err = bad ? 1u : 0u;
+    }
   }
 
   const int pieces = a.nsrc * nch * 4;  // 16-byte pieces, [vector][chunk][part]
@@ -216,15 +292,15 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
   }
   __syncthreads();
 
-  // 2. the units: unit (item j, step) of this wave
+  // 2. the units: unit (item, term, step) of this wave
   const UnpackK K = unpack_consts();
   float acc[1] = {0.0f};
-  int cs = 0, c_s = s_first, c_p = p_first;  // unit being computed
+  int cs = 0, ct = term_first, c_s = s_first, c_p = p_first;  // unit being computed
   for (int t0 = 0; t0 < units; t0 += U) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       if (t0 + j < units) {  // uniform
-        const int s = c_s, p = c_p;
+        const int s = DOWN ? slot_of(c_s, ct) : c_s, p = c_p;
         const int e = s_expert[s], l = s_vec[s];
         const int ch = cs * SH::kLanes + c;
         if (ch < nch) {
@@ -257,14 +333,39 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
             float q4[4];
             quarter_sums(acc[0], q4);
             const float v = lane == 0 ? q4[0] : lane == 1 ? q4[1] : lane == 2 ? q4[2] : q4[3];
-            if (e >= 0 && lane < 4) a.d[(size_t)s * a.rows + 4 * p + lane] = v * g;
+            const float dv = v * g;
+            if (lane < 4) {
+              if (e >= 0) a.d[(size_t)s * a.rows + 4 * p + lane] = dv;
+              dq[((size_t)(c_s * a.pairs + p - ib0) * J + ct) * 4 + lane] = dv;
+            }
           }
           acc[0] = 0.0f;
         }
-        if (++cs == S) { cs = 0; advance(c_s, c_p); }
+        advance_unit(cs, ct, c_s, c_p);
       }
-      load_unit(lj, l_s, l_p, ls, buf[j], true);
-      if (++ls == S) { ls = 0; ++lj; advance(l_s, l_p); }
+      load_unit(t0 + j + U, l_s, l_p, lt, ls, buf[j], true);
+      advance_unit(ls, lt, l_s, l_p);
+    }
+  }
+
+  if constexpr (DOWN) {
+    // the combine: one wave per item, lanes 0-3 its four outputs, the terms
+    // in order, dropped slots skipped
+    __syncthreads();
+    for (int il = wave; il < ib1 - ib0; il += WAVES) {
+      const int item = ib0 + il, tok = item / a.pairs, p = item - tok * a.pairs;
+      if (lane < 4) {
+        float y = 0.0f;
+        for (int j = 0; j < J; ++j) {
+          const int sl = slot_of(tok, j);
+          if (s_expert[sl] >= 0) y = __builtin_fmaf(s_w[sl], dq[((size_t)il * J + j) * 4 + lane], y);
+        }
+        const size_t o = (size_t)tok * a.rows + 4 * p + lane;
+        if (a.y_bf16)
+          ((uint16_t *)a.y)[o] = (uint16_t)float_to_bf16(y);
+        else
+          ((float *)a.y)[o] = y;
+      }
     }
   }
 }
@@ -286,8 +387,11 @@ struct MoeGemvCfg {
   int u, waves, wpc;
 };
 
-MoeGemvCfg moe_gemv_cfg() {
-  MoeGemvCfg c{2, 16, 1};  // measured best on the 512-expert decode layer
+MoeGemvCfg moe_gemv_cfg(bool down) {
+  // measured best on the 512-expert decode layer (the down launch: 2 units in
+  // flight 14.4 us, 4 15.1 us, 8 16.4 us)
+  (void)down;
+  MoeGemvCfg c{2, 16, 1};
 #ifdef QMM_TUNE
   if (const char *e = getenv("QMM_MOE_U")) c.u = atoi(e);
   if (const char *e = getenv("QMM_MOE_WAVES")) c.waves = atoi(e);
@@ -329,9 +433,8 @@ hipError_t launch_cfg(const MoeGemvCfg &c, const MoeGemvArgs &a, size_t lds, int
 }
 
 template <bool DOWN>
-hipError_t launch_fmt(int format, const MoeGemvArgs &a, size_t lds, hipStream_t s) {
-  const MoeGemvCfg c = moe_gemv_cfg();
-  const int grid = cu_count_moe() * c.wpc;
+hipError_t launch_fmt(int format, const MoeGemvArgs &a, size_t lds, int grid, hipStream_t s) {
+  const MoeGemvCfg c = moe_gemv_cfg(DOWN);
   switch (format) {
     case QMM_AFFINE4_G64: return launch_cfg<QMM_AFFINE4_G64, DOWN>(c, a, lds, grid, s);
     case QMM_MXFP4: return launch_cfg<QMM_MXFP4, DOWN>(c, a, lds, grid, s);
@@ -344,6 +447,16 @@ size_t stage_lds(int format, int k, int nsrc) {
   const int sums = format == QMM_AFFINE4_G64 ? 1 : (format == QMM_Q6_K ? 2 : 0);
   const size_t nch = (size_t)k / 32;
   return nch * moe_gemv_stride(nsrc) * 4 + (size_t)nsrc * sums * nch * 4;
+}
+
+int moe_grid() { return cu_count_moe() * moe_gemv_cfg(true).wpc; }
+
+// the down launch: staged h, then the d quads of the workgroup's items
+size_t down_lds(const qmm_weight &dn, int t, int topk, int num_shared, int grid) {
+  const int slots = t * (topk + num_shared);
+  const size_t items = (size_t)t * (dn.n / 4);
+  const size_t per_wg = (items + grid - 1) / grid;
+  return stage_lds(dn.format, dn.k, slots) + per_wg * (topk + num_shared) * 16;
 }
 
 MoeGemvArgs weight_args(const qmm_weight &w) {
@@ -369,13 +482,15 @@ bool moe_gemv_fits(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, 
   if (t > kMoeGemvMaxTokens) return false;
   const int slots = t * (topk + num_shared);
   if (slots > kMoeGemvMaxSlots || dn.n % 4 != 0) return false;
+  if (cu_count_moe() <= 0) return false;
   return stage_lds(gu.format, gu.k, t) <= kLdsLimit &&
-         stage_lds(dn.format, dn.k, slots) <= kLdsLimit && cu_count_moe() > 0;
+         down_lds(dn, t, topk, num_shared, moe_grid()) <= kLdsLimit;
 }
 
 hipError_t launch_moe_gemv(const qmm_weight &gu, const qmm_weight &dn, int num_routed,
                            int num_shared, const void *x, int t, const int32_t *topk_ids,
-                           int topk, const MoeTables &tb, hipStream_t s) {
+                           const float *topk_w, int topk, const float *shared_w, void *y,
+                           int y_bf16, const MoeTables &tb, hipStream_t s) {
   const int slots = t * (topk + num_shared);
   const int inter = gu.n / 2;
 
@@ -392,7 +507,8 @@ hipError_t launch_moe_gemv(const qmm_weight &gu, const qmm_weight &dn, int num_r
   g.src = (const uint16_t *)x;
   g.nsrc = t;
   g.h = tb.h;
-  hipError_t e = launch_fmt<false>(gu.format, g, stage_lds(gu.format, gu.k, t), s);
+  const int grid = moe_grid();
+  hipError_t e = launch_fmt<false>(gu.format, g, stage_lds(gu.format, gu.k, t), grid, s);
   if (e != hipSuccess) return e;
 
   MoeGemvArgs d = weight_args(dn);
@@ -408,7 +524,12 @@ hipError_t launch_moe_gemv(const qmm_weight &gu, const qmm_weight &dn, int num_r
   d.src = tb.h;
   d.nsrc = slots;
   d.d = tb.d;
-  return launch_fmt<true>(dn.format, d, stage_lds(dn.format, dn.k, slots), s);
+  d.topk_w = topk_w;
+  d.shared_w = shared_w;
+  d.y = y;
+  d.y_bf16 = y_bf16;
+  d.err = tb.err;
+  return launch_fmt<true>(dn.format, d, down_lds(dn, t, topk, num_shared, grid), grid, s);
 }
 
 }  // namespace qmm

@@ -96,7 +96,8 @@ bool moe_gemv_fits(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, 
 bool moe_uses_gemv(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_shared);
 hipError_t launch_moe_gemv(const qmm_weight &gu, const qmm_weight &dn, int num_routed,
                            int num_shared, const void *x, int t, const int32_t *topk_ids,
-                           int topk, const MoeTables &tb, hipStream_t s);
+                           const float *topk_w, int topk, const float *shared_w, void *y,
+                           int y_bf16, const MoeTables &tb, hipStream_t s);
 hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed, int num_shared,
                       const void *x, int t, const int32_t *topk_ids, const float *topk_w,
                       int topk, const float *shared_w, void *y, int y_dtype, void *workspace,

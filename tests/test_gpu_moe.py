@@ -72,6 +72,8 @@ def run_gpu(q, gu, dn, x, ids, w, E, S, shared_w=None, y_dtype=torch.float32, wd
         r["active"] = _u32(ws, L["active"], n_active)
         r["tiles"] = _u32(ws, L["tiles"], 3 * n_tiles).reshape(-1, 3)
     r["h"] = ws[L["h"]:L["h"] + rows * I * 2].view(torch.int16).cpu().numpy().view(np.uint16).reshape(rows, I)
+    H = dn.n
+    r["d"] = ws[L["d"]:L["d"] + rows * H * 4].view(torch.float32).cpu().numpy().reshape(rows, H)
     if y.dtype == torch.bfloat16:
         yh = oracle.bf16(y.view(torch.int16).cpu().numpy().view(np.uint16))
     else:
@@ -233,6 +235,51 @@ def test_moe_invalid_expert_ids_contribute_nothing(T):
     for b in bad:
         hd[b] = np.zeros(I, np.uint16)
     check_y(gu, dn, x, ids2, w2, E, 1, yh, hd, tokens)
+
+
+def _fma_f32(a, b, c):
+    """fma(a, b, c) in float32: the exact a * b + c rounded once to nearest
+    even (exact rational arithmetic, then the nearest float32)."""
+    from fractions import Fraction
+    exact = Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c))
+    f = np.float32(float(exact))
+    best = None
+    for cand in (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))):
+        err = abs(Fraction(float(cand)) - exact)
+        key = (err, int(np.array(cand, np.float32).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, cand)
+    return np.float32(best[1])
+
+
+@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("y_dtype", [torch.float32, torch.bfloat16])
+def test_moe_decode_combine_is_the_fixed_fma_chain(T, y_dtype):
+    """The decode form runs the combine inside its down launch: each output is
+    the float32 chain acc = fma(w_j, d_j, acc) over the token's terms (routed
+    slots in list order, skipping dropped ids, then the shared experts), from
+    0, the chain the grouped form's combine kernel runs.  Checked bit for bit
+    against that chain evaluated exactly on the d rows the launch wrote."""
+    q = _q()
+    E, S, H, I, topk = 12, 2, 256, 128, 4
+    gu, dn, x, ids, w = make_case(F.NVFP4, F.AFFINE4_G64, E, S, H, I, T, topk, f"moefc{T}")
+    ids = ids.copy()
+    ids[0, 2] = E + 3  # a dropped slot
+    sw = np.linspace(0.5, 1.5, T).astype(np.float32)
+    yh, r = run_gpu(q, gu, dn, x, ids, w, E, S, shared_w=sw, y_dtype=y_dtype)
+    assert r["slot_rows"]
+    d = r["d"]
+    for t in range(T):
+        terms = [(t * topk + j, w[t, j]) for j in range(topk) if 0 <= ids[t, j] < E]
+        terms += [(T * topk + s * T + t, sw[t]) for s in range(S)]
+        acc = np.zeros(H, np.float32)
+        for row, wt in terms:
+            acc = np.array([_fma_f32(wt, d[row, n], acc[n]) for n in range(H)], np.float32)
+        if y_dtype == torch.bfloat16:
+            want = oracle.bf16(oracle.bf16_round(acc))
+        else:
+            want = acc.astype(np.float64)
+        assert np.array_equal(yh[t], want), f"token {t}"
 
 
 @pytest.mark.parametrize("T", [4, 300])
