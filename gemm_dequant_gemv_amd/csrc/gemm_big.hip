@@ -210,8 +210,10 @@ void gemm_big_kernel(GemmArgs a) {
       // this wave's share of slice s is in LDS once at most the loads issued
       // after it (kStages - 2 slices) are outstanding; the barrier then makes
       // every wave's share visible and frees the stage read in iteration s - 1
+      // (whose operands are already in registers).  A bare s_barrier: the
+      // fence of __syncthreads would also wait for the slices still in flight.
       __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kLoadsPerSlice));
-      __syncthreads();
+      __builtin_amdgcn_s_barrier();
       const int sn = min(s + kStages - 1, slices - 1);
       load_x(sn);
       wr[(u + kStages - 1) % kStages] = load_run<FMT>(ws, sn);

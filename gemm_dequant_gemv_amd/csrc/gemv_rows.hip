@@ -155,6 +155,9 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
   const int o_h = lane & 1, o_m = min(lane >> 1, M - 1);
   const uint32_t v_res = ((uint32_t)o_m * a.n + o_h) * 2;
 
+  // 0. the NVFP4 tensor scale (used at every pair's store)
+  float gscale = (FMT == QMM_NVFP4 && a.tensor_scale) ? a.tensor_scale[0] : 1.0f;
+
   // 1. the activations, first, so that they do not queue behind the codes.
   //    Every thread issues kXPieces loads (so the compiler counts outstanding
   //    loads exactly); a load with no piece to fetch points past the end of
@@ -253,7 +256,10 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
   __syncthreads();
 
   const UnpackK K = unpack_consts();
-  const float gscale = (FMT == QMM_NVFP4 && a.tensor_scale) ? a.tensor_scale[0] : 1.0f;
+  // gscale's load completed before the barrier above (loads complete in
+  // order and x was loaded after it); the empty asm tells the compiler so,
+  // which keeps it from waiting for every load in flight at each pair's store
+  asm volatile("" : "+v"(gscale));
   auto store = [&](int row, float v) {
     if (a.y_bf16)
       ((uint16_t *)a.y)[(size_t)o_m * a.n + row] = (uint16_t)float_to_bf16(v);

@@ -83,8 +83,6 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
   using T = FmtTraits<FMT>;
   constexpr int kNS = T::kSums;
   extern __shared__ __align__(16) uint32_t smem[];
-  __shared__ int s_expert[kMoeGemvMaxSlots];  // expert of each slot, -1 if dropped
-  __shared__ int s_vec[kMoeGemvMaxSlots];     // staged vector of each slot
   __shared__ float s_w[DOWN ? kMoeGemvMaxSlots : 1];  // combine weight of each slot
   const int nch = a.k / 32;
   const int stride = (int)moe_gemv_stride(a.nsrc);
@@ -185,6 +183,30 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
     p += pW;
     if (p >= a.pairs) { p -= a.pairs; ++s; }
   };
+  // Slot table in registers: lane l holds slot l (tab0, gsc0) and slot
+  // 64 + l (tab1, gsc1): valid << 31 | expert << 16 | staged vector (an
+  // invalid slot reads expert 0's rows), and the expert's NVFP4 tensor scale;
+  // read back with v_readlane at a uniform lane, so every lookup lands in
+  // scalar registers.  (An LDS table, or a global load of the tensor scale
+  // per item, made the compiler wait for every weight load in flight before
+  // each lookup, which undid the load pipeline.)
+  uint32_t tab0 = 0, tab1 = 0;
+  float gsc0 = 1.0f, gsc1 = 1.0f;
+  auto table_entry = [&](int sl, float &gs) {
+    const int e = slot_expert(sl);
+    gs = (FMT == QMM_NVFP4 && a.tensor_scale && e >= 0) ? a.tensor_scale[e] : 1.0f;
+    return (e >= 0 ? 0x80000000u : 0u) | ((uint32_t)max(e, 0) << 16) | (uint32_t)slot_vector(sl);
+  };
+  auto lookup = [&](int sl) {
+    const uint32_t v0 = (uint32_t)__builtin_amdgcn_readlane((int)tab0, sl & 63);
+    const uint32_t v1 = (uint32_t)__builtin_amdgcn_readlane((int)tab1, sl & 63);
+    return sl < 64 ? v0 : v1;
+  };
+  auto tensor_scale_of = [&](int sl) {
+    const float v0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gsc0), sl & 63));
+    const float v1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gsc1), sl & 63));
+    return sl < 64 ? v0 : v1;
+  };
   auto load_unit = [&](int u, int s, int p, int term, int s_step, RowData &rd, bool from_lds) {
     if (u >= units) {  // uniform: re-read the wave's last unit (or its first job)
       s = s_last;
@@ -194,7 +216,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
     }
     if constexpr (DOWN) s = slot_of(min(s, a.t - 1), term);
     s = min(s, slots - 1);
-    const int e = max(from_lds ? s_expert[s] : slot_expert(s), 0);
+    const int e = from_lds ? (int)((lookup(s) >> 16) & 0x7FFFu) : max(slot_expert(s), 0);
     const uint32_t row0 = (uint32_t)(e * a.rows + p * a.pair_step);
     rd.q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
         rc, v_code, row0 * (k / 2) + (uint32_t)s_step * (kStepK / 2), 2));
@@ -229,10 +251,10 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
     advance_unit(ls, lt, l_s, l_p);
   }
   __builtin_amdgcn_sched_barrier(0);
-  for (int i = tid; i < slots; i += kThreads) {
-    s_expert[i] = slot_expert(i);
-    s_vec[i] = slot_vector(i);
-    if constexpr (DOWN) s_w[i] = slot_weight(i);
+  if (lane < slots) tab0 = table_entry(lane, gsc0);
+  if (lane + 64 < slots) tab1 = table_entry(lane + 64, gsc1);
+  if constexpr (DOWN) {
+    for (int i = tid; i < slots; i += kThreads) s_w[i] = slot_weight(i);
   }
   if constexpr (DOWN) {
     // the decode form has no routing pass: report dropped ids here
@@ -292,6 +314,11 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
   }
   __syncthreads();
 
+  // The table's loads were waited for at the barrier above (loads complete
+  // in order and the staged vectors were loaded after them); passing the
+  // values through an empty asm tells the compiler so, which keeps it from
+  // waiting for every load in flight at each lookup in the loop below.
+  asm volatile("" : "+v"(tab0), "+v"(tab1), "+v"(gsc0), "+v"(gsc1));
   // 2. the units: unit (item, term, step) of this wave
   const UnpackK K = unpack_consts();
   float acc[1] = {0.0f};
@@ -301,7 +328,9 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
     for (int j = 0; j < U; ++j) {
       if (t0 + j < units) {  // uniform
         const int s = DOWN ? slot_of(c_s, ct) : c_s, p = c_p;
-        const int e = s_expert[s], l = s_vec[s];
+        const uint32_t ent = lookup(s);
+        const bool valid = (ent >> 31) != 0;
+        const int l = (int)(ent & 0xFFFFu);
         const int ch = cs * SH::kLanes + c;
         if (ch < nch) {
           uint32_t X[1][16];
@@ -320,11 +349,11 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
           row_step<FMT, 1>(buf[j], X, Sx, acc, K);
         }
         if (cs == S - 1) {  // the item's rows are complete
-          const float g = (FMT == QMM_NVFP4 && a.tensor_scale && e >= 0) ? a.tensor_scale[e] : 1.0f;
+          const float g = tensor_scale_of(s);
           if constexpr (!DOWN) {
             float s0, s1;
             half_sums(acc[0], s0, s1);
-            if (e >= 0 && lane == 0) {
+            if (valid && lane == 0) {
               const float gv = s0 * g, uv = s1 * g;
               const float hv = gv / (1.0f + expf(-gv)) * uv;
               a.h[(size_t)s * a.pairs + p] = (uint16_t)float_to_bf16(hv);
@@ -335,7 +364,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
             const float v = lane == 0 ? q4[0] : lane == 1 ? q4[1] : lane == 2 ? q4[2] : q4[3];
             const float dv = v * g;
             if (lane < 4) {
-              if (e >= 0) a.d[(size_t)s * a.rows + 4 * p + lane] = dv;
+              if (valid) a.d[(size_t)s * a.rows + 4 * p + lane] = dv;
               dq[((size_t)(c_s * a.pairs + p - ib0) * J + ct) * 4 + lane] = dv;
             }
           }
@@ -358,7 +387,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
         float y = 0.0f;
         for (int j = 0; j < J; ++j) {
           const int sl = slot_of(tok, j);
-          if (s_expert[sl] >= 0) y = __builtin_fmaf(s_w[sl], dq[((size_t)il * J + j) * 4 + lane], y);
+          if (lookup(sl) >> 31) y = __builtin_fmaf(s_w[sl], dq[((size_t)il * J + j) * 4 + lane], y);
         }
         const size_t o = (size_t)tok * a.rows + 4 * p + lane;
         if (a.y_bf16)

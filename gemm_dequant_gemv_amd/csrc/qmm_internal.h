@@ -91,7 +91,7 @@ hipError_t launch_moe_gemm_down(const qmm_weight &dn, const MoeTables &t, int ma
                                 hipStream_t s);
 // decode form of qmoe_grouped: grouped GEMV over token slots (t <= 4)
 constexpr int kMoeGemvMaxTokens = 4;
-constexpr int kMoeGemvMaxSlots = 512;
+constexpr int kMoeGemvMaxSlots = 128;  // token slots of the decode form (register table)
 bool moe_gemv_fits(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_shared);
 bool moe_uses_gemv(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_shared);
 hipError_t launch_moe_gemv(const qmm_weight &gu, const qmm_weight &dn, int num_routed,
