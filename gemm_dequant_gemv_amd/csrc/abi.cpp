@@ -174,19 +174,17 @@ int qgemv(const qmm_weight *w, const void *x, int32_t m, const void *residual, v
 }
 
 size_t qgemm_workspace_size(const qmm_weight *w, int32_t m) {
-  (void)w;
-  (void)m;
-  return 0;
+  if (check_weight(w) || w->batch != 1 || w->k % 64 != 0 || m < 1) return 0;
+  return qmm::gemm_workspace_size(*w, m);
 }
 
 int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, void *y,
           void *workspace, size_t workspace_bytes, void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   int st = check_weight(w);
   if (st) return st;
   if (w->batch != 1) return QMM_ERR_SHAPE;
   if (w->k % 64 != 0) return QMM_ERR_SHAPE;
+  if (workspace && !aligned(workspace, 256)) return QMM_ERR_ALIGN;
   if (m < 1) return QMM_ERR_M_RANGE;
   if (!x || !y) return QMM_ERR_NULL;
   if (!aligned(x, 16) || !aligned(y, 16) || (residual && !aligned(residual, 16)))
@@ -198,7 +196,14 @@ int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, v
   if (residual) ins[ni++] = range(residual, (size_t)m * w->n * 2);
   for (int i = 0; i < ni; ++i)
     if (overlap(ry, ins[i])) return QMM_ERR_ALIAS;
-  return hip_status(qmm::launch_gemm(*w, x, m, residual, y, (hipStream_t)stream));
+  if (workspace) {
+    const Range rw = range(workspace, workspace_bytes);
+    if (overlap(rw, ry)) return QMM_ERR_ALIAS;
+    for (int i = 0; i < ni; ++i)
+      if (overlap(rw, ins[i])) return QMM_ERR_ALIAS;
+  }
+  return hip_status(
+      qmm::launch_gemm(*w, x, m, residual, y, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
 size_t qmoe_workspace_size(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,

@@ -278,15 +278,20 @@ GemmArgs weight_args(const qmm_weight &w) {
 
 }  // namespace
 
+size_t gemm_workspace_size(const qmm_weight &w, int m) {
+  return gemm_big_fits(w, (size_t)m) ? gemm_big_workspace(w, m) : 0;
+}
+
 hipError_t launch_gemm(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
-                       hipStream_t s) {
+                       void *workspace, size_t workspace_bytes, hipStream_t s) {
   // weights decoded straight into MFMA operands (gemm_big.hip) wherever its
   // 32-bit offsets reach; this LDS-staged kernel otherwise
   bool big = true;
 #ifdef QMM_TUNE
   if (const char *e = getenv("QMM_GEMM_BIG")) big = atoi(e) != 0;
 #endif
-  if (big && gemm_big_fits(w, (size_t)m)) return launch_gemm_big(w, x, m, residual, y, s);
+  if (big && gemm_big_fits(w, (size_t)m))
+    return launch_gemm_big(w, x, m, residual, y, workspace, workspace_bytes, s);
   GemmArgs a = weight_args(w);
   a.x = (const uint16_t *)x;
   a.residual = (const uint16_t *)residual;

@@ -31,6 +31,7 @@
 // one, same tiles: 3-15% faster up to 512 rows, the same from 2048 on, where
 // the matrix cores' clock sets the pace: with random operands a bare MFMA
 // loop runs both at ~1.75 PFLOP/s on MI355X, the clock falling to ~1.8 GHz.)
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 
@@ -41,7 +42,9 @@ namespace {
 
 using namespace gemm;
 
-constexpr int kStages = 3;      // LDS stages of X = slices in flight
+constexpr int kStages = 3;  // LDS stages of X = slices in flight
+// (6 or 8 stages for the 32- and 64-row tiles measured 10% faster unsplit but
+// slower split, and the split form is the faster one for those calls)
 constexpr int kXRow = kBK * 2;  // bytes of one X row in a slice
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -109,11 +112,13 @@ void gemm_big_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];  // kStages x [BM rows][128 bytes]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int m0, n0, mrows, wrow0 = 0, expert = 0;
+  int m0, n0, mrows, wrow0 = 0, expert = 0, tile = 0, split = 0;
   if constexpr (MODE == kDense) {
     const int tiles_m = (a.m + BM - 1) / BM;
-    m0 = (blockIdx.x % tiles_m) * BM;
-    n0 = (blockIdx.x / tiles_m) * kBN;
+    tile = (int)blockIdx.x / a.splits;
+    split = (int)blockIdx.x - tile * a.splits;
+    m0 = (tile % tiles_m) * BM;
+    n0 = (tile / tiles_m) * kBN;
     mrows = a.m - m0;
   } else {
     if (blockIdx.x >= *a.n_tiles) return;  // beyond this call's tiles (whole workgroup)
@@ -124,7 +129,10 @@ void gemm_big_kernel(GemmArgs a) {
     n0 = blockIdx.y * kBN;
     wrow0 = expert * a.n;  // first row of the expert's matrix
   }
+  // this workgroup's slices [s_begin, s_end)
   const int slices = a.k / kBK;
+  const int s_begin = MODE == kDense ? split * a.sps : 0;
+  const int s_end = MODE == kDense ? min(s_begin + a.sps, slices) : slices;
   const uint32_t k = (uint32_t)a.k;
   const int lr = lane & 31, h = lane >> 5;
 
@@ -197,16 +205,16 @@ void gemm_big_kernel(GemmArgs a) {
   constexpr int kLoadsPerSlice = XI + w_loads_per_run<FMT>();
 #pragma unroll
   for (int p = 0; p < kStages - 1; ++p) {
-    const int sp = min(p, slices - 1);
+    const int sp = min(s_begin + p, s_end - 1);
     load_x(sp);
     wr[p] = load_run<FMT>(ws, sp);
   }
 
-  for (int s0 = 0; s0 < slices; s0 += kStages) {
+  for (int s0 = s_begin; s0 < s_end; s0 += kStages) {
 #pragma unroll
     for (int u = 0; u < kStages; ++u) {
       const int s = s0 + u;
-      if (s >= slices) break;  // uniform
+      if (s >= s_end) break;  // uniform
       // this wave's share of slice s is in LDS once at most the loads issued
       // after it (kStages - 2 slices) are outstanding; the barrier then makes
       // every wave's share visible and frees the stage read in iteration s - 1
@@ -214,7 +222,7 @@ void gemm_big_kernel(GemmArgs a) {
       // fence of __syncthreads would also wait for the slices still in flight.
       __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kLoadsPerSlice));
       __builtin_amdgcn_s_barrier();
-      const int sn = min(s + kStages - 1, slices - 1);
+      const int sn = min(s + kStages - 1, s_end - 1);
       load_x(sn);
       wr[(u + kStages - 1) % kStages] = load_run<FMT>(ws, sn);
 
@@ -244,6 +252,65 @@ void gemm_big_kernel(GemmArgs a) {
 
   // epilogue: lane (lr, h) holds D[n = 8b + 4h + r][m = lr] of each tile as
   // value 4b + r: four consecutive W rows per b
+  if constexpr (MODE == kDense) {
+    if (a.splits > 1) {
+      // split K: this split's float32 sums of the tile's valid rows go out as
+      // 16-byte stores with the sc1 cache bit (written through to where every
+      // XCD sees them, without flushing the L2s); every wave waits for its
+      // stores before the barrier that precedes the counter increment, so the
+      // workgroup that takes the count to splits - 1 sees every split's
+      // partials (read with sc1 loads, which miss the non-coherent L2), adds
+      // them in split order and runs the epilogue below on the sums.  n is a
+      // multiple of 4 whenever the host splits.
+      constexpr int kSc1 = 16;  // cache-policy bit of gfx950 buffer operations
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.partials, 0xFFFFFFFFu);
+      const uint32_t split_off = (uint32_t)split * (uint32_t)a.m * (uint32_t)a.n;
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const int ml = 32 * t + lr;
+        if (ml >= mrows) continue;
+        const uint32_t row_off = split_off + (uint32_t)(m0 + ml) * (uint32_t)a.n;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int nb = n0 + 32 * wave + 8 * b + 4 * h;
+          if (nb < a.n)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4_t, f32x4_t{acc[t][4 * b], acc[t][4 * b + 1], acc[t][4 * b + 2],
+                                                    acc[t][4 * b + 3]}),
+                rp, (row_off + (uint32_t)nb) * 4u, 0, kSc1);
+        }
+      }
+      __shared__ int s_last;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0)
+        s_last = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(a.splits - 1);
+      __syncthreads();
+      if (!s_last) return;
+      const uint32_t split_stride = (uint32_t)a.m * (uint32_t)a.n * 4u;
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const int ml = 32 * t + lr;
+        if (ml >= mrows) continue;
+        const uint32_t row_off = (uint32_t)(m0 + ml) * (uint32_t)a.n;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int nb = n0 + 32 * wave + 8 * b + 4 * h;
+          if (nb >= a.n) continue;
+          f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+          for (int sp = 0; sp < a.splits; ++sp) {
+            v += __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, (row_off + (uint32_t)nb) * 4u + sp * split_stride, 0, kSc1));
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[t][4 * b + r] = v[r];
+        }
+      }
+      if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   const float gs = (FMT == QMM_NVFP4 && a.tensor_scale) ? a.tensor_scale[expert] : 1.0f;
 #pragma unroll
   for (int t = 0; t < TM; ++t) {
@@ -345,8 +412,39 @@ long compute_units() {
   return v;
 }
 
+// Small calls (m <= 256 rows): the activation tile height and the number of
+// K splits, from a sweep on 17408 x 5120 (MI355X, kernel trace, medians of 24
+// cold-weight launches; unsplit 128-row tiles take ~55 us for any m, a
+// workgroup walking its 80 slices in series):
+//   m <= 16: 32-row tiles, 4 splits  (35.6 us at m = 1, 36.4 at 8, 38.8 at 16)
+//   m <= 32: 32-row tiles, 2 splits  (42.6 us)
+//   m <= 64: 64-row tiles, unsplit   (46.7 us; splits cost more than they save)
+//   else:    128-row tiles, unsplit  (57 us at m = 128; 2 splits 75 us)
+// A split writes and reads back m x n float32 partials, so it pays only while
+// m is small.
+int small_m_tile(int m) { return m <= 32 ? 1 : (m <= 64 ? 2 : 4); }
+
+int small_m_splits(const qmm_weight &w, int m) {
+  if (m > 256 || w.n % 4 != 0) return 1;
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_GEMM_SPLITS")) return std::max(1, atoi(e));
+#endif
+  int sk = m <= 16 ? 4 : (m <= 32 ? 2 : 1);
+  const int slices = w.k / kBK;
+  while (sk > 1 && ((slices + sk - 1) / sk < 4 || (double)sk * m * w.n * 4 >= 4294967296.0))
+    sk /= 2;  // keep the three-stage pipeline busy; 32-bit partial offsets
+  return sk;
+}
+
+size_t split_counters_bytes(const qmm_weight &w, int m) {
+  const size_t tiles = (size_t)((m + 31) / 32) * ((w.n + 127) / 128);  // 32-row tiles at most
+  return (tiles * 4 + 255) / 256 * 256;
+}
+
 GemmArgs big_args(const qmm_weight &w) {
   GemmArgs a{};
+  a.splits = 1;
+  a.sps = w.k / kBK;
   a.codes = (const uint8_t *)w.codes;
   a.codes_hi = (const uint8_t *)w.codes_hi;
   a.scales = (const uint8_t *)w.scales;
@@ -360,20 +458,26 @@ GemmArgs big_args(const qmm_weight &w) {
 
 }  // namespace
 
+size_t gemm_big_workspace(const qmm_weight &w, int m) {
+  const int sk = small_m_splits(w, m);
+  if (sk == 1) return 0;
+  return split_counters_bytes(w, m) + (size_t)sk * m * w.n * 4;
+}
+
 bool gemm_big_fits(const qmm_weight &w, size_t x_rows) {
   // 32-bit buffer offsets for X and every weight plane
   return x_rows * (size_t)w.k * 2 < (1ull << 32) && (size_t)w.batch * w.n * w.k < (1ull << 32);
 }
 
 hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
-                           hipStream_t s) {
+                           void *workspace, size_t workspace_bytes, hipStream_t s) {
   GemmArgs a = big_args(w);
   a.x = (const uint16_t *)x;
   a.residual = (const uint16_t *)residual;
   a.y = (uint16_t *)y;
   a.m = m;
   auto grid = [&](int bm, int bn) {
-    return dim3((unsigned)(((m + bm - 1) / bm) * ((w.n + bn - 1) / bn)));
+    return dim3((unsigned)(((m + bm - 1) / bm) * ((w.n + bn - 1) / bn) * a.splits));
   };
   // 8 waves of 32 W rows x 256 X rows: each decoded weight feeds twice the
   // MFMAs of the 4-wave 64 x 128 form (measured 1.3x faster from M = 512 on);
@@ -395,6 +499,20 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
 #endif
   if (cfg == 0) return launch_big_mode<8, 8, kDense>(w.format, a, grid(256, bn_of(8)), s);
   if (cfg == 4) return launch_big_mode<6, 8, kDense>(w.format, a, grid(192, bn_of(8)), s);
+  // up to 256 rows: split K when the caller's workspace holds the partials
+  const int sk = small_m_splits(w, m);
+  if (sk > 1 && workspace && workspace_bytes >= gemm_big_workspace(w, m)) {
+    a.splits = sk;
+    a.sps = (w.k / kBK + sk - 1) / sk;
+    a.counters = (uint32_t *)workspace;
+    a.partials = (float *)((char *)workspace + split_counters_bytes(w, m));
+  }
+  int tm = small_m_tile(m);
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_SMALL_TM")) tm = atoi(e);
+#endif
+  if (tm == 1) return launch_big_mode<1, 4, kDense>(w.format, a, grid(32, bn_of(4)), s);
+  if (tm == 2) return launch_big_mode<2, 4, kDense>(w.format, a, grid(64, bn_of(4)), s);
   return launch_big_mode<4, 4, kDense>(w.format, a, grid(128, bn_of(4)), s);
 }
 

@@ -34,6 +34,11 @@ struct GemmArgs {
   const uint16_t *residual;
   uint16_t *y;
   int m, n, k;
+  // dense split-K: workgroup (tile, split) sums slices [split * sps, ...) and
+  // leaves float32 partials; the last of a tile's splits adds them in order
+  int splits, sps;
+  float *partials;     // [splits][m][n]
+  uint32_t *counters;  // [tiles], zero between calls
   int wrows;                     // rows of the weight planes (all experts)
   // grouped (MoE) modes
   const uint32_t *tiles;         // [max_tiles][3] = (expert, first grouped row, rows)

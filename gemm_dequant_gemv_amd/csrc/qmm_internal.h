@@ -75,7 +75,9 @@ hipError_t launch_gemv(const qmm_weight &w, const void *x, int m, const void *re
                        void *y, int y_dtype, void *workspace, const GemvPlan &p,
                        hipStream_t s);
 hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void *residual,
-                           void *y, hipStream_t s);
+                           void *y, void *workspace, size_t workspace_bytes, hipStream_t s);
+// workspace that lets a dense call of m rows split K (0: it never splits)
+size_t gemm_big_workspace(const qmm_weight &w, int m);
 // the 256-row-tile kernels (gemm_big.hip) address X (x_rows rows) and the
 // weight planes with 32-bit offsets
 bool gemm_big_fits(const qmm_weight &w, size_t x_rows);
@@ -84,7 +86,8 @@ hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const Moe
 hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
                                hipStream_t s);
 hipError_t launch_gemm(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
-                       hipStream_t s);
+                       void *workspace, size_t workspace_bytes, hipStream_t s);
+size_t gemm_workspace_size(const qmm_weight &w, int m);
 hipError_t launch_moe_gemm_gate_up(const qmm_weight &gu, const void *x, const MoeTables &t,
                                    int max_tiles, hipStream_t s);
 hipError_t launch_moe_gemm_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,

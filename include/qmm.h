@@ -188,8 +188,15 @@ int qbench_mfma_peak(int32_t iters, int32_t blocks, void *sink, double *flops, v
  * x         bf16 [m][k], m >= 1 (tuned for m >= 128)
  * residual  bf16 [m][n] or NULL
  * y         bf16 [m][n], rounded to nearest even
- * x, y and residual must be 16-byte aligned.  No workspace is needed today
- * (qgemm_workspace_size returns 0); the arguments are kept for split variants.
+ * x, y and residual must be 16-byte aligned.
+ * workspace  optional.  For calls of up to 32 rows, qgemm_workspace_size
+ *            returns the bytes (256-byte aligned, zero-filled once, left
+ *            zero-filled) with which the call splits K over several
+ *            workgroups: each writes float32 partial sums and the last of a
+ *            tile's workgroups adds them in split order (a fixed order, so
+ *            results are the same on every run; they differ from an unsplit
+ *            call's only in summation order).  With a NULL or smaller
+ *            workspace the call runs unsplit.  Above 32 rows it returns 0.
  */
 size_t qgemm_workspace_size(const qmm_weight *w, int32_t m);
 int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, void *y,

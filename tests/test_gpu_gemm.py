@@ -117,21 +117,51 @@ def test_gemm_rejects():
 
 
 # The prefill workload's own sizes, in the tile configurations the library
-# picks for them (256-row activation tiles at M = 8192, 192-row at 2048): the
-# GPU computes the whole product; the oracle checks sampled activation rows
-# (every output column of each), including both edges of the tiles.
+# picks for them (256-row activation tiles at M = 8192, 192-row at 2048, and
+# the mid band's tiles: 32 rows with 4 K splits at M = 8, 64 rows at 48, 128
+# rows at 96): the GPU computes
+# the whole product; the oracle checks sampled activation rows (every output
+# column of each), including both edges of the tiles.
 FULL_N, FULL_K = 17408, 5120
 
 
-@pytest.mark.parametrize("fmt,m", [(F.AFFINE4_G64, 8192), (F.NVFP4, 2048)])
+@pytest.mark.parametrize("fmt,m", [(F.AFFINE4_G64, 8192), (F.NVFP4, 2048), (F.AFFINE4_G64, 8),
+                                   (F.NVFP4, 48), (F.Q6_K, 96)])
 def test_gemm_prefill_full_size_sampled(fmt, m):
     q = _q()
     p = quant.synthetic_weight(fmt, FULL_N, FULL_K, name=f"gfull{fmt}")
     x = quant.synthetic_bf16(m, FULL_K, name=f"gfullx{m}")
     w = q.Weight.from_host(p)
     y = _host_f64(q.gemm(w, _dev_bf16(x)))
-    edges = [0, 1, 127, 128, 191, 192, 255, 256, m // 2, m - 2, m - 1]
+    edges = [0, 1, 31, 32, 63, 64, 127, 128, 191, 192, 255, 256, m // 2, m - 2, m - 1]
     rows = np.unique(np.concatenate([edges, rng.randint_bytes(71, f"gfr{m}", 21, 0, 256).astype(np.int64) * (m // 256)]))
     rows = rows[rows < m]
     yref, mag = oracle.gemm(p, x[rows])
     _check(y[rows], yref, mag)
+
+
+@pytest.mark.parametrize("fmt", [F.AFFINE4_G64, F.NVFP4, F.Q6_K])
+@pytest.mark.parametrize("m", [3, 16, 29])
+def test_gemm_split_k(fmt, m):
+    """Up to 32 rows a call with qgemm_workspace_size bytes of workspace
+    splits K (4 splits up to 16 rows, 2 above); one without runs unsplit.  Both meet the oracle's bar, the split
+    one is bitwise the same on every call, and it leaves its tile counters
+    zero for the next call."""
+    q = _q()
+    n, k = 700, 4096
+    p = quant.synthetic_weight(fmt, n, k, outlier_rate=0.01, name=f"gsk{fmt}")
+    x = quant.synthetic_bf16(m, k, name=f"gskx{m}")
+    r = quant.synthetic_bf16(m, n, name=f"gskr{m}")
+    w = q.Weight.from_host(p)
+    need = int(q.lib_handle().qgemm_workspace_size(w.c, m))
+    assert need > 0
+    ws = q.new_workspace(need)
+    ys = [q.gemm(w, _dev_bf16(x), _dev_bf16(r), workspace=ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert int(ws[:256].sum()) == 0  # the counters lead the workspace
+    for y in ys[1:]:
+        assert torch.equal(ys[0].view(torch.int16), y.view(torch.int16))
+    y1 = q.gemm(w, _dev_bf16(x), _dev_bf16(r), workspace=q.new_workspace(256))  # too small: unsplit
+    yref, mag = oracle.gemm(p, x, r)
+    _check(_host_f64(ys[0]), yref, mag)
+    _check(_host_f64(y1), yref, mag)
