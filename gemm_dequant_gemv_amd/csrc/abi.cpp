@@ -211,7 +211,8 @@ size_t qmoe_workspace_size(const qmm_weight *gate_up, const qmm_weight *down, in
   if (check_weight(gate_up) || check_weight(down) || num_routed < 1 || num_shared < 0 ||
       t < 1 || topk < 1)
     return 0;
-  return qmm::moe_layout(num_routed + num_shared, t, topk, num_shared, gate_up->n / 2, down->n)
+  return qmm::moe_layout(num_routed + num_shared, t, topk, num_shared, gate_up->n / 2, down->n,
+                         qmm::moe_tile_rows(*gate_up, *down, t, topk, num_routed))
       .bytes;
 }
 
@@ -221,11 +222,13 @@ int qmoe_workspace_layout(const qmm_weight *gate_up, const qmm_weight *down, int
   if (check_weight(gate_up) || check_weight(down) || num_routed < 1 || num_shared < 0 ||
       t < 1 || topk < 1)
     return QMM_ERR_ARG;
-  const qmm::MoeLayout L = qmm::moe_layout(num_routed + num_shared, t, topk, num_shared,
-                                           gate_up->n / 2, down->n);
+  const qmm::MoeLayout L =
+      qmm::moe_layout(num_routed + num_shared, t, topk, num_shared, gate_up->n / 2, down->n,
+                      qmm::moe_tile_rows(*gate_up, *down, t, topk, num_routed));
   *out = qmoe_layout{L.counts, L.offsets, L.row_of_slot, L.row_of_shared, L.token_of_row,
                      L.active, L.scalars, L.tiles, L.h, L.d, L.bytes, L.max_rows, L.max_tiles,
-                     qmm::moe_uses_gemv(*gate_up, *down, t, topk, num_shared) ? 1u : 0u};
+                     qmm::moe_uses_gemv(*gate_up, *down, t, topk, num_shared) ? 1u : 0u,
+                     L.tile_rows};
   return QMM_OK;
 }
 
@@ -251,7 +254,8 @@ int qmoe_grouped(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
       (shared_w && !aligned(shared_w, 4)))
     return QMM_ERR_ALIGN;
-  const qmm::MoeLayout L = qmm::moe_layout(experts, t, topk, num_shared, inter, down->n);
+  const qmm::MoeLayout L = qmm::moe_layout(experts, t, topk, num_shared, inter, down->n,
+                                           qmm::moe_tile_rows(*gate_up, *down, t, topk, num_routed));
   if (!workspace || workspace_bytes < L.bytes) return QMM_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return QMM_ERR_ALIGN;
   const int hidden = down->n;

@@ -109,6 +109,7 @@ void gemm_big_kernel(GemmArgs a) {
   constexpr int BM = 32 * TM;
   constexpr int kXStage = BM * kXRow;   // bytes per LDS stage
   constexpr int XI = BM / (8 * WAVES);  // X load instructions per wave and slice (8 rows each)
+  static_assert(XI >= 1 && XI * 8 * WAVES == BM, "every wave loads the same X rows per slice");
   extern __shared__ __align__(16) uint8_t lds[];  // kStages x [BM rows][128 bytes]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -367,8 +368,8 @@ void gemm_big_kernel(GemmArgs a) {
 
 template <int FMT, int TM, int WAVES, int MODE>
 hipError_t launch_big(const GemmArgs &a, dim3 grid, hipStream_t s) {
-  static_assert(MODE == kDense || 32 * TM == kMoeTileRows,
-                "X tiles are the routing table's tiles of kMoeTileRows rows");
+  static_assert(MODE == kDense || 32 * TM <= kMoeTileRows,
+                "X tiles hold the routing table's tiles of at most kMoeTileRows rows");
   constexpr size_t lds = (size_t)kStages * 32 * TM * kXRow;
   // more than 64 KiB of dynamic LDS must be allowed once per device
   static std::atomic<uint64_t> configured{0};
@@ -517,7 +518,7 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
 }
 
 hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const MoeTables &t,
-                                  int max_tiles, hipStream_t s) {
+                                  int max_tiles, int tile_rows, hipStream_t s) {
   GemmArgs a = big_args(gu);
   a.x = (const uint16_t *)x;
   a.tiles = t.tiles;
@@ -525,13 +526,22 @@ hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const Moe
   a.token_of_row = t.token_of_row;
   a.h = t.h;
   a.inter = gu.n / 2;
-  // each workgroup covers 128 intermediate columns (256 interleaved rows)
+  // each workgroup covers 128 intermediate columns (256 interleaved rows) of
+  // one routing tile (tile_rows activation rows); a 32-row tile is four X load
+  // instructions a slice, so it takes 4 waves (64 columns)
   constexpr int bn = bn_of(8);
-  return launch_big_mode<8, 8, kMoeGateUp>(gu.format, a, dim3(max_tiles, (gu.n + bn - 1) / bn), s);
+  const dim3 grid(max_tiles, (gu.n + bn - 1) / bn);
+  switch (tile_rows) {
+    case 32: return launch_big_mode<1, 4, kMoeGateUp>(
+        gu.format, a, dim3(max_tiles, (gu.n + bn_of(4) - 1) / bn_of(4)), s);
+    case 64: return launch_big_mode<2, 8, kMoeGateUp>(gu.format, a, grid, s);
+    case 128: return launch_big_mode<4, 8, kMoeGateUp>(gu.format, a, grid, s);
+    default: return launch_big_mode<8, 8, kMoeGateUp>(gu.format, a, grid, s);
+  }
 }
 
 hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
-                               hipStream_t s) {
+                               int tile_rows, hipStream_t s) {
   GemmArgs a = big_args(dn);
   a.tiles = t.tiles;
   a.n_tiles = t.n_tiles;
@@ -539,7 +549,14 @@ hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max
   a.d = t.d;
   a.inter = dn.k;
   constexpr int bn = bn_of(8);
-  return launch_big_mode<8, 8, kMoeDown>(dn.format, a, dim3(max_tiles, (dn.n + bn - 1) / bn), s);
+  const dim3 grid(max_tiles, (dn.n + bn - 1) / bn);
+  switch (tile_rows) {
+    case 32: return launch_big_mode<1, 4, kMoeDown>(
+        dn.format, a, dim3(max_tiles, (dn.n + bn_of(4) - 1) / bn_of(4)), s);
+    case 64: return launch_big_mode<2, 8, kMoeDown>(dn.format, a, grid, s);
+    case 128: return launch_big_mode<4, 8, kMoeDown>(dn.format, a, grid, s);
+    default: return launch_big_mode<8, 8, kMoeDown>(dn.format, a, grid, s);
+  }
 }
 
 }  // namespace qmm

@@ -30,6 +30,7 @@ constexpr int kRun = 16;  // slots per thread and pass in the route kernel
 struct RouteArgs {
   const int32_t *topk_ids;
   int t, topk, num_routed, num_shared;
+  int tile_rows;  // rows per routing tile
   MoeTables tb;
 };
 
@@ -143,13 +144,13 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
       tb.token_of_row[row] = (uint32_t)t;
     }
 
-  // 4. experts with rows (in expert order) and their tiles of kMoeTileRows rows
+  // 4. experts with rows (in expert order) and their tiles of tile_rows rows
   uint32_t nact = 0, ntile = 0;
   for (int j = 0; j < PER; ++j) {
     const int e = tid * PER + j;
     if (e < ne && s_count[e]) {
       nact += 1;
-      ntile += (s_count[e] + kMoeTileRows - 1) / kMoeTileRows;
+      ntile += (s_count[e] + a.tile_rows - 1) / a.tile_rows;
     }
   }
   uint32_t act_base = block_exclusive_scan(nact, s_scan, &s_total);
@@ -161,11 +162,11 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
     if (e >= ne || !s_count[e]) continue;
     tb.active[act_base++] = (uint32_t)e;
     const uint32_t cnt = s_count[e];
-    for (uint32_t r = 0; r < cnt; r += kMoeTileRows) {
+    for (uint32_t r = 0; r < cnt; r += a.tile_rows) {
       uint32_t *tl = tb.tiles + 3 * (size_t)tile_base++;
       tl[0] = (uint32_t)e;
       tl[1] = s_off[e] + r;
-      tl[2] = min(cnt - r, (uint32_t)kMoeTileRows);
+      tl[2] = min(cnt - r, (uint32_t)a.tile_rows);
     }
   }
 }
@@ -236,11 +237,29 @@ size_t align_up(size_t v) { return (v + 255) / 256 * 256; }
 
 }  // namespace
 
-MoeLayout moe_layout(int num_experts, int t, int topk, int num_shared, int inter, int hidden) {
+// Routing tiles as tall as about twice an average routed expert's rows (t x
+// topk / E), from 32 to 256: tokens spread over many experts leave each with
+// a few rows, and a 256-row tile (the grouped GEMMs' tallest) would be almost
+// all padding.  Measured on the 512-expert layer (T = 5 .. 64: 97 .. 532 us
+// per layer with 256-row tiles).  The LDS-staged kernel (where 32-bit offsets
+// do not reach) takes 256-row tiles only.
+int moe_tile_rows(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_routed) {
+  const size_t rows = (size_t)t * (topk + (gu.batch - num_routed));
+  const bool big = gemm_big_fits(gu, (size_t)t) && gemm_big_fits(dn, rows) && (gu.n / 2) % 2 == 0;
+  if (!big) return kMoeTileRows;
+  const double avg = (double)t * topk / num_routed;
+  int tr = 32;
+  while (tr < kMoeTileRows && tr < 2.0 * avg) tr *= 2;
+  return tr;
+}
+
+MoeLayout moe_layout(int num_experts, int t, int topk, int num_shared, int inter, int hidden,
+                     int tile_rows) {
   MoeLayout L{};
   const size_t rows = (size_t)t * topk + (size_t)t * num_shared;
   L.max_rows = rows;
-  L.max_tiles = (rows + kMoeTileRows - 1) / kMoeTileRows + (size_t)num_experts;
+  L.tile_rows = (size_t)tile_rows;
+  L.max_tiles = (rows + tile_rows - 1) / tile_rows + (size_t)num_experts;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -290,7 +309,8 @@ hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed
                       const void *x, int t, const int32_t *topk_ids, const float *topk_w,
                       int topk, const float *shared_w, void *y, int y_dtype, void *workspace,
                       hipStream_t s) {
-  const MoeLayout L = moe_layout(num_routed + num_shared, t, topk, num_shared, gu.n / 2, dn.n);
+  const MoeLayout L = moe_layout(num_routed + num_shared, t, topk, num_shared, gu.n / 2, dn.n,
+                                moe_tile_rows(gu, dn, t, topk, num_routed));
   const MoeTables tb = moe_tables(L, workspace);
   hipError_t e;
   if (moe_uses_gemv(gu, dn, t, topk, num_shared)) {
@@ -298,7 +318,7 @@ hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed
     return launch_moe_gemv(gu, dn, num_routed, num_shared, x, t, topk_ids, topk_w, topk, shared_w,
                            y, y_dtype == QMM_BF16, tb, s);
   } else {
-    RouteArgs ra{topk_ids, t, topk, num_routed, num_shared, tb};
+    RouteArgs ra{topk_ids, t, topk, num_routed, num_shared, (int)L.tile_rows, tb};
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ra);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -308,10 +328,12 @@ hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed
 #ifdef QMM_TUNE
     if (const char *ev = getenv("QMM_MOE_BIG")) big = big && atoi(ev) != 0;
 #endif
-    e = big ? launch_moe_big_gate_up(gu, x, tb, (int)L.max_tiles, s)
+    big = big && L.tile_rows <= (size_t)kMoeTileRows;
+    if (!big && L.tile_rows != (size_t)kMoeTileRows) return hipErrorInvalidValue;  // not reached
+    e = big ? launch_moe_big_gate_up(gu, x, tb, (int)L.max_tiles, (int)L.tile_rows, s)
             : launch_moe_gemm_gate_up(gu, x, tb, (int)L.max_tiles, s);
     if (e != hipSuccess) return e;
-    e = big ? launch_moe_big_down(dn, tb, (int)L.max_tiles, s)
+    e = big ? launch_moe_big_down(dn, tb, (int)L.max_tiles, (int)L.tile_rows, s)
             : launch_moe_gemm_down(dn, tb, (int)L.max_tiles, s);
     if (e != hipSuccess) return e;
   }

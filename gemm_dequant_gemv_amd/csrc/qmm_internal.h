@@ -42,7 +42,7 @@ size_t gemv_rows_lds(int format, int k, int m);
 // Prefill GEMM / grouped MoE tiles: rows of activations per workgroup.
 constexpr int kGemmBM = 128;
 // rows per tile of the MoE routing table (the grouped GEMMs' activation tiles)
-constexpr int kMoeTileRows = 256;
+constexpr int kMoeTileRows = 256;  // routing tile rows at most (the LDS-staged kernel's height)
 // Experts (routed + shared) one MoE call may have.
 constexpr int kMoeMaxExperts = 4096;
 
@@ -62,10 +62,13 @@ struct MoeTables {
 
 struct MoeLayout {
   size_t counts, offsets, row_of_slot, row_of_shared, token_of_row, active, scalars, tiles, h, d;
-  size_t bytes, max_rows, max_tiles;
+  size_t bytes, max_rows, max_tiles, tile_rows;
 };
 
-MoeLayout moe_layout(int num_experts, int t, int topk, int num_shared, int inter, int hidden);
+MoeLayout moe_layout(int num_experts, int t, int topk, int num_shared, int inter, int hidden,
+                     int tile_rows);
+// rows per routing tile of the grouped form: 32 .. kMoeTileRows
+int moe_tile_rows(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_routed);
 MoeTables moe_tables(const MoeLayout &L, void *ws);
 
 hipError_t launch_dequant(const qmm_weight &w, int out_dtype, void *out, hipStream_t s);
@@ -82,9 +85,9 @@ size_t gemm_big_workspace(const qmm_weight &w, int m);
 // weight planes with 32-bit offsets
 bool gemm_big_fits(const qmm_weight &w, size_t x_rows);
 hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const MoeTables &t,
-                                  int max_tiles, hipStream_t s);
+                                  int max_tiles, int tile_rows, hipStream_t s);
 hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
-                               hipStream_t s);
+                               int tile_rows, hipStream_t s);
 hipError_t launch_gemm(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
                        void *workspace, size_t workspace_bytes, hipStream_t s);
 size_t gemm_workspace_size(const qmm_weight &w, int m);
@@ -92,8 +95,9 @@ hipError_t launch_moe_gemm_gate_up(const qmm_weight &gu, const void *x, const Mo
                                    int max_tiles, hipStream_t s);
 hipError_t launch_moe_gemm_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
                                 hipStream_t s);
-// decode form of qmoe_grouped: grouped GEMV over token slots (t <= 4)
-constexpr int kMoeGemvMaxTokens = 4;
+// decode form of qmoe_grouped: grouped GEMV over token slots (t <= 16 and
+// at most kMoeGemvMaxSlots slots, when the staged vectors fit in LDS)
+constexpr int kMoeGemvMaxTokens = 16;
 constexpr int kMoeGemvMaxSlots = 128;  // token slots of the decode form (register table)
 bool moe_gemv_fits(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_shared);
 bool moe_uses_gemv(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_shared);

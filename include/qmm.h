@@ -228,10 +228,13 @@ int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, v
  *              the routing tables, h and d.  No zero-fill is needed.
  * The gate/up and down weights may use different formats.
  *
- * Two forms, the same result contract: up to 4 tokens (when the activations
+ * Two forms, the same result contract: up to 16 tokens with at most 128 token
+ * slots (t * (topk + S)), when the activations
  * fit in LDS) take the decode form, one grouped matrix-vector launch per
- * projection over the token slots plus the combine ("TurboEXL3" section 3.1:
- * decode verifies 1 to 4 tokens); more tokens take the grouped-GEMM form
+ * projection over the token slots, the second also running the combine
+ * ("TurboEXL3" section 3.1: decode verifies 1 to 4 tokens; more here, where
+ * one pass per token slot still costs less than the grouped form's mostly
+ * empty tiles); more tokens take the grouped-GEMM form
  * (route, gate/up, down, combine; section 4.1).  qmoe_workspace_layout says
  * which form a call takes.
  */
@@ -258,18 +261,23 @@ typedef struct {
   size_t active;        /* uint32 [n_active] experts with at least one row, ascending */
   size_t scalars;       /* uint32 [3]       n_active, n_tiles, err (1 = an id was
                            outside [0, E) and its slot was dropped)                 */
-  size_t tiles;         /* uint32 [n_tiles][3] expert, first grouped row, rows (<= 256)
-                           of each row tile, experts ascending                      */
+  size_t tiles;         /* uint32 [n_tiles][3] expert, first grouped row, rows
+                           (<= tile_rows) of each row tile, experts ascending       */
   size_t h;             /* bf16  [rows][I]  SwiGLU outputs                          */
   size_t d;             /* float [rows][H]  down-projection outputs                  */
   size_t bytes;         /* = qmoe_workspace_size                                     */
   size_t max_rows, max_tiles;
-  size_t slot_rows;     /* 1: the call takes the decode form (t <= 4 and the
+  size_t slot_rows;     /* 1: the call takes the decode form (t <= 16, t * (topk + S)
+                           <= 128 and the
                            vectors fit in LDS): no routing pass; h and d row s is
                            token slot s (routed slots in list order, then shared
                            expert j's slot of token i at t*topk + j*t + i); of the
                            tables only scalars[2] (err) is written.
                            0: the grouped form; every table above is written.   */
+  size_t tile_rows;     /* rows per routing tile of the grouped form: 32, 64, 128 or
+                           256, about twice an average routed expert's rows
+                           (t * topk / E), so that tiles of few-row experts are
+                           not mostly padding                                     */
 } qmoe_layout;
 
 /* Fill *out for these arguments (host-side arithmetic only, no launch).
