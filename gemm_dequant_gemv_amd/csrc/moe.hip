@@ -1,10 +1,13 @@
 // qmoe_grouped: one mixture-of-experts layer (routed experts plus optional
-// shared experts).  Up to 4 tokens take the decode form (two grouped GEMV
-// launches over the token slots, moe_gemv.hip, the second also running the
-// combine); more tokens take the grouped-GEMM form ("TurboEXL3" section 4.1):
-//   1. route:    one launch counts each expert's tokens, groups the token slots
-//                by expert and builds the table of row tiles, all in one
-//                pass instead of sorting first and tabulating afterwards;
+// shared experts).  Up to 16 tokens with at most 128 token slots take the
+// decode form (two grouped GEMV launches over the token slots, moe_gemv.hip,
+// the second also running the combine); more tokens take the grouped-GEMM form
+// ("TurboEXL3" section 4.1):
+//   1. route:    count each expert's tokens, group the token slots by expert
+//                and build the table of row tiles, instead of sorting first
+//                and tabulating afterwards: one launch for calls with few
+//                slots, three (per-workgroup counts, one scan, placement)
+//                for calls with many;
 //   2. gate/up:  one grouped GEMM over the tile table, activations gathered by
 //                token, weights decoded once per K-slice per workgroup; SwiGLU
 //                in float32 in its epilogue -> bf16 h;
@@ -15,6 +18,7 @@
 // one expert's group comes from LDS atomics and is not fixed, but every row is
 // computed independently of its neighbours and the combine reads rows by slot,
 // so the layer's output is the same on every run.
+#include <algorithm>
 #include <cstdlib>
 
 #include "qmm_device.h"
@@ -52,50 +56,15 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *buf, uint32_t *to
   return incl - v;
 }
 
-__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
-  __shared__ uint32_t s_count[kMoeMaxExperts];
-  __shared__ uint32_t s_off[kMoeMaxExperts];
-  __shared__ uint32_t s_scan[kRouteThreads];
-  __shared__ uint32_t s_total;
+// Steps 2 to 4 of the route, given each expert's row count in s_count:
+// group offsets (exclusive scan over experts), the shared experts' rows (every
+// token, in token order), the experts with rows and their tiles of tile_rows
+// rows.  s_off receives the offsets.
+__device__ void group_and_tile(const RouteArgs &a, uint32_t *s_count, uint32_t *s_off,
+                               uint32_t *s_scan, uint32_t *s_total) {
   const int tid = threadIdx.x;
   const int ne = a.num_routed + a.num_shared;
-  const int slots = a.t * a.topk;
   const MoeTables &tb = a.tb;
-
-  for (int e = tid; e < ne; e += kRouteThreads) s_count[e] = 0;
-  if (tid == 0) *tb.err = 0;
-  __syncthreads();
-  // 1. position of every routed slot inside its expert's group.  A pass
-  //    covers kRun x 1024 slots (slot b + 1024 j for thread j-th of the pass;
-  //    consecutive threads, consecutive slots); a thread loads all its ids of
-  //    the pass before its atomics, so that it waits on memory once per pass
-  //    rather than once per slot.
-  constexpr int kStride = kRouteThreads;
-  for (int b0 = 0; b0 < slots; b0 += kRouteThreads * kRun) {
-    const int b = b0 + tid;
-    int32_t id[kRun];
-#pragma unroll
-    for (int j = 0; j < kRun; ++j) id[j] = b + kStride * j < slots ? a.topk_ids[b + kStride * j] : 0;
-    uint32_t pos[kRun];
-#pragma unroll
-    for (int j = 0; j < kRun; ++j) {
-      const int e = id[j];
-      pos[j] = kInvalidRow;
-      if (b + kStride * j >= slots) continue;
-      if (e < 0 || e >= a.num_routed) {
-        atomicOr(tb.err, 1u);  // contributes nothing; reported in err
-        continue;
-      }
-      pos[j] = atomicAdd(&s_count[e], 1u);
-    }
-#pragma unroll
-    for (int j = 0; j < kRun; ++j)
-      if (b + kStride * j < slots) tb.row_of_slot[b + kStride * j] = pos[j];
-  }
-  // shared experts see every token, in token order
-  for (int e = a.num_routed + tid; e < ne; e += kRouteThreads) s_count[e] = (uint32_t)a.t;
-  __syncthreads();
-
   // 2. group offsets (exclusive scan over experts, kMoeMaxExperts / 1024 per thread)
   constexpr int PER = kMoeMaxExperts / kRouteThreads;
   uint32_t local = 0;
@@ -103,7 +72,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
     const int e = tid * PER + j;
     local += e < ne ? s_count[e] : 0u;
   }
-  uint32_t base = block_exclusive_scan(local, s_scan, &s_total);
+  uint32_t base = block_exclusive_scan(local, s_scan, s_total);
   for (int j = 0; j < PER; ++j) {
     const int e = tid * PER + j;
     if (e < ne) {
@@ -113,30 +82,10 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
       base += s_count[e];
     }
   }
-  if (tid == 0) tb.offsets[ne] = s_total;
+  if (tid == 0) tb.offsets[ne] = *s_total;
   __syncthreads();
 
-  // 3. grouped row of every slot, and the token each grouped row reads (the
-  //    same passes as in 1: this thread wrote these slots' positions)
-  for (int b0 = 0; b0 < slots; b0 += kRouteThreads * kRun) {
-    const int b = b0 + tid;
-    uint32_t pos[kRun];
-    int32_t id[kRun];
-#pragma unroll
-    for (int j = 0; j < kRun; ++j) {
-      const int i = b + kStride * j;
-      pos[j] = i < slots ? tb.row_of_slot[i] : kInvalidRow;
-      id[j] = i < slots ? a.topk_ids[i] : 0;
-    }
-#pragma unroll
-    for (int j = 0; j < kRun; ++j) {
-      if (pos[j] == kInvalidRow) continue;
-      const int i = b + kStride * j;
-      const uint32_t row = s_off[id[j]] + pos[j];
-      tb.row_of_slot[i] = row;
-      tb.token_of_row[row] = (uint32_t)(i / a.topk);
-    }
-  }
+  // 3. (shared experts) every token, in token order
   for (int s = 0; s < a.num_shared; ++s)
     for (int t = tid; t < a.t; t += kRouteThreads) {
       const uint32_t row = s_off[a.num_routed + s] + t;
@@ -153,10 +102,10 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
       ntile += (s_count[e] + a.tile_rows - 1) / a.tile_rows;
     }
   }
-  uint32_t act_base = block_exclusive_scan(nact, s_scan, &s_total);
-  if (tid == 0) *tb.n_active = s_total;
-  uint32_t tile_base = block_exclusive_scan(ntile, s_scan, &s_total);
-  if (tid == 0) *tb.n_tiles = s_total;
+  uint32_t act_base = block_exclusive_scan(nact, s_scan, s_total);
+  if (tid == 0) *tb.n_active = *s_total;
+  uint32_t tile_base = block_exclusive_scan(ntile, s_scan, s_total);
+  if (tid == 0) *tb.n_tiles = *s_total;
   for (int j = 0; j < PER; ++j) {
     const int e = tid * PER + j;
     if (e >= ne || !s_count[e]) continue;
@@ -169,6 +118,171 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
       tl[2] = min(cnt - r, (uint32_t)a.tile_rows);
     }
   }
+}
+
+// Positions of the routed slots [i0, i1) inside their experts' groups, by
+// LDS atomics on s_count (the order inside a group is not fixed); a dropped
+// id gets kInvalidRow and sets *bad.  A pass covers kRun x 1024 slots (slot
+// b + 1024 j for thread j-th of the pass: consecutive threads, consecutive
+// slots); a thread loads all its ids of the pass before its atomics, so that
+// it waits on memory once per pass rather than once per slot.
+__device__ void count_slots(const RouteArgs &a, int i0, int i1, uint32_t *s_count, int *bad) {
+  const int tid = threadIdx.x;
+  constexpr int kStride = kRouteThreads;
+  for (int b0 = i0; b0 < i1; b0 += kRouteThreads * kRun) {
+    const int b = b0 + tid;
+    int32_t id[kRun];
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) id[j] = b + kStride * j < i1 ? a.topk_ids[b + kStride * j] : 0;
+    uint32_t pos[kRun];
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      const int e = id[j];
+      pos[j] = kInvalidRow;
+      if (b + kStride * j >= i1) continue;
+      if (e < 0 || e >= a.num_routed) {
+        *bad = 1;  // contributes nothing; reported in err
+        continue;
+      }
+      pos[j] = atomicAdd(&s_count[e], 1u);
+    }
+#pragma unroll
+    for (int j = 0; j < kRun; ++j)
+      if (b + kStride * j < i1) a.tb.row_of_slot[b + kStride * j] = pos[j];
+  }
+}
+
+// Grouped rows of the routed slots [i0, i1): base(expert) (the expert's
+// offset, plus the workgroup's first position in the parallel route) plus the
+// slot's position; the token each grouped row reads.  The passes are those of
+// count_slots, so each thread reads back the positions it wrote.
+template <typename Base>
+__device__ void place_slots(const RouteArgs &a, int i0, int i1, Base base) {
+  const int tid = threadIdx.x;
+  constexpr int kStride = kRouteThreads;
+  for (int b0 = i0; b0 < i1; b0 += kRouteThreads * kRun) {
+    const int b = b0 + tid;
+    uint32_t pos[kRun];
+    int32_t id[kRun];
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      const int i = b + kStride * j;
+      pos[j] = i < i1 ? a.tb.row_of_slot[i] : kInvalidRow;
+      id[j] = i < i1 ? a.topk_ids[i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      if (pos[j] == kInvalidRow) continue;
+      const int i = b + kStride * j;
+      const uint32_t row = base(id[j]) + pos[j];
+      a.tb.row_of_slot[i] = row;
+      a.tb.token_of_row[row] = (uint32_t)(i / a.topk);
+    }
+  }
+}
+
+// One workgroup: the whole route in one launch (calls with few slots).
+__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
+  __shared__ uint32_t s_count[kMoeMaxExperts];
+  __shared__ uint32_t s_off[kMoeMaxExperts];
+  __shared__ uint32_t s_scan[kRouteThreads];
+  __shared__ uint32_t s_total;
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  const int ne = a.num_routed + a.num_shared;
+  const int slots = a.t * a.topk;
+
+  for (int e = tid; e < ne; e += kRouteThreads) s_count[e] = 0;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  // 1. position of every routed slot inside its expert's group
+  count_slots(a, 0, slots, s_count, &s_bad);
+  // shared experts see every token
+  for (int e = a.num_routed + tid; e < ne; e += kRouteThreads) s_count[e] = (uint32_t)a.t;
+  __syncthreads();
+  if (tid == 0) *a.tb.err = s_bad ? 1u : 0u;
+  group_and_tile(a, s_count, s_off, s_scan, &s_total);
+  // 5. grouped row of every routed slot
+  place_slots(a, 0, slots, [&](int e) { return s_off[e]; });
+}
+
+// The parallel route (calls with many slots): workgroup g counts the routed
+// slots of its chunk [g c, (g+1) c) in LDS and writes its counts; one
+// workgroup then turns each expert's counts into per-workgroup first
+// positions (workgroup order) and runs steps 2 to 4; every workgroup then
+// places its chunk's slots.  Rows are grouped by expert as in the one-
+// workgroup route; their order inside a group is workgroup order, then the
+// order of the LDS atomics.
+struct RouteParArgs {
+  RouteArgs r;
+  int chunk;  // routed slots per workgroup
+};
+
+__global__ __launch_bounds__(kRouteThreads) void moe_route_count_kernel(RouteParArgs p) {
+  __shared__ uint32_t s_count[kMoeMaxExperts];
+  __shared__ int s_bad;
+  const RouteArgs &a = p.r;
+  const int tid = threadIdx.x, g = blockIdx.x;
+  const int ne = a.num_routed + a.num_shared;
+  const int slots = a.t * a.topk;
+  const int i0 = min(g * p.chunk, slots), i1 = min(i0 + p.chunk, slots);
+  for (int e = tid; e < ne; e += kRouteThreads) s_count[e] = 0;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  count_slots(a, i0, i1, s_count, &s_bad);
+  __syncthreads();
+  for (int e = tid; e < a.num_routed; e += kRouteThreads)
+    a.tb.wg_counts[(size_t)g * ne + e] = s_count[e];
+  if (tid == 0) a.tb.wg_err[g] = s_bad ? 1u : 0u;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void moe_route_scan_kernel(RouteParArgs p) {
+  __shared__ uint32_t s_count[kMoeMaxExperts];
+  __shared__ uint32_t s_off[kMoeMaxExperts];
+  __shared__ uint32_t s_scan[kRouteThreads];
+  __shared__ uint32_t s_total;
+  const RouteArgs &a = p.r;
+  const int tid = threadIdx.x;
+  const int ne = a.num_routed + a.num_shared;
+  const int groups = a.tb.route_groups;
+  // each expert's total, and each workgroup's first position in its group
+  for (int e = tid; e < ne; e += kRouteThreads) {
+    if (e < a.num_routed) {
+      // batches of 16 loads before their stores: one wait on memory per batch
+      uint32_t run = 0;
+      for (int g0 = 0; g0 < groups; g0 += 16) {
+        uint32_t v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          v[j] = g0 + j < groups ? a.tb.wg_counts[(size_t)(g0 + j) * ne + e] : 0u;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (g0 + j < groups) {
+            a.tb.wg_counts[(size_t)(g0 + j) * ne + e] = run;
+            run += v[j];
+          }
+      }
+      s_count[e] = run;
+    } else {
+      s_count[e] = (uint32_t)a.t;  // shared experts see every token
+    }
+  }
+  int bad = 0;
+  for (int g = tid; g < groups; g += kRouteThreads) bad |= a.tb.wg_err[g] != 0u;
+  bad = __syncthreads_or(bad);
+  if (tid == 0) *a.tb.err = bad ? 1u : 0u;
+  group_and_tile(a, s_count, s_off, s_scan, &s_total);
+}
+
+__global__ __launch_bounds__(kRouteThreads) void moe_route_place_kernel(RouteParArgs p) {
+  const RouteArgs &a = p.r;
+  const int g = blockIdx.x;
+  const int ne = a.num_routed + a.num_shared;
+  const int slots = a.t * a.topk;
+  const int i0 = min(g * p.chunk, slots), i1 = min(i0 + p.chunk, slots);
+  const uint32_t *offsets = a.tb.offsets;
+  const uint32_t *wgb = a.tb.wg_counts + (size_t)g * ne;
+  place_slots(a, i0, i1, [&](int e) { return offsets[e] + wgb[e]; });
 }
 
 struct CombineArgs {
@@ -263,6 +377,18 @@ int moe_tile_rows(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, i
   return tr;
 }
 
+// Workgroups of the route pass: one up to kRouteParallelSlots routed slots
+// (its single pass is cheaper than three launches there); above, one per
+// kRouteSlotsPerGroup slots, at most kRouteMaxGroups.
+constexpr size_t kRouteParallelSlots = 16384;
+constexpr size_t kRouteSlotsPerGroup = 2048;
+constexpr int kRouteMaxGroups = 128;
+
+int route_groups(size_t slots) {
+  if (slots <= kRouteParallelSlots) return 1;
+  return (int)std::min<size_t>((slots + kRouteSlotsPerGroup - 1) / kRouteSlotsPerGroup, kRouteMaxGroups);
+}
+
 MoeLayout moe_layout(int num_experts, int t, int topk, int num_shared, int inter, int hidden,
                      int tile_rows) {
   MoeLayout L{};
@@ -286,6 +412,9 @@ MoeLayout moe_layout(int num_experts, int t, int topk, int num_shared, int inter
   L.tiles = take(L.max_tiles * 12);
   L.h = take(rows * (size_t)inter * 2);
   L.d = take(rows * (size_t)hidden * 4);
+  L.route_groups = (size_t)route_groups((size_t)t * topk);
+  L.wg_counts = take(L.route_groups > 1 ? L.route_groups * num_experts * 4 : 0);
+  L.wg_err = take(L.route_groups > 1 ? L.route_groups * 4 : 0);
   L.bytes = o;
   return L;
 }
@@ -305,6 +434,9 @@ MoeTables moe_tables(const MoeLayout &L, void *ws) {
   t.tiles = (uint32_t *)(b + L.tiles);
   t.h = (uint16_t *)(b + L.h);
   t.d = (float *)(b + L.d);
+  t.wg_counts = (uint32_t *)(b + L.wg_counts);
+  t.wg_err = (uint32_t *)(b + L.wg_err);
+  t.route_groups = (int)L.route_groups;
   return t;
 }
 
@@ -329,7 +461,15 @@ hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed
                            y, y_dtype == QMM_BF16, tb, s);
   } else {
     RouteArgs ra{topk_ids, t, topk, num_routed, num_shared, (int)L.tile_rows, tb};
-    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ra);
+    if (tb.route_groups <= 1) {
+      hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ra);
+    } else {
+      const int slots = t * topk;
+      RouteParArgs rp{ra, (slots + tb.route_groups - 1) / tb.route_groups};
+      hipLaunchKernelGGL(moe_route_count_kernel, dim3(tb.route_groups), dim3(kRouteThreads), 0, s, rp);
+      hipLaunchKernelGGL(moe_route_scan_kernel, dim3(1), dim3(kRouteThreads), 0, s, rp);
+      hipLaunchKernelGGL(moe_route_place_kernel, dim3(tb.route_groups), dim3(kRouteThreads), 0, s, rp);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // 256-row weight tiles decoded straight into MFMA operands (gemm_big.hip)

@@ -58,10 +58,15 @@ struct MoeTables {
   uint32_t *tiles;          // [max_tiles][3] (expert, first row, rows)
   uint16_t *h;              // bf16 [rows][inter]
   float *d;                 // float32 [rows][hidden]
+  uint32_t *wg_counts;      // parallel route: [groups][experts] rows per workgroup, then
+                            // each workgroup's first position in the expert's group
+  uint32_t *wg_err;         // parallel route: [groups] dropped ids seen
+  int route_groups;         // 1: the one-workgroup route; else workgroups of the parallel one
 };
 
 struct MoeLayout {
   size_t counts, offsets, row_of_slot, row_of_shared, token_of_row, active, scalars, tiles, h, d;
+  size_t wg_counts, wg_err, route_groups;
   size_t bytes, max_rows, max_tiles, tile_rows;
 };
 

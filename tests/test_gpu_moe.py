@@ -243,6 +243,38 @@ def test_moe_invalid_expert_ids_contribute_nothing(T):
     check_y(gu, dn, x, ids2, w2, E, 1, yh, hd, tokens)
 
 
+@pytest.mark.parametrize("T", [1638, 1700, 4000])
+def test_moe_many_slots_route(T):
+    """Calls with more than 16384 routed slots group them over many workgroups
+    (per-workgroup counts, one scan, placement); 1638 x 10 slots is the largest
+    call of the one-workgroup route.  Dropped ids sit in the first, a middle
+    and the last (ragged) chunk; the tables must still match the oracle's."""
+    q = _q()
+    E, S, H, I, topk = 64, 1, 256, 128, 10
+    gu, dn, x, ids, w = make_case(F.NVFP4, F.AFFINE4_G64, E, S, H, I, T, topk, f"moemany{T}")
+    ids = ids.copy()
+    bad = [(0, 3), (T // 2, 0), (T - 1, topk - 1)]
+    ids[bad[0]] = E
+    ids[bad[1]] = -7
+    ids[bad[2]] = 1 << 20
+    yh, r = run_gpu(q, gu, dn, x, ids, w, E, S)
+    assert not r["slot_rows"]
+    assert all(r["row_of_slot"][b] == 0xFFFFFFFF for b in bad)
+    assert r["err"] == 1
+    check_grouping(r, ids, E, S)
+    w2 = w.copy()
+    for b in bad:
+        w2[b] = 0.0
+    ids2 = np.where((ids < 0) | (ids >= E), 0, ids).astype(np.int32)
+    tokens = [0, 1, T // 2, T // 2 + 1, T - 2, T - 1]
+    hd = gpu_h_dict(r, T, topk, S, tokens)
+    clean = [1, T // 2 + 1, T - 2]
+    check_h(gu, x, ids, E, S, {k: v for k, v in hd.items() if k[0] in clean}, clean)
+    for b in bad:
+        hd[b] = np.zeros(I, np.uint16)
+    check_y(gu, dn, x, ids2, w2, E, S, yh, hd, tokens)
+
+
 def _fma_f32(a, b, c):
     """fma(a, b, c) in float32: the exact a * b + c rounded once to nearest
     even (exact rational arithmetic, then the nearest float32)."""
