@@ -227,26 +227,42 @@ void gemm_big_kernel(GemmArgs a) {
       load_x(sn);
       wr[(u + kStages - 1) % kStages] = load_run<FMT>(ws, sn);
 
-      // the run's 32 weights: k-step st takes values 8 st .. 8 st + 7
-      uint32_t o[16];
-      decode_piece<FMT>(wr[u], o);
-      bf16x8_t af[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        af[st] = __builtin_bit_cast(bf16x8_t, u32x4_t{o[4 * st], o[4 * st + 1], o[4 * st + 2], o[4 * st + 3]});
+      // the run's 32 weights: k-step st takes values 8 st .. 8 st + 7.  The
+      // decode of k-step st + 1's weights is interleaved with k-step st's
+      // MFMAs (each MFMA occupies the matrix core for many cycles, in which
+      // the wave issues independent vector instructions), so that only the
+      // first k-step's decode runs with the matrix core idle.
+      const PieceScale sc = piece_scale<FMT>(wr[u]);
+      uint32_t o[4];
+      decode_part<FMT>(wr[u], sc, 0, o);
+      bf16x8_t af = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
 
+      // Likewise the activation operands of k-step st + 1 are read from LDS
+      // during k-step st's MFMAs, so that no k-step but the first waits on LDS.
       const uint8_t *stg = lds + (s % kStages) * kXStage;
+      bf16x8_t bfr[TM];
+#pragma unroll
+      for (int t = 0; t < TM; ++t) bfr[t] = *(const bf16x8_t *)(stg + t * 32 * kXRow + xo[0]);
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        // all of this k-step's activation operands first, so that the MFMAs
-        // below do not wait on LDS after each one
-        bf16x8_t bfr[TM];
+        // MFMA t, then one LDS read and part of the decode for k-step st + 1,
+        // in this order (the scheduler is kept from regrouping them)
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t on[4] = {0u, 0u, 0u, 0u};
+        bf16x8_t bfn[TM];
 #pragma unroll
-        for (int t = 0; t < TM; ++t) bfr[t] = *(const bf16x8_t *)(stg + t * 32 * kXRow + xo[st]);
-        if constexpr (FMT != QMM_Q6_K) __builtin_amdgcn_sched_barrier(0);
+        for (int t = 0; t < TM; ++t) {
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[t], acc[t], 0, 0, 0);
+          if (st < 3) {
+            bfn[t] = *(const bf16x8_t *)(stg + t * 32 * kXRow + xo[st + 1]);
 #pragma unroll
-        for (int t = 0; t < TM; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[st], bfr[t], acc[t], 0, 0, 0);
+            for (int i = t * 4 / TM; i < (t + 1) * 4 / TM; ++i) on[i] = decode_word<FMT>(wr[u], sc, st + 1, i);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        af = __builtin_bit_cast(bf16x8_t, u32x4_t{on[0], on[1], on[2], on[3]});
+#pragma unroll
+        for (int t = 0; t < TM; ++t) bfr[t] = bfn[t];
       }
     }
   }

@@ -83,67 +83,89 @@ __device__ __forceinline__ Piece load_piece(const GemmArgs &a, int row, int kc) 
   return p;
 }
 
+// Per-piece scale terms of decode_part, computed once per piece.
+struct PieceScale {
+  float a, b;  // affine: scale, bias; MXFP4: scale; NVFP4: the two block scales; Q6_K: d
+};
+
+template <int FMT>
+__device__ __forceinline__ PieceScale piece_scale(const Piece &p) {
+  if constexpr (FMT == QMM_AFFINE4_G64) {
+    return {half_to_float(p.s & 0xFFFFu), half_to_float(p.s >> 16)};
+  } else if constexpr (FMT == QMM_MXFP4) {
+    return {e8m0_to_float(p.s), 0.0f};
+  } else if constexpr (FMT == QMM_NVFP4) {
+    PieceScale r;
+    e4m3x2_to_float(p.s, r.a, r.b);
+    return r;
+  } else {
+    return {half_to_float(p.d), 0.0f};
+  }
+}
+
+// Weights 8j + 2i and 8j + 2i + 1 of the piece (code word j) as one bf16
+// pair.
+template <int FMT>
+__device__ __forceinline__ uint32_t decode_word(const Piece &p, const PieceScale &sc, int j, int i) {
+  const uint32_t w = p.q[j];
+  if constexpr (FMT == QMM_AFFINE4_G64) {
+    // even codes to the bytes of one word, odd codes to the bytes of another,
+    // so that each code becomes a float with one v_cvt_f32_ubyteN (the empty
+    // asm keeps the compiler from folding the mask into a bit-field extract
+    // per code)
+    uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
+    asm("" : "+v"(ev));
+    asm("" : "+v"(od));
+    const float lo = __builtin_fmaf(sc.a, (float)((ev >> (8 * i)) & 0xFFu), sc.b);
+    const float hi = __builtin_fmaf(sc.a, (float)((od >> (8 * i)) & 0xFFu), sc.b);
+    return pack_bf16(lo, hi);
+  } else if constexpr (FMT == QMM_MXFP4) {
+    // the conversions take the byte index as an immediate
+    switch (i) {
+      case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc.a, 0));
+      case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc.a, 1));
+      case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc.a, 2));
+      default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc.a, 3));
+    }
+  } else if constexpr (FMT == QMM_NVFP4) {
+    const float bs = j < 2 ? sc.a : sc.b;
+    // E2M1 pair -> two float32 (hardware conversion, unit scale), times the
+    // E4M3 block scale (exact), -> bfloat16 pair (exact)
+    const f32x2_t e = i == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)
+                    : i == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)
+                    : i == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
+                             : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    return pack_bf16(e[0] * bs, e[1] * bs);
+  } else {  // Q6_K
+    const uint32_t hw[2] = {p.h.x, p.h.y};
+    const float dsc = sc.a * (float)(int8_t)(p.s >> (8 * (j / 2)));
+    const int v0 = 8 * j + 2 * i;  // value index within the piece (even)
+    const uint32_t q0 = ((w >> (8 * i)) & 15u) | (((hw[v0 / 16] >> (2 * (v0 % 16))) & 3u) << 4);
+    const uint32_t q1 = ((w >> (8 * i + 4)) & 15u) |
+                        (((hw[(v0 + 1) / 16] >> (2 * ((v0 + 1) % 16))) & 3u) << 4);
+    return pack_bf16(dsc * (float)((int)q0 - 32), dsc * (float)((int)q1 - 32));
+  }
+}
+
+// Weights 8j .. 8j+7 of the piece (code word j) as 4 bf16 pairs in natural
+// order.
+template <int FMT>
+__device__ __forceinline__ void decode_part(const Piece &p, const PieceScale &sc, int j,
+                                            uint32_t (&o)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = decode_word<FMT>(p, sc, j, i);
+}
+
 // The piece's 32 weights as 16 bf16 pairs in natural order.
 template <int FMT>
 __device__ __forceinline__ void decode_piece(const Piece &p, uint32_t (&o)[16]) {
-  const uint32_t w[4] = {p.q[0], p.q[1], p.q[2], p.q[3]};
-  if constexpr (FMT == QMM_AFFINE4_G64) {
-    const float s = half_to_float(p.s & 0xFFFFu), b = half_to_float(p.s >> 16);
+  const PieceScale sc = piece_scale<FMT>(p);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // even codes to the bytes of one word, odd codes to the bytes of another,
-      // so that each code becomes a float with one v_cvt_f32_ubyteN (the
-      // empty asm keeps the compiler from folding the mask into a bit-field
-      // extract per code)
-      uint32_t ev = w[j] & 0x0F0F0F0Fu, od = (w[j] >> 4) & 0x0F0F0F0Fu;
-      asm volatile("" : "+v"(ev));
-      asm volatile("" : "+v"(od));
+  for (int j = 0; j < 4; ++j) {
+    uint32_t t[4];
+    decode_part<FMT>(p, sc, j, t);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float lo = __builtin_fmaf(s, (float)((ev >> (8 * i)) & 0xFFu), b);
-        const float hi = __builtin_fmaf(s, (float)((od >> (8 * i)) & 0xFFu), b);
-        o[4 * j + i] = pack_bf16(lo, hi);
-      }
-    }
-  } else if constexpr (FMT == QMM_MXFP4) {
-    const float sc = e8m0_to_float(p.s);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      o[4 * j + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 0));
-      o[4 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 1));
-      o[4 * j + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 2));
-      o[4 * j + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 3));
-    }
-  } else if constexpr (FMT == QMM_NVFP4) {
-    float s0, s1;
-    e4m3x2_to_float(p.s, s0, s1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float sc = j < 2 ? s0 : s1;
-      // E2M1 pair -> two float32 (hardware conversion, unit scale), times the
-      // E4M3 block scale (exact), -> bfloat16 pair (exact)
-      const f32x2_t e[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 0),
-                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 1),
-                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 2),
-                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 3)};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[4 * j + i] = pack_bf16(e[i][0] * sc, e[i][1] * sc);
-    }
-  } else {  // Q6_K
-    const float dd = half_to_float(p.d);
-    const uint32_t hw[2] = {p.h.x, p.h.y};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float dsc = dd * (float)(int8_t)(p.s >> (8 * (j / 2)));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v0 = 8 * j + 2 * i;  // value index within the piece (even)
-        const uint32_t q0 = ((w[j] >> (8 * i)) & 15u) | (((hw[v0 / 16] >> (2 * (v0 % 16))) & 3u) << 4);
-        const uint32_t q1 = ((w[j] >> (8 * i + 4)) & 15u) |
-                            (((hw[(v0 + 1) / 16] >> (2 * ((v0 + 1) % 16))) & 3u) << 4);
-        o[4 * j + i] = pack_bf16(dsc * (float)((int)q0 - 32), dsc * (float)((int)q1 - 32));
-      }
-    }
+    for (int i = 0; i < 4; ++i) o[4 * j + i] = t[i];
   }
 }
 
