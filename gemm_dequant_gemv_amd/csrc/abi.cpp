@@ -232,10 +232,15 @@ int qmoe_workspace_layout(const qmm_weight *gate_up, const qmm_weight *down, int
   return QMM_OK;
 }
 
-int qmoe_grouped(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
-                 int32_t num_shared, const void *x, int32_t t, const int32_t *topk_ids,
-                 const float *topk_w, int32_t topk, const float *shared_w, void *y,
-                 int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Every argument check of qmoe_grouped (QMM_OK or the error it returns).
+int qmoe_grouped_check(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
+                       int32_t num_shared, const void *x, int32_t t, const int32_t *topk_ids,
+                       const float *topk_w, int32_t topk, const float *shared_w, const void *y,
+                       int32_t y_dtype, const void *workspace, size_t workspace_bytes) {
   int st = check_weight(gate_up);
   if (st) return st;
   st = check_weight(down);
@@ -273,6 +278,69 @@ int qmoe_grouped(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_
   const Range rw = range(workspace, L.bytes);
   for (int i = 0; i < ni - 1; ++i)
     if (overlap(rw, ins[i])) return QMM_ERR_ALIAS;
+  return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmoe_grouped(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
+                 int32_t num_shared, const void *x, int32_t t, const int32_t *topk_ids,
+                 const float *topk_w, int32_t topk, const float *shared_w, void *y,
+                 int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  const int st = qmoe_grouped_check(gate_up, down, num_routed, num_shared, x, t, topk_ids, topk_w,
+                                    topk, shared_w, y, y_dtype, workspace, workspace_bytes);
+  if (st) return st;
+  return hip_status(qmm::launch_moe(*gate_up, *down, num_routed, num_shared, x, t, topk_ids,
+                                    topk_w, topk, shared_w, y, y_dtype, workspace,
+                                    (hipStream_t)stream));
+}
+
+int qmoe_router(const float *logits, int32_t t, int32_t num_experts, int32_t topk,
+                int32_t *topk_ids, float *topk_w, void *stream) {
+  if (!logits || !topk_ids || !topk_w) return QMM_ERR_NULL;
+  if (num_experts < 1 || num_experts > qmm::kMoeMaxExperts) return QMM_ERR_ARG;
+  if (topk < 1 || topk > 64 || topk > num_experts) return QMM_ERR_ARG;
+  if (t < 1 || (int64_t)t * num_experts >= (1ll << 31)) return QMM_ERR_M_RANGE;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return QMM_ERR_ALIGN;
+  const Range rl = range(logits, (size_t)t * num_experts * 4);
+  const Range ri = range(topk_ids, (size_t)t * topk * 4);
+  const Range rw = range(topk_w, (size_t)t * topk * 4);
+  if (overlap(ri, rl) || overlap(rw, rl) || overlap(ri, rw)) return QMM_ERR_ALIAS;
+  return hip_status(qmm::launch_router(logits, t, num_experts, topk, topk_ids, topk_w,
+                                       (hipStream_t)stream));
+}
+
+int qmoe_grouped_logits(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
+                        int32_t num_shared, const void *x, int32_t t, const float *logits,
+                        int32_t topk, int32_t *topk_ids, float *topk_w, const float *shared_w,
+                        void *y, int32_t y_dtype, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  // every check of both calls before either launches
+  if (!logits) return QMM_ERR_NULL;
+  int st = qmoe_grouped_check(gate_up, down, num_routed, num_shared, x, t, topk_ids, topk_w, topk,
+                              shared_w, y, y_dtype, workspace, workspace_bytes);
+  if (st) return st;
+  if (topk > num_routed) return QMM_ERR_ARG;
+  if (!aligned(logits, 4)) return QMM_ERR_ALIGN;
+  const Range rl = range(logits, (size_t)t * num_routed * 4);
+  const Range ri = range(topk_ids, (size_t)t * topk * 4);
+  const Range rw = range(topk_w, (size_t)t * topk * 4);
+  const Range ry = range(y, (size_t)t * down->n * (y_dtype == QMM_F32 ? 4 : 2));
+  const Range rs = range(workspace, workspace_bytes);
+  if (overlap(ri, rl) || overlap(rw, rl) || overlap(ri, rw) || overlap(ry, rl) || overlap(rs, rl))
+    return QMM_ERR_ALIAS;
+  // the router's outputs must not land on the layer's other inputs
+  Range ins[16];
+  int ni = weight_ranges(*gate_up, ins);
+  ni += weight_ranges(*down, ins + ni);
+  ins[ni++] = range(x, (size_t)t * gate_up->k * 2);
+  if (shared_w) ins[ni++] = range(shared_w, (size_t)t * 4);
+  for (int i = 0; i < ni; ++i)
+    if (overlap(ri, ins[i]) || overlap(rw, ins[i])) return QMM_ERR_ALIAS;
+  st = qmoe_router(logits, t, num_routed, topk, topk_ids, topk_w, stream);
+  if (st) return st;
   return hip_status(qmm::launch_moe(*gate_up, *down, num_routed, num_shared, x, t, topk_ids,
                                     topk_w, topk, shared_w, y, y_dtype, workspace,
                                     (hipStream_t)stream));

@@ -115,6 +115,9 @@ hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed
                       int topk, const float *shared_w, void *y, int y_dtype, void *workspace,
                       hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+// router top-k + softmax: one wave per token (router.hip)
+hipError_t launch_router(const float *logits, int t, int e, int k, int32_t *ids, float *w,
+                         hipStream_t s);
 hipError_t launch_mfma_peak(int iters, float *sink, int blocks, hipStream_t s);
 double mfma_peak_flops(int iters, int blocks);
 hipError_t launch_stream_read(const void *p, size_t bytes, uint32_t *sink, int blocks,

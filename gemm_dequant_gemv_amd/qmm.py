@@ -21,7 +21,8 @@ F32, BF16 = 0, 1
 FORMATS = {"affine4_g64": AFFINE4_G64, "mxfp4": MXFP4, "nvfp4": NVFP4, "q6_k": Q6_K}
 
 ENTRY_POINTS = ("qdequant", "qgemv", "qgemv_workspace_size", "qgemm", "qgemm_workspace_size",
-                "qmoe_grouped", "qmoe_workspace_size", "qmoe_workspace_layout",
+                "qmoe_grouped", "qmoe_workspace_size", "qmoe_workspace_layout", "qmoe_router",
+                "qmoe_grouped_logits",
                 "qworkspace_init", "qbench_stream_read", "qbench_mfma_peak", "qstatus_string",
                 "qlast_hip_error")
 
@@ -70,6 +71,9 @@ def _lib():
         lib.qmoe_workspace_size.restype = SZ
         lib.qmoe_workspace_layout.argtypes = [P, P, I32, I32, I32, I32, ctypes.POINTER(QmoeLayoutC)]
         lib.qmoe_grouped.argtypes = [P, P, I32, I32, VP, I32, VP, VP, I32, VP, VP, I32, VP, SZ, VP]
+        lib.qmoe_router.argtypes = [VP, I32, I32, I32, VP, VP, VP]
+        lib.qmoe_grouped_logits.argtypes = [P, P, I32, I32, VP, I32, VP, I32, VP, VP, VP, VP, I32,
+                                            VP, SZ, VP]
         lib.qworkspace_init.argtypes = [VP, SZ, VP]
         lib.qbench_stream_read.argtypes = [VP, SZ, VP, I32, VP]
         lib.qbench_mfma_peak.argtypes = [I32, I32, VP, ctypes.POINTER(ctypes.c_double), VP]
@@ -214,6 +218,41 @@ def moe(gate_up: Weight, down: Weight, x, topk_ids, topk_w, num_routed: int, num
                                _ptr(topk_ids), _ptr(topk_w), topk, _ptr(shared_w), _ptr(out), dt,
                                _ptr(workspace), ws_bytes, _stream(stream)), "qmoe_grouped")
     return out
+
+
+def moe_router(logits, topk: int, ids=None, w=None, stream=None):
+    """Router top-k and softmax: logits float32 [t][E] -> (ids int32 [t][topk],
+    weights float32 [t][topk])."""
+    t, e = logits.shape
+    if ids is None:
+        ids = torch.empty((t, topk), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((t, topk), dtype=torch.float32, device=logits.device)
+    _check(_lib().qmoe_router(_ptr(logits), t, e, topk, _ptr(ids), _ptr(w), _stream(stream)),
+           "qmoe_router")
+    return ids, w
+
+
+def moe_from_logits(gate_up: Weight, down: Weight, x, logits, topk: int, num_routed: int,
+                    num_shared: int, shared_w=None, y_dtype=torch.float32, out=None,
+                    workspace=None, stream=None):
+    """One MoE layer from router logits float32 [t][num_routed]; returns (y,
+    ids, weights)."""
+    t = logits.shape[0]
+    if out is None:
+        out = torch.empty((t, down.n), dtype=y_dtype, device=x.device)
+    ids = torch.empty((t, topk), dtype=torch.int32, device=x.device)
+    w = torch.empty((t, topk), dtype=torch.float32, device=x.device)
+    need = moe_workspace_size(gate_up, down, num_routed, num_shared, t, topk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    dt = F32 if out.dtype == torch.float32 else BF16
+    _check(_lib().qmoe_grouped_logits(gate_up.c, down.c, num_routed, num_shared, _ptr(x), t,
+                                      _ptr(logits), topk, _ptr(ids), _ptr(w), _ptr(shared_w),
+                                      _ptr(out), dt, _ptr(workspace), ws_bytes, _stream(stream)),
+           "qmoe_grouped_logits")
+    return out, ids, w
 
 
 def workspace_init(ws, stream=None):

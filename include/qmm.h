@@ -246,6 +246,45 @@ int qmoe_grouped(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_
                  int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * qmoe_router -- the router's top-k and softmax ("TurboEXL3" section 4.2: in
+ * the decode chain the router's top-k and softmax run on the GPU, in the
+ * layer's first launch; the model routes each token to 10 of 512 experts).
+ *
+ *   topk_ids[t][0..k-1] = the k experts with the largest logits[t][*], in
+ *                         descending logit order; equal logits go to the lower
+ *                         expert id, and -0 equals +0
+ *   topk_w[t][r]        = exp(l_r - l_0) / sum_{j<k} exp(l_j - l_0) in float32
+ *                         (l_r the logit of topk_ids[t][r]; the sum runs in a
+ *                         fixed order, so the same logits give the same bits)
+ *
+ * logits       float32 [t][num_experts], finite (a NaN gets an unspecified but
+ *              repeatable place in the order)
+ * num_experts  1 .. 4096;  topk  1 .. min(64, num_experts);  t >= 1
+ * topk_ids     int32 [t][topk] (out);  topk_w  float32 [t][topk] (out)
+ * All pointers 4-byte aligned; the outputs must not overlap the logits or each
+ * other (QMM_ERR_ALIAS).  No workspace.
+ */
+int qmoe_router(const float *logits, int32_t t, int32_t num_experts, int32_t topk,
+                int32_t *topk_ids, float *topk_w, void *stream);
+
+/*
+ * qmoe_grouped_logits -- qmoe_grouped from router logits: qmoe_router over the
+ * num_routed routed experts into topk_ids / topk_w (outputs, also kept for the
+ * caller), then qmoe_grouped with them, on one stream.  The result is
+ * bit-identical to calling the two in sequence.  Every argument check of both
+ * calls runs before anything is launched; in addition the router's outputs
+ * must not overlap the logits, x, the weights, shared_w, y or the workspace
+ * (QMM_ERR_ALIAS).  The workspace is qmoe_workspace_size(...) bytes as for
+ * qmoe_grouped.  (The router is its own launch ahead of the layer's; the
+ * pages fold it into the decode chain's prepare launch.)
+ */
+int qmoe_grouped_logits(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
+                        int32_t num_shared, const void *x, int32_t t, const float *logits,
+                        int32_t topk, int32_t *topk_ids, float *topk_w, const float *shared_w,
+                        void *y, int32_t y_dtype, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/*
  * Where a qmoe_grouped call with these arguments keeps its intermediates inside
  * the workspace, for inspection after the call.  Byte offsets from the
  * workspace start; rows = t * (topk + S) grouped rows (slots sorted by expert).

@@ -38,6 +38,10 @@ What it computes, and where the pages define it:
   score-weighted sum of each token's ten expert outputs), rounding only where
   the library's contract rounds: h = bf16(silu(g) * u), y = sum_k w_k d_k
   (+ w_s d_shared).
+* The MoE router ("TurboEXL3" section 4.2, the router's top-k and softmax;
+  the model description: 10 of 512 experts per token): the k largest logits
+  (equal logits in ascending expert id, -0 equal to +0), in descending order,
+  weighted by the softmax over those k, in float64.
 * Alongside every output, its magnitude sum sum_k |w||x| (+ |r|), which sets the
   tolerance |y - y_ref| <= 2e-3 * magnitude.
 
@@ -240,6 +244,26 @@ def moe(gate_up, down, x_bits, topk_ids, topk_w, num_routed: int, num_shared: in
         ys.append(y)
         mags.append(mag)
     return np.array(ys), np.array(mags), hs
+
+
+def router(logits, k: int):
+    """Router top-k and softmax ("TurboEXL3" section 4.2: the router's top-k
+    and softmax).  ``logits`` float [T][E] (taken exactly); returns (ids int32
+    [T][k], weights float64 [T][k]): per token the experts ordered by
+    descending logit, equal logits by ascending id (-0 == +0), first k kept,
+    weights exp(l_r - max) / sum over the k chosen of exp(l_j - max)."""
+    lg = np.asarray(logits, dtype=np.float64)
+    T, E = lg.shape
+    ids = np.empty((T, k), np.int32)
+    wts = np.empty((T, k))
+    for t in range(T):
+        # sort key: (-logit, id); -0.0 and +0.0 compare equal as floats
+        order = sorted(range(E), key=lambda e: (-lg[t, e], e))[:k]
+        top = lg[t, order]
+        z = np.exp(top - top.max())
+        ids[t] = order
+        wts[t] = z / z.sum()
+    return ids, wts
 
 
 def moe_grouping(topk_ids, num_routed: int, num_shared: int, tile_rows: int = 128):

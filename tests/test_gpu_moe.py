@@ -365,3 +365,69 @@ def test_moe_full_layer(full_layer, T, y_dtype):
     check_y(gu, dn, x, ids, w, c["E"], c["S"], yh, hd, tokens,
             bf16_out=y_dtype == torch.bfloat16)
     assert np.isfinite(yh).all()
+
+
+# ------------------------------------------------------------ router
+
+def _router_case(T, E, k, kind):
+    if kind == "normal":
+        lg = routing.router_logits(T, E, name=f"rt{T}/{E}")
+    elif kind == "ties":  # few distinct values: many equal logits per token
+        lg = np.floor(routing.router_logits(T, E, name=f"rtt{T}/{E}") * 2.0).astype(np.float32)
+    else:  # signed zeros among negative logits
+        lg = -np.abs(routing.router_logits(T, E, name=f"rtz{T}/{E}"))
+        lg[:, ::3] = 0.0
+        lg[:, 1::3] = -0.0
+        lg = lg.astype(np.float32)
+    return np.ascontiguousarray(lg, dtype=np.float32)
+
+
+@pytest.mark.parametrize("T,E,k,kind", [(1, 512, 10, "normal"), (4, 512, 10, "normal"),
+                                        (37, 512, 10, "normal"), (8192, 512, 10, "normal"),
+                                        (5, 64, 1, "normal"), (3, 4096, 64, "normal"),
+                                        (7, 100, 7, "normal"), (6, 130, 5, "ties"),
+                                        (9, 512, 10, "ties"), (5, 300, 12, "zeros")])
+def test_router_parity(T, E, k, kind):
+    """Expert ids exactly as the oracle orders them (both sides compare the same
+    float32 logits); weights within 2e-6 relative of the float64 softmax."""
+    q = _q()
+    lg = _router_case(T, E, k, kind)
+    ids, w = q.moe_router(torch.from_numpy(lg).cuda(), k)
+    torch.cuda.synchronize()
+    rid, rw = oracle.router(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    wg = w.cpu().numpy().astype(np.float64)
+    assert (np.abs(wg - rw) <= 2e-6 * rw + 1e-12).all()
+    # repeatable bits
+    ids2, w2 = q.moe_router(torch.from_numpy(lg).cuda(), k)
+    assert torch.equal(ids, ids2) and torch.equal(w, w2)
+
+
+@pytest.mark.parametrize("T", [4, 100])
+def test_moe_from_logits_is_router_then_layer(T):
+    """qmoe_grouped_logits gives the bits of qmoe_router followed by
+    qmoe_grouped (decode form at 4 tokens, grouped form at 100)."""
+    q = _q()
+    c = SMALL
+    gu, dn, x, _, _ = make_case(F.NVFP4, F.AFFINE4_G64, c["E"], c["S"], c["H"], c["I"], T,
+                                c["topk"], f"moelg{T}")
+    lg = torch.from_numpy(routing.router_logits(T, c["E"], name=f"moelg{T}/r")).cuda()
+    gud, dnd = q.Weight.from_host(gu), q.Weight.from_host(dn)
+    xd = _dev_bf16(x)
+    y1, ids1, w1 = q.moe_from_logits(gud, dnd, xd, lg, c["topk"], c["E"], c["S"])
+    ids2, w2 = q.moe_router(lg, c["topk"])
+    y2 = q.moe(gud, dnd, xd, ids2, w2, c["E"], c["S"])
+    torch.cuda.synchronize()
+    assert torch.equal(ids1, ids2) and torch.equal(w1, w2)
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    rid, _ = oracle.router(lg.cpu().numpy(), c["topk"])
+    assert np.array_equal(ids1.cpu().numpy(), rid)
+
+
+def test_router_argument_errors():
+    q = _q()
+    lg = torch.zeros((2, 8), dtype=torch.float32, device="cuda")
+    with pytest.raises(q.QmmError):
+        q.moe_router(lg, 9)  # topk > experts
+    with pytest.raises(q.QmmError):
+        q.moe_router(lg, 0)

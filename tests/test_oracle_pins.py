@@ -467,3 +467,51 @@ def test_moe_grouping_invariants_at_prefill_size():
         covered[r0:r0 + rows] += 1
     assert (covered == 1).all()
     assert len(g["tiles"]) == int(np.sum((c + 127) // 128))
+
+
+# ------------------------------------------------------------ router
+
+def test_router_equal_logits_closed_form():
+    """All logits equal: the k lowest ids, each with weight exactly 1/k."""
+    ids, w = oracle.router(np.full((3, 16), 0.75, np.float32), 4)
+    assert (ids == np.arange(4)).all()
+    assert (w == 0.25).all()
+
+
+def test_router_single_expert_weight_one():
+    lg = rng.normal_matrix(rng.BASE_SEED, "pin/router1", 5, 40, 1.0).astype(np.float32)
+    ids, w = oracle.router(lg, 1)
+    assert (ids[:, 0] == np.argmax(lg, axis=1)).all()
+    assert (w == 1.0).all()
+
+
+def test_router_ties_and_signed_zero():
+    ids, w = oracle.router(np.array([[1.0, 3.0, 3.0, 2.0], [0.0, -0.0, 0.0, -1.0]], np.float32), 2)
+    assert ids.tolist() == [[1, 2], [0, 1]]
+    assert (w == 0.5).all()
+
+
+def test_router_brute_force_and_library_softmax():
+    """The chosen set is the k-subset with the largest logit sum (brute force
+    over all subsets, distinct logits); the weights are scipy's softmax over
+    all experts renormalised over the chosen ones; the order is descending."""
+    from itertools import combinations
+
+    from scipy.special import softmax
+    lg = rng.normal_matrix(rng.BASE_SEED, "pin/router_bf", 6, 9, 1.0).astype(np.float32)
+    ids, w = oracle.router(lg, 3)
+    for t in range(lg.shape[0]):
+        row = lg[t].astype(np.float64)
+        best = max(combinations(range(9), 3), key=lambda c: sum(row[list(c)]))
+        assert sorted(ids[t].tolist()) == sorted(best)
+        assert (np.diff(row[ids[t]]) <= 0).all()
+        p = softmax(row)
+        np.testing.assert_allclose(w[t], p[ids[t]] / p[ids[t]].sum(), rtol=1e-14)
+
+
+def test_router_shift_invariant():
+    lg = rng.normal_matrix(rng.BASE_SEED, "pin/router_sh", 4, 64, 1.0)
+    ids0, w0 = oracle.router(lg, 10)
+    ids1, w1 = oracle.router(lg + 7.5, 10)
+    assert (ids0 == ids1).all()
+    np.testing.assert_allclose(w0, w1, rtol=1e-12)
