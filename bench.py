@@ -306,8 +306,19 @@ def moe_section(q, torch, dev):
              "TFLOPs": round(flops / (med * 1e-3) / 1e12, 2),
              "active_weight_GBps": round(active * per_expert / (med * 1e-3) / 1e9, 1),
              "y_dtype": "bf16" if ydt == torch.bfloat16 else "f32"}
+        # the router's top-k and softmax on the GPU (qmoe_router) for the same
+        # tokens, timed alone, and the layer from router logits (router + layer)
+        lg = torch.from_numpy(routing.router_logits(T, E, name=f"bench/moe/r{T}")).to(dev)
+        rid = torch.empty((T, topk), dtype=torch.int32, device=dev)
+        rw = torch.empty((T, topk), dtype=torch.float32, device=dev)
+        rmed, _ = timed(torch, lambda: q.moe_router(lg, topk, rid, rw), 20)
+        c["router_us"] = round(rmed * 1e3, 2)
+        ws = torch.empty(q.moe_workspace_size(gu, dn, E, S, T, topk), dtype=torch.uint8, device=dev)
+        lmed, _ = timed(torch, lambda: q.moe_from_logits(gu, dn, x, lg, topk, E, S, y_dtype=ydt,
+                                                         out=y, workspace=ws), 20 if T == 4 else 8)
+        c["ms_from_logits"] = round(lmed, 4)
         out.append(c)
-        del x, y, call
+        del x, y, call, lg, ws
     return {"unit": "ms per layer", "launches_per_layer": 4,
             "config": "512 routed + 1 shared experts, hidden 2048, intermediate 512, nvfp4, top-10",
             "cases": out}

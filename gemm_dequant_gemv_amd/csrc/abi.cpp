@@ -339,11 +339,9 @@ int qmoe_grouped_logits(const qmm_weight *gate_up, const qmm_weight *down, int32
   if (shared_w) ins[ni++] = range(shared_w, (size_t)t * 4);
   for (int i = 0; i < ni; ++i)
     if (overlap(ri, ins[i]) || overlap(rw, ins[i])) return QMM_ERR_ALIAS;
-  st = qmoe_router(logits, t, num_routed, topk, topk_ids, topk_w, stream);
-  if (st) return st;
-  return hip_status(qmm::launch_moe(*gate_up, *down, num_routed, num_shared, x, t, topk_ids,
-                                    topk_w, topk, shared_w, y, y_dtype, workspace,
-                                    (hipStream_t)stream));
+  return hip_status(qmm::launch_moe_logits(*gate_up, *down, num_routed, num_shared, x, t, logits,
+                                           topk_ids, topk_w, topk, shared_w, y, y_dtype, workspace,
+                                           (hipStream_t)stream));
 }
 
 }  // extern "C"

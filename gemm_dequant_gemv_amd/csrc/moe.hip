@@ -497,4 +497,21 @@ hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed
   return hipGetLastError();
 }
 
+hipError_t launch_moe_logits(const qmm_weight &gu, const qmm_weight &dn, int num_routed,
+                             int num_shared, const void *x, int t, const float *logits,
+                             int32_t *topk_ids, float *topk_w, int topk, const float *shared_w,
+                             void *y, int y_dtype, void *workspace, hipStream_t s) {
+  if (moe_uses_gemv(gu, dn, t, topk, num_shared) && moe_router_folds(num_routed)) {
+    const MoeLayout L = moe_layout(num_routed + num_shared, t, topk, num_shared, gu.n / 2, dn.n,
+                                  moe_tile_rows(gu, dn, t, topk, num_routed));
+    return launch_moe_gemv(gu, dn, num_routed, num_shared, x, t, nullptr, nullptr, topk, shared_w,
+                           y, y_dtype == QMM_BF16, moe_tables(L, workspace), s, logits, topk_ids,
+                           topk_w);
+  }
+  hipError_t e = launch_router(logits, t, num_routed, topk, topk_ids, topk_w, s);
+  if (e != hipSuccess) return e;
+  return launch_moe(gu, dn, num_routed, num_shared, x, t, topk_ids, topk_w, topk, shared_w, y,
+                    y_dtype, workspace, s);
+}
+
 }  // namespace qmm

@@ -32,6 +32,7 @@
 #include <cstdlib>
 
 #include "gemv_step.h"
+#include "router_device.h"
 
 namespace qmm {
 namespace {
@@ -60,7 +61,15 @@ struct MoeGemvArgs {
   void *y;                // [t][H] float32, or bfloat16 when y_bf16
   int y_bf16;
   uint32_t *err;          // 1 when an id was outside [0, E)
+  // gate/up with the router folded in: logits [t][num_routed] in; the routing
+  // out (written by workgroup 0, read by the down launch)
+  const float *logits;
+  int32_t *ids_out;
+  float *w_out;
 };
+
+// The router folded into the gate/up launch takes up to 64 x 8 routed experts.
+constexpr int kRouterFoldPer = 8;
 
 // LDS layout of the staged vectors: chunk ch (32 values) of vector l at u32
 // offset ch * stride + 16 l, stride = 16 nsrc + 4 (the pad spreads the chunks
@@ -75,8 +84,9 @@ struct MoeShape {
   static constexpr int kStepK = 32 * kLanes;        // values per row per step
 };
 
-template <int FMT, bool DOWN, int U, int WAVES>
+template <int FMT, bool DOWN, int U, int WAVES, bool ROUTER>
 __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
+  static_assert(!(ROUTER && DOWN), "the router folds into the gate/up launch");
   constexpr int kThreads = 64 * WAVES;
   using SH = MoeShape<DOWN>;
   constexpr int kStepK = SH::kStepK;
@@ -149,10 +159,32 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
   const uint32_t v_hi = hr * (k / 4) + 8 * c;
   const uint32_t v_d = (hr * (k / 256) + c / 8) * 2;
 
+  // 0. (router folded in) every workgroup routes the call's tokens itself,
+  //    one wave per token ("TurboEXL3" section 4.2: the router's top-k and
+  //    softmax run inside the chain's first launch), into LDS; workgroup 0
+  //    also writes the routing out for the down launch and the caller
+  __shared__ int32_t s_rid[ROUTER ? kMoeGemvMaxSlots : 1];
+  if constexpr (ROUTER) {
+    for (int tk = wave; tk < a.t; tk += WAVES) {
+      int id;
+      float w;
+      router::topk_softmax_wave<kRouterFoldPer>(a.logits + (size_t)tk * a.num_routed,
+                                                a.num_routed, a.topk, id, w);
+      if (lane < a.topk) {
+        s_rid[tk * a.topk + lane] = id;
+        if (blockIdx.x == 0) {
+          a.ids_out[tk * a.topk + lane] = id;
+          a.w_out[tk * a.topk + lane] = w;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
   // slot -> expert (-1 for an id outside [0, E)) and staged vector
   auto slot_expert = [&](int s) {
     if (s < routed) {
-      const int e = a.topk_ids[s];
+      const int e = ROUTER ? s_rid[s] : a.topk_ids[s];
       return (e < 0 || e >= a.num_routed) ? -1 : e;
     }
     return a.num_routed + (s - routed) / a.t;
@@ -429,7 +461,7 @@ MoeGemvCfg moe_gemv_cfg(bool down) {
   return c;
 }
 
-template <int FMT, bool DOWN, int U, int WAVES>
+template <int FMT, bool DOWN, int U, int WAVES, bool ROUTER>
 hipError_t launch_one(const MoeGemvArgs &a, size_t lds, int grid, hipStream_t s) {
   static std::atomic<uint64_t> raised{0};
   int dev = 0;
@@ -437,12 +469,12 @@ hipError_t launch_one(const MoeGemvArgs &a, size_t lds, int grid, hipStream_t s)
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(raised.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute((const void *)moe_gemv_kernel<FMT, DOWN, U, WAVES>,
+    e = hipFuncSetAttribute((const void *)moe_gemv_kernel<FMT, DOWN, U, WAVES, ROUTER>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     if (e != hipSuccess) return e;
     raised.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((moe_gemv_kernel<FMT, DOWN, U, WAVES>), dim3(grid), dim3(64 * WAVES), lds, s, a);
+  hipLaunchKernelGGL((moe_gemv_kernel<FMT, DOWN, U, WAVES, ROUTER>), dim3(grid), dim3(64 * WAVES), lds, s, a);
   return hipGetLastError();
 }
 
@@ -452,23 +484,23 @@ hipError_t launch_one(const MoeGemvArgs &a, size_t lds, int grid, hipStream_t s)
 #define QMM_MOE_GEMV_CONFIGS(X) X(2, 16)
 #endif
 
-template <int FMT, bool DOWN>
+template <int FMT, bool DOWN, bool ROUTER>
 hipError_t launch_cfg(const MoeGemvCfg &c, const MoeGemvArgs &a, size_t lds, int grid, hipStream_t s) {
 #define QMM_CASE(UU, WW) \
-  if (c.u == UU && c.waves == WW) return launch_one<FMT, DOWN, UU, WW>(a, lds, grid, s);
+  if (c.u == UU && c.waves == WW) return launch_one<FMT, DOWN, UU, WW, ROUTER>(a, lds, grid, s);
   QMM_MOE_GEMV_CONFIGS(QMM_CASE)
 #undef QMM_CASE
   return hipErrorInvalidConfiguration;
 }
 
-template <bool DOWN>
+template <bool DOWN, bool ROUTER = false>
 hipError_t launch_fmt(int format, const MoeGemvArgs &a, size_t lds, int grid, hipStream_t s) {
   const MoeGemvCfg c = moe_gemv_cfg(DOWN);
   switch (format) {
-    case QMM_AFFINE4_G64: return launch_cfg<QMM_AFFINE4_G64, DOWN>(c, a, lds, grid, s);
-    case QMM_MXFP4: return launch_cfg<QMM_MXFP4, DOWN>(c, a, lds, grid, s);
-    case QMM_NVFP4: return launch_cfg<QMM_NVFP4, DOWN>(c, a, lds, grid, s);
-    default: return launch_cfg<QMM_Q6_K, DOWN>(c, a, lds, grid, s);
+    case QMM_AFFINE4_G64: return launch_cfg<QMM_AFFINE4_G64, DOWN, ROUTER>(c, a, lds, grid, s);
+    case QMM_MXFP4: return launch_cfg<QMM_MXFP4, DOWN, ROUTER>(c, a, lds, grid, s);
+    case QMM_NVFP4: return launch_cfg<QMM_NVFP4, DOWN, ROUTER>(c, a, lds, grid, s);
+    default: return launch_cfg<QMM_Q6_K, DOWN, ROUTER>(c, a, lds, grid, s);
   }
 }
 
@@ -516,10 +548,17 @@ bool moe_gemv_fits(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, 
          down_lds(dn, t, topk, num_shared, moe_grid()) <= kLdsLimit;
 }
 
+bool moe_router_folds(int num_routed) { return num_routed <= 64 * kRouterFoldPer; }
+
 hipError_t launch_moe_gemv(const qmm_weight &gu, const qmm_weight &dn, int num_routed,
                            int num_shared, const void *x, int t, const int32_t *topk_ids,
                            const float *topk_w, int topk, const float *shared_w, void *y,
-                           int y_bf16, const MoeTables &tb, hipStream_t s) {
+                           int y_bf16, const MoeTables &tb, hipStream_t s, const float *logits,
+                           int32_t *ids_out, float *w_out) {
+  if (logits) {  // the router folded into the gate/up launch writes the routing
+    topk_ids = ids_out;
+    topk_w = w_out;
+  }
   const int slots = t * (topk + num_shared);
   const int inter = gu.n / 2;
 
@@ -537,7 +576,11 @@ hipError_t launch_moe_gemv(const qmm_weight &gu, const qmm_weight &dn, int num_r
   g.nsrc = t;
   g.h = tb.h;
   const int grid = moe_grid();
-  hipError_t e = launch_fmt<false>(gu.format, g, stage_lds(gu.format, gu.k, t), grid, s);
+  g.logits = logits;
+  g.ids_out = ids_out;
+  g.w_out = w_out;
+  hipError_t e = logits ? launch_fmt<false, true>(gu.format, g, stage_lds(gu.format, gu.k, t), grid, s)
+                        : launch_fmt<false>(gu.format, g, stage_lds(gu.format, gu.k, t), grid, s);
   if (e != hipSuccess) return e;
 
   MoeGemvArgs d = weight_args(dn);

@@ -106,14 +106,26 @@ constexpr int kMoeGemvMaxTokens = 16;
 constexpr int kMoeGemvMaxSlots = 128;  // token slots of the decode form (register table)
 bool moe_gemv_fits(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_shared);
 bool moe_uses_gemv(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_shared);
+// logits non-null: the router runs inside the gate/up launch (num_routed <=
+// 512, moe_router_folds) and writes the routing to ids_out / w_out, which
+// the down launch reads (topk_ids / topk_w are then ignored)
+bool moe_router_folds(int num_routed);
 hipError_t launch_moe_gemv(const qmm_weight &gu, const qmm_weight &dn, int num_routed,
                            int num_shared, const void *x, int t, const int32_t *topk_ids,
                            const float *topk_w, int topk, const float *shared_w, void *y,
-                           int y_bf16, const MoeTables &tb, hipStream_t s);
+                           int y_bf16, const MoeTables &tb, hipStream_t s,
+                           const float *logits = nullptr, int32_t *ids_out = nullptr,
+                           float *w_out = nullptr);
 hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed, int num_shared,
                       const void *x, int t, const int32_t *topk_ids, const float *topk_w,
                       int topk, const float *shared_w, void *y, int y_dtype, void *workspace,
                       hipStream_t s);
+// qmoe_grouped from router logits: the router folded into the decode form's
+// first launch where it can be, else its own launch ahead of the layer
+hipError_t launch_moe_logits(const qmm_weight &gu, const qmm_weight &dn, int num_routed,
+                             int num_shared, const void *x, int t, const float *logits,
+                             int32_t *topk_ids, float *topk_w, int topk, const float *shared_w,
+                             void *y, int y_dtype, void *workspace, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 // router top-k + softmax: one wave per token (router.hip)
 hipError_t launch_router(const float *logits, int t, int e, int k, int32_t *ids, float *w,

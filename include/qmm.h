@@ -275,8 +275,10 @@ int qmoe_router(const float *logits, int32_t t, int32_t num_experts, int32_t top
  * calls runs before anything is launched; in addition the router's outputs
  * must not overlap the logits, x, the weights, shared_w, y or the workspace
  * (QMM_ERR_ALIAS).  The workspace is qmoe_workspace_size(...) bytes as for
- * qmoe_grouped.  (The router is its own launch ahead of the layer's; the
- * pages fold it into the decode chain's prepare launch.)
+ * qmoe_grouped.  In the decode form with up to 512 routed experts the
+ * router runs inside the layer's first launch (every workgroup routes the
+ * tokens itself; "TurboEXL3" section 4.2); otherwise it is its own launch ahead
+ * of the layer's.
  */
 int qmoe_grouped_logits(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
                         int32_t num_shared, const void *x, int32_t t, const float *logits,

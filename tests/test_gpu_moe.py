@@ -403,10 +403,12 @@ def test_router_parity(T, E, k, kind):
     assert torch.equal(ids, ids2) and torch.equal(w, w2)
 
 
-@pytest.mark.parametrize("T", [4, 100])
+@pytest.mark.parametrize("T", [1, 4, 16, 100])
 def test_moe_from_logits_is_router_then_layer(T):
     """qmoe_grouped_logits gives the bits of qmoe_router followed by
-    qmoe_grouped (decode form at 4 tokens, grouped form at 100)."""
+    qmoe_grouped: the decode form (up to 16 tokens here) with the router folded
+    into its first launch, the grouped form (100 tokens) with the router as
+    its own launch."""
     q = _q()
     c = SMALL
     gu, dn, x, _, _ = make_case(F.NVFP4, F.AFFINE4_G64, c["E"], c["S"], c["H"], c["I"], T,
@@ -431,3 +433,24 @@ def test_router_argument_errors():
         q.moe_router(lg, 9)  # topk > experts
     with pytest.raises(q.QmmError):
         q.moe_router(lg, 0)
+
+
+def test_moe_from_logits_full_layer_decode(full_layer):
+    """The 512-expert layer at 4 tokens from router logits (router folded into
+    the first launch) against qmoe_router + qmoe_grouped, bit for bit, and the
+    routing against the oracle's."""
+    q = _q()
+    c = FULL
+    gu, dn, wdev = full_layer
+    T = 4
+    x = _dev_bf16(quant.synthetic_bf16(T, c["H"], name="moe_full/xlg"))
+    lg = torch.from_numpy(routing.router_logits(T, c["E"], name="moe_full/lg")).cuda()
+    y1, ids1, w1 = q.moe_from_logits(wdev[0], wdev[1], x, lg, c["topk"], c["E"], c["S"])
+    ids2, w2 = q.moe_router(lg, c["topk"])
+    y2 = q.moe(wdev[0], wdev[1], x, ids2, w2, c["E"], c["S"])
+    torch.cuda.synchronize()
+    assert torch.equal(ids1, ids2) and torch.equal(w1, w2)
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    rid, rw = oracle.router(lg.cpu().numpy(), c["topk"])
+    assert np.array_equal(ids1.cpu().numpy(), rid)
+    assert (np.abs(w1.cpu().numpy() - rw) <= 2e-6 * rw + 1e-12).all()
