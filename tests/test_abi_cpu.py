@@ -107,3 +107,52 @@ def test_status_strings(lib):
     for s in range(-10, 1):
         assert lib.qstatus_string(s)
     assert lib.qlast_hip_error() == 0
+
+
+VP = ctypes.c_void_p
+
+
+def _router(lib, logits=0x42000000, t=4, e=64, k=8, ids=0x40000000, w=0x41000000):
+    return lib.qmoe_router(VP(logits) if logits else None, t, e, k, VP(ids) if ids else None,
+                           VP(w) if w else None, None)
+
+
+def test_router_rejects_bad_calls(lib):
+    assert _router(lib, logits=0) == -1
+    assert _router(lib, ids=0) == -1
+    assert _router(lib, w=0) == -1
+    assert _router(lib, k=0) == -10
+    assert _router(lib, k=65, e=128) == -10
+    assert _router(lib, k=9, e=8) == -10         # more picks than experts
+    assert _router(lib, e=0) == -10
+    assert _router(lib, e=4097) == -10
+    assert _router(lib, t=0) == -5
+    assert _router(lib, logits=0x42000002) == -4
+    assert _router(lib, ids=0x42000000 + 64) == -7   # ids over the logits
+    assert _router(lib, w=0x40000000 + 16) == -7     # weights over the ids
+
+
+def _moe_weights(E=4, S=1, H=256, I=128):
+    gu = _w(fmt=1, n=2 * I, k=H, batch=E + S, codes=0x10000000, sc=0x11000000)
+    dn = _w(fmt=1, n=H, k=I, batch=E + S, codes=0x12000000, sc=0x13000000)
+    return gu, dn
+
+
+def _moe_logits(lib, topk=2, logits=0x42000000, ids=0x40000000, w=0x41000000, x=0x20000000,
+                y=0x21000000, t=4, E=4, S=1):
+    gu, dn = _moe_weights(E, S)
+    need = lib.qmoe_workspace_size(ctypes.byref(gu), ctypes.byref(dn), E, S, t, max(topk, 1))
+    return lib.qmoe_grouped_logits(ctypes.byref(gu), ctypes.byref(dn), E, S, VP(x), t,
+                                   VP(logits) if logits else None, topk, VP(ids), VP(w), None,
+                                   VP(y), 0, VP(0x30000000), need, None)
+
+
+def test_moe_from_logits_rejects_bad_calls(lib):
+    assert _moe_logits(lib, logits=0) == -1
+    assert _moe_logits(lib, topk=5) == -10            # more picks than routed experts
+    assert _moe_logits(lib, topk=0) == -10
+    assert _moe_logits(lib, logits=0x42000002) == -4
+    assert _moe_logits(lib, ids=0x20000000) == -7     # routing written over x
+    assert _moe_logits(lib, w=0x10000000) == -7       # routing written over the weights
+    assert _moe_logits(lib, logits=0x21000000) == -7  # logits under y
+    assert _moe_logits(lib, ids=0x42000000) == -7     # ids over the logits
