@@ -358,8 +358,8 @@ def main():
         record_traffic(*args.record_traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); how the path would "
-              "shard is described in DESIGN.md, and no multi-GPU run is made.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); no multi-GPU run is "
+              "made.", file=sys.stderr)
         sys.exit(2)
     import torch
 
