@@ -386,7 +386,9 @@ def _router_case(T, E, k, kind):
                                         (37, 512, 10, "normal"), (8192, 512, 10, "normal"),
                                         (5, 64, 1, "normal"), (3, 4096, 64, "normal"),
                                         (7, 100, 7, "normal"), (6, 130, 5, "ties"),
-                                        (9, 512, 10, "ties"), (5, 300, 12, "zeros")])
+                                        (9, 512, 10, "ties"), (5, 300, 12, "zeros"),
+                                        (3, 1, 1, "normal"), (4, 65, 64, "normal"),
+                                        (2, 4096, 10, "ties")])
 def test_router_parity(T, E, k, kind):
     """Expert ids exactly as the oracle orders them (both sides compare the same
     float32 logits); weights within 2e-6 relative of the float64 softmax."""
