@@ -302,14 +302,6 @@ def moe_grouping(topk_ids, num_routed: int, num_shared: int, tile_rows: int = 12
                 tiles=np.array(tiles, np.int64).reshape(-1, 3), err=int((~valid).any()))
 
 
-def moe_gate_up(gate_up, x_bits, e: int, rows_tokens):
-    """Gate/up outputs (float64) and magnitudes of expert ``e`` for the
-    listed tokens: [len][2I]."""
-    w = dequant(gate_up, e)
-    x = bf16(x_bits[np.asarray(rows_tokens)])
-    return x @ w.T, np.abs(x) @ np.abs(w).T
-
-
 def within_tolerance(y, y_ref, mag, rel: float = 2e-3):
     """Elementwise |y - y_ref| <= rel * mag (the parity rule for products)."""
     return np.abs(np.asarray(y, np.float64) - y_ref) <= rel * mag

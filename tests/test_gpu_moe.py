@@ -33,7 +33,7 @@ def make_case(fmt_gu, fmt_dn, E, S, H, I, T, topk, tag):
     gu = quant.synthetic_weight(fmt_gu, 2 * I, H, batch=E + S, name=f"{tag}/gu")
     dn = quant.synthetic_weight(fmt_dn, H, I, batch=E + S, name=f"{tag}/dn")
     x = quant.synthetic_bf16(T, H, name=f"{tag}/x")
-    ids, w = routing.synthetic_routing(T, E, topk, name=f"{tag}/r")
+    ids, w = routing.random_routing(T, E, topk, name=f"{tag}/r")
     return gu, dn, x, ids, w
 
 
@@ -354,7 +354,7 @@ def test_moe_full_layer(full_layer, T, y_dtype):
     c = FULL
     gu, dn, wdev = full_layer
     x = quant.synthetic_bf16(T, c["H"], name=f"moe_full/x{T}")
-    ids, w = routing.synthetic_routing(T, c["E"], c["topk"], name=f"moe_full/r{T}")
+    ids, w = routing.random_routing(T, c["E"], c["topk"], name=f"moe_full/r{T}")
     print(f"moe full layer T={T}", flush=True)
     yh, r = run_gpu(q, gu, dn, x, ids, w, c["E"], c["S"], y_dtype=y_dtype, wdev=wdev)
     assert r["slot_rows"] == decode_form(T, c["topk"], c["S"])

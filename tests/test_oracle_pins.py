@@ -323,19 +323,24 @@ def test_one_hot_block_addressing(fmt):
 # ------------------------------------------------------------ routing
 
 def test_routing_statistics_against_printed_values():
+    """The oracle router on N(0, 1) logits reproduces the routing statistics
+    the pages print: ten slots per token, 160 rows per expert at 8192 tokens,
+    and about 39 distinct experts in a 4-token call (expectation
+    512 (1 - (1 - 10/512)^4) = 38.84)."""
     g = {r[0]: int(r[1]) for r in _golden("routing.txt")}
     E, k = g["experts"], g["topk"]
-    ids, w = routing.synthetic_routing(g["tokens_prefill"], E, k)
+    lg = routing.router_logits(g["tokens_prefill"], E)
+    ids, w = oracle.router(lg, k)
     counts = np.bincount(ids.ravel(), minlength=E)
     assert counts.sum() == g["tokens_prefill"] * k
     assert counts.mean() == g["mean_tokens_per_expert"]
-    assert np.allclose(w.sum(1), 1.0, atol=1e-6)
+    assert np.allclose(w.sum(1), 1.0, atol=1e-12)
     assert np.all(np.diff(w, axis=1) <= 0)
     assert np.all([len(set(r)) == k for r in ids[:200]])
-    # distinct experts in a 4-token call: expectation 512 (1 - (1 - 10/512)^4)
     dist = []
     for s in range(400):
-        ids4, _ = routing.synthetic_routing(g["tokens_decode"], E, k, seed=1000 + s, name="r4")
+        ids4, _ = oracle.router(routing.router_logits(g["tokens_decode"], E, seed=1000 + s,
+                                                      name="r4"), k)
         dist.append(len(np.unique(ids4)))
     expect = E * (1 - (1 - k / E) ** g["tokens_decode"])
     assert abs(expect - 38.84) < 0.01
@@ -344,13 +349,27 @@ def test_routing_statistics_against_printed_values():
     assert ids4.size == g["slots_decode"]
 
 
+def test_random_routing_generator_is_valid():
+    """The parity tests' routing generator: k distinct ids in range per
+    token, every expert about equally often, weights positive summing to 1."""
+    ids, w = routing.random_routing(8192, 512, 10, name="pin/rr")
+    assert ids.dtype == np.int32 and w.dtype == np.float32
+    assert ((ids >= 0) & (ids < 512)).all()
+    assert all(len(set(r)) == 10 for r in ids)
+    c = np.bincount(ids.ravel(), minlength=512)
+    assert c.sum() == 81920 and c.min() > 100 and c.max() < 230
+    assert (w > 0).all() and np.allclose(w.sum(1), 1.0, atol=1e-6)
+    ids1, _ = routing.random_routing(3, 5, 5, name="pin/rr5")
+    assert (np.sort(ids1, 1) == np.arange(5)).all()
+
+
 def test_topk_softmax_equals_full_softmax_renormalised():
     lg = routing.router_logits(64, 512, name="sm")
-    ids, w = routing.topk_softmax(lg, 10)
+    ids, w = oracle.router(lg, 10)
     full = np.exp(lg.astype(np.float64) - lg.max(1, keepdims=True))
     full /= full.sum(1, keepdims=True)
     sel = np.take_along_axis(full, ids, 1)
-    assert np.allclose(sel / sel.sum(1, keepdims=True), w, rtol=1e-6)
+    assert np.allclose(sel / sel.sum(1, keepdims=True), w, rtol=1e-12)
 
 
 # ------------------------------------------------------------ SwiGLU and MoE
@@ -361,6 +380,73 @@ def test_silu_closed_forms():
     assert s[300] == 0.0
     assert np.allclose(s - oracle.silu(-g), g, rtol=0, atol=1e-12)   # x s(x) + x s(-x) = x
     assert np.allclose(s[-1], 30.0, rtol=1e-12) and abs(s[0]) < 1e-11
+
+
+# E2M1 code of each value used below (sign in bit 3)
+_E2M1_CODE = {0.5: 1, 1.0: 2, 1.5: 3, 2.0: 4, 3.0: 5, 4.0: 6, 6.0: 7}
+
+
+def _e2m1_code(v):
+    return _E2M1_CODE[abs(v)] | (8 if v < 0 else 0)
+
+
+def _bf16_bits_by_torch(v):
+    """float64 -> float32 (struct, round to nearest) -> bfloat16 bits (torch)."""
+    import struct
+    f32 = struct.unpack("<f", struct.pack("<f", v))[0]
+    return int(torch.tensor([f32], dtype=torch.float32).to(torch.bfloat16)
+               .view(torch.int16).item()) & 0xFFFF
+
+
+def test_moe_swiglu_wiring_hand_built_expert():
+    """One hand-built MXFP4 expert with unit scales and a one-hot input, so
+    that every gate and up sum is a known exact value: gate row i holds a_i
+    and up row I + i holds b_i at column 0, x is 1 at column 0 and 0
+    elsewhere.  Then h_i = bf16(f32(silu(a_i) * b_i)) with silu(g) =
+    g / (1 + e^-g) ("TurboEXL3" section 4.1: SwiGLU in 32-bit between the
+    gate/up and down multiplies), computed here with math.exp, struct and
+    torch rounding.  The down matrix is a one-hot identity on the first I
+    outputs, so y_j = w * h_j exactly.  A gate/up swap, a missing or extra
+    rounding of h, or a wrong combine weight fails."""
+    import math
+    inter, H = 32, 128
+    pairs = [(1.0, 3.0), (-2.0, 1.5), (0.5, -4.0), (6.0, 0.5), (-1.0, -3.0), (3.0, 2.0),
+             (1.5, -6.0), (-0.5, 4.0)]
+    gu = F.empty(F.MXFP4, 2 * inter, H, 1)
+    gu.scales[:] = 127                                      # E8M0 1.0
+    q = np.zeros((2 * inter, H), np.uint8)
+    for i, (a, b) in enumerate(pairs):
+        q[i, 0] = _e2m1_code(a)
+        q[inter + i, 0] = _e2m1_code(b)
+    gu.codes[0] = F.pack_nibbles(q)
+    dn = F.empty(F.MXFP4, H, inter, 1)
+    dn.scales[:] = 127
+    qd = np.zeros((H, inter), np.uint8)
+    for j in range(inter):
+        qd[j, j] = _e2m1_code(1.0)
+    dn.codes[0] = F.pack_nibbles(qd)
+    x = np.zeros((1, H), np.uint16)
+    x[0, 0] = 0x3F80                                        # 1.0
+    ids = np.zeros((1, 1), np.int32)
+    wt = np.array([[0.5]], np.float32)
+    y, _, hs = oracle.moe(gu, dn, x, ids, wt, num_routed=1, num_shared=0)
+    h = np.asarray(hs[(0, 0)])
+    for i in range(inter):
+        a, b = pairs[i] if i < len(pairs) else (0.0, 0.0)
+        expect = _bf16_bits_by_torch(a / (1.0 + math.exp(-a)) * b)
+        assert int(h[i]) == expect, (i, hex(int(h[i])), hex(expect))
+        hv = float(torch.tensor([expect], dtype=torch.int32).to(torch.int16)
+                   .view(torch.bfloat16).float().item())
+        assert y[0, i] == 0.5 * hv
+    assert (y[0, inter:] == 0).all()
+    # the swapped wiring would give different values for every pair above,
+    # and h is not representable in bfloat16 before its rounding
+    import struct
+    for a, b in pairs:
+        f32 = struct.unpack("<f", struct.pack("<f", a / (1 + math.exp(-a)) * b))[0]
+        assert struct.unpack("<I", struct.pack("<f", f32))[0] & 0xFFFF != 0
+        assert _bf16_bits_by_torch(a / (1 + math.exp(-a)) * b) != \
+            _bf16_bits_by_torch(b / (1 + math.exp(-b)) * a)
 
 
 def test_moe_single_expert_reduces_to_two_gemvs():
@@ -384,7 +470,7 @@ def test_moe_shared_expert_and_weights_linear():
     gu = quant.synthetic_weight(F.NVFP4, 2 * inter, H, batch=E + 1, name="lgu")
     dn = quant.synthetic_weight(F.NVFP4, H, inter, batch=E + 1, name="ldn")
     x = quant.synthetic_bf16(T, H, name="lx")
-    ids, w = routing.synthetic_routing(T, E, 2, name="lr")
+    ids, w = routing.random_routing(T, E, 2, name="lr")
     y, _, hs = oracle.moe(gu, dn, x, ids, w, E, 1)
     # recompose by hand from the per-slot outputs
     for t in range(T):
@@ -454,7 +540,7 @@ def test_moe_grouping_invariants_at_prefill_size():
     """8192 tokens, top-10 of 512: the counts add to the slot total, the mean
     is the 160 rows per expert the pages derive ("TurboEXL3" section 3.1),
     every tile lies inside its expert's rows and the tiles cover them once."""
-    ids, _ = routing.synthetic_routing(8192, 512, 10, name="pin/group")
+    ids, _ = routing.random_routing(8192, 512, 10, name="pin/group")
     g = oracle.moe_grouping(ids, 512, 1)
     c = g["counts"]
     assert c[:512].sum() == 81920 and c[512] == 8192
