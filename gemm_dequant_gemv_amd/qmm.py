@@ -101,6 +101,54 @@ def _check(status: int, where: str):
         raise QmmError(status, where)
 
 
+def _tensor(where: str, name: str, t, dtypes, shape=None, device=None):
+    """Check one tensor argument before anything is launched: its dtype, its
+    shape, that it is contiguous and (when ``device`` is given) that it lives
+    on that GPU.  Raises TypeError or ValueError."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{where}: {name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        want = ", ".join(str(d) for d in dtypes)
+        raise TypeError(f"{where}: {name} has dtype {t.dtype}, expected {want}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{where}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{where}: {name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{where}: {name} is on {t.device}, expected {device}")
+
+
+def _require_gpu(where: str, dev):
+    """Checked after the dtypes and shapes: the call's tensors, which share
+    device ``dev``, must live on a GPU."""
+    if dev.type != "cuda":
+        raise ValueError(f"{where}: tensors must live on a GPU, not {dev}")
+    return dev
+
+
+def _check_gemv(where, w, x, residual, out, workspace, out_dtypes):
+    """Checks of a qgemv / qgemm call's tensors; returns (device, m)."""
+    dev = w.codes.device
+    _tensor(where, "x", x, _BF16, None, dev)
+    if x.dim() != 2 or x.shape[1] != w.k:
+        raise ValueError(f"{where}: x has shape {tuple(x.shape)}, expected (m, {w.k})")
+    m = x.shape[0]
+    if residual is not None:
+        _tensor(where, "residual", residual, _BF16, (m, w.n), dev)
+    if out is not None:
+        _tensor(where, "out", out, out_dtypes, (m, w.n), dev)
+    if workspace is not None:
+        _tensor(where, "workspace", workspace, _U8, None, dev)
+    return _require_gpu(where, dev), m
+
+
+_BF16 = (torch.bfloat16,)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+_U8 = (torch.uint8,)
+_OUT = (torch.float32, torch.bfloat16)
+
+
 class Weight:
     """A packed weight (or batch of experts) resident on the device.
 
@@ -108,9 +156,39 @@ class Weight:
     u8 [batch][n][k/4] (Q6_K), ``scales`` (format dependent), ``scales2``
     f16 [batch][n][k/256] (Q6_K), ``tensor_scale`` f32 [batch] (NVFP4)."""
 
+    # dtype of the ``scales`` plane and K values per scales element, per format
+    _SCALES = {AFFINE4_G64: (torch.float16, 32), MXFP4: (torch.uint8, 32),
+               NVFP4: (torch.uint8, 16), Q6_K: (torch.int8, 16)}
+
     def __init__(self, fmt: int, n: int, k: int, batch: int, codes, scales,
                  codes_hi=None, scales2=None, tensor_scale=None):
         self.fmt, self.n, self.k, self.batch = int(fmt), int(n), int(k), int(batch)
+        if self.fmt not in self._SCALES:
+            raise ValueError(f"Weight: unknown format {fmt}")
+        if self.n < 1 or self.k < 1 or self.batch < 1:
+            raise ValueError(f"Weight: n, k, batch must be >= 1, got {n}, {k}, {batch}")
+        rows = self.batch * self.n
+        sdt, per = self._SCALES[self.fmt]
+        q6 = self.fmt == Q6_K
+        planes = [("codes", codes, _U8, rows * self.k // 2),
+                  ("scales", scales, (sdt,), rows * self.k // per)]
+        if q6:
+            planes += [("codes_hi", codes_hi, _U8, rows * self.k // 4),
+                       ("scales2", scales2, (torch.float16,), rows * (self.k // 256))]
+        elif codes_hi is not None or scales2 is not None:
+            raise ValueError("Weight: codes_hi and scales2 belong to Q6_K only")
+        if self.fmt == NVFP4:
+            if tensor_scale is not None:
+                planes.append(("tensor_scale", tensor_scale, _F32, self.batch))
+        elif tensor_scale is not None:
+            raise ValueError("Weight: tensor_scale belongs to NVFP4 only")
+        for name, t, dts, numel in planes:
+            if t is None:
+                raise ValueError(f"Weight: plane {name} is missing")
+            _tensor("Weight", name, t, dts, device=codes.device)
+            if t.numel() != numel:
+                raise ValueError(f"Weight: plane {name} holds {t.numel()} elements, expected "
+                                 f"{numel} for format {fmt}, n={n}, k={k}, batch={batch}")
         self.codes, self.scales = codes, scales
         self.codes_hi, self.scales2, self.tensor_scale = codes_hi, scales2, tensor_scale
         self._c = QmmWeightC(self.fmt, self.n, self.k, self.batch, self.codes.data_ptr(),
@@ -141,8 +219,11 @@ class Weight:
 
 
 def dequant(w: Weight, out_dtype=torch.float32, out=None, stream=None):
+    dev = w.codes.device
     if out is None:
-        out = torch.empty((w.batch, w.n, w.k), dtype=out_dtype, device=w.codes.device)
+        out = torch.empty((w.batch, w.n, w.k), dtype=out_dtype, device=dev)
+    _tensor("qdequant", "out", out, _OUT, (w.batch, w.n, w.k), dev)
+    _require_gpu("qdequant", dev)
     dt = F32 if out.dtype == torch.float32 else BF16
     _check(_lib().qdequant(w.c, dt, _ptr(out), _stream(stream)), "qdequant")
     return out
@@ -153,7 +234,8 @@ def gemv_workspace_size(w: Weight, m: int) -> int:
 
 
 def new_workspace(nbytes: int, device="cuda"):
-    """A zero-filled workspace (the library leaves it zero-filled after each call)."""
+    """A workspace of ``nbytes`` bytes (zero-filled here, though no call needs
+    that: the library accepts any contents)."""
     if nbytes == 0:
         return None
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
@@ -162,12 +244,13 @@ def new_workspace(nbytes: int, device="cuda"):
 def gemv(w: Weight, x, residual=None, y_dtype=torch.float32, out=None, workspace=None,
          stream=None):
     """y[m][n] = sum_k w[n][k] x[m][k] (+ residual), m = x.shape[0] in 1..4."""
-    m = x.shape[0]
+    dev, m = _check_gemv("qgemv", w, x, residual, out, workspace, _OUT)
     if out is None:
-        out = torch.empty((m, w.n), dtype=y_dtype, device=x.device)
+        out = torch.empty((m, w.n), dtype=y_dtype, device=dev)
+        _tensor("qgemv", "out", out, _OUT)  # y_dtype must be float32 or bfloat16
     need = gemv_workspace_size(w, m)
     if workspace is None and need:
-        workspace = new_workspace(need, x.device)
+        workspace = new_workspace(need, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     dt = F32 if out.dtype == torch.float32 else BF16
     _check(_lib().qgemv(w.c, _ptr(x), m, _ptr(residual), _ptr(out), dt, _ptr(workspace),
@@ -177,12 +260,12 @@ def gemv(w: Weight, x, residual=None, y_dtype=torch.float32, out=None, workspace
 
 def gemm(w: Weight, x, residual=None, out=None, workspace=None, stream=None):
     """y[m][n] = bf16(sum_k w16[n][k] x[m][k] (+ residual)), x bf16 [m][k]."""
-    m = x.shape[0]
+    dev, m = _check_gemv("qgemm", w, x, residual, out, workspace, _BF16)
     if out is None:
-        out = torch.empty((m, w.n), dtype=torch.bfloat16, device=x.device)
+        out = torch.empty((m, w.n), dtype=torch.bfloat16, device=dev)
     need = int(_lib().qgemm_workspace_size(w.c, m))
     if workspace is None and need:
-        workspace = new_workspace(need, x.device)
+        workspace = new_workspace(need, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib().qgemm(w.c, _ptr(x), m, _ptr(residual), _ptr(out), _ptr(workspace), ws_bytes,
                         _stream(stream)), "qgemm")
@@ -206,12 +289,16 @@ def moe_workspace_layout(gate_up: Weight, down: Weight, num_routed: int, num_sha
 def moe(gate_up: Weight, down: Weight, x, topk_ids, topk_w, num_routed: int, num_shared: int,
         shared_w=None, y_dtype=torch.float32, out=None, workspace=None, stream=None):
     """One MoE layer; x bf16 [t][H], topk_ids int32 [t][topk], topk_w f32 [t][topk]."""
+    dev = _check_moe_routing("qmoe_grouped", gate_up, down, x, topk_ids, topk_w, shared_w, out)
     t, topk = topk_ids.shape
     if out is None:
-        out = torch.empty((t, down.n), dtype=y_dtype, device=x.device)
+        out = torch.empty((t, down.n), dtype=y_dtype, device=dev)
+        _tensor("qmoe_grouped", "out", out, _OUT)
+    if workspace is not None:
+        _tensor("qmoe_grouped", "workspace", workspace, _U8, None, dev)
     need = moe_workspace_size(gate_up, down, num_routed, num_shared, t, topk)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     dt = F32 if out.dtype == torch.float32 else BF16
     _check(_lib().qmoe_grouped(gate_up.c, down.c, num_routed, num_shared, _ptr(x), t,
@@ -220,14 +307,47 @@ def moe(gate_up: Weight, down: Weight, x, topk_ids, topk_w, num_routed: int, num
     return out
 
 
+def _moe_check(where, gate_up, down, x, shared_w):
+    dev = gate_up.codes.device
+    if down.codes.device != dev:
+        raise ValueError(f"{where}: gate_up and down weights are on different devices")
+    _tensor(where, "x", x, _BF16, None, dev)
+    if x.dim() != 2 or x.shape[1] != gate_up.k:
+        raise ValueError(f"{where}: x has shape {tuple(x.shape)}, expected (t, {gate_up.k})")
+    if shared_w is not None:
+        _tensor(where, "shared_w", shared_w, _F32, (x.shape[0],), dev)
+    return dev
+
+
+def _check_moe_routing(where, gate_up, down, x, topk_ids, topk_w, shared_w, out):
+    dev = _moe_check(where, gate_up, down, x, shared_w)
+    _tensor(where, "topk_ids", topk_ids, _I32, None, dev)
+    if topk_ids.dim() != 2 or topk_ids.shape[0] != x.shape[0]:
+        raise ValueError(f"{where}: topk_ids has shape {tuple(topk_ids.shape)}, "
+                         f"expected ({x.shape[0]}, topk)")
+    _tensor(where, "topk_w", topk_w, _F32, tuple(topk_ids.shape), dev)
+    if out is not None:
+        _tensor(where, "out", out, _OUT, (x.shape[0], down.n), dev)
+    return _require_gpu(where, dev)
+
+
 def moe_router(logits, topk: int, ids=None, w=None, stream=None):
     """Router top-k and softmax: logits float32 [t][E] -> (ids int32 [t][topk],
     weights float32 [t][topk])."""
+    _tensor("qmoe_router", "logits", logits, _F32)
+    if logits.dim() != 2:
+        raise ValueError(f"qmoe_router: logits must be 2-D [t][E], got {tuple(logits.shape)}")
+    dev = logits.device
     t, e = logits.shape
+    if ids is not None:
+        _tensor("qmoe_router", "ids", ids, _I32, (t, topk), dev)
+    if w is not None:
+        _tensor("qmoe_router", "w", w, _F32, (t, topk), dev)
+    _require_gpu("qmoe_router", dev)
     if ids is None:
-        ids = torch.empty((t, topk), dtype=torch.int32, device=logits.device)
+        ids = torch.empty((t, topk), dtype=torch.int32, device=dev)
     if w is None:
-        w = torch.empty((t, topk), dtype=torch.float32, device=logits.device)
+        w = torch.empty((t, topk), dtype=torch.float32, device=dev)
     _check(_lib().qmoe_router(_ptr(logits), t, e, topk, _ptr(ids), _ptr(w), _stream(stream)),
            "qmoe_router")
     return ids, w
@@ -238,14 +358,22 @@ def moe_from_logits(gate_up: Weight, down: Weight, x, logits, topk: int, num_rou
                     workspace=None, stream=None):
     """One MoE layer from router logits float32 [t][num_routed]; returns (y,
     ids, weights)."""
-    t = logits.shape[0]
+    dev = _moe_check("qmoe_grouped_logits", gate_up, down, x, shared_w)
+    t = x.shape[0]
+    _tensor("qmoe_grouped_logits", "logits", logits, _F32, (t, num_routed), dev)
+    if out is not None:
+        _tensor("qmoe_grouped_logits", "out", out, _OUT, (t, down.n), dev)
+    if workspace is not None:
+        _tensor("qmoe_grouped_logits", "workspace", workspace, _U8, None, dev)
+    _require_gpu("qmoe_grouped_logits", dev)
     if out is None:
-        out = torch.empty((t, down.n), dtype=y_dtype, device=x.device)
-    ids = torch.empty((t, topk), dtype=torch.int32, device=x.device)
-    w = torch.empty((t, topk), dtype=torch.float32, device=x.device)
+        out = torch.empty((t, down.n), dtype=y_dtype, device=dev)
+        _tensor("qmoe_grouped_logits", "out", out, _OUT)
+    ids = torch.empty((t, topk), dtype=torch.int32, device=dev)
+    w = torch.empty((t, topk), dtype=torch.float32, device=dev)
     need = moe_workspace_size(gate_up, down, num_routed, num_shared, t, topk)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     dt = F32 if out.dtype == torch.float32 else BF16
     _check(_lib().qmoe_grouped_logits(gate_up.c, down.c, num_routed, num_shared, _ptr(x), t,
@@ -256,6 +384,7 @@ def moe_from_logits(gate_up: Weight, down: Weight, x, logits, topk: int, num_rou
 
 
 def workspace_init(ws, stream=None):
+    _tensor("qworkspace_init", "ws", ws, _U8)
     _check(_lib().qworkspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "qworkspace_init")
 
@@ -281,6 +410,7 @@ class PreparedGemv:
     the kernel on the stream given here (the current stream by default)."""
 
     def __init__(self, w: Weight, x, out, residual=None, workspace=None, stream=None):
+        _check_gemv("qgemv", w, x, residual, out, workspace, _OUT)
         self.w, self.x, self.out, self.residual, self.workspace = w, x, out, residual, workspace
         need = gemv_workspace_size(w, x.shape[0])
         if need and workspace is None:
@@ -314,7 +444,7 @@ class _Prepared:
 
 
 def prepare_gemm(w: Weight, x, out, residual=None, stream=None):
-    m = x.shape[0]
+    _, m = _check_gemv("qgemm", w, x, residual, out, None, _BF16)
     need = int(_lib().qgemm_workspace_size(w.c, m))
     ws = new_workspace(need, x.device) if need else None
     ws_bytes = 0 if ws is None else ws.numel()
@@ -324,6 +454,7 @@ def prepare_gemm(w: Weight, x, out, residual=None, stream=None):
 
 def prepare_moe(gate_up: Weight, down: Weight, x, topk_ids, topk_w, num_routed: int,
                 num_shared: int, out, shared_w=None, stream=None):
+    _check_moe_routing("qmoe_grouped", gate_up, down, x, topk_ids, topk_w, shared_w, out)
     t, topk = topk_ids.shape
     need = moe_workspace_size(gate_up, down, num_routed, num_shared, t, topk)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
