@@ -186,6 +186,8 @@ int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, v
   if (w->k % 64 != 0) return QMM_ERR_SHAPE;
   if (workspace && !aligned(workspace, 256)) return QMM_ERR_ALIGN;
   if (m < 1) return QMM_ERR_M_RANGE;
+  // the kernel addresses x and the weight planes with 32-bit offsets
+  if (!qmm::gemm_big_fits(*w, (size_t)m)) return QMM_ERR_SHAPE;
   if (!x || !y) return QMM_ERR_NULL;
   if (!aligned(x, 16) || !aligned(y, 16) || (residual && !aligned(residual, 16)))
     return QMM_ERR_ALIGN;
@@ -203,7 +205,7 @@ int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, v
       if (overlap(rw, ins[i])) return QMM_ERR_ALIAS;
   }
   return hip_status(
-      qmm::launch_gemm(*w, x, m, residual, y, workspace, workspace_bytes, (hipStream_t)stream));
+      qmm::launch_gemm_big(*w, x, m, residual, y, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
 size_t qmoe_workspace_size(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
@@ -255,6 +257,11 @@ int qmoe_grouped_check(const qmm_weight *gate_up, const qmm_weight *down, int32_
   if (gate_up->n % 128 != 0 || down->k != inter || down->n != gate_up->k) return QMM_ERR_SHAPE;
   if (gate_up->k % 64 != 0 || down->k % 64 != 0) return QMM_ERR_SHAPE;
   if (y_dtype != QMM_F32 && y_dtype != QMM_BF16) return QMM_ERR_DTYPE;
+  // the grouped form addresses x, h and the weight planes with 32-bit offsets
+  if (!qmm::moe_uses_gemv(*gate_up, *down, t, topk, num_shared) &&
+      !(qmm::gemm_big_fits(*gate_up, (size_t)t) &&
+        qmm::gemm_big_fits(*down, (size_t)t * (size_t)(topk + num_shared))))
+    return QMM_ERR_SHAPE;
   if (!x || !topk_ids || !topk_w || !y) return QMM_ERR_NULL;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
       (shared_w && !aligned(shared_w, 4)))

@@ -1,8 +1,6 @@
-// qgemm with 256-row weight tiles, for prefill with many activation rows
-// (dense mode).  Same arithmetic as gemm.hip -- each weight decoded once per
-// tile into bfloat16 ("TurboEXL3" section 4.1: decode once, multiply many
-// times), bf16 MFMA with float32 sums over K in slice order -- on a different
-// data path:
+// qgemm and the grouped MoE multiplies: each weight decoded once per tile into
+// bfloat16 ("TurboEXL3" section 4.1: decode once, multiply many times), bf16
+// MFMA with float32 sums over K in slice order, on this data path:
 //
 //   * the activation tile (32 TM rows) goes from memory straight into LDS
 //     (buffer_load_dwordx4 ... lds), three 64-wide K slices in flight, with no
@@ -26,8 +24,8 @@
 //
 // Per slice and wave (dense, TM = 8): 32 MFMAs, 32 decoded weights per lane,
 // 32 KB of LDS operand reads; per workgroup 32 KB of activations and 9-14 KB
-// of weight codes from memory, about half of what the 128 x 128 tiles of
-// gemm.hip move per flop.  (The 32 x 32 x 16 form against the 16 x 16 x 32
+// of weight codes from memory, about half of what 128 x 128 tiles staged
+// through LDS moved per flop.  (The 32 x 32 x 16 form against the 16 x 16 x 32
 // one, same tiles: 3-15% faster up to 512 rows, the same from 2048 on, where
 // the matrix cores' clock sets the pace: with random operands a bare MFMA
 // loop runs both at ~1.75 PFLOP/s on MI355X, the clock falling to ~1.8 GHz.)
@@ -98,7 +96,7 @@ constexpr int w_loads_per_run() { return FMT == QMM_Q6_K ? 4 : 2; }
 
 // A wave owns 32 rows of W and computes them against the workgroup's BM =
 // 32 TM rows of X as TM v_mfma_f32_32x32x16_bf16 tiles; the WAVES waves cover
-// BN = 32 WAVES rows of W.  MODE as in gemm.hip: dense, or the grouped MoE
+// BN = 32 WAVES rows of W.  MODE (gemm_common.h): dense, or the grouped MoE
 // gate/up (rows of x gathered by token, gate and up weight rows interleaved,
 // SwiGLU epilogue) and down products over the routing tile table (tiles of BM
 // grouped rows, one expert each).
@@ -325,7 +323,6 @@ void gemm_big_kernel(GemmArgs a) {
           for (int r = 0; r < 4; ++r) acc[t][4 * b + r] = v[r];
         }
       }
-      if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   const float gs = (FMT == QMM_NVFP4 && a.tensor_scale) ? a.tensor_scale[expert] : 1.0f;
@@ -481,6 +478,10 @@ size_t gemm_big_workspace(const qmm_weight &w, int m) {
   return split_counters_bytes(w, m) + (size_t)sk * m * w.n * 4;
 }
 
+size_t gemm_workspace_size(const qmm_weight &w, int m) {
+  return gemm_big_fits(w, (size_t)m) ? gemm_big_workspace(w, m) : 0;
+}
+
 bool gemm_big_fits(const qmm_weight &w, size_t x_rows) {
   // 32-bit buffer offsets for X and every weight plane
   return x_rows * (size_t)w.k * 2 < (1ull << 32) && (size_t)w.batch * w.n * w.k < (1ull << 32);
@@ -503,8 +504,8 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
   // takes about 0.85 of a 256-row one): M = 2048 at 17408 rows is 544
   // workgroups of 256 (2.1 rounds) or 748 of 192 (2.9 rounds), measured 1.14x
   // faster; M = 300 and 512 1.2x, M >= 3072 no gain.  Up to 256 rows of X: 4 waves of 32 x 128, whose 128-row W tiles
-  // give a 128-row call 136 workgroups (1.9x faster than the LDS-staged kernel
-  // at M = 128, 1.4x at M = 256).
+  // give a 128-row call 136 workgroups (1.9x faster than 128 x 128 tiles
+  // staged through LDS at M = 128, 1.4x at M = 256).
   int cfg = 1;
   if (m > 256) {
     const long nt = (w.n + bn_of(8) - 1) / bn_of(8), cus = compute_units();
@@ -523,6 +524,10 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
     a.sps = (w.k / kBK + sk - 1) / sk;
     a.counters = (uint32_t *)workspace;
     a.partials = (float *)((char *)workspace + split_counters_bytes(w, m));
+    // the workspace may hold anything: the tile counters start from zero,
+    // cleared by a kernel ahead of the split launch on the same stream
+    const hipError_t e = launch_zero(workspace, split_counters_bytes(w, m), s);
+    if (e != hipSuccess) return e;
   }
   int tm = small_m_tile(m);
 #ifdef QMM_TUNE

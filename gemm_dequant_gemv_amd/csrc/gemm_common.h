@@ -1,5 +1,5 @@
-// Pieces shared by the two GEMM kernels: the argument block, the 32-weight
-// piece loads and their decode to bfloat16 pairs.
+// Pieces of the GEMM kernels: the argument block, the 32-weight piece loads
+// and their decode to bfloat16 pairs.
 #pragma once
 
 #include "qmm_device.h"
@@ -38,7 +38,7 @@ struct GemmArgs {
   // leaves float32 partials; the last of a tile's splits adds them in order
   int splits, sps;
   float *partials;     // [splits][m][n]
-  uint32_t *counters;  // [tiles], zero between calls
+  uint32_t *counters;  // [tiles], cleared ahead of each split launch
   int wrows;                     // rows of the weight planes (all experts)
   // grouped (MoE) modes
   const uint32_t *tiles;         // [max_tiles][3] = (expert, first grouped row, rows)

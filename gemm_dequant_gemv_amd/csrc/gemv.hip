@@ -34,7 +34,10 @@
 // Products are v_dot2_f32_bf16 (two bf16 products + fp32 accumulate).  The 8
 // lanes of a row are reduced with cross-lane shuffles at the end; with K split
 // over several workgroups each writes float32 partial sums and the last one to
-// arrive adds them in split order, so results do not depend on timing.
+// arrive adds them in split order, so results do not depend on timing.  The
+// per-tile arrival counters live at the head of the caller's workspace and
+// are cleared by a small kernel ahead of each split launch, so the workspace
+// needs no particular contents on entry.
 #include <algorithm>
 #include <cstdlib>
 
@@ -361,7 +364,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     else
       ((float *)a.y)[(size_t)m * a.n + row] = v;
   }
-  if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int FMT, int M, int R>
@@ -477,6 +479,12 @@ hipError_t launch_gemv(const qmm_weight &w, const void *x, int m, const void *re
   a.y = y;
   a.counters = (uint32_t *)workspace;
   a.partials = workspace ? (float *)((char *)workspace + p.counters_bytes) : nullptr;
+  if (p.splits > 1) {
+    // the workspace may hold anything: the tile counters start from zero,
+    // cleared by a kernel ahead of the split launch on the same stream
+    const hipError_t e = launch_zero(workspace, p.counters_bytes, s);
+    if (e != hipSuccess) return e;
+  }
   a.n = w.n;
   a.k = w.k;
   a.steps = p.steps;

@@ -365,12 +365,10 @@ size_t align_up(size_t v) { return (v + 255) / 256 * 256; }
 // topk / E), from 32 to 256: tokens spread over many experts leave each with
 // a few rows, and a 256-row tile (the grouped GEMMs' tallest) would be almost
 // all padding.  Measured on the 512-expert layer (T = 5 .. 64: 97 .. 532 us
-// per layer with 256-row tiles).  The LDS-staged kernel (where 32-bit offsets
-// do not reach) takes 256-row tiles only.
+// per layer with 256-row tiles).
 int moe_tile_rows(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_routed) {
-  const size_t rows = (size_t)t * (topk + (gu.batch - num_routed));
-  const bool big = gemm_big_fits(gu, (size_t)t) && gemm_big_fits(dn, rows) && (gu.n / 2) % 2 == 0;
-  if (!big) return kMoeTileRows;
+  (void)gu;
+  (void)dn;
   const double avg = (double)t * topk / num_routed;
   int tr = 32;
   while (tr < kMoeTileRows && tr < 2.0 * avg) tr *= 2;
@@ -472,19 +470,11 @@ hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // 256-row weight tiles decoded straight into MFMA operands (gemm_big.hip)
-    // where their 32-bit offsets reach; the LDS-staged 128 x 128 tiles else
-    bool big = gemm_big_fits(gu, (size_t)t) && gemm_big_fits(dn, L.max_rows) && (gu.n / 2) % 2 == 0;
-#ifdef QMM_TUNE
-    if (const char *ev = getenv("QMM_MOE_BIG")) big = big && atoi(ev) != 0;
-#endif
-    big = big && L.tile_rows <= (size_t)kMoeTileRows;
-    if (!big && L.tile_rows != (size_t)kMoeTileRows) return hipErrorInvalidValue;  // not reached
-    e = big ? launch_moe_big_gate_up(gu, x, tb, (int)L.max_tiles, (int)L.tile_rows, s)
-            : launch_moe_gemm_gate_up(gu, x, tb, (int)L.max_tiles, s);
+    // weight tiles decoded straight into MFMA operands (gemm_big.hip; the host
+    // checks reject calls whose 32-bit offsets it would not reach)
+    e = launch_moe_big_gate_up(gu, x, tb, (int)L.max_tiles, (int)L.tile_rows, s);
     if (e != hipSuccess) return e;
-    e = big ? launch_moe_big_down(dn, tb, (int)L.max_tiles, (int)L.tile_rows, s)
-            : launch_moe_gemm_down(dn, tb, (int)L.max_tiles, s);
+    e = launch_moe_big_down(dn, tb, (int)L.max_tiles, (int)L.tile_rows, s);
     if (e != hipSuccess) return e;
   }
 

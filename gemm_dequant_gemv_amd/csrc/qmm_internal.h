@@ -39,10 +39,8 @@ GemvPlan plan_gemv(int format, int n, int k, int m);
 bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p);
 size_t gemv_rows_lds(int format, int k, int m);
 
-// Prefill GEMM / grouped MoE tiles: rows of activations per workgroup.
-constexpr int kGemmBM = 128;
 // rows per tile of the MoE routing table (the grouped GEMMs' activation tiles)
-constexpr int kMoeTileRows = 256;  // routing tile rows at most (the LDS-staged kernel's height)
+constexpr int kMoeTileRows = 256;  // routing tile rows at most (the grouped GEMMs' tallest X tile)
 // Experts (routed + shared) one MoE call may have.
 constexpr int kMoeMaxExperts = 4096;
 
@@ -93,13 +91,7 @@ hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const Moe
                                   int max_tiles, int tile_rows, hipStream_t s);
 hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
                                int tile_rows, hipStream_t s);
-hipError_t launch_gemm(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
-                       void *workspace, size_t workspace_bytes, hipStream_t s);
 size_t gemm_workspace_size(const qmm_weight &w, int m);
-hipError_t launch_moe_gemm_gate_up(const qmm_weight &gu, const void *x, const MoeTables &t,
-                                   int max_tiles, hipStream_t s);
-hipError_t launch_moe_gemm_down(const qmm_weight &dn, const MoeTables &t, int max_tiles,
-                                hipStream_t s);
 // decode form of qmoe_grouped: grouped GEMV over token slots (t <= 16 and
 // at most kMoeGemvMaxSlots slots, when the staged vectors fit in LDS)
 constexpr int kMoeGemvMaxTokens = 16;

@@ -53,10 +53,12 @@
  * scales.  No C++ exception crosses this interface.
  *
  * Workspaces.  Calls that split a reduction across workgroups take a caller-
- * owned workspace of at least *_workspace_size() bytes, 256-byte aligned.  It
- * must be zero-filled once before its first use (qworkspace_init, hipMemset or
- * torch.zeros); every call leaves it zero-filled again on the stream.  One
- * workspace serves one call at a time: calls that may overlap need their own.
+ * owned workspace of at least *_workspace_size() bytes, 256-byte aligned.  Its
+ * contents on entry do not matter and it needs no zero-fill: a call that uses
+ * it writes everything it later reads, and the arrival counters of a split
+ * reduction are cleared by a small kernel of the call's own, on its stream,
+ * before the split launch.  One workspace serves one call at a time: calls
+ * that may overlap (other streams) need their own.
  *
  * Determinism.  Every sum runs in a fixed order and no floating-point atomics
  * are used, so the same inputs give bitwise identical outputs on every run
@@ -120,11 +122,17 @@ typedef struct qmm_weight {
 } qmm_weight;
 
 /*
- * qdequant -- expand every weight of every matrix of `w` to out[batch][n][k].
+ * qdequant -- expand every weight of every matrix of `w` to out[batch][n][k]
+ * ("TurboEXL3", section 4.3: past the GEMM paths' row counts the weights are
+ * decoded to 16 bits and handed to a plain matrix multiply; section 2.1 for
+ * each format's dequantization).
  * out_dtype QMM_F32: the exact weight rounded once to nearest float32; for
  * AFFINE4_G64 that is fma(s, q, b), for NVFP4 (e2m1*e4m3)*g; MXFP4 and Q6_K are
- * exact.  QMM_BF16: that float32 rounded to nearest-even bfloat16.  Used for
- * bit-exact checks of the decoders and as a decode-then-multiply building block.
+ * exact.  QMM_BF16: that float32 rounded to nearest-even bfloat16.
+ * out  device, 16-byte aligned, batch*n*k elements of 4 (F32) or 2 (BF16)
+ *      bytes; must not overlap the weight planes (QMM_ERR_ALIAS).
+ * Used for bit-exact checks of the decoders and as a decode-then-multiply
+ * building block.  No workspace.
  */
 int qdequant(const qmm_weight *w, int32_t out_dtype, void *out, void *stream);
 
@@ -184,19 +192,21 @@ int qbench_mfma_peak(int32_t iters, int32_t blocks, void *sink, double *flops, v
  * affine and Q6_K values are rounded to nearest even, a relative error of at
  * most 2^-9 per weight), summed in float32 on the matrix cores.
  *
- * w         one matrix (batch must be 1); k must be a multiple of 64
- * x         bf16 [m][k], m >= 1 (tuned for m >= 128)
+ * w         one matrix (batch must be 1); k must be a multiple of 64; fewer
+ *           than 2^32 weights (QMM_ERR_SHAPE otherwise)
+ * x         bf16 [m][k], m >= 1 (tuned for m >= 128); m * k * 2 < 4 GiB
+ *           (QMM_ERR_SHAPE otherwise: x is addressed with 32-bit offsets)
  * residual  bf16 [m][n] or NULL
  * y         bf16 [m][n], rounded to nearest even
  * x, y and residual must be 16-byte aligned.
  * workspace  optional.  For calls of up to 32 rows, qgemm_workspace_size
- *            returns the bytes (256-byte aligned, zero-filled once, left
- *            zero-filled) with which the call splits K over several
- *            workgroups: each writes float32 partial sums and the last of a
- *            tile's workgroups adds them in split order (a fixed order, so
- *            results are the same on every run; they differ from an unsplit
- *            call's only in summation order).  With a NULL or smaller
- *            workspace the call runs unsplit.  Above 32 rows it returns 0.
+ *            returns the bytes (256-byte aligned, any contents) with which
+ *            the call splits K over several workgroups: each writes float32
+ *            partial sums and the last of a tile's workgroups adds them in
+ *            split order (a fixed order, so results are the same on every
+ *            run; they differ from an unsplit call's only in summation
+ *            order).  With a NULL or smaller workspace the call runs
+ *            unsplit.  Above 32 rows it returns 0.
  */
 size_t qgemm_workspace_size(const qmm_weight *w, int32_t m);
 int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, void *y,
@@ -226,6 +236,9 @@ int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, v
  * y            [t][H], float32 (QMM_F32) or bf16 rounded to nearest even (QMM_BF16)
  * workspace    at least qmoe_workspace_size(...) bytes, 256-byte aligned; it holds
  *              the routing tables, h and d.  No zero-fill is needed.
+ * The grouped form addresses x, h and the weight planes with 32-bit offsets:
+ * t * H * 2 and t * (topk + S) * I * 2 must stay below 4 GiB and each weight
+ * below 2^32 elements (QMM_ERR_SHAPE otherwise).
  * The gate/up and down weights may use different formats.
  *
  * Two forms, the same result contract: up to 16 tokens with at most 128 token
@@ -326,7 +339,9 @@ typedef struct {
 int qmoe_workspace_layout(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
                           int32_t num_shared, int32_t t, int32_t topk, qmoe_layout *out);
 
-/* Zero-fill a workspace on `stream` (a kernel, not a memset node). */
+/* Zero-fill a workspace on `stream` (a kernel, not a memset node).  No call
+ * needs it: workspaces may hold anything on entry.  For callers that want a
+ * known state, e.g. to compare workspaces between runs. */
 int qworkspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static description of a status code. */
