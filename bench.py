@@ -24,12 +24,14 @@ own configurations and reported under "sections" (each with its own unit):
     prefill  X [M][5120] x W 17408 x 5120, affine4_g64 and nvfp4,
              M in 128, 512, 2048, 8192 -> TFLOP/s (2 M N K per launch)
     moe      512 routed + 1 shared expert, hidden 2048, intermediate 512,
-             nvfp4, top-10 of softmaxed N(0, 1) logits, T = 4 and 8192
+             nvfp4, top-10 of N(0, 1) logits by the library's router, T = 4
+             (warm and cold) and 8192
     fp4      mxfp4 and nvfp4 matvecs (1% outliers at 8x), 5120 x 5120,
              5120 x 6144 and 248320 x 5120, M = 1..4 -> weight GB/s
 
-Prints one JSON line.  The oracle (CPU, float64) is timed on a bounded sample
-of the decode workload for the cpu_baseline field.
+Prints one JSON line.  The oracle (CPU, float64) is timed on bounded samples
+of the decode, prefill and MoE workloads for the cpu_baseline field (all BLAS
+threads and one thread; the host's core count and CPU model are recorded).
 
 --record-traffic turns two rocprofv3 counter CSVs (FETCH_SIZE, then
 WRITE_SIZE, each from `rocprofv3 --pmc <counter> --output-format csv -- python3
@@ -66,7 +68,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--sections", default="decode,prefill,moe,fp4")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     return ap.parse_args()
@@ -214,24 +216,36 @@ def record_traffic(fetch_csv, write_csv):
     print(json.dumps(rec))
 
 
-def cpu_baseline(cases, seconds):
-    """The oracle as it stands, on sampled rows of the same matrices: passes
-    over the decode cases, 1024 rows of each matrix per pass (a new row block
-    each pass), until `seconds` of oracle time have been spent."""
-    import oracle
-    from synth import quant
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = 1
-    t_total, bytes_total, rows_done, calls = 0.0, 0, 0, 0
-    rows = 1024
-    p_idx = 0
+        return 1
+
+
+def _decode_leg(cases, seconds, tag):
+    """Oracle GEMVs on 1024-row blocks of the decode matrices (a new block
+    each pass) until `seconds` of oracle time: (GB/s of packed weights,
+    calls, rows, bytes, time)."""
+    import oracle
+    from synth import quant
+    t_total, bytes_total, rows_done, calls, p_idx, rows = 0.0, 0, 0, 0, 0, 1024
     while t_total < seconds:
         for c in cases:
             name = f"bench/{c['tag']}/{c['fmt']}"
-            p = quant.synthetic_weight(c["fmt"], rows, c["k"], name=f"{name}/cpu{p_idx}")
+            p = quant.synthetic_weight(c["fmt"], rows, c["k"], name=f"{name}/cpu{tag}{p_idx}")
             x = quant.synthetic_bf16(c["m"], c["k"], name=name + "/x")
             r = quant.synthetic_bf16(c["m"], rows, name=name + "/r") if c["residual"] else None
             t0 = time.perf_counter()
@@ -243,11 +257,80 @@ def cpu_baseline(cases, seconds):
             if t_total >= seconds:
                 break
         p_idx += 1
-    gbs = bytes_total / t_total / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{rows}-row blocks of the decode matrices ({calls} oracle calls, "
-                      f"{rows_done} rows, {bytes_total / 1e6:.1f} MB of packed weights), "
-                      f"float64 numpy oracle, {t_total:.1f} s of oracle time"}
+    return bytes_total / t_total / 1e9, calls, rows_done, bytes_total, t_total
+
+
+def _prefill_leg(seconds):
+    """Oracle GEMM of 128 activation rows against 256-row blocks of the
+    17408 x 5120 affine prefill matrix: GFLOP/s."""
+    import oracle
+    from synth import formats as F
+    from synth import quant
+    m, rows, k = 128, 256, 5120
+    x = quant.synthetic_bf16(m, k, name="bench/prefill/x128")
+    t_total, flops, blocks = 0.0, 0.0, 0
+    while t_total < seconds:
+        p = quant.synthetic_weight(F.AFFINE4_G64, rows, k, name=f"bench/prefill/cpu{blocks}")
+        t0 = time.perf_counter()
+        oracle.gemm(p, x)
+        t_total += time.perf_counter() - t0
+        flops += 2.0 * m * rows * k
+        blocks += 1
+    return flops / t_total / 1e9, blocks, t_total
+
+
+def _moe_leg(seconds):
+    """The oracle's MoE layer on 4 tokens, top-10 routed + 1 shared expert of
+    the hidden 2048 / intermediate 512 NVFP4 shape, over a pool of 32 routed
+    experts (the per-token work is the full layer's; only the pool of
+    weights it draws from is smaller): tokens/s."""
+    import oracle
+    from synth import formats as F
+    from synth import quant, routing
+    E, S, H, I, T, topk = 32, 1, 2048, 512, 4, 10
+    gu = quant.synthetic_weight(F.NVFP4, 2 * I, H, batch=E + S, name="bench/moe/cpu_gu")
+    dn = quant.synthetic_weight(F.NVFP4, H, I, batch=E + S, name="bench/moe/cpu_dn")
+    t_total, tokens, calls = 0.0, 0, 0
+    while t_total < seconds:
+        x = quant.synthetic_bf16(T, H, name=f"bench/moe/cpu_x{calls}")
+        ids, w = oracle.router(routing.router_logits(T, E, name=f"bench/moe/cpu_r{calls}"), topk)
+        t0 = time.perf_counter()
+        oracle.moe(gu, dn, x, ids, w.astype(np.float32), E, S)
+        t_total += time.perf_counter() - t0
+        tokens += T
+        calls += 1
+    return tokens / t_total, calls, t_total
+
+
+def cpu_baseline(cases, seconds):
+    """The oracle as it stands (float64 numpy; its matrix products use the
+    BLAS thread pool), timed on bounded samples of the workloads, on this
+    host's cores.  value = the decode leg's GB/s of packed weights with every
+    BLAS thread; beside it the same leg on one thread, a prefill GEMM leg and
+    an MoE layer leg."""
+    threads = _blas_threads()
+    gbs, calls, rows_done, bytes_total, t_dec = _decode_leg(cases, 0.45 * seconds, "a")
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            gbs1, calls1, _, _, t1 = _decode_leg(cases, 0.2 * seconds, "b")
+    except Exception:
+        gbs1, calls1, t1 = None, 0, 0.0
+    gf, blocks, t_pre = _prefill_leg(0.15 * seconds)
+    tok, mcalls, t_moe = _moe_leg(0.2 * seconds)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"decode leg: 1024-row blocks of the decode matrices ({calls} oracle calls, "
+                      f"{rows_done} rows, {bytes_total / 1e6:.1f} MB of packed weights, "
+                      f"{t_dec:.1f} s), float64 numpy oracle, {threads} BLAS threads",
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
+            "one_thread": {"value": None if gbs1 is None else round(gbs1, 4), "unit": "GB/s",
+                           "sample": f"decode leg again on 1 thread ({calls1} calls, {t1:.1f} s)"},
+            "prefill": {"value": round(gf, 3), "unit": "GFLOP/s",
+                        "sample": f"128 x 5120 bf16 activations against {blocks} blocks of 256 rows "
+                                  f"of the 17408 x 5120 affine4_g64 matrix ({t_pre:.1f} s)"},
+            "moe": {"value": round(tok, 2), "unit": "tokens/s",
+                    "sample": f"{mcalls} layers of 4 tokens, top-10 of 32 routed + 1 shared "
+                              f"NVFP4 experts, hidden 2048, intermediate 512 ({t_moe:.1f} s)"}}
 
 
 FMT_NAME = {1: "affine4_g64", 2: "mxfp4", 3: "nvfp4", 4: "q6_k"}
@@ -284,31 +367,54 @@ def prefill_section(q, torch, dev):
 
 
 def moe_section(q, torch, dev):
+    """The MoE layer on the GPU.  Routing comes from the library's own router
+    (qmoe_router) on N(0, 1) logits, as a model would run it.
+
+    T = 4 is timed two ways: warm (the same call back to back, so the ~72 MB
+    of touched experts can stay in the 256 MB Infinity Cache) and cold (calls
+    rotate over 8 device copies of the layer's weights and 16 routings, so
+    that about 500 MB of other expert weights pass between two reads of the
+    same bytes)."""
     from synth import formats as F
     from synth import quant, routing
     E, S, H, I, topk = 512, 1, 2048, 512, 10
     gu_p = quant.synthetic_weight(F.NVFP4, 2 * I, H, batch=E + S, name="bench/moe/gate_up")
     dn_p = quant.synthetic_weight(F.NVFP4, H, I, batch=E + S, name="bench/moe/down")
     gu, dn = q.Weight.from_host(gu_p, dev), q.Weight.from_host(dn_p, dev)
+    del gu_p, dn_p
     per_expert = (gu.nbytes() + dn.nbytes()) / (E + S)
+    copies, n_route = 8, 16
+
+    def clone(w):
+        return q.Weight(w.fmt, w.n, w.k, w.batch, w.codes.clone(), w.scales.clone(), None, None,
+                        w.tensor_scale.clone())
+
     out = []
     for T, ydt in ((4, torch.float32), (8192, torch.bfloat16)):
         x = dev_bf16(torch, quant.synthetic_bf16(T, H, name=f"bench/moe/x{T}"), dev)
-        ids, wts = routing.synthetic_routing(T, E, topk, name=f"bench/moe/r{T}")
+        lg = torch.from_numpy(routing.router_logits(T, E, name=f"bench/moe/r{T}")).to(dev)
+        ids, wts = q.moe_router(lg, topk)
         y = torch.empty((T, H), dtype=ydt, device=dev)
-        call = q.prepare_moe(gu, dn, x, torch.from_numpy(ids).to(dev),
-                             torch.from_numpy(wts).to(dev), E, S, y)
+        call = q.prepare_moe(gu, dn, x, ids, wts, E, S, y)
         med, _ = timed(torch, call, 20 if T == 4 else 8)
+        layout = q.moe_workspace_layout(gu, dn, E, S, T, topk)
+        decode_form = layout["slot_rows"] == 1
+        if decode_form:
+            launches = 2
+        else:
+            launches = 3 + (1 if T * topk <= 16384 else 3)  # route, gate/up, down, combine
         rows = T * (topk + S)
         flops = 2.0 * rows * (2 * I * H + H * I)
-        active = len(np.unique(ids)) + S
+        active = len(np.unique(ids.cpu().numpy())) + S
         c = {"tokens": T, "ms": round(med, 4), "rows": rows, "active_experts": int(active),
              "TFLOPs": round(flops / (med * 1e-3) / 1e12, 2),
              "active_weight_GBps": round(active * per_expert / (med * 1e-3) / 1e9, 1),
-             "y_dtype": "bf16" if ydt == torch.bfloat16 else "f32"}
+             "y_dtype": "bf16" if ydt == torch.bfloat16 else "f32",
+             "form": "decode (grouped GEMV over token slots)" if decode_form else
+                     "grouped (route, gate/up GEMM, down GEMM, combine)",
+             "launches": launches, "routing": "qmoe_router on N(0, 1) logits"}
         # the router's top-k and softmax on the GPU (qmoe_router) for the same
         # tokens, timed alone, and the layer from router logits (router + layer)
-        lg = torch.from_numpy(routing.router_logits(T, E, name=f"bench/moe/r{T}")).to(dev)
         rid = torch.empty((T, topk), dtype=torch.int32, device=dev)
         rw = torch.empty((T, topk), dtype=torch.float32, device=dev)
         rmed, _ = timed(torch, lambda: q.moe_router(lg, topk, rid, rw), 20)
@@ -317,9 +423,37 @@ def moe_section(q, torch, dev):
         lmed, _ = timed(torch, lambda: q.moe_from_logits(gu, dn, x, lg, topk, E, S, y_dtype=ydt,
                                                          out=y, workspace=ws), 20 if T == 4 else 8)
         c["ms_from_logits"] = round(lmed, 4)
+        if T == 4:
+            c["ms_warm"] = c["ms"]
+            wcopies = [(gu, dn)] + [(clone(gu), clone(dn)) for _ in range(copies - 1)]
+            lgs = [torch.from_numpy(routing.router_logits(T, E, name=f"bench/moe/cold{j}")).to(dev)
+                   for j in range(n_route)]
+            routes = [q.moe_router(g, topk) for g in lgs]
+            calls = [q.prepare_moe(wcopies[j % copies][0], wcopies[j % copies][1], x, routes[j][0],
+                                   routes[j][1], E, S, y) for j in range(n_route)]
+            it = iter(range(1 << 30))
+            cmed, _ = timed(torch, lambda: calls[next(it) % n_route](), 4 * n_route)
+            it2 = iter(range(1 << 30))
+            ws2 = torch.empty(q.moe_workspace_size(gu, dn, E, S, T, topk), dtype=torch.uint8,
+                              device=dev)
+
+            def from_logits_cold():
+                j = next(it2) % n_route
+                q.moe_from_logits(wcopies[j % copies][0], wcopies[j % copies][1], x, lgs[j], topk,
+                                  E, S, y_dtype=ydt, out=y, workspace=ws2)
+
+            clmed, _ = timed(torch, from_logits_cold, 4 * n_route)
+            act = [len(np.unique(r[0].cpu().numpy())) + S for r in routes]
+            c["ms_cold"] = round(cmed, 4)
+            c["ms_from_logits_cold"] = round(clmed, 4)
+            c["active_weight_GBps_cold"] = round(float(np.mean(act)) * per_expert / (cmed * 1e-3) / 1e9, 1)
+            c["cold_rotation"] = (f"{copies} device copies of the layer's weights x {n_route} "
+                                  "routings, one call each in turn")
+            del wcopies, calls, routes, lgs, ws2
+            torch.cuda.empty_cache()
         out.append(c)
         del x, y, call, lg, ws
-    return {"unit": "ms per layer", "launches_per_layer": 4,
+    return {"unit": "ms per layer",
             "config": "512 routed + 1 shared experts, hidden 2048, intermediate 512, nvfp4, top-10",
             "cases": out}
 
