@@ -5,6 +5,6 @@ activations.  The C ABI is include/qmm.h; this package is its ctypes binding.
 
 from .qmm import (AFFINE4_G64, BF16, F32, FORMATS, MXFP4, NVFP4, Q6_K, PreparedGemv, QmmError,  # noqa: F401
                   Weight, bench_mfma_peak, bench_stream_read, dequant, gemm, gemv, moe, moe_from_logits,
-                  moe_router, moe_workspace_layout,
+                  moe_noalloc, moe_router, moe_workspace_layout,
                   moe_workspace_size, gemv_workspace_size, lib_handle, new_workspace,
                   workspace_init, prepare_gemm, prepare_moe)

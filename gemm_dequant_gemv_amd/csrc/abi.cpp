@@ -89,6 +89,7 @@ const char *qstatus_string(int status) {
     case QMM_ERR_HIP: return "a HIP runtime call failed";
     case QMM_ERR_DTYPE: return "unknown output dtype";
     case QMM_ERR_ARG: return "argument out of range";
+    case QMM_ERR_SCRATCH: return "the call needs more scratch than the static 16 MiB buffer of the no-allocation entry point holds";
     default: return "unknown status";
   }
 }
@@ -302,6 +303,23 @@ int qmoe_grouped(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_
   return hip_status(qmm::launch_moe(*gate_up, *down, num_routed, num_shared, x, t, topk_ids,
                                     topk_w, topk, shared_w, y, y_dtype, workspace,
                                     (hipStream_t)stream));
+}
+
+int qmoe_grouped_noalloc(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
+                         int32_t num_shared, const void *x, int32_t t, const int32_t *topk_ids,
+                         const float *topk_w, int32_t topk, const float *shared_w, void *y,
+                         int32_t y_dtype, void *stream) {
+  // the size check first: it needs no device
+  const size_t need = qmoe_workspace_size(gate_up, down, num_routed, num_shared, t, topk);
+  if (need > qmm::kNoallocScratchBytes) return QMM_ERR_SCRATCH;
+  void *ws = nullptr;
+  const hipError_t e = qmm::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  const int st = qmoe_grouped_check(gate_up, down, num_routed, num_shared, x, t, topk_ids, topk_w,
+                                    topk, shared_w, y, y_dtype, ws, qmm::kNoallocScratchBytes);
+  if (st) return st;
+  return hip_status(qmm::launch_moe(*gate_up, *down, num_routed, num_shared, x, t, topk_ids,
+                                    topk_w, topk, shared_w, y, y_dtype, ws, (hipStream_t)stream));
 }
 
 int qmoe_router(const float *logits, int32_t t, int32_t num_experts, int32_t topk,

@@ -119,6 +119,10 @@ hipError_t launch_moe_logits(const qmm_weight &gu, const qmm_weight &dn, int num
                              int32_t *topk_ids, float *topk_w, int topk, const float *shared_w,
                              void *y, int y_dtype, void *workspace, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+// the static scratch of qmoe_grouped_noalloc (noalloc.hip): its size, and the
+// device address of the current device's copy (looked up once per device)
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(void **out);
 // router top-k + softmax: one wave per token (router.hip)
 hipError_t launch_router(const float *logits, int t, int e, int k, int32_t *ids, float *w,
                          hipStream_t s);

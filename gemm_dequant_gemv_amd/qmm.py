@@ -22,7 +22,7 @@ FORMATS = {"affine4_g64": AFFINE4_G64, "mxfp4": MXFP4, "nvfp4": NVFP4, "q6_k": Q
 
 ENTRY_POINTS = ("qdequant", "qgemv", "qgemv_workspace_size", "qgemm", "qgemm_workspace_size",
                 "qmoe_grouped", "qmoe_workspace_size", "qmoe_workspace_layout", "qmoe_router",
-                "qmoe_grouped_logits",
+                "qmoe_grouped_logits", "qmoe_grouped_noalloc",
                 "qworkspace_init", "qbench_stream_read", "qbench_mfma_peak", "qstatus_string",
                 "qlast_hip_error")
 
@@ -71,6 +71,8 @@ def _lib():
         lib.qmoe_workspace_size.restype = SZ
         lib.qmoe_workspace_layout.argtypes = [P, P, I32, I32, I32, I32, ctypes.POINTER(QmoeLayoutC)]
         lib.qmoe_grouped.argtypes = [P, P, I32, I32, VP, I32, VP, VP, I32, VP, VP, I32, VP, SZ, VP]
+        lib.qmoe_grouped_noalloc.argtypes = [P, P, I32, I32, VP, I32, VP, VP, I32, VP, VP, I32,
+                                             VP]
         lib.qmoe_router.argtypes = [VP, I32, I32, I32, VP, VP, VP]
         lib.qmoe_grouped_logits.argtypes = [P, P, I32, I32, VP, I32, VP, I32, VP, VP, VP, VP, I32,
                                             VP, SZ, VP]
@@ -317,6 +319,20 @@ def _moe_check(where, gate_up, down, x, shared_w):
     if shared_w is not None:
         _tensor(where, "shared_w", shared_w, _F32, (x.shape[0],), dev)
     return dev
+
+
+def moe_noalloc(gate_up: Weight, down: Weight, x, topk_ids, topk_w, num_routed: int,
+                num_shared: int, out, shared_w=None, stream=None):
+    """qmoe_grouped_noalloc: one MoE layer into ``out`` (float32 or bf16
+    [t][H], allocated by the caller) with the library's static scratch in
+    place of a workspace; the call allocates nothing."""
+    _check_moe_routing("qmoe_grouped_noalloc", gate_up, down, x, topk_ids, topk_w, shared_w, out)
+    t, topk = topk_ids.shape
+    dt = F32 if out.dtype == torch.float32 else BF16
+    _check(_lib().qmoe_grouped_noalloc(gate_up.c, down.c, num_routed, num_shared, _ptr(x), t,
+                                       _ptr(topk_ids), _ptr(topk_w), topk, _ptr(shared_w),
+                                       _ptr(out), dt, _stream(stream)), "qmoe_grouped_noalloc")
+    return out
 
 
 def _check_moe_routing(where, gate_up, down, x, topk_ids, topk_w, shared_w, out):

@@ -88,7 +88,9 @@ enum qmm_status {
   QMM_ERR_ALIAS = -7,     /* an output overlaps an input                        */
   QMM_ERR_HIP = -8,       /* a HIP runtime call failed (see qlast_hip_error)    */
   QMM_ERR_DTYPE = -9,     /* unknown output dtype                               */
-  QMM_ERR_ARG = -10       /* another argument out of range (topk, experts ...)  */
+  QMM_ERR_ARG = -10,      /* another argument out of range (topk, experts ...)  */
+  QMM_ERR_SCRATCH = -11   /* the call needs more than qmoe_grouped_noalloc's
+                             static scratch holds                              */
 };
 
 /*
@@ -257,6 +259,32 @@ int qmoe_grouped(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_
                  int32_t num_shared, const void *x, int32_t t, const int32_t *topk_ids,
                  const float *topk_w, int32_t topk, const float *shared_w, void *y,
                  int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * qmoe_grouped_noalloc -- qmoe_grouped for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, result and kernels as qmoe_grouped
+ * (bit-identical output), but no workspace argument: the routing tables, h
+ * and d go to a static device buffer of 16 MiB that the library holds on each
+ * GPU it runs on until the process ends.  The call allocates nothing.
+ *
+ * Size limit: calls whose qmoe_workspace_size(...) exceeds 16 MiB return
+ * QMM_ERR_SCRATCH before anything is checked further or launched (on the
+ * 512 + 1-expert layer, hidden 2048, intermediate 512, top-10: up to about
+ * 160 tokens).
+ * Concurrency: every call on one GPU uses that GPU's single buffer, so calls
+ * that may overlap on one GPU (different streams, or different host threads
+ * without ordering) race on it and give undefined results; serialize them.
+ * The buffer keeps the last call's contents; the call needs no particular
+ * contents on entry.
+ * The first call on each device looks up that device's buffer address
+ * (hipGetSymbolAddress) with the device current; a failure there returns
+ * QMM_ERR_HIP.
+ */
+int qmoe_grouped_noalloc(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
+                         int32_t num_shared, const void *x, int32_t t, const int32_t *topk_ids,
+                         const float *topk_w, int32_t topk, const float *shared_w, void *y,
+                         int32_t y_dtype, void *stream);
 
 /*
  * qmoe_router -- the router's top-k and softmax ("TurboEXL3" section 4.2: in
