@@ -231,7 +231,7 @@ int qmoe_workspace_layout(const qmm_weight *gate_up, const qmm_weight *down, int
   *out = qmoe_layout{L.counts, L.offsets, L.row_of_slot, L.row_of_shared, L.token_of_row,
                      L.active, L.scalars, L.tiles, L.h, L.d, L.bytes, L.max_rows, L.max_tiles,
                      qmm::moe_uses_gemv(*gate_up, *down, t, topk, num_shared) ? 1u : 0u,
-                     L.tile_rows};
+                     L.tile_rows, L.slot_of_row};
   return QMM_OK;
 }
 

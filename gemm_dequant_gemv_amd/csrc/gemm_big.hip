@@ -45,16 +45,6 @@ constexpr int kStages = 3;  // LDS stages of X = slices in flight
 // slower split, and the split form is the faster one for those calls)
 constexpr int kXRow = kBK * 2;  // bytes of one X row in a slice
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// 16 bytes per lane from buffer `r` (lane's byte offset voff + soff) to LDS at
-// dst + 16 * lane (an ordinary function, so that host passes over the kernel
-// templates never see the LDS address space)
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void *dst, uint32_t voff,
-                                                  uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, voff, soff, 0, 0);
-}
-
 // Buffer descriptors and the per-lane constant parts of a lane's weight
 // offsets (its row and half); the slice's part goes in the scalar offset.
 struct WSrc {
@@ -87,9 +77,6 @@ __device__ __forceinline__ Piece load_run(const WSrc &w, int s) {
 // chunk) then land on distinct bank groups; measured on gfx950 at 119 TB/s of
 // LDS reads against 71 TB/s for a plain (row / 2) swizzle.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-
-// s_waitcnt with vmcnt <= n and the other counters left free (gfx9 encoding)
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int FMT>
 constexpr int w_loads_per_run() { return FMT == QMM_Q6_K ? 4 : 2; }
@@ -184,6 +171,13 @@ void gemm_big_kernel(GemmArgs a) {
     ws.v_d = r * (k / 256) * 2;
   }
   Piece wr[kStages];
+  // down mode: the token slot (row of d) of each of this lane's TM rows, read
+  // ahead of the pipeline so that the epilogue does not wait for it
+  uint32_t drow_of[MODE == kMoeDown ? TM : 1];
+  if constexpr (MODE == kMoeDown) {
+#pragma unroll
+    for (int t = 0; t < TM; ++t) drow_of[t] = a.slot_of_row[m0 + min(32 * t + lr, mrows - 1)];
+  }
 
   f32x16_t acc[TM];
 #pragma unroll
@@ -347,11 +341,13 @@ void gemm_big_kernel(GemmArgs a) {
         }
         continue;
       } else if constexpr (MODE == kMoeDown) {
+        // grouped row m goes to its token slot's row of d
+        const size_t drow = (size_t)drow_of[t];
         const int nb = n0 + nl;
         if (nb + 3 < a.n) {
-          *(float4 *)(a.d + (size_t)m * a.n + nb) = make_float4(v[0], v[1], v[2], v[3]);
+          *(float4 *)(a.d + drow * a.n + nb) = make_float4(v[0], v[1], v[2], v[3]);
         } else {
-          for (int r = 0; r < 4 && nb + r < a.n; ++r) a.d[(size_t)m * a.n + nb + r] = v[r];
+          for (int r = 0; r < 4 && nb + r < a.n; ++r) a.d[drow * a.n + nb + r] = v[r];
         }
         continue;
       }
@@ -478,8 +474,19 @@ size_t gemm_big_workspace(const qmm_weight &w, int m) {
   return split_counters_bytes(w, m) + (size_t)sk * m * w.n * 4;
 }
 
+// 5 to 8 rows whose activations fit in LDS take the row-streaming GEMV
+// (gemv_rows.hip, which holds the measurements) instead of the MFMA tiles.
+bool gemm_uses_rows(const qmm_weight &w, int m) {
+  bool rows = gemm_rows_fits(w, m);
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_GEMM_ROWS")) rows = rows && atoi(e) != 0;
+#endif
+  return rows;
+}
+
 size_t gemm_workspace_size(const qmm_weight &w, int m) {
-  return gemm_big_fits(w, (size_t)m) ? gemm_big_workspace(w, m) : 0;
+  if (!gemm_big_fits(w, (size_t)m) || gemm_uses_rows(w, m)) return 0;
+  return gemm_big_workspace(w, m);
 }
 
 bool gemm_big_fits(const qmm_weight &w, size_t x_rows) {
@@ -489,6 +496,7 @@ bool gemm_big_fits(const qmm_weight &w, size_t x_rows) {
 
 hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void *residual, void *y,
                            void *workspace, size_t workspace_bytes, hipStream_t s) {
+  if (gemm_uses_rows(w, m)) return launch_gemm_rows(w, x, m, residual, y, s);
   GemmArgs a = big_args(w);
   a.x = (const uint16_t *)x;
   a.residual = (const uint16_t *)residual;
@@ -557,6 +565,7 @@ hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const Moe
         gu.format, a, dim3(max_tiles, (gu.n + bn_of(4) - 1) / bn_of(4)), s);
     case 64: return launch_big_mode<2, 8, kMoeGateUp>(gu.format, a, grid, s);
     case 128: return launch_big_mode<4, 8, kMoeGateUp>(gu.format, a, grid, s);
+    case 192: return launch_big_mode<6, 8, kMoeGateUp>(gu.format, a, grid, s);
     default: return launch_big_mode<8, 8, kMoeGateUp>(gu.format, a, grid, s);
   }
 }
@@ -568,6 +577,7 @@ hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max
   a.n_tiles = t.n_tiles;
   a.h = t.h;
   a.d = t.d;
+  a.slot_of_row = t.slot_of_row;
   a.inter = dn.k;
   constexpr int bn = bn_of(8);
   const dim3 grid(max_tiles, (dn.n + bn - 1) / bn);
@@ -576,6 +586,7 @@ hipError_t launch_moe_big_down(const qmm_weight &dn, const MoeTables &t, int max
         dn.format, a, dim3(max_tiles, (dn.n + bn_of(4) - 1) / bn_of(4)), s);
     case 64: return launch_big_mode<2, 8, kMoeDown>(dn.format, a, grid, s);
     case 128: return launch_big_mode<4, 8, kMoeDown>(dn.format, a, grid, s);
+    case 192: return launch_big_mode<6, 8, kMoeDown>(dn.format, a, grid, s);
     default: return launch_big_mode<8, 8, kMoeDown>(dn.format, a, grid, s);
   }
 }

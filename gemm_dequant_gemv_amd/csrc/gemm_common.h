@@ -44,6 +44,7 @@ struct GemmArgs {
   const uint32_t *tiles;         // [max_tiles][3] = (expert, first grouped row, rows)
   const uint32_t *n_tiles;       // device count of valid tiles
   const uint32_t *token_of_row;  // grouped row -> token (gate/up gather)
+  const uint32_t *slot_of_row;   // grouped row -> token slot = row of d (down)
   uint16_t *h;                   // bf16 [rows][inter]   (gate/up output, down input)
   float *d;                      // float32 [rows][n]    (down output)
   int inter;                     // I: gate/up rows are 2I

@@ -51,10 +51,18 @@
 namespace qmm {
 namespace {
 
-constexpr int kWaves = 16;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kStepK = 1024;       // values of one row per step (32 lanes x 32)
-constexpr int kXPieces = 9;        // 16-byte activation pieces per thread, at most
+
+// Waves per workgroup (one workgroup per compute unit) and the 16-byte
+// activation pieces each thread stages at most.  Up to 4 activation rows: 16
+// waves (at most 128 registers each); 5 to 8 rows: 8 waves, so that a wave
+// can hold the 8 x 32 activation values of a unit (256 registers each).
+template <int M>
+struct RowsShape {
+  static constexpr int kWaves = M <= 4 ? 16 : 8;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kXPieces = M <= 4 ? 9 : 18;
+};
 constexpr size_t kLdsLimit = 160 * 1024 - 2048;  // dynamic part; the static part is <= 1 KB
 
 // LDS image of the activations, one record per 32-value chunk ch: M x 64
@@ -64,17 +72,21 @@ constexpr size_t kLdsLimit = 160 * 1024 - 2048;  // dynamic part; the static par
 // The 8 lanes of one ds_read_b128 group read consecutive records at the same
 // offset, and an odd multiple of 16 bytes sends them to 8 distinct groups of
 // 4 banks; every read of a unit is one lane base plus an immediate offset.
+constexpr int record_pad(int m, int ns) {
+  return m * ns * 4 <= 16 ? 16 : m * ns * 4 <= 48 ? 48 : m * ns * 4 <= 80 ? 80 : 112;
+}
+
 template <int M, int NS>
 struct XLayout {
   static constexpr int kSumOff = 64 * M;                   // bytes
-  static constexpr int kPad = M * NS * 4 <= 16 ? 16 : 48;  // sums fit, stride/16 odd
+  static constexpr int kPad = record_pad(M, NS);           // sums fit, stride/16 odd
   static constexpr int kStride = 64 * M + kPad;            // bytes per record
   static_assert(M * NS * 4 <= kPad && (kStride / 16) % 2 == 1, "record layout");
 };
 
 // The balanced split where the per-unit vector work is heavy.
 constexpr bool use_balanced(int format, int m) {
-  return format == QMM_Q6_K || (format == QMM_AFFINE4_G64 && m >= 2);
+  return format == QMM_Q6_K || (format == QMM_AFFINE4_G64 && m >= 2) || m >= 5;
 }
 
 constexpr int sums_per_chunk(int format) {
@@ -95,7 +107,10 @@ struct RowsArgs {
 };
 
 template <int FMT, int M, int U, bool BAL>
-__global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
+__global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsArgs a) {
+  constexpr int kWaves = RowsShape<M>::kWaves;
+  constexpr int kThreads = RowsShape<M>::kThreads;
+  constexpr int kXPieces = RowsShape<M>::kXPieces;
   using T = FmtTraits<FMT>;
   constexpr int kNS = T::kSums;
   using XL = XLayout<M, kNS>;
@@ -177,37 +192,37 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // 2. the first U units of weights.  Every load is unconditional (a unit
-  //    past the wave's range re-reads its last one; the row past n of an odd
-  //    n and lanes past K read whatever the buffer holds there, or zeros
-  //    beyond its end, and their results are never used), so the compiler can
-  //    count outstanding loads exactly.
+  // 2. the first U units of weights.  Every load is unconditional, so that
+  //    the compiler can count outstanding loads exactly: a unit past the
+  //    wave's range points every load past the end of its buffer, which
+  //    returns zeros at once without touching memory (re-reading real data
+  //    there delayed each wave's exit by a memory round trip); the row past n
+  //    of an odd n and lanes past K read whatever the buffer holds there, or
+  //    zeros beyond its end, and their results are never used.
   auto load_unit = [&](int t, int j, int s, RowData &rd, uint32_t &res) {
-    if (t >= units) {  // uniform
-      j = jl;
-      s = sl;
-    }
+    const bool past = t >= units;  // uniform
     const uint32_t row0 = 2u * (uint32_t)(pbase + j * pstride);
+    auto at = [past](uint32_t off, uint32_t bytes) { return past ? bytes : off; };
     rd.q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-        rc, v_code, row0 * (k / 2) + (uint32_t)s * (kStepK / 2), 2));
+        rc, v_code, at(row0 * (k / 2) + (uint32_t)s * (kStepK / 2), a.codes_bytes), 2));
     if constexpr (FMT == QMM_AFFINE4_G64) {
       rd.s = __builtin_amdgcn_raw_buffer_load_b32(
-          rs, v_scale, row0 * (k / 16) + (uint32_t)s * (kStepK / 16), 0);
+          rs, v_scale, at(row0 * (k / 16) + (uint32_t)s * (kStepK / 16), a.scales_bytes), 0);
     } else if constexpr (FMT == QMM_MXFP4) {
       rd.s = __builtin_amdgcn_raw_buffer_load_b8(
-          rs, v_scale, row0 * (k / 32) + (uint32_t)s * (kStepK / 32), 0);
+          rs, v_scale, at(row0 * (k / 32) + (uint32_t)s * (kStepK / 32), a.scales_bytes), 0);
     } else {
       rd.s = __builtin_amdgcn_raw_buffer_load_b16(
-          rs, v_scale, row0 * (k / 16) + (uint32_t)s * (kStepK / 16), 0);
+          rs, v_scale, at(row0 * (k / 16) + (uint32_t)s * (kStepK / 16), a.scales_bytes), 0);
     }
     if constexpr (FMT == QMM_Q6_K) {
       rd.h = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-          rh, v_hi, row0 * (k / 4) + (uint32_t)s * (kStepK / 4), 2));
+          rh, v_hi, at(row0 * (k / 4) + (uint32_t)s * (kStepK / 4), a.hi_bytes), 2));
       rd.d = __builtin_amdgcn_raw_buffer_load_b16(
-          rs2, v_d, (row0 * (k / 256) + (uint32_t)s * (kStepK / 256)) * 2, 0);
+          rs2, v_d, at((row0 * (k / 256) + (uint32_t)s * (kStepK / 256)) * 2, a.scales2_bytes), 0);
     }
     // a null residual has a zero-sized buffer, whose loads return 0
-    res = __builtin_amdgcn_raw_buffer_load_b16(rr, v_res, row0 * 2u, 0);
+    res = __builtin_amdgcn_raw_buffer_load_b16(rr, v_res, at(row0 * 2u, a.residual_bytes), 0);
   };
 
   RowData buf[U];
@@ -253,7 +268,13 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
       *(uint4 *)(rec + (m * 4 + part_) * 16) = o;
     }
   }
-  __syncthreads();
+  // A bare barrier: this wave's LDS writes are complete (lgkmcnt), while its
+  // weight loads stay in flight.  __syncthreads() would also wait for those
+  // (vmcnt(0)), so that every wave drained its pipeline here and restarted it
+  // from empty.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 
   const UnpackK K = unpack_consts();
   // gscale's load completed before the barrier above (loads complete in
@@ -354,6 +375,7 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(RowsArgs a) {
 
 template <int FMT, int M, int U, bool BAL>
 hipError_t launch_rows_cfg(const RowsArgs &a, size_t lds, int grid, hipStream_t s) {
+  constexpr int kThreads = RowsShape<M>::kThreads;
   // the dynamic LDS limit is raised once per device for each instantiation
   static std::atomic<uint64_t> raised{0};
   int dev = 0;
@@ -392,7 +414,11 @@ hipError_t launch_rows_f(const RowsArgs &a, int m, const GemvPlan &p, hipStream_
     case 1: return launch_rows_fm<FMT, 1>(a, p, s);
     case 2: return launch_rows_fm<FMT, 2>(a, p, s);
     case 3: return launch_rows_fm<FMT, 3>(a, p, s);
-    default: return launch_rows_fm<FMT, 4>(a, p, s);
+    case 4: return launch_rows_fm<FMT, 4>(a, p, s);
+    case 5: return launch_rows_fm<FMT, 5>(a, p, s);
+    case 6: return launch_rows_fm<FMT, 6>(a, p, s);
+    case 7: return launch_rows_fm<FMT, 7>(a, p, s);
+    default: return launch_rows_fm<FMT, 8>(a, p, s);
   }
 }
 
@@ -411,14 +437,15 @@ int cu_count() {
 }  // namespace
 
 size_t gemv_rows_lds(int format, int k, int m) {
-  const int ns = sums_per_chunk(format);
-  const int pad = m * ns * 4 <= 16 ? 16 : 48;
-  return (size_t)(k / 32) * (size_t)(64 * m + pad);
+  return (size_t)(k / 32) * (size_t)(64 * m + record_pad(m, sums_per_chunk(format)));
 }
 
 bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p) {
+  if (m < 1 || m > kRowsMaxM) return false;
   const size_t lds = gemv_rows_lds(format, k, m);
-  if (lds > kLdsLimit || (size_t)k / 32 * 4 * m > (size_t)kXPieces * kThreads) return false;
+  const size_t threads = m <= 4 ? RowsShape<4>::kThreads : RowsShape<8>::kThreads;
+  const size_t pieces = m <= 4 ? RowsShape<4>::kXPieces : RowsShape<8>::kXPieces;
+  if (lds > kLdsLimit || (size_t)k / 32 * 4 * m > pieces * threads) return false;
   const int cus = cu_count();
   if (cus <= 0) return false;
   p = GemvPlan{};
@@ -466,6 +493,33 @@ hipError_t launch_gemv_rows(const qmm_weight &w, const void *x, int m, const voi
     case QMM_NVFP4: return launch_rows_f<QMM_NVFP4>(a, m, p, s);
     default: return launch_rows_f<QMM_Q6_K>(a, m, p, s);
   }
+}
+
+}  // namespace qmm
+
+namespace qmm {
+
+// qgemm's mid band, 5 to 8 activation rows ("TurboEXL3" section 4.3, the
+// trunk: 5 to 16 rows take a GEMV chain that decodes each weight once per
+// chunk of up to 8 rows): the row-streaming kernel, which reads and decodes
+// the weights once, with the exact weights (no bfloat16 rounding of the
+// weights, unlike the MFMA tiles) and a bfloat16 y.  Measured on 17408 x 5120
+// (cold weights, us, GEMV / MFMA tiles): affine 5 rows 23.9 / 38.0, 8 rows
+// 28.9 / 38.0; NVFP4 23.0 / 37.6, 27.1 / 38.2; Q6_K 31.6 / 55.6, 37.3 / 55.3;
+// MXFP4 21.8 / 37.2, 26.4 / 37.5.  Two chunks for 9 to 16 rows lost to the
+// MFMA tiles (affine 9 rows 42.2 / 38.2, 16 rows 56.7 / 40.3), so those rows
+// stay there.
+bool gemm_rows_fits(const qmm_weight &w, int m) {
+  if (m < 5 || m > kRowsMaxM || w.batch != 1) return false;
+  GemvPlan p;
+  return plan_gemv_rows(w.format, w.n, w.k, m, p);
+}
+
+hipError_t launch_gemm_rows(const qmm_weight &w, const void *x, int m, const void *residual,
+                            void *y, hipStream_t s) {
+  GemvPlan p;
+  if (!plan_gemv_rows(w.format, w.n, w.k, m, p)) return hipErrorInvalidValue;
+  return launch_gemv_rows(w, x, m, residual, y, QMM_BF16, p, s);
 }
 
 }  // namespace qmm

@@ -91,6 +91,7 @@ __device__ void group_and_tile(const RouteArgs &a, uint32_t *s_count, uint32_t *
       const uint32_t row = s_off[a.num_routed + s] + t;
       tb.row_of_shared[(size_t)s * a.t + t] = row;
       tb.token_of_row[row] = (uint32_t)t;
+      tb.slot_of_row[row] = (uint32_t)a.t * (uint32_t)a.topk + (uint32_t)(s * a.t + t);
     }
 
   // 4. experts with rows (in expert order) and their tiles of tile_rows rows
@@ -177,6 +178,7 @@ __device__ void place_slots(const RouteArgs &a, int i0, int i1, Base base) {
       const uint32_t row = base(id[j]) + pos[j];
       a.tb.row_of_slot[i] = row;
       a.tb.token_of_row[row] = (uint32_t)(i / a.topk);
+      a.tb.slot_of_row[row] = (uint32_t)i;
     }
   }
 }
@@ -294,21 +296,26 @@ struct CombineArgs {
   int y_bf16;
 };
 
-// y[t][n] = sum_j w[t][j] d[row(t, j)][n] + sum_s ws[t] d[row_s(t)][n], fixed order
-// (one fma per term; the decode form runs the same chain in its down launch).
-// A block serves one token: the token's rows and weights go to LDS in chunks
-// of 64 slots, then each thread issues its d loads 8 at a time before adding
-// them, so that no load waits for the previous one.  VEC columns per thread
-// (4: 16-byte loads of d when H is a multiple of 4; the kernel reads every
-// row of d once, 738 MB at T = 8192 on the 512-expert layer).
+// y[t][n] = sum_j w[t][j] d[t topk + j][n] + sum_s ws[t] d[T topk + s T + t][n],
+// fixed order (one fma per term; the decode form runs the same chain in its
+// down launch).  d holds one row per token slot (the down launch writes each
+// grouped row to its slot's row), so a token's routed rows are consecutive.
+// A block serves VEC x 256 columns of one token (the blocks of one token are
+// adjacent in launch order, so the token's rows are read front to back): the
+// slots' weights and whether each was dropped go to LDS in chunks of 64
+// slots, then each thread issues its d loads 16 at a time before adding them
+// (a token's 10 + 1 rows in one batch), so that no load waits for the
+// previous one.  VEC columns per thread (4: 16-byte loads of d when H is a
+// multiple of 4; the kernel reads every row of d once, 738 MB at T = 8192 on
+// the 512-expert layer).
 template <int VEC>
 __global__ __launch_bounds__(256) void moe_combine_kernel(CombineArgs a) {
-  constexpr int kChunk = 64, kBatch = 8;
+  constexpr int kChunk = 64, kBatch = 16;
   typedef __attribute__((ext_vector_type(VEC))) float fv_t;
   __shared__ uint32_t s_row[kChunk];
   __shared__ float s_w[kChunk];
-  const int t = blockIdx.x;
-  const int n = (blockIdx.y * 256 + threadIdx.x) * VEC;  // first of this thread's columns
+  const int t = blockIdx.y;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * VEC;  // first of this thread's columns
   const int total = a.topk + a.num_shared;
   const int nn = min(n, a.h - VEC);
   fv_t acc = {};
@@ -321,11 +328,11 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(CombineArgs a) {
       float w;
       if (j < a.topk) {
         const int slot = t * a.topk + j;
-        row = a.tb.row_of_slot[slot];
+        row = a.tb.row_of_slot[slot] == kInvalidRow ? kInvalidRow : (uint32_t)slot;
         w = a.topk_w[slot];
       } else {
         const int sh = j - a.topk;
-        row = a.tb.row_of_shared[(size_t)sh * a.t + t];
+        row = (uint32_t)a.t * (uint32_t)a.topk + (uint32_t)(sh * a.t + t);
         w = a.shared_w ? a.shared_w[t] : 1.0f;
       }
       s_row[threadIdx.x] = row;
@@ -336,7 +343,8 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(CombineArgs a) {
       fv_t v[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        const uint32_t r = j0 + u < cnt ? s_row[j0 + u] : kInvalidRow;
+        if (j0 + u >= cnt) break;  // uniform
+        const uint32_t r = s_row[j0 + u];
         v[u] = *(const fv_t *)(a.tb.d + (size_t)(r == kInvalidRow ? 0u : r) * a.h + nn);
       }
 #pragma unroll
@@ -361,17 +369,24 @@ size_t align_up(size_t v) { return (v + 255) / 256 * 256; }
 
 }  // namespace
 
-// Routing tiles as tall as about twice an average routed expert's rows (t x
-// topk / E), from 32 to 256: tokens spread over many experts leave each with
-// a few rows, and a 256-row tile (the grouped GEMMs' tallest) would be almost
-// all padding.  Measured on the 512-expert layer (T = 5 .. 64: 97 .. 532 us
-// per layer with 256-row tiles).
+// Routing tiles: the smallest of 32, 64, 128, 192 and 256 rows that holds 1.2
+// times an average routed expert's rows (t x topk / E).  A tile much taller
+// than most experts' rows is mostly padding (the MFMAs of its empty rows
+// still run); one much shorter splits most experts in two.  Measured on the
+// 512-expert layer, NVFP4, time per layer for tiles of 32 / 64 / 128 / 192 /
+// 256 rows: T = 1024 (20 rows per expert) 0.48 / 0.50 / 0.52 / 0.63 / 0.76 ms;
+// T = 2048 0.81 / 0.55 / 0.59 / 0.68 / 0.80; T = 4096 1.28 / 0.97 / 0.73 /
+// 0.81 / 0.92; T = 8192 2.22 / 1.65 / 1.38 / 1.09 / 1.17.
 int moe_tile_rows(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, int num_routed) {
   (void)gu;
   (void)dn;
-  const double avg = (double)t * topk / num_routed;
-  int tr = 32;
-  while (tr < kMoeTileRows && tr < 2.0 * avg) tr *= 2;
+  const double need = 1.2 * (double)t * topk / num_routed;
+  int tr = 256;
+  for (int c : {192, 128, 64, 32})
+    if (c >= need) tr = c;
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_MOE_TILE")) tr = atoi(e);
+#endif
   return tr;
 }
 
@@ -405,6 +420,7 @@ MoeLayout moe_layout(int num_experts, int t, int topk, int num_shared, int inter
   L.row_of_slot = take((size_t)t * topk * 4);
   L.row_of_shared = take((size_t)t * num_shared * 4 + 4);
   L.token_of_row = take(rows * 4 + 4);
+  L.slot_of_row = take(rows * 4 + 4);
   L.active = take((size_t)num_experts * 4);
   L.scalars = take(16);  // n_active, n_tiles, err
   L.tiles = take(L.max_tiles * 12);
@@ -425,6 +441,7 @@ MoeTables moe_tables(const MoeLayout &L, void *ws) {
   t.row_of_slot = (uint32_t *)(b + L.row_of_slot);
   t.row_of_shared = (uint32_t *)(b + L.row_of_shared);
   t.token_of_row = (uint32_t *)(b + L.token_of_row);
+  t.slot_of_row = (uint32_t *)(b + L.slot_of_row);
   t.active = (uint32_t *)(b + L.active);
   t.n_active = (uint32_t *)(b + L.scalars);
   t.n_tiles = t.n_active + 1;
@@ -481,9 +498,9 @@ hipError_t launch_moe(const qmm_weight &gu, const qmm_weight &dn, int num_routed
   CombineArgs ca{topk_w, shared_w, t, topk, num_routed, num_shared, dn.n, tb, y,
                  y_dtype == QMM_BF16};
   if (dn.n % 4 == 0)
-    hipLaunchKernelGGL(moe_combine_kernel<4>, dim3(t, (dn.n + 1023) / 1024), dim3(256), 0, s, ca);
+    hipLaunchKernelGGL(moe_combine_kernel<4>, dim3((dn.n + 1023) / 1024, t), dim3(256), 0, s, ca);
   else
-    hipLaunchKernelGGL(moe_combine_kernel<1>, dim3(t, (dn.n + 255) / 256), dim3(256), 0, s, ca);
+    hipLaunchKernelGGL(moe_combine_kernel<1>, dim3((dn.n + 255) / 256, t), dim3(256), 0, s, ca);
   return hipGetLastError();
 }
 

@@ -72,6 +72,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                            0x00020000);
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from buffer `r` (lane's byte offset voff + soff) straight
+// to LDS at dst + 16 * lane, without passing through registers (buffer_load
+// ... lds); dst must be wave-uniform.  The load counts in vmcnt like any other
+// vector memory load.  (An ordinary function, so that host passes over kernel
+// templates never see the LDS address space.)
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void *dst, uint32_t voff,
+                                                  uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt with vmcnt <= n and the other counters left free (gfx9 encoding)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // float32 -> bfloat16 bits, round to nearest even, NaN kept quiet.
 __device__ __forceinline__ uint32_t float_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);

@@ -36,6 +36,9 @@ struct GemvPlan {
 };
 
 GemvPlan plan_gemv(int format, int n, int k, int m);
+// the row-streaming kernel's activation rows at most (qgemv takes 1 to 4;
+// qgemm sends it calls of 5 up to this many rows)
+constexpr int kRowsMaxM = 8;
 bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p);
 size_t gemv_rows_lds(int format, int k, int m);
 
@@ -51,6 +54,7 @@ struct MoeTables {
   uint32_t *row_of_slot;    // [t][topk] grouped row of each routed slot
   uint32_t *row_of_shared;  // [shared][t] grouped row of each shared slot
   uint32_t *token_of_row;   // [rows] token each grouped row reads
+  uint32_t *slot_of_row;    // [rows] token slot of each grouped row (its row of d)
   uint32_t *active;         // [experts] experts with rows, in expert order
   uint32_t *n_active, *n_tiles, *err;
   uint32_t *tiles;          // [max_tiles][3] (expert, first row, rows)
@@ -64,6 +68,7 @@ struct MoeTables {
 
 struct MoeLayout {
   size_t counts, offsets, row_of_slot, row_of_shared, token_of_row, active, scalars, tiles, h, d;
+  size_t slot_of_row;
   size_t wg_counts, wg_err, route_groups;
   size_t bytes, max_rows, max_tiles, tile_rows;
 };
@@ -77,6 +82,12 @@ MoeTables moe_tables(const MoeLayout &L, void *ws);
 hipError_t launch_dequant(const qmm_weight &w, int out_dtype, void *out, hipStream_t s);
 hipError_t launch_gemv_rows(const qmm_weight &w, const void *x, int m, const void *residual,
                             void *y, int y_dtype, const GemvPlan &p, hipStream_t s);
+// qgemm's 5 to kRowsMaxM rows on the row-streaming kernel (weights read and
+// decoded once), bf16 y; false when the activations do not fit in LDS (the
+// call then takes the MFMA tiles)
+bool gemm_rows_fits(const qmm_weight &w, int m);
+hipError_t launch_gemm_rows(const qmm_weight &w, const void *x, int m, const void *residual,
+                            void *y, hipStream_t s);
 hipError_t launch_gemv(const qmm_weight &w, const void *x, int m, const void *residual,
                        void *y, int y_dtype, void *workspace, const GemvPlan &p,
                        hipStream_t s);

@@ -46,7 +46,8 @@ class QmmWeightC(ctypes.Structure):
 class QmoeLayoutC(ctypes.Structure):
     _fields_ = [(name, ctypes.c_size_t) for name in (
         "counts", "offsets", "row_of_slot", "row_of_shared", "token_of_row", "active",
-        "scalars", "tiles", "h", "d", "bytes", "max_rows", "max_tiles", "slot_rows", "tile_rows")]
+        "scalars", "tiles", "h", "d", "bytes", "max_rows", "max_tiles", "slot_rows", "tile_rows",
+        "slot_of_row")]
 
 
 _LIB = None

@@ -192,7 +192,12 @@ int qbench_mfma_peak(int32_t iters, int32_t blocks, void *sink, double *flops, v
  *
  * where w16 is the weight rounded to bfloat16 (exact for MXFP4 and NVFP4;
  * affine and Q6_K values are rounded to nearest even, a relative error of at
- * most 2^-9 per weight), summed in float32 on the matrix cores.
+ * most 2^-9 per weight), summed in float32 on the matrix cores.  Calls of 5 to
+ * 8 rows whose activations fit in LDS (k * m * 2 bytes plus block sums, about
+ * k <= 8192 at 8 rows) take the decode GEMV's row-streaming kernel instead
+ * ("TurboEXL3" section 4.3: 5 to 16 rows decode each weight once per chunk of
+ * up to 8 rows), which multiplies with the exact weights; fewer than 5 rows
+ * and the rest take the MFMA tiles.
  *
  * w         one matrix (batch must be 1); k must be a multiple of 64; fewer
  *           than 2^32 weights (QMM_ERR_SHAPE otherwise)
@@ -345,8 +350,12 @@ typedef struct {
                            outside [0, E) and its slot was dropped)                 */
   size_t tiles;         /* uint32 [n_tiles][3] expert, first grouped row, rows
                            (<= tile_rows) of each row tile, experts ascending       */
-  size_t h;             /* bf16  [rows][I]  SwiGLU outputs                          */
-  size_t d;             /* float [rows][H]  down-projection outputs                  */
+  size_t h;             /* bf16  [rows][I]  SwiGLU outputs, by grouped row (grouped
+                           form) or token slot (decode form)                        */
+  size_t d;             /* float [rows][H]  down-projection outputs by token slot, in
+                           both forms: routed slot (i, j) of token i at row
+                           i * topk + j, shared expert s's slot of token i at
+                           t * topk + s * t + i                                     */
   size_t bytes;         /* = qmoe_workspace_size                                     */
   size_t max_rows, max_tiles;
   size_t slot_rows;     /* 1: the call takes the decode form (t <= 16, t * (topk + S)
@@ -356,10 +365,13 @@ typedef struct {
                            expert j's slot of token i at t*topk + j*t + i); of the
                            tables only scalars[2] (err) is written.
                            0: the grouped form; every table above is written.   */
-  size_t tile_rows;     /* rows per routing tile of the grouped form: 32, 64, 128 or
-                           256, about twice an average routed expert's rows
-                           (t * topk / E), so that tiles of few-row experts are
-                           not mostly padding                                     */
+  size_t tile_rows;     /* rows per routing tile of the grouped form: the smallest
+                           of 32, 64, 128, 192, 256 that holds 1.2 times an
+                           average routed expert's rows (t * topk / E), so that
+                           most experts fill one tile and tiles are not mostly
+                           padding                                                */
+  size_t slot_of_row;   /* uint32 [rows]    token slot of each grouped row (its row of
+                           d; grouped form only)                                    */
 } qmoe_layout;
 
 /* Fill *out for these arguments (host-side arithmetic only, no launch).

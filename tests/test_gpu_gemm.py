@@ -80,12 +80,14 @@ def _unit_scale_weight(fmt, n, k, seed):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_gemm_exact_arithmetic(fmt):
+@pytest.mark.parametrize("m", [150, 8, 13])
+def test_gemm_exact_arithmetic(fmt, m):
     """Unit scales and integer activations: every product and partial sum is an
     exact float32, so the bf16 output must be the bf16 rounding of the exact
-    sum, whatever the summation order."""
+    sum, whatever the summation order (150 and 13 rows: MFMA tiles; 8 rows:
+    the row-streaming GEMV)."""
     q = _q()
-    m, n, k = 150, 260, 5120
+    n, k = 260, 5120
     p = _unit_scale_weight(fmt, n, k, 60 + fmt)
     xi = rng.randint_bytes(61, "gex", m * k, 0, 9).astype(np.float64).reshape(m, k) - 4
     x = quant.bf16_bits(xi)
@@ -139,8 +141,8 @@ def full_weights():
 @pytest.mark.parametrize("fmt,m", [(F.AFFINE4_G64, 128), (F.AFFINE4_G64, 512),
                                    (F.AFFINE4_G64, 2048), (F.AFFINE4_G64, 8192),
                                    (F.NVFP4, 128), (F.NVFP4, 512), (F.NVFP4, 2048),
-                                   (F.NVFP4, 8192), (F.AFFINE4_G64, 8), (F.NVFP4, 48),
-                                   (F.Q6_K, 96)])
+                                   (F.NVFP4, 8192), (F.AFFINE4_G64, 8), (F.NVFP4, 16),
+                                   (F.Q6_K, 5), (F.NVFP4, 48), (F.Q6_K, 96)])
 def test_gemm_prefill_full_size_sampled(full_weights, fmt, m):
     q = _q()
     p = full_weights(fmt)
@@ -154,8 +156,29 @@ def test_gemm_prefill_full_size_sampled(full_weights, fmt, m):
     _check(y[rows], yref, mag)
 
 
+# The mid band: 5 to 8 rows whose activations fit in LDS take the
+# row-streaming GEMV (no workspace), 9 and more the MFMA tiles (split K up to
+# 32 rows); ragged n and a residual on even m; bf16 y within the product bound.
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m", [5, 6, 7, 8, 9, 12, 16])
+def test_gemm_mid_band_parity(fmt, m):
+    q = _q()
+    n, k = 515, 2048
+    p = quant.synthetic_weight(fmt, n, k, outlier_rate=0.01, name=f"gmid{fmt}")
+    x = quant.synthetic_bf16(m, k, name=f"gmidx{m}")
+    r = quant.synthetic_bf16(m, n, name=f"gmidr{m}") if m % 2 == 0 else None
+    w = q.Weight.from_host(p)
+    if m <= 8:  # the GEMV path needs no split workspace
+        assert int(q.lib_handle().qgemm_workspace_size(w.c, m)) == 0
+    y = q.gemm(w, _dev_bf16(x), None if r is None else _dev_bf16(r))
+    yref, mag = oracle.gemm(p, x, r)
+    _check(_host_f64(y), yref, mag)
+    y2 = q.gemm(w, _dev_bf16(x), None if r is None else _dev_bf16(r))
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
 @pytest.mark.parametrize("fmt", [F.AFFINE4_G64, F.NVFP4, F.Q6_K])
-@pytest.mark.parametrize("m", [3, 16, 29])
+@pytest.mark.parametrize("m", [3, 20, 29])
 def test_gemm_split_k(fmt, m):
     """Up to 32 rows a call with qgemm_workspace_size bytes of workspace
     splits K (4 splits up to 16 rows, 2 above); one without runs unsplit.

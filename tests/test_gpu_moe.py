@@ -68,6 +68,7 @@ def run_gpu(q, gu, dn, x, ids, w, E, S, shared_w=None, y_dtype=torch.float32, wd
         r["row_of_slot"] = _u32(ws, L["row_of_slot"], T * topk).reshape(T, topk)
         r["row_of_shared"] = _u32(ws, L["row_of_shared"], S * T)
         r["token_of_row"] = _u32(ws, L["token_of_row"], rows)
+        r["slot_of_row"] = _u32(ws, L["slot_of_row"], rows)
         n_active, n_tiles, _ = _u32(ws, L["scalars"], 3)
         r["active"] = _u32(ws, L["active"], n_active)
         r["tiles"] = _u32(ws, L["tiles"], 3 * n_tiles).reshape(-1, 3)
@@ -87,7 +88,7 @@ def check_grouping(r, ids, E, S):
     group's rows): every slot lands inside its expert's rows, once."""
     # the library's routing-tile height (its grouped GEMMs' activation tile) is
     # part of the layout it reports; the tiles themselves must match exactly
-    assert r["tile_rows"] in (32, 64, 128, 256)
+    assert r["tile_rows"] in (32, 64, 128, 192, 256)
     g = oracle.moe_grouping(ids, E, S, tile_rows=r["tile_rows"])
     T, topk = ids.shape
     assert r["err"] == g["err"]
@@ -111,6 +112,11 @@ def check_grouping(r, ids, E, S):
         assert np.array_equal(r["token_of_row"][rs[s]], np.arange(T))
     every = np.concatenate([rv, rs.ravel()])
     assert len(np.unique(every)) == len(every) == g["offsets"][-1]
+    # each grouped row knows its token slot (the row of d it writes)
+    slots = np.arange(T * topk).reshape(T, topk)[g["valid"]]
+    assert np.array_equal(r["slot_of_row"][rv], slots)
+    for s in range(S):
+        assert np.array_equal(r["slot_of_row"][rs[s]], T * topk + s * T + np.arange(T))
 
 
 def gpu_h_dict(r, T, topk, S, tokens):
