@@ -42,6 +42,19 @@ What it computes, and where the pages define it:
   the model description: 10 of 512 experts per token): the k largest logits
   (equal logits in ascending expert id, -0 equal to +0), in descending order,
   weighted by the softmax over those k, in float64.
+* W4A4 ("TurboEXL3" section 2.2, the W4A4 bullet: the activations are also
+  quantized to a 4-bit format on the fly, with a scale per block, so both
+  operands of the multiply are FP4).  Here the block-scaled format of the
+  activations is MXFP4 (section 2.1: E2M1 values with one E8M0 power-of-two
+  scale per 32), the format the MI355X matrix cores multiply natively.  Each
+  row of x is cut into blocks of 32 along K; a block's shared exponent is
+  E = floor(log2(amax)) - 2 (the largest E2M1 magnitude is 6 = 1.5 * 2^2; OCP
+  MX conversion, reference [3]), stored as E8M0 = E + 127 (raised to 0 where
+  that is negative; 0 with all codes 0 for an all-zero block); every value is
+  divided by 2^E and rounded to the nearest E2M1 value, ties to the even
+  code, magnitudes past 6 saturating to 6, a value that rounds to zero taking
+  code 0.  The product is then the exact sum of the dequantized weights times
+  the dequantized activation codes.
 * Alongside every output, its magnitude sum sum_k |w||x| (+ |r|), which sets the
   tolerance |y - y_ref| <= 2e-3 * magnitude.
 
@@ -300,6 +313,63 @@ def moe_grouping(topk_ids, num_routed: int, num_shared: int, tile_rows: int = 12
     return dict(counts=np.array(counts, np.int64), offsets=np.array(offsets, np.int64),
                 valid=valid, active=np.array(active, np.int64),
                 tiles=np.array(tiles, np.int64).reshape(-1, 3), err=int((~valid).any()))
+
+
+# ------------------------------------------------------------ W4A4
+
+def mxfp4_quantize(x_bits):
+    """Activations (bfloat16 bits [m][k], k a multiple of 32) -> MXFP4: codes
+    uint8 [m][k/2] (element 2j in the low nibble of byte j) and E8M0 scales
+    uint8 [m][k/32], by the rule in the module docstring."""
+    x = bf16(x_bits)
+    m, k = x.shape
+    blk = x.reshape(m, k // 32, 32)
+    amax = np.abs(blk).max(axis=-1)
+    # floor(log2(amax)) from frexp: amax = f * 2^e with f in [0.5, 1)
+    _, e = np.frexp(amax)
+    shared = (e - 1) - 2
+    e8m0 = np.where(amax > 0, np.maximum(shared + 127, 0), 0).astype(np.int64)
+    scale = np.ldexp(1.0, e8m0 - 127)[..., None]
+    v = np.where(amax[..., None] > 0, blk / scale, 0.0)
+    a = np.abs(v)
+    # nearest magnitude in the printed list, ties to the even index
+    mags = np.asarray(E2M1_MAGNITUDES)
+    dist = np.abs(a[..., None] - mags)                   # [m][k/32][32][8]
+    best = dist.min(axis=-1, keepdims=True)
+    cand = dist == best                                  # one or two nearest
+    even = cand & (np.arange(8) % 2 == 0)
+    idx = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    codes = np.where(idx > 0, idx | np.where(v < 0, 8, 0), 0).astype(np.uint8)
+    codes = codes.reshape(m, k)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, e8m0.astype(np.uint8)
+
+
+def mxfp4_dequantize_activations(codes, scales):
+    """Exact float64 activations [m][k] of MXFP4 codes [m][k/2] and E8M0
+    scales [m][k/32]."""
+    c = _nibbles(np.asarray(codes).astype(np.int64))
+    return e2m1(c) * np.repeat(e8m0(scales), 32, axis=-1)
+
+
+def gemm_w4a4(p, x_bits, residual_bits=None, rows=None):
+    """W4A4 product: y_ref [m][n_sel] = dequant(w) . dequant(mxfp4(x))^T
+    (+ residual) in float64, and its magnitude sum.  ``p`` is an MXFP4
+    weight."""
+    if p.fmt != MXFP4:
+        raise ValueError("W4A4 takes MXFP4 weights")
+    codes, scales = mxfp4_quantize(x_bits)
+    xq = mxfp4_dequantize_activations(codes, scales)
+    w = dequant(p, 0, rows)
+    y = xq @ w.T
+    mag = np.abs(xq) @ np.abs(w).T
+    if residual_bits is not None:
+        r = bf16(residual_bits)
+        if rows is not None:
+            r = r[:, np.asarray(rows)]
+        y = y + r
+        mag = mag + np.abs(r)
+    return y, mag
 
 
 def within_tolerance(y, y_ref, mag, rel: float = 2e-3):

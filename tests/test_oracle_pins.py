@@ -601,3 +601,94 @@ def test_router_shift_invariant():
     ids1, w1 = oracle.router(lg + 7.5, 10)
     assert (ids0 == ids1).all()
     np.testing.assert_allclose(w0, w1, rtol=1e-12)
+
+
+# ------------------------------------------------------------ W4A4
+
+def _bf16_bits_of(tok):
+    if tok.startswith("0x"):
+        return int(tok, 16)
+    return int(torch.tensor([float(tok)], dtype=torch.float32).to(torch.bfloat16)
+               .view(torch.int16).item()) & 0xFFFF
+
+
+def test_mxfp4_activation_quantizer_hand_worked_blocks():
+    """Blocks worked by hand from the MXFP4 conversion rule
+    (tests/golden/w4a4_blocks.txt): shared exponent, ties to even,
+    saturation, zero blocks, subnormal and huge inputs."""
+    rows = []
+    with open(os.path.join(GOLDEN, "w4a4_blocks.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line)
+    x = np.zeros((1, 32 * len(rows)), np.uint16)
+    expect_s, expect_c = [], np.zeros(32 * len(rows), np.int64)
+    for b, line in enumerate(rows):
+        left, right = line.split("|")
+        tok = left.split()
+        expect_s.append(int(tok[1]))
+        vals = [_bf16_bits_of(t) for t in tok[2:]]
+        x[0, 32 * b:32 * b + len(vals)] = vals
+        codes = [int(c) for c in right.split()]
+        expect_c[32 * b:32 * b + len(codes)] = codes
+    codes, scales = oracle.mxfp4_quantize(x)
+    assert scales[0].tolist() == expect_s
+    got = np.stack([codes[0] & 15, codes[0] >> 4], axis=-1).reshape(-1)
+    assert got.tolist() == expect_c.tolist()
+
+
+def test_w4a4_equals_w4a16_on_grid_activations():
+    """Activations already on the MXFP4 grid (each block's largest magnitude
+    6 * 2^E, every value an E2M1 magnitude times 2^E) are quantized without
+    loss, so W4A4 equals the W4A16 product on them, bit for bit in float64."""
+    n, k, m = 24, 256, 3
+    p = quant.synthetic_weight(F.MXFP4, n, k, name="pin/w4a4w")
+    codes = rng.randint_bytes(rng.BASE_SEED, "pin/w4a4c", m * k, 0, 16).astype(np.int64)
+    mags = np.asarray(oracle.E2M1_MAGNITUDES)
+    v = np.where(codes & 8, -1.0, 1.0) * mags[codes & 7]
+    v = v.reshape(m, k // 32, 32)
+    v[..., 0] = 6.0                                    # amax 6 in every block
+    ex = rng.randint_bytes(rng.BASE_SEED, "pin/w4a4e", m * k // 32, 0, 9).astype(np.int64) - 4
+    x = (v * np.ldexp(1.0, ex).reshape(m, k // 32, 1)).reshape(m, k)
+    xb = quant.bf16_bits(x)
+    assert np.array_equal(oracle.bf16(xb), x)          # exact in bf16
+    y4, mag4 = oracle.gemm_w4a4(p, xb)
+    y16, mag16 = oracle.gemv(p, xb)
+    assert np.array_equal(y4, y16) and np.array_equal(mag4, mag16)
+    c, sc = oracle.mxfp4_quantize(xb)
+    assert (sc.astype(np.int64) == ex.reshape(m, k // 32) + 127 - 0).all()
+
+
+def test_w4a4_is_w4a16_on_the_dequantized_activations():
+    """For any activations, the W4A4 product is the W4A16 product on the
+    dequantized MXFP4 activations (exactly representable in bf16: 3
+    significant bits)."""
+    n, k, m = 40, 512, 5
+    p = quant.synthetic_weight(F.MXFP4, n, k, outlier_rate=0.01, name="pin/w4a4b")
+    xb = quant.synthetic_bf16(m, k, name="pin/w4a4x")
+    codes, scales = oracle.mxfp4_quantize(xb)
+    xq = oracle.mxfp4_dequantize_activations(codes, scales)
+    xqb = quant.bf16_bits(xq)
+    assert np.array_equal(oracle.bf16(xqb), xq)
+    y4, mag4 = oracle.gemm_w4a4(p, xb)
+    y16, mag16 = oracle.gemv(p, xqb)
+    assert np.array_equal(y4, y16) and np.array_equal(mag4, mag16)
+
+
+def test_mxfp4_quantizer_error_bound_and_scale():
+    """Every value lands within half a grid step of its scaled value (the
+    grid step at |v| is .5 below 2, 1 from 2 to 4, 2 from 4 to 6), the block
+    maximum within [4, 8) after scaling, and saturation only above 6."""
+    xb = quant.synthetic_bf16(16, 1024, name="pin/w4a4err", std=3.0)
+    codes, scales = oracle.mxfp4_quantize(xb)
+    x = oracle.bf16(xb).reshape(16, 32, 32)
+    sc = np.ldexp(1.0, scales.astype(np.int64) - 127)[..., None]
+    v = x / sc
+    q = oracle.mxfp4_dequantize_activations(codes, scales).reshape(16, 32, 32) / sc
+    a = np.abs(v)
+    step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    assert (np.abs(q - v) <= step / 2 + 1e-12)[a <= 6].all()
+    assert (np.abs(q)[a > 6] == 6).all()
+    amax = a.max(-1)
+    assert ((amax >= 4) & (amax < 8)).all()
