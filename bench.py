@@ -22,7 +22,11 @@ After the timed steps the other rows of the hot path are measured on their
 own configurations and reported under "sections" (each with its own unit):
 
     prefill  X [M][5120] x W 17408 x 5120, affine4_g64 and nvfp4,
-             M in 128, 512, 2048, 8192 -> TFLOP/s (2 M N K per launch)
+             M in 128, 512, 2048, 8192 -> TFLOP/s (2 M N K per launch);
+             and W4A4: the same matrix in mxfp4 against activations
+             quantized to mxfp4 on the GPU (against the FP4 MFMA peak)
+    mid      17408 x 5120 at 5, 8 (row-streaming GEMV) and 16 rows (MFMA
+             tiles), affine4_g64 and nvfp4 -> us per call
     moe      512 routed + 1 shared expert, hidden 2048, intermediate 512,
              nvfp4, top-10 of N(0, 1) logits by the library's router, T = 4
              (warm and cold) and 8192
@@ -57,6 +61,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP4_MFMA_PEAK_TFLOPS = 10100.0
 METRIC = "dequant-GEMV weight GB/s (% of HBM peak) at M=1..4; prefill TFLOP/s"
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemv_decode_traffic.json")
 GEMV_SOURCES = ("gemv.hip", "gemv_rows.hip", "gemv_step.h", "qmm_device.h")
@@ -69,7 +74,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
-    ap.add_argument("--sections", default="decode,prefill,moe,fp4")
+    ap.add_argument("--sections", default="decode,prefill,mid,moe,fp4")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     return ap.parse_args()
 
@@ -361,9 +366,59 @@ def prefill_section(q, torch, dev):
     mfma_peak = measured_mfma_peak(q, torch, dev)
     for c in out:
         c["frac_measured_mfma_peak"] = round(c["TFLOPs"] / mfma_peak["TFLOPs"], 4)
+    # W4A4: the same 17408 x 5120 matrix in MXFP4 against activations
+    # quantized to MXFP4 on the GPU (qquant_mxfp4 + FP4 MFMA GEMM, both timed)
+    w4 = []
+    w = q.Weight.from_host(quant.synthetic_weight(F.MXFP4, n, k, name="bench/prefill/w4a4"), dev)
+    for m in (128, 512, 2048, 8192):
+        x = dev_bf16(torch, quant.synthetic_bf16(m, k, name=f"bench/prefill/x{m}"), dev)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        call = q.prepare_gemm_w4a4(w, x, y)
+        med, _ = timed(torch, call, 20 if m <= 512 else 8)
+        tf = 2.0 * m * n * k / (med * 1e-3) / 1e12
+        w4.append({"format": "mxfp4 weights x mxfp4 activations", "m": m, "shape": f"{n}x{k}",
+                   "ms": round(med, 4), "TFLOPs": round(tf, 1),
+                   "frac_fp4_mfma_peak": round(tf / FP4_MFMA_PEAK_TFLOPS, 4),
+                   "frac_bf16_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)})
+        del x, y, call
+    del w
+    torch.cuda.empty_cache()
     return {"unit": "TFLOP/s", "kernel": "gemm_big_kernel (dequant in registers, bf16 MFMA)",
             "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS, "measured_mfma_peak": mfma_peak,
-            "best_at_M_ge_2048": best, "cases": out}
+            "best_at_M_ge_2048": best, "cases": out,
+            "w4a4": {"kernel": "quant_mxfp4_kernel + gemm_w4a4_kernel "
+                               "(v_mfma_scale_f32_32x32x64_f8f6f4)",
+                     "peak_TFLOPs": FP4_MFMA_PEAK_TFLOPS, "cases": w4}}
+
+
+def mid_section(q, torch, dev):
+    """qgemm at 5 and 8 rows (the mid band: the row-streaming GEMV) and 16
+    rows (MFMA tiles) on 17408 x 5120, cold weights: microseconds and weight
+    GB/s."""
+    from synth import formats as F
+    from synth import quant
+    out = []
+    n, k = 17408, 5120
+    for fmt in (F.AFFINE4_G64, F.NVFP4):
+        p = quant.synthetic_weight(fmt, n, k, name=f"bench/mid/{fmt}")
+        w0 = q.Weight.from_host(p, dev)
+        copies = max(2, int(np.ceil(800e6 / w0.nbytes())))
+        ws_ = [w0] + [q.Weight.from_host(p, dev) for _ in range(copies - 1)]
+        del p
+        for m in (5, 8, 16):
+            x = dev_bf16(torch, quant.synthetic_bf16(m, k, name=f"bench/mid/x{m}"), dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            calls = [q.prepare_gemm(w, x, y) for w in ws_]
+            it = iter(range(1 << 30))
+            med, _ = timed(torch, lambda: calls[next(it) % copies](), 4 * copies)
+            out.append({"format": FMT_NAME[fmt], "m": m, "shape": f"{n}x{k}",
+                        "us": round(med * 1e3, 2),
+                        "path": "row-streaming GEMV" if m <= 8 else "MFMA tiles",
+                        "weight_GBps": round(w0.nbytes() / (med * 1e-3) / 1e9, 1)})
+            del x, y, calls
+        del ws_, w0
+        torch.cuda.empty_cache()
+    return {"unit": "us per call", "cases": out}
 
 
 def moe_section(q, torch, dev):
@@ -583,6 +638,8 @@ def main():
     extra = {}
     if "prefill" in sections:
         extra["prefill"] = prefill_section(q, torch, dev)
+    if "mid" in sections:
+        extra["mid"] = mid_section(q, torch, dev)
     if "moe" in sections:
         extra["moe"] = moe_section(q, torch, dev)
     if "fp4" in sections:

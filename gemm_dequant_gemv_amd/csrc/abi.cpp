@@ -209,6 +209,49 @@ int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, v
       qmm::launch_gemm_big(*w, x, m, residual, y, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
+int qquant_mxfp4(const void *x, int32_t m, int32_t k, void *codes, void *scales, void *stream) {
+  if (!x || !codes || !scales) return QMM_ERR_NULL;
+  if (m < 1) return QMM_ERR_M_RANGE;
+  if (k < 32 || k % 32 != 0 || (uint64_t)m * (uint64_t)k >= (1ull << 32)) return QMM_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(codes, 16)) return QMM_ERR_ALIGN;
+  const Range rx = range(x, (size_t)m * k * 2);
+  const Range rc = range(codes, (size_t)m * (k / 2));
+  const Range rs = range(scales, (size_t)m * (k / 32));
+  if (overlap(rc, rx) || overlap(rs, rx) || overlap(rc, rs)) return QMM_ERR_ALIAS;
+  return hip_status(qmm::launch_quant_mxfp4(x, m, k, codes, scales, (hipStream_t)stream));
+}
+
+size_t qgemm_w4a4_workspace_size(const qmm_weight *w, int32_t m) {
+  if (check_weight(w) || w->format != QMM_MXFP4 || w->batch != 1 || m < 1) return 0;
+  return qmm::w4a4_workspace_size(m, w->k);
+}
+
+int qgemm_w4a4(const qmm_weight *w, const void *x, int32_t m, const void *residual, void *y,
+               void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_weight(w);
+  if (st) return st;
+  if (w->format != QMM_MXFP4) return QMM_ERR_FORMAT;
+  if (w->batch != 1) return QMM_ERR_SHAPE;
+  if (m < 1) return QMM_ERR_M_RANGE;
+  if (!qmm::w4a4_fits(*w, m)) return QMM_ERR_SHAPE;
+  if (!x || !y) return QMM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16) || (residual && !aligned(residual, 16)))
+    return QMM_ERR_ALIGN;
+  const size_t need = qmm::w4a4_workspace_size(m, w->k);
+  if (!workspace || workspace_bytes < need) return QMM_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return QMM_ERR_ALIGN;
+  const Range ry = range(y, (size_t)m * w->n * 2);
+  const Range rw = range(workspace, need);
+  Range ins[8];
+  int ni = weight_ranges(*w, ins);
+  ins[ni++] = range(x, (size_t)m * w->k * 2);
+  if (residual) ins[ni++] = range(residual, (size_t)m * w->n * 2);
+  if (overlap(ry, rw)) return QMM_ERR_ALIAS;
+  for (int i = 0; i < ni; ++i)
+    if (overlap(ry, ins[i]) || overlap(rw, ins[i])) return QMM_ERR_ALIAS;
+  return hip_status(qmm::launch_gemm_w4a4(*w, x, m, residual, y, workspace, (hipStream_t)stream));
+}
+
 size_t qmoe_workspace_size(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
                            int32_t num_shared, int32_t t, int32_t topk) {
   if (check_weight(gate_up) || check_weight(down) || num_routed < 1 || num_shared < 0 ||

@@ -130,6 +130,14 @@ hipError_t launch_moe_logits(const qmm_weight &gu, const qmm_weight &dn, int num
                              int32_t *topk_ids, float *topk_w, int topk, const float *shared_w,
                              void *y, int y_dtype, void *workspace, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+// W4A4 (w4a4.hip): MXFP4 activation quantizer and the FP4 x FP4 GEMM; the
+// workspace holds the quantized activations (codes, then E8M0 scales)
+size_t w4a4_workspace_size(int m, int k);
+bool w4a4_fits(const qmm_weight &w, int m);
+hipError_t launch_quant_mxfp4(const void *x, int m, int k, void *codes, void *scales,
+                              hipStream_t s);
+hipError_t launch_gemm_w4a4(const qmm_weight &w, const void *x, int m, const void *residual,
+                            void *y, void *workspace, hipStream_t s);
 // the static scratch of qmoe_grouped_noalloc (noalloc.hip): its size, and the
 // device address of the current device's copy (looked up once per device)
 constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;

@@ -1,0 +1,305 @@
+// W4A4: both operands of the multiply in MXFP4 ("TurboEXL3" section 2.2, the
+// W4A4 bullet: the activations are quantized to a 4-bit block format on the
+// fly, so both operands are FP4; section 2.1: MXFP4 is E2M1 values with one
+// E8M0 power-of-two scale per 32).  gfx950's block-scaled matrix cores take
+// exactly this pair: v_mfma_scale_f32_32x32x64_f8f6f4 multiplies E2M1 codes
+// of both operands, each lane's 32 values scaled by its own E8M0 byte.
+//
+//   quant_mxfp4_kernel: x bf16 [m][k] -> codes u8 [m][k/2] and E8M0 u8
+//     [m][k/32].  One thread per block of 32: amax, the shared exponent
+//     E = floor(log2 amax) - 2 (E8M0 = max(E + 127, 0); an all-zero block
+//     gets 0 and zero codes), then every value times 2^-E compared with the
+//     E2M1 decision points (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; a value on a
+//     point goes to the neighbour with the even index; past 6 saturates),
+//     sign in bit 3, a value that rounds to zero coded 0.
+//   gemm_w4a4_kernel: the product of the MXFP4 weights and the quantized
+//     activations, float32 sums, bf16 y (+ residual).  A workgroup of 8 waves
+//     owns 256 weight rows x 32 TM activation rows; per 128-wide K slice the
+//     activation codes and scales go from memory straight into LDS (three
+//     slices in flight) and each wave loads its own 32 weight rows' codes and
+//     scales into registers (three slices ahead).  The codes are the MFMA
+//     operands as they are: there is no decode step.  Inside a slice, lane
+//     half h multiplies K blocks 2h and 2h + 1 (k-steps 0 and 1) for both
+//     operands, so a lane reads 32 contiguous code bytes of its weight row.
+//   The products of E2M1 values and powers of two are exact; only the float32
+//   sums round, in a fixed order (slices in order, the two lane halves inside
+//   the matrix core).
+#include "qmm_device.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+namespace {
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_w __attribute__((ext_vector_type(16)));
+
+constexpr int kSliceK = 128;         // K values per slice: two k-steps of 64
+constexpr int kRowBytes = 64;        // code bytes of one row per slice
+constexpr int kW4Stages = 3;         // slices in flight
+constexpr int kW4Waves = 8;
+constexpr int kW4BN = 32 * kW4Waves; // weight rows per workgroup
+
+// ---------------------------------------------------------------- quantizer
+
+__global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t *__restrict__ x,
+                                                          uint8_t *__restrict__ codes,
+                                                          uint8_t *__restrict__ scales,
+                                                          uint32_t blocks) {
+  const uint32_t b = blockIdx.x * 256u + threadIdx.x;
+  if (b >= blocks) return;
+  const uint4 *src = (const uint4 *)(x + (size_t)b * 32);
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = src[i];
+    w[4 * i] = v.x;
+    w[4 * i + 1] = v.y;
+    w[4 * i + 2] = v.z;
+    w[4 * i + 3] = v.w;
+  }
+  // largest magnitude, as bfloat16 bits (finite values order as integers)
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  uint32_t e8 = 0;
+  int sh = 0;  // the values are multiplied by 2^sh = 2^(127 - E8M0)
+  if (amax != 0) {
+    const int ex = (int)(amax >> 7);
+    // floor(log2 amax): the exponent field, or for a subnormal mantissa m
+    // (value m * 2^-133) the position of its top bit
+    const int fl = ex > 0 ? ex - 127 : (31 - __builtin_clz(amax & 0x7Fu)) - 133;
+    const int e8i = max(fl - 2 + 127, 0);
+    e8 = (uint32_t)e8i;
+    sh = 127 - e8i;
+  }
+  uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t hbits = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    const float a = __builtin_ldexpf(__uint_as_float((hbits & 0x7FFFu) << 16), sh);
+    const uint32_t idx = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                         (uint32_t)(a > 5.0f);
+    const uint32_t code = idx ? (idx | ((hbits >> 12) & 8u)) : 0u;
+    out[j >> 3] |= code << (4 * (j & 7));
+  }
+  *(uint4 *)(codes + (size_t)b * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+  scales[b] = (uint8_t)e8;
+}
+
+// ---------------------------------------------------------------- GEMM
+
+struct W4A4Args {
+  const uint8_t *wcodes, *wscales;  // MXFP4 weight [n][k/2], [n][k/32]
+  const uint8_t *xcodes, *xscales;  // quantized activations [m][k/2], [m][k/32]
+  const uint16_t *residual;         // bf16 [m][n] or null
+  uint16_t *y;                      // bf16 [m][n]
+  int m, n, k;
+};
+
+// Physical 16-byte chunk of logical chunk c of activation row r in a slice's
+// LDS image (64 bytes per row): the 16 rows one ds_read_b128 lane group reads
+// at one logical chunk land on 16 distinct bank groups.
+__device__ __forceinline__ int xchunk(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+template <int TM>
+__global__ __launch_bounds__(64 * kW4Waves) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_w4a4_kernel(W4A4Args a) {
+  constexpr int BM = 32 * TM;
+  constexpr int kCodeStage = BM * kRowBytes;  // activation codes of one slice
+  constexpr int kStage = kCodeStage + BM * 4; // + their scales (4 per row)
+  constexpr int XI = BM / 16 / kW4Waves;      // code-load instructions per wave and slice
+  constexpr int SI = BM / 64;                 // scale-load instructions per slice
+  static_assert(XI >= 1 && XI * 16 * kW4Waves == BM && SI >= 1 && SI <= kW4Waves, "tiles");
+  constexpr int kLoads = XI + 1 + 3;          // per wave and slice: X codes, X scales, W
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, h = lane >> 5;
+  const int tiles_m = (a.m + BM - 1) / BM;
+  const int m0 = ((int)blockIdx.x % tiles_m) * BM;
+  const int n0 = ((int)blockIdx.x / tiles_m) * kW4BN;
+  const int mrows = a.m - m0;
+  const int slices = a.k / kSliceK;
+  const uint32_t kb = (uint32_t)a.k / 2, kq = (uint32_t)a.k / 32;
+
+  // activation codes: lane L of this wave's instruction i writes LDS piece
+  // P = (wave + 8 i) 64 + L of the stage, i.e. row P / 4, physical chunk
+  // P % 4, which holds the row's logical chunk xchunk(row, P % 4)
+  const __amdgpu_buffer_rsrc_t rxc = make_rsrc(a.xcodes, (uint32_t)((size_t)a.m * kb));
+  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(a.xscales, (uint32_t)((size_t)a.m * kq));
+  uint32_t v_x[XI];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int P = (wave + kW4Waves * i) * 64 + lane;
+    const int r = P >> 2;
+    v_x[i] = (uint32_t)(m0 + min(r, mrows - 1)) * kb + (uint32_t)xchunk(r, P & 3) * 16u;
+  }
+  // activation scales: instruction wave % SI covers rows 64 (wave % SI) ..;
+  // waves past SI repeat one (the same bytes to the same place)
+  const int si = wave % SI;
+  const uint32_t v_xs = (uint32_t)(m0 + min(si * 64 + lane, mrows - 1)) * kq;
+  auto load_x = [&](int s) __attribute__((always_inline)) {
+    uint8_t *st = lds + (s % kW4Stages) * kStage;
+#pragma unroll
+    for (int i = 0; i < XI; ++i)
+      buffer_load_lds16(rxc, st + (wave + kW4Waves * i) * 1024, v_x[i], (uint32_t)s * kRowBytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, (lds_void_t *)(st + kCodeStage + si * 256), 4,
+                                             v_xs, (uint32_t)s * 4u, 0, 0);
+  };
+
+  // weights: lane (lr, h) holds weight row n0 + 32 wave + lr; per slice its
+  // code bytes 32 h .. 32 h + 31 (K blocks 2h, 2h + 1) and the row's 4 scales
+  const __amdgpu_buffer_rsrc_t rwc = make_rsrc(a.wcodes, (uint32_t)((size_t)a.n * kb));
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(a.wscales, (uint32_t)((size_t)a.n * kq));
+  const uint32_t wrow = (uint32_t)min(n0 + 32 * wave + lr, a.n - 1);
+  const uint32_t v_wc = wrow * kb + 32u * (uint32_t)h, v_ws = wrow * kq;
+  struct WPiece {
+    u32x4_t q0, q1;  // K blocks 2h, 2h + 1
+    uint32_t s;      // the row's 4 E8M0 scales of the slice
+  };
+  auto load_w = [&](int s) __attribute__((always_inline)) {
+    WPiece p;
+    p.q0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rwc, v_wc, (uint32_t)s * kRowBytes, 2));
+    p.q1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rwc, v_wc, (uint32_t)s * kRowBytes + 16u, 2));
+    p.s = __builtin_amdgcn_raw_buffer_load_b32(rws, v_ws, (uint32_t)s * 4u, 0);
+    return p;
+  };
+  WPiece wr[kW4Stages];
+
+  f32x16_w acc[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+
+  // this lane's activation operand reads: row 32 t + lr, logical chunk
+  // 2h + ks at its physical place ((32 t + lr) >> 2 & 3 = lr >> 2 & 3)
+  uint32_t xo[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) xo[ks] = (uint32_t)lr * kRowBytes + (uint32_t)xchunk(lr, 2 * h + ks) * 16u;
+  const int sshift0 = 8 * (2 * h), sshift1 = 8 * (2 * h + 1);
+
+#pragma unroll
+  for (int p = 0; p < kW4Stages - 1; ++p) {
+    const int sp = min(p, slices - 1);
+    load_x(sp);
+    wr[p] = load_w(sp);
+  }
+
+  for (int s0 = 0; s0 < slices; s0 += kW4Stages) {
+#pragma unroll
+    for (int u = 0; u < kW4Stages; ++u) {
+      const int s = s0 + u;
+      if (s >= slices) break;  // uniform
+      // slice s is in LDS (this wave's share) once at most the loads of the
+      // kW4Stages - 2 slices issued after it are outstanding; the barrier
+      // makes every wave's share visible and frees the stage of slice s - 1
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((kW4Stages - 2) * kLoads));
+      __builtin_amdgcn_s_barrier();
+      const int sn = min(s + kW4Stages - 1, slices - 1);
+      load_x(sn);
+      wr[(u + kW4Stages - 1) % kW4Stages] = load_w(sn);
+
+      const uint8_t *stg = lds + (s % kW4Stages) * kStage;
+      const WPiece &wp = wr[u];
+      const int sa0 = (int)((wp.s >> sshift0) & 0xFFu), sa1 = (int)((wp.s >> sshift1) & 0xFFu);
+      const v8i_t a0 = {(int)wp.q0.x, (int)wp.q0.y, (int)wp.q0.z, (int)wp.q0.w, 0, 0, 0, 0};
+      const v8i_t a1 = {(int)wp.q1.x, (int)wp.q1.y, (int)wp.q1.z, (int)wp.q1.w, 0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const uint8_t *row = stg + t * 32 * kRowBytes;
+        const u32x4_t b0 = *(const u32x4_t *)(row + xo[0]);
+        const u32x4_t b1 = *(const u32x4_t *)(row + xo[1]);
+        const uint32_t xsc = *(const uint32_t *)(stg + kCodeStage + (32 * t + lr) * 4);
+        const v8i_t bv0 = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
+        const v8i_t bv1 = {(int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w, 0, 0, 0, 0};
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            a0, bv0, acc[t], 4, 4, 0, sa0, 0, (int)((xsc >> sshift0) & 0xFFu));
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            a1, bv1, acc[t], 4, 4, 0, sa1, 0, (int)((xsc >> sshift1) & 0xFFu));
+      }
+    }
+  }
+
+  // epilogue: lane (lr, h) holds D[n = 8b + 4h + r][m = lr] of each tile as
+  // value 4b + r: four consecutive weight rows per b
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    const int ml = 32 * t + lr;
+    if (ml >= mrows) continue;
+    const int m = m0 + ml;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int nb = n0 + 32 * wave + 8 * b + 4 * h;
+      float v[4] = {acc[t][4 * b], acc[t][4 * b + 1], acc[t][4 * b + 2], acc[t][4 * b + 3]};
+      const size_t base = (size_t)m * a.n + nb;
+      if (nb + 3 < a.n && (a.n & 3) == 0) {  // 8-byte aligned: 4 bf16 at once
+        if (a.residual) {
+          const uint2 r = *(const uint2 *)(a.residual + base);
+          v[0] += bf_lo(r.x);
+          v[1] += bf_hi(r.x);
+          v[2] += bf_lo(r.y);
+          v[3] += bf_hi(r.y);
+        }
+        *(uint2 *)(a.y + base) = make_uint2(float_to_bf16(v[0]) | (float_to_bf16(v[1]) << 16),
+                                            float_to_bf16(v[2]) | (float_to_bf16(v[3]) << 16));
+        continue;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (nb + r >= a.n) break;
+        float o = v[r];
+        if (a.residual) o += bf_lo(a.residual[base + r]);
+        a.y[base + r] = (uint16_t)float_to_bf16(o);
+      }
+    }
+  }
+}
+
+constexpr size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t w4a4_workspace_size(int m, int k) {
+  return align256((size_t)m * (size_t)(k / 2)) + align256((size_t)m * (size_t)(k / 32));
+}
+
+bool w4a4_fits(const qmm_weight &w, int m) {
+  // 32-bit buffer offsets for both operands' planes
+  return (size_t)m * (size_t)(w.k / 2) < (1ull << 32) && (size_t)w.n * (size_t)(w.k / 2) < (1ull << 32);
+}
+
+hipError_t launch_quant_mxfp4(const void *x, int m, int k, void *codes, void *scales,
+                              hipStream_t s) {
+  const uint32_t blocks = (uint32_t)((size_t)m * (size_t)(k / 32));
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_mxfp4_kernel, dim3((blocks + 255) / 256), dim3(256), 0, s,
+                     (const uint16_t *)x, (uint8_t *)codes, (uint8_t *)scales, blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a4(const qmm_weight &w, const void *x, int m, const void *residual,
+                            void *y, void *workspace, hipStream_t s) {
+  uint8_t *xc = (uint8_t *)workspace;
+  uint8_t *xs = xc + align256((size_t)m * (size_t)(w.k / 2));
+  hipError_t e = launch_quant_mxfp4(x, m, w.k, xc, xs, s);
+  if (e != hipSuccess) return e;
+  W4A4Args a;
+  a.wcodes = (const uint8_t *)w.codes;
+  a.wscales = (const uint8_t *)w.scales;
+  a.xcodes = xc;
+  a.xscales = xs;
+  a.residual = (const uint16_t *)residual;
+  a.y = (uint16_t *)y;
+  a.m = m;
+  a.n = w.n;
+  a.k = w.k;
+  constexpr int TM = 8;
+  constexpr size_t lds = (size_t)kW4Stages * (32 * TM * kRowBytes + 32 * TM * 4);
+  const unsigned grid = (unsigned)(((m + 32 * TM - 1) / (32 * TM)) * ((w.n + kW4BN - 1) / kW4BN));
+  hipLaunchKernelGGL((gemm_w4a4_kernel<TM>), dim3(grid), dim3(64 * kW4Waves), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace qmm

@@ -22,7 +22,8 @@ FORMATS = {"affine4_g64": AFFINE4_G64, "mxfp4": MXFP4, "nvfp4": NVFP4, "q6_k": Q
 
 ENTRY_POINTS = ("qdequant", "qgemv", "qgemv_workspace_size", "qgemm", "qgemm_workspace_size",
                 "qmoe_grouped", "qmoe_workspace_size", "qmoe_workspace_layout", "qmoe_router",
-                "qmoe_grouped_logits", "qmoe_grouped_noalloc",
+                "qmoe_grouped_logits", "qmoe_grouped_noalloc", "qquant_mxfp4",
+                "qgemm_w4a4_workspace_size", "qgemm_w4a4",
                 "qworkspace_init", "qbench_stream_read", "qbench_mfma_peak", "qstatus_string",
                 "qlast_hip_error")
 
@@ -68,6 +69,10 @@ def _lib():
         lib.qgemm_workspace_size.argtypes = [P, I32]
         lib.qgemm_workspace_size.restype = SZ
         lib.qgemm.argtypes = [P, VP, I32, VP, VP, VP, SZ, VP]
+        lib.qquant_mxfp4.argtypes = [VP, I32, I32, VP, VP, VP]
+        lib.qgemm_w4a4_workspace_size.argtypes = [P, I32]
+        lib.qgemm_w4a4_workspace_size.restype = SZ
+        lib.qgemm_w4a4.argtypes = [P, VP, I32, VP, VP, VP, SZ, VP]
         lib.qmoe_workspace_size.argtypes = [P, P, I32, I32, I32, I32]
         lib.qmoe_workspace_size.restype = SZ
         lib.qmoe_workspace_layout.argtypes = [P, P, I32, I32, I32, I32, ctypes.POINTER(QmoeLayoutC)]
@@ -273,6 +278,53 @@ def gemm(w: Weight, x, residual=None, out=None, workspace=None, stream=None):
     _check(_lib().qgemm(w.c, _ptr(x), m, _ptr(residual), _ptr(out), _ptr(workspace), ws_bytes,
                         _stream(stream)), "qgemm")
     return out
+
+
+def quant_mxfp4(x, codes=None, scales=None, stream=None):
+    """qquant_mxfp4: bf16 x [m][k] -> (codes uint8 [m][k/2], E8M0 scales
+    uint8 [m][k/32])."""
+    _tensor("qquant_mxfp4", "x", x, _BF16)
+    if x.dim() != 2:
+        raise ValueError(f"qquant_mxfp4: x must be 2-D [m][k], got {tuple(x.shape)}")
+    m, k = x.shape
+    dev = x.device
+    if codes is not None:
+        _tensor("qquant_mxfp4", "codes", codes, _U8, (m, k // 2), dev)
+    if scales is not None:
+        _tensor("qquant_mxfp4", "scales", scales, _U8, (m, k // 32), dev)
+    _require_gpu("qquant_mxfp4", dev)
+    if codes is None:
+        codes = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((m, k // 32), dtype=torch.uint8, device=dev)
+    _check(_lib().qquant_mxfp4(_ptr(x), m, k, _ptr(codes), _ptr(scales), _stream(stream)),
+           "qquant_mxfp4")
+    return codes, scales
+
+
+def gemm_w4a4_workspace_size(w: Weight, m: int) -> int:
+    return int(_lib().qgemm_w4a4_workspace_size(w.c, m))
+
+
+def gemm_w4a4(w: Weight, x, residual=None, out=None, workspace=None, stream=None):
+    """W4A4: y[m][n] = bf16(sum_k w[n][k] q(x)[m][k] (+ residual)), MXFP4 w,
+    x bf16 [m][k] quantized to MXFP4 on the GPU."""
+    dev, m = _check_gemv("qgemm_w4a4", w, x, residual, out, workspace, _BF16)
+    if out is None:
+        out = torch.empty((m, w.n), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(gemm_w4a4_workspace_size(w, m), 1), dtype=torch.uint8,
+                                device=dev)
+    _check(_lib().qgemm_w4a4(w.c, _ptr(x), m, _ptr(residual), _ptr(out), _ptr(workspace),
+                             workspace.numel(), _stream(stream)), "qgemm_w4a4")
+    return out
+
+
+def prepare_gemm_w4a4(w: Weight, x, out, residual=None, stream=None):
+    _, m = _check_gemv("qgemm_w4a4", w, x, residual, out, None, _BF16)
+    ws = torch.empty(max(gemm_w4a4_workspace_size(w, m), 1), dtype=torch.uint8, device=x.device)
+    return _Prepared("qgemm_w4a4", (w.c, _ptr(x), m, _ptr(residual), _ptr(out), _ptr(ws),
+                                    ws.numel(), _stream(stream)), (w, x, out, residual, ws))
 
 
 def moe_workspace_size(gate_up: Weight, down: Weight, num_routed: int, num_shared: int,

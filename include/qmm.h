@@ -258,6 +258,48 @@ int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, v
  * (route, gate/up, down, combine; section 4.1).  qmoe_workspace_layout says
  * which form a call takes.
  */
+/*
+ * qquant_mxfp4 -- quantize bfloat16 activations to MXFP4 on the GPU, the
+ * activation half of W4A4 ("TurboEXL3", section 2.2, W4A4 bullet: the
+ * activations are quantized to a 4-bit block format on the fly; section 2.1,
+ * MXFP4: E2M1 values with one E8M0 power-of-two scale per 32).  Per row of x
+ * and block of 32 values along K: E = floor(log2 amax) - 2 (the largest E2M1
+ * magnitude is 1.5 * 2^2), stored as E8M0 = max(E + 127, 0); each value is
+ * divided by 2^(E8M0 - 127) and rounded to the nearest E2M1 value, ties to
+ * the even code, past 6 saturating to 6; a value that rounds to zero gets
+ * code 0; an all-zero block gets E8M0 0 and zero codes.
+ *
+ * x       bf16 [m][k], finite values, 16-byte aligned; k a multiple of 32
+ * codes   u8 [m][k/2] (out), element 2j in the low nibble of byte j, 16-byte
+ *         aligned
+ * scales  u8 [m][k/32] (out), E8M0
+ * The outputs must not overlap x or each other (QMM_ERR_ALIAS).
+ */
+int qquant_mxfp4(const void *x, int32_t m, int32_t k, void *codes, void *scales, void *stream);
+
+/*
+ * qgemm_w4a4 -- W4A4 matrix multiply: MXFP4 weights times activations
+ * quantized to MXFP4 on the fly (qquant_mxfp4, into the workspace), both
+ * operands multiplied as FP4 on the block-scaled matrix cores with float32
+ * sums ("TurboEXL3", section 2.2, W4A4 bullet).  The result differs from the
+ * W4A16 qgemm by design: every activation is rounded to 4 bits.
+ *
+ *   y[m][n] = bf16( sum_k w[n][k] * q(x)[m][k]  (+ residual[m][n]) )
+ *
+ * w          one MXFP4 matrix (QMM_ERR_FORMAT otherwise), batch 1
+ * x          bf16 [m][k], m >= 1, finite; residual bf16 [m][n] or NULL
+ * y          bf16 [m][n], rounded to nearest even
+ * x, y and residual 16-byte aligned; m * k / 2 and n * k / 2 below 4 GiB
+ * workspace  at least qgemm_w4a4_workspace_size(w, m) bytes, 256-byte
+ *            aligned, any contents: the quantized activations (codes, then
+ *            E8M0 scales at the next 256-byte boundary)
+ * Two launches on the stream (quantizer, GEMM).  The products are exact;
+ * sums run in a fixed order, so results are the same on every run.
+ */
+size_t qgemm_w4a4_workspace_size(const qmm_weight *w, int32_t m);
+int qgemm_w4a4(const qmm_weight *w, const void *x, int32_t m, const void *residual, void *y,
+               void *workspace, size_t workspace_bytes, void *stream);
+
 size_t qmoe_workspace_size(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
                            int32_t num_shared, int32_t t, int32_t topk);
 int qmoe_grouped(const qmm_weight *gate_up, const qmm_weight *down, int32_t num_routed,
