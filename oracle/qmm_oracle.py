@@ -55,6 +55,14 @@ What it computes, and where the pages define it:
   code, magnitudes past 6 saturating to 6, a value that rounds to zero taking
   code 0.  The product is then the exact sum of the dequantized weights times
   the dequantized activation codes.
+* The EXL3 rotation stages ("TurboEXL3" section 3.1, prepare and finish;
+  section 2.3: sign-randomized Hadamard transforms in blocks of 128, with one
+  16-bit scale per input and per output channel as the only scales), on
+  their own: prepare(x) = bf16(H (s_in * x)) and finish(y) = s_out * (H y),
+  block by block of 128 values, H the orthonormal 128-point Hadamard matrix
+  H_128 / sqrt(128) built by Sylvester's doubling (H_1 = [1], H_2n = [[H_n,
+  H_n], [H_n, -H_n]]), the random signs carried by the sign bits of the
+  float16 channel scales.
 * Alongside every output, its magnitude sum sum_k |w||x| (+ |r|), which sets the
   tolerance |y - y_ref| <= 2e-3 * magnitude.
 
@@ -370,6 +378,53 @@ def gemm_w4a4(p, x_bits, residual_bits=None, rows=None):
         y = y + r
         mag = mag + np.abs(r)
     return y, mag
+
+
+# ------------------------------------------------------------ Hadamard stages
+
+HADAMARD_BLOCK = 128
+
+
+def sylvester_hadamard(n: int) -> np.ndarray:
+    """The n x n Sylvester Hadamard matrix (n a power of two), entries +-1."""
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def _blocks_transform(v):
+    """[rows][len] -> each 128-block multiplied by H_128 / sqrt(128)."""
+    rows, ln = v.shape
+    h = sylvester_hadamard(HADAMARD_BLOCK) / np.sqrt(HADAMARD_BLOCK)
+    b = v.reshape(rows, ln // HADAMARD_BLOCK, HADAMARD_BLOCK)
+    return (b @ h.T).reshape(rows, ln)
+
+
+def hadamard_prepare(x_bits, scale_f16=None):
+    """Prepare stage: bf16 x [m][k] -> (float64 H(s * x) before its output
+    rounding [m][k], bf16 bits of it, magnitude sum per output
+    sum |H_ij| |s_j x_j| = sum |s_j x_j| / sqrt(128) over the block)."""
+    x = bf16(x_bits)
+    s = np.ones(x.shape[1]) if scale_f16 is None else fp16(scale_f16)
+    v = x * s
+    y = _blocks_transform(v)
+    m, k = v.shape
+    mag = np.repeat(np.abs(v).reshape(m, k // HADAMARD_BLOCK, HADAMARD_BLOCK).sum(-1)
+                    / np.sqrt(HADAMARD_BLOCK), HADAMARD_BLOCK, axis=-1).reshape(m, k)
+    return y, bf16_round(y.astype(np.float32)), mag
+
+
+def hadamard_finish(y, scale_f16=None):
+    """Finish stage: float32 y [m][n] -> (float64 s * H y [m][n], magnitude
+    sum |s| sum |y| / sqrt(128) over the block)."""
+    v = np.asarray(y, np.float64)
+    s = np.ones(v.shape[1]) if scale_f16 is None else fp16(scale_f16)
+    out = _blocks_transform(v) * s
+    m, n = v.shape
+    mag = np.repeat(np.abs(v).reshape(m, n // HADAMARD_BLOCK, HADAMARD_BLOCK).sum(-1)
+                    / np.sqrt(HADAMARD_BLOCK), HADAMARD_BLOCK, axis=-1).reshape(m, n) * np.abs(s)
+    return out, mag
 
 
 def within_tolerance(y, y_ref, mag, rel: float = 2e-3):

@@ -692,3 +692,53 @@ def test_mxfp4_quantizer_error_bound_and_scale():
     assert (np.abs(q)[a > 6] == 6).all()
     amax = a.max(-1)
     assert ((amax >= 4) & (amax < 8)).all()
+
+
+# ------------------------------------------------------------ Hadamard stages
+
+def test_sylvester_hadamard_is_the_library_matrix():
+    """The oracle's H_128 is scipy's Hadamard matrix (Sylvester's
+    construction) and H H^T = 128 I."""
+    from scipy.linalg import hadamard
+    h = oracle.sylvester_hadamard(128)
+    assert np.array_equal(h, hadamard(128))
+    assert np.array_equal(h @ h.T, 128 * np.eye(128))
+
+
+def test_hadamard_prepare_closed_forms():
+    """A one-hot block gives column j of H / sqrt(128) (entries +-2^-3.5) times
+    the channel scale; a constant block gives sqrt(128) c at index 0 and zero
+    elsewhere; blocks are independent; the transform preserves the norm."""
+    from scipy.linalg import hadamard
+    k = 256
+    x = np.zeros((3, k))
+    x[0, 5] = 1.0                  # one-hot in block 0
+    x[1, 128:] = 0.5               # constant block 1
+    x[2, 130] = -2.0
+    s = np.ones(k, np.float16)
+    s[5] = -1.0                    # a negative scale flips the sign
+    y, _, _ = oracle.hadamard_prepare(quant.bf16_bits(x), s.view(np.uint16))
+    np.testing.assert_allclose(y[0, :128], -hadamard(128)[:, 5] / np.sqrt(128), rtol=1e-15)
+    assert (y[0, 128:] == 0).all()
+    np.testing.assert_allclose(y[1, 128], 0.5 * np.sqrt(128), rtol=1e-15)
+    assert np.abs(y[1, 129:]).max() < 1e-15 and (y[1, :128] == 0).all()
+    np.testing.assert_allclose(y[2, 128:], -2.0 * hadamard(128)[:, 2] / np.sqrt(128), rtol=1e-15)
+    xr = quant.synthetic_bf16(4, 512, name="pin/had")
+    yr, _, _ = oracle.hadamard_prepare(xr)
+    xb = oracle.bf16(xr).reshape(4, 4, 128)
+    np.testing.assert_allclose(np.linalg.norm(yr.reshape(4, 4, 128), axis=-1),
+                               np.linalg.norm(xb, axis=-1), rtol=1e-12)
+
+
+def test_hadamard_finish_inverts_prepare():
+    """H / sqrt(128) is symmetric and orthogonal, so finish (unit scales)
+    applied to prepare's exact output returns the scaled input; with scales
+    the finish multiplies after the transform."""
+    x = quant.synthetic_bf16(3, 384, name="pin/had2")
+    s = (rng.uniform_matrix(rng.BASE_SEED, "pin/hads", 1, 384)[0] * 2 - 1).astype(np.float16)
+    y, _, _ = oracle.hadamard_prepare(x, s.view(np.uint16))
+    back, _ = oracle.hadamard_finish(y)
+    np.testing.assert_allclose(back, oracle.bf16(x) * s.astype(np.float64), rtol=1e-12, atol=1e-12)
+    out, mag = oracle.hadamard_finish(y, s.view(np.uint16))
+    np.testing.assert_allclose(out, back * s.astype(np.float64), rtol=1e-15)
+    assert (mag >= np.abs(out) - 1e-12).all()
