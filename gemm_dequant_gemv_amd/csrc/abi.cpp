@@ -209,6 +209,40 @@ int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, v
       qmm::launch_gemm_big(*w, x, m, residual, y, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
+namespace {
+
+int hadamard_check(const void *in, int32_t m, int32_t len, size_t in_esz, const void *scale,
+                   const void *out, size_t out_esz) {
+  if (!in || !out) return QMM_ERR_NULL;
+  if (m < 1) return QMM_ERR_M_RANGE;
+  if (len < 128 || len % 128 != 0 || (uint64_t)m * (uint64_t)len >= (1ull << 31))
+    return QMM_ERR_SHAPE;
+  if (!aligned(in, in_esz) || !aligned(out, out_esz) || (scale && !aligned(scale, 2)))
+    return QMM_ERR_ALIGN;
+  const Range ro = range(out, (size_t)m * len * out_esz);
+  if (overlap(ro, range(in, (size_t)m * len * in_esz))) return QMM_ERR_ALIAS;
+  if (scale && overlap(ro, range(scale, (size_t)len * 2))) return QMM_ERR_ALIAS;
+  return QMM_OK;
+}
+
+}  // namespace
+
+int qhadamard_prepare(const void *x, int32_t m, int32_t k, const void *in_scale, void *out,
+                      void *stream) {
+  const int st = hadamard_check(x, m, k, 2, in_scale, out, 2);
+  if (st) return st;
+  return hip_status(qmm::launch_hadamard(true, x, m, k, in_scale, out, 1, (hipStream_t)stream));
+}
+
+int qhadamard_finish(const float *y, int32_t m, int32_t n, const void *out_scale, void *out,
+                     int32_t out_dtype, void *stream) {
+  if (out_dtype != QMM_F32 && out_dtype != QMM_BF16) return QMM_ERR_DTYPE;
+  const int st = hadamard_check(y, m, n, 4, out_scale, out, out_dtype == QMM_F32 ? 4 : 2);
+  if (st) return st;
+  return hip_status(qmm::launch_hadamard(false, y, m, n, out_scale, out, out_dtype == QMM_BF16,
+                                         (hipStream_t)stream));
+}
+
 int qquant_mxfp4(const void *x, int32_t m, int32_t k, void *codes, void *scales, void *stream) {
   if (!x || !codes || !scales) return QMM_ERR_NULL;
   if (m < 1) return QMM_ERR_M_RANGE;

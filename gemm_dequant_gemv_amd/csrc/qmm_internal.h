@@ -130,6 +130,10 @@ hipError_t launch_moe_logits(const qmm_weight &gu, const qmm_weight &dn, int num
                              int32_t *topk_ids, float *topk_w, int topk, const float *shared_w,
                              void *y, int y_dtype, void *workspace, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+// EXL3 rotation stages (hadamard.hip): prepare (bf16 in and out) or finish
+// (float32 in, float32 or bf16 out), per 128-value block
+hipError_t launch_hadamard(bool prepare, const void *in, int rows, int len, const void *scale,
+                           void *out, int out_bf16, hipStream_t s);
 // W4A4 (w4a4.hip): MXFP4 activation quantizer and the FP4 x FP4 GEMM; the
 // workspace holds the quantized activations (codes, then E8M0 scales)
 size_t w4a4_workspace_size(int m, int k);

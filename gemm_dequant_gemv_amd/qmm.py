@@ -23,6 +23,7 @@ FORMATS = {"affine4_g64": AFFINE4_G64, "mxfp4": MXFP4, "nvfp4": NVFP4, "q6_k": Q
 ENTRY_POINTS = ("qdequant", "qgemv", "qgemv_workspace_size", "qgemm", "qgemm_workspace_size",
                 "qmoe_grouped", "qmoe_workspace_size", "qmoe_workspace_layout", "qmoe_router",
                 "qmoe_grouped_logits", "qmoe_grouped_noalloc", "qquant_mxfp4",
+                "qhadamard_prepare", "qhadamard_finish",
                 "qgemm_w4a4_workspace_size", "qgemm_w4a4",
                 "qworkspace_init", "qbench_stream_read", "qbench_mfma_peak", "qstatus_string",
                 "qlast_hip_error")
@@ -70,6 +71,8 @@ def _lib():
         lib.qgemm_workspace_size.restype = SZ
         lib.qgemm.argtypes = [P, VP, I32, VP, VP, VP, SZ, VP]
         lib.qquant_mxfp4.argtypes = [VP, I32, I32, VP, VP, VP]
+        lib.qhadamard_prepare.argtypes = [VP, I32, I32, VP, VP, VP]
+        lib.qhadamard_finish.argtypes = [VP, I32, I32, VP, VP, I32, VP]
         lib.qgemm_w4a4_workspace_size.argtypes = [P, I32]
         lib.qgemm_w4a4_workspace_size.restype = SZ
         lib.qgemm_w4a4.argtypes = [P, VP, I32, VP, VP, VP, SZ, VP]
@@ -277,6 +280,46 @@ def gemm(w: Weight, x, residual=None, out=None, workspace=None, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib().qgemm(w.c, _ptr(x), m, _ptr(residual), _ptr(out), _ptr(workspace), ws_bytes,
                         _stream(stream)), "qgemm")
+    return out
+
+
+def hadamard_prepare(x, in_scale=None, out=None, stream=None):
+    """qhadamard_prepare: bf16 x [m][k] -> bf16 H (s_in * x) per 128-block."""
+    _tensor("qhadamard_prepare", "x", x, _BF16)
+    if x.dim() != 2:
+        raise ValueError(f"qhadamard_prepare: x must be 2-D, got {tuple(x.shape)}")
+    m, k = x.shape
+    dev = x.device
+    if in_scale is not None:
+        _tensor("qhadamard_prepare", "in_scale", in_scale, (torch.float16,), (k,), dev)
+    if out is not None:
+        _tensor("qhadamard_prepare", "out", out, _BF16, (m, k), dev)
+    _require_gpu("qhadamard_prepare", dev)
+    if out is None:
+        out = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    _check(_lib().qhadamard_prepare(_ptr(x), m, k, _ptr(in_scale), _ptr(out), _stream(stream)),
+           "qhadamard_prepare")
+    return out
+
+
+def hadamard_finish(y, out_scale=None, out=None, out_dtype=torch.float32, stream=None):
+    """qhadamard_finish: float32 y [m][n] -> s_out * H y per 128-block."""
+    _tensor("qhadamard_finish", "y", y, _F32)
+    if y.dim() != 2:
+        raise ValueError(f"qhadamard_finish: y must be 2-D, got {tuple(y.shape)}")
+    m, n = y.shape
+    dev = y.device
+    if out_scale is not None:
+        _tensor("qhadamard_finish", "out_scale", out_scale, (torch.float16,), (n,), dev)
+    if out is not None:
+        _tensor("qhadamard_finish", "out", out, _OUT, (m, n), dev)
+    _require_gpu("qhadamard_finish", dev)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+        _tensor("qhadamard_finish", "out", out, _OUT)
+    dt = F32 if out.dtype == torch.float32 else BF16
+    _check(_lib().qhadamard_finish(_ptr(y), m, n, _ptr(out_scale), _ptr(out), dt,
+                                   _stream(stream)), "qhadamard_finish")
     return out
 
 

@@ -259,6 +259,36 @@ int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, v
  * which form a call takes.
  */
 /*
+ * qhadamard_prepare / qhadamard_finish -- the rotation stages that surround
+ * an EXL3 projection's inner product ("TurboEXL3", section 3.1: prepare
+ * scales the input by the input-channel vector and applies the Hadamard
+ * transform one 128-element block at a time; finish applies the transform to
+ * the output, then scales it by the output-channel vector; section 2.3: the
+ * transforms are sign-randomized Hadamard transforms in blocks of 128, and
+ * the two 16-bit channel vectors are a matrix's only scales).
+ *
+ *   prepare: out[m][j] = bf16( sum_i H[j%128][i] * s_in[b+i] * x[m][b+i] )
+ *   finish:  out[m][j] = s_out[j] * sum_i H[j%128][i] * y[m][b+i]
+ *            (b = 128 * (j / 128): the block of j)
+ *
+ * H is the orthonormal 128-point Hadamard matrix H_128 / sqrt(128), H_128 in
+ * Sylvester's order (entry (i, j) = (-1)^popcount(i & j)); the pages do not
+ * say where the random signs are kept: here they are the sign bits of the
+ * float16 channel scales.  Sums are float32.
+ *
+ * x          bf16 [m][k]; y float32 [m][n]; k and n multiples of 128
+ * in_scale, out_scale  float16 [k] or [n], or NULL (all ones)
+ * out        prepare: bf16 [m][k]; finish: [m][n] float32 (out_dtype QMM_F32)
+ *            or bf16 rounded to nearest even (QMM_BF16); must not overlap
+ *            the input or the scale (QMM_ERR_ALIAS)
+ * Element alignment for every pointer.  No workspace.
+ */
+int qhadamard_prepare(const void *x, int32_t m, int32_t k, const void *in_scale, void *out,
+                      void *stream);
+int qhadamard_finish(const float *y, int32_t m, int32_t n, const void *out_scale, void *out,
+                     int32_t out_dtype, void *stream);
+
+/*
  * qquant_mxfp4 -- quantize bfloat16 activations to MXFP4 on the GPU, the
  * activation half of W4A4 ("TurboEXL3", section 2.2, W4A4 bullet: the
  * activations are quantized to a 4-bit block format on the fly; section 2.1,
