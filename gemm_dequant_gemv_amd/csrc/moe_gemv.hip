@@ -1,7 +1,8 @@
-// qmoe_grouped for decode (1-4 tokens): the expert multiplies as one grouped
-// GEMV launch per projection ("TurboEXL3" section 3.1: decode passes 1 to 4
+// qmoe_grouped for decode (up to 16 tokens and 128 token slots, when the
+// staged vectors fit in LDS): the expert multiplies as one grouped GEMV
+// launch per projection ("TurboEXL3" section 3.1: decode passes 1 to 4
 // tokens, and a layer's work must not split into many small dependent
-// launches; section 4.3: few rows take the GEMV form).
+// launches; section 4.2: 1 to 16 rows take the GEMV chain).
 //
 // With so few tokens nearly every active expert serves one row, so row tiles
 // of an MFMA GEMM would be almost empty.  Instead every token slot (routed
