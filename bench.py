@@ -657,7 +657,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(),
-                     "kernel": "qgemv kernels (gemv_rows_kernel; split-K gemv_kernel for Q6_K 5120x17408 at M=4)",
+                     "kernel": "qgemv row-streaming kernel (gemv_rows_kernel)",
                      "algorithmic_bytes_per_launch": int(tot_alg / len(cases)),
                      "mean_launch_us": round(launch_s * 1e6, 2),
                      "launch_time": "GPU time of the timed steps (one HIP event pair) / launches",

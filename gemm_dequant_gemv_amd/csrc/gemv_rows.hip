@@ -75,13 +75,21 @@ constexpr size_t kLdsLimit = 160 * 1024 - 2048;  // dynamic part; the static par
 constexpr int record_pad(int m, int ns) {
   return m * ns * 4 <= 16 ? 16 : m * ns * 4 <= 48 ? 48 : m * ns * 4 <= 80 ? 80 : 112;
 }
+// The tight record: the sums rounded up to 16 bytes and no more, for calls
+// whose padded image does not fit in LDS (Q6_K at 3 or 4 rows and K up to
+// 17408-18432).  A stride of 16 x (an odd number times 2) still sends 8
+// lanes to 8 distinct groups of 4 banks.
+constexpr int record_tight(int m, int ns) { return (m * ns * 4 + 15) / 16 * 16; }
+constexpr bool has_tight(int format, int m) {
+  return format == QMM_Q6_K && (m == 3 || m == 4);
+}
 
-template <int M, int NS>
+template <int M, int NS, bool TIGHT>
 struct XLayout {
   static constexpr int kSumOff = 64 * M;                   // bytes
-  static constexpr int kPad = record_pad(M, NS);           // sums fit, stride/16 odd
+  static constexpr int kPad = TIGHT ? record_tight(M, NS) : record_pad(M, NS);
   static constexpr int kStride = 64 * M + kPad;            // bytes per record
-  static_assert(M * NS * 4 <= kPad && (kStride / 16) % 2 == 1, "record layout");
+  static_assert(M * NS * 4 <= kPad && (kStride / 16) % (TIGHT ? 4 : 2) != 0, "record layout");
 };
 
 // The balanced split where the per-unit vector work is heavy.
@@ -106,14 +114,14 @@ struct RowsArgs {
   int n, k, steps, y_bf16;
 };
 
-template <int FMT, int M, int U, bool BAL>
+template <int FMT, int M, int U, bool BAL, bool TIGHT>
 __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsArgs a) {
   constexpr int kWaves = RowsShape<M>::kWaves;
   constexpr int kThreads = RowsShape<M>::kThreads;
   constexpr int kXPieces = RowsShape<M>::kXPieces;
   using T = FmtTraits<FMT>;
   constexpr int kNS = T::kSums;
-  using XL = XLayout<M, kNS>;
+  using XL = XLayout<M, kNS, TIGHT>;
   static_assert(kNS == sums_per_chunk(FMT), "sums per chunk");
   constexpr int kChunks = kStepK / 32;  // chunks per step
   constexpr int kOut = 2 * M;           // outputs of one pair
@@ -373,7 +381,7 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
   }
 }
 
-template <int FMT, int M, int U, bool BAL>
+template <int FMT, int M, int U, bool BAL, bool TIGHT>
 hipError_t launch_rows_cfg(const RowsArgs &a, size_t lds, int grid, hipStream_t s) {
   constexpr int kThreads = RowsShape<M>::kThreads;
   // the dynamic LDS limit is raised once per device for each instantiation
@@ -383,12 +391,12 @@ hipError_t launch_rows_cfg(const RowsArgs &a, size_t lds, int grid, hipStream_t 
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(raised.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute((const void *)gemv_rows_kernel<FMT, M, U, BAL>,
+    e = hipFuncSetAttribute((const void *)gemv_rows_kernel<FMT, M, U, BAL, TIGHT>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     if (e != hipSuccess) return e;
     raised.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((gemv_rows_kernel<FMT, M, U, BAL>), dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((gemv_rows_kernel<FMT, M, U, BAL, TIGHT>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -401,8 +409,18 @@ hipError_t launch_rows_cfg(const RowsArgs &a, size_t lds, int grid, hipStream_t 
 template <int FMT, int M>
 hipError_t launch_rows_fm(const RowsArgs &a, const GemvPlan &p, hipStream_t s) {
   constexpr bool kBal = use_balanced(FMT, M);
+  if constexpr (has_tight(FMT, M)) {
+    if (p.tight) {
 #define QMM_CASE(UU) \
-  if (p.depth == UU) return launch_rows_cfg<FMT, M, UU, kBal>(a, p.lds_bytes, p.tiles, s);
+  if (p.depth == UU) return launch_rows_cfg<FMT, M, UU, kBal, true>(a, p.lds_bytes, p.tiles, s);
+      QMM_ROWS_CONFIGS(QMM_CASE)
+#undef QMM_CASE
+      return hipErrorInvalidConfiguration;
+    }
+  }
+  if (p.tight) return hipErrorInvalidConfiguration;
+#define QMM_CASE(UU) \
+  if (p.depth == UU) return launch_rows_cfg<FMT, M, UU, kBal, false>(a, p.lds_bytes, p.tiles, s);
   QMM_ROWS_CONFIGS(QMM_CASE)
 #undef QMM_CASE
   return hipErrorInvalidConfiguration;
@@ -436,13 +454,19 @@ int cu_count() {
 
 }  // namespace
 
-size_t gemv_rows_lds(int format, int k, int m) {
-  return (size_t)(k / 32) * (size_t)(64 * m + record_pad(m, sums_per_chunk(format)));
+size_t gemv_rows_lds(int format, int k, int m, bool tight) {
+  const int ns = sums_per_chunk(format);
+  return (size_t)(k / 32) * (size_t)(64 * m + (tight ? record_tight(m, ns) : record_pad(m, ns)));
 }
 
 bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p) {
   if (m < 1 || m > kRowsMaxM) return false;
-  const size_t lds = gemv_rows_lds(format, k, m);
+  size_t lds = gemv_rows_lds(format, k, m, false);
+  bool tight = false;
+  if (lds > kLdsLimit && has_tight(format, m)) {
+    lds = gemv_rows_lds(format, k, m, true);
+    tight = true;
+  }
   const size_t threads = m <= 4 ? RowsShape<4>::kThreads : RowsShape<8>::kThreads;
   const size_t pieces = m <= 4 ? RowsShape<4>::kXPieces : RowsShape<8>::kXPieces;
   if (lds > kLdsLimit || (size_t)k / 32 * 4 * m > pieces * threads) return false;
@@ -463,6 +487,7 @@ bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p) {
   p.tiles = cus;  // one workgroup per compute unit
   p.splits = 1;
   p.lds_bytes = lds;
+  p.tight = tight;
   (void)n;
   return true;
 }

@@ -25,6 +25,7 @@ struct GemvPlan {
   int depth;          // D: steps (row-streaming: units) of weights in flight per lane
   int early;          // split-K: code loads issued before waiting for activations and scales
   int balanced;       // row-streaming: pairs in per-workgroup blocks split evenly over the waves
+  int tight;          // row-streaming: activation records without the bank padding
   int lanes_k;        // lanes sharing a row (each reads 16 bytes per step)
   int steps;      // steps per row
   int tiles;      // split-K: ceil(n / rows per workgroup); row-streaming: workgroups
@@ -40,7 +41,6 @@ GemvPlan plan_gemv(int format, int n, int k, int m);
 // qgemm sends it calls of 5 up to this many rows)
 constexpr int kRowsMaxM = 8;
 bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p);
-size_t gemv_rows_lds(int format, int k, int m);
 
 // rows per tile of the MoE routing table (the grouped GEMMs' activation tiles)
 constexpr int kMoeTileRows = 256;  // routing tile rows at most (the grouped GEMMs' tallest X tile)

@@ -101,8 +101,8 @@ def _check_tol(y, yref, mag):
 # Shapes with ragged row counts and ragged last K steps.  Up to K = 17408 the
 # activations fit in LDS and the row-streaming kernel runs (no workspace);
 # K = 81920 exceeds that at every M and takes the split-K kernel, whose
-# workgroups finish split rows through the workspace, as does Q6_K at 4
-# rows of 17408 values.
+# workgroups finish split rows through the workspace.  (Q6_K at 4 rows of
+# 17408 values fits only with the records' bank padding left out.)
 SHAPES = [(300, 896), (257, 2304), (128, 256), (1, 512), (515, 4096), (64, 6144), (40, 17408),
           (40, 81920)]
 SPLIT_K = 81920
@@ -122,7 +122,7 @@ def test_gemv_parity(fmt, m, shape):
     # the activations do not fit in LDS, row-streaming otherwise
     if k == SPLIT_K:
         assert q.gemv_workspace_size(w, m) > 0
-    elif m <= 2 or k <= 6144 or fmt != F.Q6_K:
+    else:
         assert q.gemv_workspace_size(w, m) == 0
     y = q.gemv(w, _to_dev_bf16(x), None if r is None else _to_dev_bf16(r))
     yref, mag = oracle.gemv(p, x, r)
