@@ -299,60 +299,67 @@ struct CombineArgs {
 // y[t][n] = sum_j w[t][j] d[t topk + j][n] + sum_s ws[t] d[T topk + s T + t][n],
 // fixed order (one fma per term; the decode form runs the same chain in its
 // down launch).  d holds one row per token slot (the down launch writes each
-// grouped row to its slot's row), so a token's routed rows are consecutive.
-// A block serves VEC x 256 columns of one token (the blocks of one token are
-// adjacent in launch order, so the token's rows are read front to back): the
-// slots' weights and whether each was dropped go to LDS in chunks of 64
-// slots, then each thread issues its d loads 16 at a time before adding them
-// (a token's 10 + 1 rows in one batch), so that no load waits for the
-// previous one.  VEC columns per thread (4: 16-byte loads of d when H is a
-// multiple of 4; the kernel reads every row of d once, 738 MB at T = 8192 on
-// the 512-expert layer).
+// grouped row to its slot's row), so a token's routed rows are consecutive
+// and every row's address follows from the token alone.  A block serves VEC x
+// 256 columns of one token (the blocks of one token are adjacent in launch
+// order, so the token's rows are read front to back).  Each thread issues its
+// d loads 16 rows at a time together with the wave's scalar loads of those
+// slots' weights and drop marks, so nothing waits on a table before the d
+// traffic starts (a dropped slot's row is read and left out of the sum).
+// VEC columns per thread (4: 16-byte loads of d when H is a multiple of 4;
+// the kernel reads every row of d once, 738 MB at T = 8192 on the 512-expert
+// layer, with non-temporal loads).  Measured on that layer (bench, ms per
+// layer): table staged in LDS before the loads 1.143, this form with normal
+// loads 1.119, with non-temporal loads 1.091; 8 columns per thread (one
+// block per token) 1.14.
 template <int VEC>
 __global__ __launch_bounds__(256) void moe_combine_kernel(CombineArgs a) {
-  constexpr int kChunk = 64, kBatch = 16;
+  constexpr int kBatch = 16;
   typedef __attribute__((ext_vector_type(VEC))) float fv_t;
-  __shared__ uint32_t s_row[kChunk];
-  __shared__ float s_w[kChunk];
   const int t = blockIdx.y;
   const int n = (blockIdx.x * 256 + threadIdx.x) * VEC;  // first of this thread's columns
   const int total = a.topk + a.num_shared;
   const int nn = min(n, a.h - VEC);
+  const size_t slot0 = (size_t)t * a.topk;
   fv_t acc = {};
-  for (int c0 = 0; c0 < total; c0 += kChunk) {
-    const int cnt = min(kChunk, total - c0);
-    __syncthreads();  // the previous chunk is consumed
-    if ((int)threadIdx.x < cnt) {
-      const int j = c0 + threadIdx.x;
-      uint32_t row;
-      float w;
-      if (j < a.topk) {
-        const int slot = t * a.topk + j;
-        row = a.tb.row_of_slot[slot] == kInvalidRow ? kInvalidRow : (uint32_t)slot;
-        w = a.topk_w[slot];
-      } else {
-        const int sh = j - a.topk;
-        row = (uint32_t)a.t * (uint32_t)a.topk + (uint32_t)(sh * a.t + t);
-        w = a.shared_w ? a.shared_w[t] : 1.0f;
-      }
-      s_row[threadIdx.x] = row;
-      s_w[threadIdx.x] = w;
+  for (int j0 = 0; j0 < total; j0 += kBatch) {
+    // every loop below runs all kBatch iterations (rows past the token's
+    // last are not loaded and not added), so the arrays stay in registers;
+    // the sum is a select, not a branch, so that no load is sunk into a
+    // conditional use and all of the batch's loads are in flight together
+    fv_t v[kBatch];
+    float w[kBatch];
+    bool ok[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int j = j0 + u;
+      const size_t row = j < a.topk ? slot0 + j
+                                    : (size_t)a.t * a.topk + (size_t)(j - a.topk) * a.t + t;
+      if (j < total)  // uniform
+        v[u] = __builtin_nontemporal_load((const fv_t *)(a.tb.d + row * a.h + nn));
+      else
+        v[u] = fv_t{};
     }
-    __syncthreads();
-    for (int j0 = 0; j0 < cnt; j0 += kBatch) {
-      fv_t v[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (j0 + u >= cnt) break;  // uniform
-        const uint32_t r = s_row[j0 + u];
-        v[u] = *(const fv_t *)(a.tb.d + (size_t)(r == kInvalidRow ? 0u : r) * a.h + nn);
+    for (int u = 0; u < kBatch; ++u) {
+      const int j = j0 + u;
+      ok[u] = false;
+      w[u] = 0.0f;
+      if (j < a.topk) {
+        ok[u] = a.tb.row_of_slot[slot0 + j] != kInvalidRow;
+        w[u] = a.topk_w[slot0 + j];
+      } else if (j < total) {
+        ok[u] = true;
+        w[u] = a.shared_w ? a.shared_w[t] : 1.0f;
       }
+    }
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (j0 + u < cnt && s_row[j0 + u] != kInvalidRow) {
+    for (int u = 0; u < kBatch; ++u) {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[e] = __builtin_fmaf(s_w[j0 + u], v[u][e], acc[e]);
-        }
+      for (int e = 0; e < VEC; ++e) {
+        const float f = __builtin_fmaf(w[u], v[u][e], acc[e]);
+        acc[e] = ok[u] ? f : acc[e];
+      }
     }
   }
   if (n >= a.h) return;
