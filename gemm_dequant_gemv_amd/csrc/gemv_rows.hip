@@ -1,8 +1,10 @@
 // qgemv, row-streaming form: decode matrix-vector products for 1-4 activation
-// rows, weights dequantized in registers ("TurboEXL3" section 2.2: W4A16, each
-// weight expanded to 16 bits in the kernel, 16-bit products, 32-bit sums).
+// rows (and qgemm's 5-8), weights dequantized in registers ("TurboEXL3"
+// section 2.2: W4A16, each weight expanded to 16 bits in the kernel, 16-bit
+// products, 32-bit sums).  The products are v_dot2 per activation row for 1,
+// 2 (and 5) rows, and the matrix cores' 4 x 4 x 4 form for more (below).
 //
-// One workgroup of 16 waves per compute unit.  The workgroup first stages the
+// One workgroup of 16 waves (8 for 5-8 rows) per compute unit.  The workgroup first stages the
 // whole activation block x [M][K] in LDS (one padded record per 32-value
 // chunk: its x in pair order, then its block sums), then its waves stream
 // weight rows:
@@ -114,6 +116,176 @@ struct RowsArgs {
   int n, k, steps, y_bf16;
 };
 
+// ---- the matrix-core form (2 to 8 activation rows)
+//
+// v_mfma_f32_4x4x4_16b_bf16 runs 16 independent 4 x 4 x 4 products, block b
+// in lanes 4b .. 4b+3.  Lane 4b + i loads row (i >> 1) of the pair at chunk
+// 2b + (i & 1) of the step (the same 2 x 512 contiguous bytes per load
+// instruction as the scalar form) and supplies that row's weights as row i
+// of A; as column i of B it supplies activations: for M = 2 row (i & 1) of x
+// at chunk 2b + (i >> 1), for M >= 3 row 4g + i at chunk 2b + h, one product
+// per (h, g).  An entry D[i][j] is a useful partial sum where A's chunk is
+// B's chunk (half of them); lane 4b + j receives column j, so it holds its
+// activation row's partial sums for both weight rows.  Per k-step of 4
+// values a lane issues 1 (M = 2), 2 (M = 3, 4) or 4 (M = 5..8) products
+// instead of 2, 4 or 8 v_dot2 per activation row, and reads from LDS only
+// its own activation row's 64 bytes per chunk instead of every row's.  The
+// block scales are applied per chunk in float32 after the product, taken
+// from the loading lane by DPP quad permutations.
+// Where the matrix-core form runs.  Measured against the v_dot2 form on the
+// decode shapes (cold weights, events around 4 x copies launches, two runs):
+// 4 rows 6-17% faster, 3 rows 0-6%, 6-8 rows (17408 x 5120) 5-27%; 2 rows
+// 0-4% slower (half of each product's columns idle against 32 v_dot2 per
+// unit), 5 rows 3-6% slower for affine and NVFP4 (5 of 8 columns used) and
+// 2-4% faster for Q6_K.
+constexpr bool use_mfma(int format, int m) {
+  return m >= 3 && (m != 5 || format == QMM_Q6_K);
+}
+
+template <int M>
+struct MfShape {
+  static constexpr int kG = M <= 2 ? 1 : (M + 3) / 4;  // groups of 4 activation rows
+  static constexpr int kH = M <= 2 ? 1 : 2;            // chunk halves per lane
+};
+constexpr int kXSlack = 256;  // LDS bytes after the last record (reads of rows past M)
+
+// The scale terms of the lane's own (row, chunk): affine (s, b - 128 s),
+// MXFP4 (scale, -), NVFP4 (s0, s1), Q6_K (d sc0, d sc1).
+template <int FMT>
+__device__ __forceinline__ void mf_scales(const RowData &rd, float &t0, float &t1) {
+  if constexpr (FMT == QMM_AFFINE4_G64) {
+    t0 = half_to_float(rd.s & 0xFFFFu);
+    t1 = __builtin_fmaf(-128.0f, t0, half_to_float(rd.s >> 16));
+  } else if constexpr (FMT == QMM_MXFP4) {
+    t0 = e8m0_to_float(rd.s);
+    t1 = 0.0f;
+  } else if constexpr (FMT == QMM_NVFP4) {
+    e4m3x2_to_float(rd.s, t0, t1);
+  } else {
+    const float dd = half_to_float(rd.d);
+    t0 = dd * (float)(int8_t)(rd.s & 0xFFu);
+    t1 = dd * (float)(int8_t)((rd.s >> 8) & 0xFFu);
+  }
+}
+
+// acc += the chunk's partial sum of one weight row: D0 (and D1, the second
+// 16-value sub-block or the odd k-steps) scaled by the row's terms t0, t1,
+// with the block sums Sx0, Sx1 of the activation row for the zero points.
+template <int FMT>
+__device__ __forceinline__ float mf_apply(float acc, float d0, float d1, float t0, float t1,
+                                          float sx0, float sx1) {
+  if constexpr (FMT == QMM_AFFINE4_G64) {
+    acc = __builtin_fmaf(t0, d0 + d1, acc);
+    return __builtin_fmaf(t1, sx0, acc);
+  } else if constexpr (FMT == QMM_MXFP4) {
+    return __builtin_fmaf(t0, d0 + d1, acc);
+  } else if constexpr (FMT == QMM_NVFP4) {
+    acc = __builtin_fmaf(t0, d0, acc);
+    return __builtin_fmaf(t1, d1, acc);
+  } else {
+    acc = __builtin_fmaf(t0, __builtin_fmaf(-160.0f, sx0, d0), acc);
+    return __builtin_fmaf(t1, __builtin_fmaf(-160.0f, sx1, d1), acc);
+  }
+}
+
+// One unit in the matrix-core form.  xb / sb: this lane's activation words
+// and block sums in the unit's record (B role); P: the lane's unpacked
+// weights (A role); t0, t1 its scale terms.
+template <int FMT, int M, int STRIDE>
+__device__ __forceinline__ void mf_unit(const uint32_t (&P)[16], float t0, float t1,
+                                        const char *xb, const char *sb, int qi,
+                                        float (&acc)[MfShape<M>::kG][2]) {
+  using MS = MfShape<M>;
+  constexpr bool kTwoSub = FMT == QMM_NVFP4 || FMT == QMM_Q6_K;
+  constexpr int kNS = FmtTraits<FMT>::kSums;
+#pragma unroll
+  for (int h = 0; h < MS::kH; ++h) {
+#pragma unroll
+    for (int g = 0; g < MS::kG; ++g) {
+      const char *xr = xb + h * STRIDE + g * 256;
+      uint32_t X[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = *(const uint4 *)(xr + 16 * q);
+        X[4 * q + 0] = v.x;
+        X[4 * q + 1] = v.y;
+        X[4 * q + 2] = v.z;
+        X[4 * q + 3] = v.w;
+      }
+      float sx0 = 0.0f, sx1 = 0.0f;
+      if constexpr (kNS > 0) {
+        const float *sr = (const float *)(sb + h * STRIDE + g * 16 * kNS);
+        sx0 = sr[0];
+        if constexpr (kNS > 1) sx1 = sr[1];
+      }
+      // two chains: the sub-blocks (k-steps 0-3, 4-7), or even and odd k-steps
+      mf_v4f_t D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int s0 = kTwoSub ? st : 2 * st, s1 = kTwoSub ? st + 4 : 2 * st + 1;
+        D0 = mfma4(P[2 * s0], P[2 * s0 + 1], X[2 * s0], X[2 * s0 + 1], D0);
+        D1 = mfma4(P[2 * s1], P[2 * s1 + 1], X[2 * s1], X[2 * s1 + 1], D1);
+      }
+      // useful entries: weight row r at this lane's chunk, D[2r + chunk half]
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        float d0, d1, a0, a1;
+        if constexpr (M <= 2) {
+          const bool odd = (qi >> 1) != 0;  // B chunk half of this lane
+          d0 = odd ? D0[2 * r + 1] : D0[2 * r];
+          d1 = odd ? D1[2 * r + 1] : D1[2 * r];
+          a0 = r == 0 ? quad_perm<0x50>(t0) : quad_perm<0xFA>(t0);  // lanes [0,0,1,1] / [2,2,3,3]
+          a1 = r == 0 ? quad_perm<0x50>(t1) : quad_perm<0xFA>(t1);
+        } else {
+          d0 = D0[2 * r + h];
+          d1 = D1[2 * r + h];
+          // the loading lane 2r + h of the quad
+          constexpr int kC0 = 0x00, kC1 = 0x55, kC2 = 0xAA, kC3 = 0xFF;
+          if (2 * r + h == 0) { a0 = quad_perm<kC0>(t0); a1 = quad_perm<kC0>(t1); }
+          else if (2 * r + h == 1) { a0 = quad_perm<kC1>(t0); a1 = quad_perm<kC1>(t1); }
+          else if (2 * r + h == 2) { a0 = quad_perm<kC2>(t0); a1 = quad_perm<kC2>(t1); }
+          else { a0 = quad_perm<kC3>(t0); a1 = quad_perm<kC3>(t1); }
+        }
+        acc[g][r] = mf_apply<FMT>(acc[g][r], d0, d1, a0, a1, sx0, sx1);
+      }
+    }
+  }
+}
+
+// v + v rotated by 4 or 8 lanes within each row of 16 (DPP row_ror)
+template <int CTRL>
+__device__ __forceinline__ float ror_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// A pair's outputs in the matrix-core form: each partial sum is added over
+// its copies (the 16 blocks, and for M = 2 the two chunk halves of a quad)
+// in a fixed order; lane 2m + r returns weight row r of activation row m.
+template <int M>
+__device__ __forceinline__ float mf_finish(float (&acc)[MfShape<M>::kG][2], int lane) {
+  float out = 0.0f;
+  const int m = lane >> 1, r_out = lane & 1;
+#pragma unroll
+  for (int g = 0; g < MfShape<M>::kG; ++g) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      float v = acc[g][r];
+      acc[g][r] = 0.0f;
+      if constexpr (M <= 2) v += quad_perm<0x4E>(v);  // lanes [2,3,0,1]: the other half
+      v = ror_add<0x124>(v);                          // row_ror:4
+      v = ror_add<0x128>(v);                          // row_ror:8
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      // every lane at quad position j now holds the total of activation row
+      // (M = 2: j & 1; else 4g + j)
+      const float t = __shfl(v, M <= 2 ? (m & 1) : (m & 3));
+      if (r_out == r && m < M && (M <= 2 || (m >> 2) == g)) out = t;
+    }
+  }
+  return out;
+}
+
 template <int FMT, int M, int U, bool BAL, bool TIGHT>
 __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsArgs a) {
   constexpr int kWaves = RowsShape<M>::kWaves;
@@ -167,13 +339,18 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
   const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(a.scales2, a.scales2_bytes);
   const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.residual, a.residual_bytes);
 
-  // per-lane constant parts of the load offsets (row 2p + hf, chunk c)
-  const uint32_t v_code = hf * (k / 2) + 16 * c;
-  const uint32_t v_scale = FMT == QMM_AFFINE4_G64 ? hf * (k / 16) + (c / 2) * 4
-                         : FMT == QMM_MXFP4 ? hf * (k / 32) + c
-                         : hf * (k / 16) + 2 * c;
-  const uint32_t v_hi = hf * (k / 4) + 8 * c;
-  const uint32_t v_d = (hf * (k / 256) + c / 8) * 2;
+  // the lane's loads: row 2p + rA of the pair, chunk cA of the step
+  // (scalar form: one row per half-wave; matrix-core form: see mf_unit)
+  constexpr bool MF = use_mfma(FMT, M);
+  const int qb = lane >> 2, qi = lane & 3;  // matrix-core block and position
+  const int rA = MF ? (qi >> 1) : hf;
+  const int cA = MF ? 2 * qb + (qi & 1) : c;
+  const uint32_t v_code = rA * (k / 2) + 16 * cA;
+  const uint32_t v_scale = FMT == QMM_AFFINE4_G64 ? rA * (k / 16) + (cA / 2) * 4
+                         : FMT == QMM_MXFP4 ? rA * (k / 32) + cA
+                         : rA * (k / 16) + 2 * cA;
+  const uint32_t v_hi = rA * (k / 4) + 8 * cA;
+  const uint32_t v_d = (rA * (k / 256) + cA / 8) * 2;
   // output lane i = 2m + h writes row 2p + h of activation row m
   const int o_h = lane & 1, o_m = min(lane >> 1, M - 1);
   const uint32_t v_res = ((uint32_t)o_m * a.n + o_h) * 2;
@@ -276,6 +453,14 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
       *(uint4 *)(rec + (m * 4 + part_) * 16) = o;
     }
   }
+  // records past the last chunk, up to a whole step, and the slack after
+  // them are zero: lanes past K read them as activations
+  {
+    const int nchp = (nch + kChunks - 1) / kChunks * kChunks;
+    const int n16 = ((nchp - nch) * XL::kStride + kXSlack) / 16;
+    uint4 *z = (uint4 *)(xs + (size_t)nch * XL::kStride);
+    for (int i = tid; i < n16; i += kThreads) z[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
   // A bare barrier: this wave's LDS writes are complete (lgkmcnt), while its
   // weight loads stay in flight.  __syncthreads() would also wait for those
   // (vmcnt(0)), so that every wave drained its pipeline here and restarted it
@@ -299,6 +484,15 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
   const char *xs_lane = xs + c * XL::kStride;
+  // matrix-core form: accumulators per (group of 4 activation rows, weight
+  // row) and the lane's activation words and block sums (B role)
+  float accv[MfShape<M>::kG][2];
+#pragma unroll
+  for (int g = 0; g < MfShape<M>::kG; ++g) accv[g][0] = accv[g][1] = 0.0f;
+  const int mB = M <= 2 ? (qi & 1) : qi;
+  const int cB = M <= 2 ? 2 * qb + (qi >> 1) : 2 * qb;
+  const char *xb_lane = xs + cB * XL::kStride + mB * 64;
+  const char *sb_lane = xs + cB * XL::kStride + XL::kSumOff + mB * 4 * (kNS > 0 ? kNS : 1);
 
   int cj = j0, cs = st0;  // unit being computed: pair index, step
   float fin_res = 0.0f;    // balanced: residual of the cut pair this wave finishes
@@ -316,7 +510,21 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       if (t0 + j < units) {  // uniform
-        if (cs * kChunks + c < nch) {
+        if constexpr (MF) {
+          // every lane takes part in the products; a lane whose chunk is past
+          // K multiplies zero activations and gets zero scale terms
+          RowData rd = buf[j];
+          if (cs * kChunks + cA >= nch) {
+            rd.s = 0u;
+            rd.d = 0u;
+          }
+          uint32_t P[16];
+          unpack_pairs<FMT>(rd, P, K);
+          float t0s, t1s;
+          mf_scales<FMT>(rd, t0s, t1s);
+          const int off = cs * (kChunks * XL::kStride);
+          mf_unit<FMT, M, XL::kStride>(P, t0s, t1s, xb_lane + off, sb_lane + off, qi, accv);
+        } else if (cs * kChunks + c < nch) {
           // this lane's record of step cs: lane base + a wave-uniform offset
           const char *rec = xs_lane + cs * (kChunks * XL::kStride);
           uint32_t X[M][16];
@@ -339,13 +547,17 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
         }
         if (cs == S - 1 || (BAL && t0 + j == units - 1)) {  // the wave is done with the pair
           float out = 0.0f;
+          if constexpr (MF) {
+            out = mf_finish<M>(accv, lane);
+          } else {
 #pragma unroll
-          for (int m = 0; m < M; ++m) {
-            float s0, s1;
-            half_sums(acc[m], s0, s1);
-            acc[m] = 0.0f;
-            if (lane == 2 * m) out = s0;
-            if (lane == 2 * m + 1) out = s1;
+            for (int m = 0; m < M; ++m) {
+              float s0, s1;
+              half_sums(acc[m], s0, s1);
+              acc[m] = 0.0f;
+              if (lane == 2 * m) out = s0;
+              if (lane == 2 * m + 1) out = s1;
+            }
           }
           if (cs == S - 1 && (!BAL || cj != j0 || st0 == 0)) {  // the whole pair
             const int row = 2 * (pbase + cj * pstride) + o_h;
@@ -456,7 +668,8 @@ int cu_count() {
 
 size_t gemv_rows_lds(int format, int k, int m, bool tight) {
   const int ns = sums_per_chunk(format);
-  return (size_t)(k / 32) * (size_t)(64 * m + (tight ? record_tight(m, ns) : record_pad(m, ns)));
+  const size_t nchp = (size_t)(k / 32 + kStepK / 32 - 1) / (kStepK / 32) * (kStepK / 32);
+  return nchp * (size_t)(64 * m + (tight ? record_tight(m, ns) : record_pad(m, ns))) + kXSlack;
 }
 
 bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p) {

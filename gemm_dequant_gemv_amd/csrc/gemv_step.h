@@ -151,6 +151,70 @@ __device__ __forceinline__ void row_step(const RowData &rd, const uint32_t (&X)[
   }
 }
 
+// ---- the matrix-core form for 2 to 8 activation rows
+
+// A row's 32 weights as 16 bfloat16 pairs, in the order row_step multiplies
+// them: pair p meets activation word p of the chunk (affine and Q6_K: 128 +
+// q, the zero points left to the caller; E2M1: the exact values).
+template <int FMT>
+__device__ __forceinline__ void unpack_pairs(const RowData &rd, uint32_t (&P)[16],
+                                             const UnpackK &K) {
+  const uint32_t w[4] = {rd.q.x, rd.q.y, rd.q.z, rd.q.w};
+  if constexpr (FMT == QMM_AFFINE4_G64) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      P[4 * j + 0] = and_or(w[j], K.lo, K.magic);
+      P[4 * j + 1] = and_or(w[j] >> 4, K.lo, K.magic);
+      P[4 * j + 2] = and_or(w[j] >> 8, K.lo, K.magic);
+      P[4 * j + 3] = and_or(w[j] >> 12, K.lo, K.magic);
+    }
+  } else if constexpr (FMT == QMM_MXFP4 || FMT == QMM_NVFP4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      P[4 * j + 0] = e2m1x2_to_bf16x2<0>(w[j]);
+      P[4 * j + 1] = e2m1x2_to_bf16x2<1>(w[j]);
+      P[4 * j + 2] = e2m1x2_to_bf16x2<2>(w[j]);
+      P[4 * j + 3] = e2m1x2_to_bf16x2<3>(w[j]);
+    }
+  } else {  // Q6_K
+    const uint32_t hw[2] = {rd.h.x, rd.h.y};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t A = w[2 * j], B = w[2 * j + 1];
+      const uint32_t H = __builtin_amdgcn_perm(hw[j], hw[j], 0x03010200u);
+      P[8 * j + 0] = and_or(H << 4, K.hi, and_or(A, K.lo, K.magic));
+      P[8 * j + 1] = and_or(H << 2, K.hi, and_or(A >> 4, K.lo, K.magic));
+      P[8 * j + 2] = and_or(H, K.hi, and_or(A >> 8, K.lo, K.magic));
+      P[8 * j + 3] = and_or(H >> 2, K.hi, and_or(A >> 12, K.lo, K.magic));
+      P[8 * j + 4] = and_or(H >> 4, K.hi, and_or(B, K.lo, K.magic));
+      P[8 * j + 5] = and_or(H >> 6, K.hi, and_or(B >> 4, K.lo, K.magic));
+      P[8 * j + 6] = and_or(H >> 8, K.hi, and_or(B >> 8, K.lo, K.magic));
+      P[8 * j + 7] = and_or(H >> 10, K.hi, and_or(B >> 12, K.lo, K.magic));
+    }
+  }
+}
+
+typedef short mf_v4s_t __attribute__((ext_vector_type(4)));
+typedef float mf_v4f_t __attribute__((ext_vector_type(4)));
+
+// One v_mfma_f32_4x4x4_16b_bf16: 16 independent 4 x 4 x 4 products, block b
+// in lanes 4b .. 4b+3.  Lane 4b+i supplies row i of A (4 bfloat16: words a0,
+// a1) and column i of B (words b0, b1); lane 4b+j receives column j of D,
+// D[i] in element i.  (Layout checked on the GPU against a CPU product.)
+__device__ __forceinline__ mf_v4f_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
+                                          mf_v4f_t c) {
+  const mf_v4s_t A = __builtin_bit_cast(mf_v4s_t, make_uint2(a0, a1));
+  const mf_v4s_t B = __builtin_bit_cast(mf_v4s_t, make_uint2(b0, b1));
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(A, B, c, 0, 0, 0);
+}
+
+// x moved within each group of four lanes by a DPP quad permutation
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
 // v + (v moved by one DPP pattern): quad permutations, half-row and row
 // mirrors, row broadcasts of lane 15 and lane 31 (rows without the mask bit
 // add zero).
