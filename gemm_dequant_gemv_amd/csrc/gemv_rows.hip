@@ -67,31 +67,56 @@ struct RowsShape {
 };
 constexpr size_t kLdsLimit = 160 * 1024 - 2048;  // dynamic part; the static part is <= 1 KB
 
-// LDS image of the activations, one record per 32-value chunk ch: M x 64
-// bytes of x (16-byte pieces p = 4m + part, in pair order for the
-// nibble-into-mantissa formats), then the chunk's block sums of x (M x NS
-// floats), padded so that the record stride is an odd multiple of 16 bytes.
-// The 8 lanes of one ds_read_b128 group read consecutive records at the same
-// offset, and an odd multiple of 16 bytes sends them to 8 distinct groups of
-// 4 banks; every read of a unit is one lane base plus an immediate offset.
+// Where the matrix-core form runs (below).  Measured against the v_dot2 form
+// on the decode shapes (cold weights, events around 4 x copies launches, two
+// runs): 4 rows 6-17% faster, 3 rows 0-6%, 6-8 rows (17408 x 5120) 5-27%;
+// 2 rows 0-4% slower (half of each product's columns idle against 32 v_dot2
+// per unit), 5 rows 3-6% slower for affine and NVFP4 (5 of 8 columns used)
+// and 2-4% faster for Q6_K.
+constexpr bool use_mfma(int format, int m) {
+  return m >= 3 && (m != 5 || format == QMM_Q6_K);
+}
+
+template <int M>
+struct MfShape {
+  static constexpr int kG = M <= 2 ? 1 : (M + 3) / 4;  // groups of 4 activation rows
+  static constexpr int kH = M <= 2 ? 1 : 2;            // chunk halves per lane
+};
+
+// LDS image of the activations, one record per 32-value chunk: the chunk's
+// x (16-byte pieces, in pair order for the nibble-into-mantissa formats),
+// then its block sums of x (M x NS floats), then padding.
+//   v_dot2 form: row m's four pieces at 64 m + 16 q; the 8 lanes of one
+//     ds_read_b128 group read consecutive records at the same offset, and a
+//     stride that is an odd multiple of 16 bytes sends them to 8 distinct
+//     groups of 4 banks.
+//   matrix-core form: piece q of row 4g + j at 256 g + 64 q + 16 j
+//     (piece-major within each group of 4 rows), stride 16 (4k + 2) bytes.
+//     Lanes 4b + j read piece q of row 4g + j of record 2b (+ h): within 16
+//     lanes the records add 0, 4, 8, 12 (mod 16) 16-byte units and j adds
+//     0-3, and within 8 lanes 0 and 4 (mod 8): distinct bank groups under
+//     either grouping.  (Row-major pieces at that stride measured 2-4-way
+//     conflicts.)
+// Every read of a unit is one lane base plus an immediate offset.
 constexpr int record_pad(int m, int ns) {
   return m * ns * 4 <= 16 ? 16 : m * ns * 4 <= 48 ? 48 : m * ns * 4 <= 80 ? 80 : 112;
 }
-// The tight record: the sums rounded up to 16 bytes and no more, for calls
-// whose padded image does not fit in LDS (Q6_K at 3 or 4 rows and K up to
-// 17408-18432).  A stride of 16 x (an odd number times 2) still sends 8
-// lanes to 8 distinct groups of 4 banks.
-constexpr int record_tight(int m, int ns) { return (m * ns * 4 + 15) / 16 * 16; }
-constexpr bool has_tight(int format, int m) {
-  return format == QMM_Q6_K && (m == 3 || m == 4);
+constexpr int mf_stride(int bytes) {
+  int u = (bytes + 15) / 16;
+  while (u % 4 != 2) ++u;
+  return 16 * u;
 }
 
-template <int M, int NS, bool TIGHT>
+template <int M, int NS, bool MFL>
 struct XLayout {
-  static constexpr int kSumOff = 64 * M;                   // bytes
-  static constexpr int kPad = TIGHT ? record_tight(M, NS) : record_pad(M, NS);
-  static constexpr int kStride = 64 * M + kPad;            // bytes per record
-  static_assert(M * NS * 4 <= kPad && (kStride / 16) % (TIGHT ? 4 : 2) != 0, "record layout");
+  static constexpr int kXBytes = MFL ? 256 * MfShape<M>::kG : 64 * M;
+  static constexpr int kSumOff = kXBytes;  // bytes
+  static constexpr int kStride = MFL ? mf_stride(kXBytes + M * NS * 4) : 64 * M + record_pad(M, NS);
+  static constexpr int piece(int m, int q) {
+    return MFL ? 256 * (m / 4) + 64 * q + 16 * (m % 4) : 64 * m + 16 * q;
+  }
+  static_assert(kSumOff + M * NS * 4 <= kStride, "record layout");
+  static_assert(MFL ? (kStride / 16) % 4 == 2 : (kStride / 16) % 2 == 1, "record stride");
 };
 
 // The balanced split where the per-unit vector work is heavy.
@@ -132,21 +157,6 @@ struct RowsArgs {
 // its own activation row's 64 bytes per chunk instead of every row's.  The
 // block scales are applied per chunk in float32 after the product, taken
 // from the loading lane by DPP quad permutations.
-// Where the matrix-core form runs.  Measured against the v_dot2 form on the
-// decode shapes (cold weights, events around 4 x copies launches, two runs):
-// 4 rows 6-17% faster, 3 rows 0-6%, 6-8 rows (17408 x 5120) 5-27%; 2 rows
-// 0-4% slower (half of each product's columns idle against 32 v_dot2 per
-// unit), 5 rows 3-6% slower for affine and NVFP4 (5 of 8 columns used) and
-// 2-4% faster for Q6_K.
-constexpr bool use_mfma(int format, int m) {
-  return m >= 3 && (m != 5 || format == QMM_Q6_K);
-}
-
-template <int M>
-struct MfShape {
-  static constexpr int kG = M <= 2 ? 1 : (M + 3) / 4;  // groups of 4 activation rows
-  static constexpr int kH = M <= 2 ? 1 : 2;            // chunk halves per lane
-};
 constexpr int kXSlack = 256;  // LDS bytes after the last record (reads of rows past M)
 
 // The scale terms of the lane's own (row, chunk): affine (s, b - 128 s),
@@ -206,7 +216,7 @@ __device__ __forceinline__ void mf_unit(const uint32_t (&P)[16], float t0, float
       uint32_t X[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 v = *(const uint4 *)(xr + 16 * q);
+        const uint4 v = *(const uint4 *)(xr + 64 * q);
         X[4 * q + 0] = v.x;
         X[4 * q + 1] = v.y;
         X[4 * q + 2] = v.z;
@@ -286,14 +296,15 @@ __device__ __forceinline__ float mf_finish(float (&acc)[MfShape<M>::kG][2], int 
   return out;
 }
 
-template <int FMT, int M, int U, bool BAL, bool TIGHT>
+template <int FMT, int M, int U, bool BAL>
 __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsArgs a) {
   constexpr int kWaves = RowsShape<M>::kWaves;
   constexpr int kThreads = RowsShape<M>::kThreads;
   constexpr int kXPieces = RowsShape<M>::kXPieces;
   using T = FmtTraits<FMT>;
   constexpr int kNS = T::kSums;
-  using XL = XLayout<M, kNS, TIGHT>;
+  constexpr bool MF = use_mfma(FMT, M);
+  using XL = XLayout<M, kNS, MF>;
   static_assert(kNS == sums_per_chunk(FMT), "sums per chunk");
   constexpr int kChunks = kStepK / 32;  // chunks per step
   constexpr int kOut = 2 * M;           // outputs of one pair
@@ -341,7 +352,6 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
 
   // the lane's loads: row 2p + rA of the pair, chunk cA of the step
   // (scalar form: one row per half-wave; matrix-core form: see mf_unit)
-  constexpr bool MF = use_mfma(FMT, M);
   const int qb = lane >> 2, qi = lane & 3;  // matrix-core block and position
   const int rA = MF ? (qi >> 1) : hf;
   const int cA = MF ? 2 * qb + (qi & 1) : c;
@@ -450,7 +460,7 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
         o.z = (v.y & 0xFFFFu) | (v.w << 16);
         o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
       }
-      *(uint4 *)(rec + (m * 4 + part_) * 16) = o;
+      *(uint4 *)(rec + XL::piece(m, part_)) = o;
     }
   }
   // records past the last chunk, up to a whole step, and the slack after
@@ -491,7 +501,7 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
   for (int g = 0; g < MfShape<M>::kG; ++g) accv[g][0] = accv[g][1] = 0.0f;
   const int mB = M <= 2 ? (qi & 1) : qi;
   const int cB = M <= 2 ? 2 * qb + (qi >> 1) : 2 * qb;
-  const char *xb_lane = xs + cB * XL::kStride + mB * 64;
+  const char *xb_lane = xs + cB * XL::kStride + XL::piece(mB, 0);
   const char *sb_lane = xs + cB * XL::kStride + XL::kSumOff + mB * 4 * (kNS > 0 ? kNS : 1);
 
   int cj = j0, cs = st0;  // unit being computed: pair index, step
@@ -533,7 +543,7 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
           for (int m = 0; m < M; ++m) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const uint4 v = *(const uint4 *)(rec + (m * 4 + q) * 16);
+              const uint4 v = *(const uint4 *)(rec + XL::piece(m, q));
               X[m][4 * q + 0] = v.x;
               X[m][4 * q + 1] = v.y;
               X[m][4 * q + 2] = v.z;
@@ -593,7 +603,7 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
   }
 }
 
-template <int FMT, int M, int U, bool BAL, bool TIGHT>
+template <int FMT, int M, int U, bool BAL>
 hipError_t launch_rows_cfg(const RowsArgs &a, size_t lds, int grid, hipStream_t s) {
   constexpr int kThreads = RowsShape<M>::kThreads;
   // the dynamic LDS limit is raised once per device for each instantiation
@@ -603,12 +613,12 @@ hipError_t launch_rows_cfg(const RowsArgs &a, size_t lds, int grid, hipStream_t 
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(raised.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute((const void *)gemv_rows_kernel<FMT, M, U, BAL, TIGHT>,
+    e = hipFuncSetAttribute((const void *)gemv_rows_kernel<FMT, M, U, BAL>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     if (e != hipSuccess) return e;
     raised.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((gemv_rows_kernel<FMT, M, U, BAL, TIGHT>), dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((gemv_rows_kernel<FMT, M, U, BAL>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -621,18 +631,8 @@ hipError_t launch_rows_cfg(const RowsArgs &a, size_t lds, int grid, hipStream_t 
 template <int FMT, int M>
 hipError_t launch_rows_fm(const RowsArgs &a, const GemvPlan &p, hipStream_t s) {
   constexpr bool kBal = use_balanced(FMT, M);
-  if constexpr (has_tight(FMT, M)) {
-    if (p.tight) {
 #define QMM_CASE(UU) \
-  if (p.depth == UU) return launch_rows_cfg<FMT, M, UU, kBal, true>(a, p.lds_bytes, p.tiles, s);
-      QMM_ROWS_CONFIGS(QMM_CASE)
-#undef QMM_CASE
-      return hipErrorInvalidConfiguration;
-    }
-  }
-  if (p.tight) return hipErrorInvalidConfiguration;
-#define QMM_CASE(UU) \
-  if (p.depth == UU) return launch_rows_cfg<FMT, M, UU, kBal, false>(a, p.lds_bytes, p.tiles, s);
+  if (p.depth == UU) return launch_rows_cfg<FMT, M, UU, kBal>(a, p.lds_bytes, p.tiles, s);
   QMM_ROWS_CONFIGS(QMM_CASE)
 #undef QMM_CASE
   return hipErrorInvalidConfiguration;
@@ -666,20 +666,17 @@ int cu_count() {
 
 }  // namespace
 
-size_t gemv_rows_lds(int format, int k, int m, bool tight) {
+size_t gemv_rows_lds(int format, int k, int m) {
   const int ns = sums_per_chunk(format);
   const size_t nchp = (size_t)(k / 32 + kStepK / 32 - 1) / (kStepK / 32) * (kStepK / 32);
-  return nchp * (size_t)(64 * m + (tight ? record_tight(m, ns) : record_pad(m, ns))) + kXSlack;
+  const int g = m <= 2 ? 1 : (m + 3) / 4;
+  const int stride = use_mfma(format, m) ? mf_stride(256 * g + m * ns * 4) : 64 * m + record_pad(m, ns);
+  return nchp * (size_t)stride + kXSlack;
 }
 
 bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p) {
   if (m < 1 || m > kRowsMaxM) return false;
-  size_t lds = gemv_rows_lds(format, k, m, false);
-  bool tight = false;
-  if (lds > kLdsLimit && has_tight(format, m)) {
-    lds = gemv_rows_lds(format, k, m, true);
-    tight = true;
-  }
+  const size_t lds = gemv_rows_lds(format, k, m);
   const size_t threads = m <= 4 ? RowsShape<4>::kThreads : RowsShape<8>::kThreads;
   const size_t pieces = m <= 4 ? RowsShape<4>::kXPieces : RowsShape<8>::kXPieces;
   if (lds > kLdsLimit || (size_t)k / 32 * 4 * m > pieces * threads) return false;
@@ -700,7 +697,6 @@ bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p) {
   p.tiles = cus;  // one workgroup per compute unit
   p.splits = 1;
   p.lds_bytes = lds;
-  p.tight = tight;
   (void)n;
   return true;
 }

@@ -25,7 +25,6 @@ struct GemvPlan {
   int depth;          // D: steps (row-streaming: units) of weights in flight per lane
   int early;          // split-K: code loads issued before waiting for activations and scales
   int balanced;       // row-streaming: pairs in per-workgroup blocks split evenly over the waves
-  int tight;          // row-streaming: activation records without the bank padding
   int lanes_k;        // lanes sharing a row (each reads 16 bytes per step)
   int steps;      // steps per row
   int tiles;      // split-K: ceil(n / rows per workgroup); row-streaming: workgroups
