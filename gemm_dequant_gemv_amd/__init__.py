@@ -9,4 +9,4 @@ from .qmm import (AFFINE4_G64, BF16, F32, FORMATS, MXFP4, NVFP4, Q6_K, PreparedG
                   moe_workspace_size, gemv_workspace_size, lib_handle, new_workspace,
                   workspace_init, prepare_gemm, prepare_moe, quant_mxfp4, gemm_w4a4,
                   gemm_w4a4_workspace_size, prepare_gemm_w4a4, hadamard_prepare,
-                  hadamard_finish)
+                  hadamard_finish, gemv_hadamard)

@@ -243,6 +243,56 @@ int qhadamard_finish(const float *y, int32_t m, int32_t n, const void *out_scale
                                          (hipStream_t)stream));
 }
 
+size_t qgemv_hadamard_workspace_size(const qmm_weight *w, int32_t m, int32_t y_dtype) {
+  if (check_weight(w) || m < 1 || m > 4) return 0;
+  if (y_dtype != QMM_BF16) return 0;
+  return ((size_t)m * w->n * 4 + 255) / 256 * 256;
+}
+
+int qgemv_hadamard(const qmm_weight *w, const void *x, int32_t m, const void *in_scale,
+                   const void *out_scale, void *y, int32_t y_dtype, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+  int st = check_weight(w);
+  if (st) return st;
+  if (w->batch != 1) return QMM_ERR_SHAPE;
+  if (m < 1 || m > 4) return QMM_ERR_M_RANGE;
+  if (y_dtype != QMM_F32 && y_dtype != QMM_BF16) return QMM_ERR_DTYPE;
+  if (!x || !y) return QMM_ERR_NULL;
+  if (w->k % 128 != 0 || w->n % 128 != 0) return QMM_ERR_SHAPE;
+  qmm::GemvPlan p;
+  if (!qmm::plan_gemv_rows(w->format, w->n, w->k, m, p)) return QMM_ERR_SHAPE;
+  const size_t esz = y_dtype == QMM_F32 ? 4 : 2;
+  if (!aligned(x, 16) || !aligned(y, esz) || (in_scale && !aligned(in_scale, 2)) ||
+      (out_scale && !aligned(out_scale, 2)))
+    return QMM_ERR_ALIGN;
+  const size_t ws = qgemv_hadamard_workspace_size(w, m, y_dtype);
+  if (ws) {
+    if (!workspace || workspace_bytes < ws) return QMM_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return QMM_ERR_ALIGN;
+  }
+  const Range ry = range(y, (size_t)m * w->n * esz);
+  Range ins[10];
+  int ni = weight_ranges(*w, ins);
+  ins[ni++] = range(x, (size_t)m * w->k * 2);
+  if (in_scale) ins[ni++] = range(in_scale, (size_t)w->k * 2);
+  if (out_scale) ins[ni++] = range(out_scale, (size_t)w->n * 2);
+  for (int i = 0; i < ni; ++i)
+    if (overlap(ry, ins[i])) return QMM_ERR_ALIAS;
+  if (ws) {
+    const Range rw = range(workspace, ws);
+    if (overlap(rw, ry)) return QMM_ERR_ALIAS;
+    for (int i = 0; i < ni; ++i)
+      if (overlap(rw, ins[i])) return QMM_ERR_ALIAS;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  // the float32 product lands in y (finish then runs in place: each wave
+  // reads its block before writing it) or, for a bf16 y, in the workspace
+  void *ylin = ws ? workspace : y;
+  hipError_t e = qmm::launch_gemv_rows(*w, x, m, nullptr, ylin, QMM_F32, p, s, true, in_scale);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(qmm::launch_hadamard(false, ylin, m, w->n, out_scale, y, y_dtype == QMM_BF16, s));
+}
+
 int qquant_mxfp4(const void *x, int32_t m, int32_t k, void *codes, void *scales, void *stream) {
   if (!x || !codes || !scales) return QMM_ERR_NULL;
   if (m < 1) return QMM_ERR_M_RANGE;

@@ -9,12 +9,10 @@
 // Sylvester's natural order (entry (i, j) = (-1)^popcount(i & j)); the random
 // signs travel in the sign bits of the float16 channel scales.
 //
-// One wave per (row, block of 128): lane l holds elements l and l + 64.  The
-// butterfly over index bit 6 pairs a lane's own two elements; those over bits
-// 5 .. 0 pair lane l with lane l ^ span (cross-lane shuffles).  All sums are
-// float32; the result is multiplied by float32(2^-3.5) at the end.  Prepare
-// reads bf16 and writes bf16 (rounded to nearest even); finish reads float32
-// and writes float32 or bf16.
+// One wave per (row, block of 128): lane l holds elements l and l + 64
+// (hadamard128_wave; qgemv_hadamard runs the same routine on its staged
+// activations).  Prepare reads bf16 and writes bf16 (rounded to nearest
+// even); finish reads float32 and writes float32 or bf16.
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
@@ -30,8 +28,6 @@ struct HadArgs {
   uint32_t len;
   int out_bf16;
 };
-
-constexpr float kInvSqrt128 = 0.08838834764831844055f;  // 2^-3.5
 
 template <bool PREPARE>
 __global__ __launch_bounds__(256) void hadamard_kernel(HadArgs a) {
@@ -55,23 +51,7 @@ __global__ __launch_bounds__(256) void hadamard_kernel(HadArgs a) {
     v0 = y[base + lane];
     v1 = y[base + lane + 64];
   }
-  // index bit 6: the lane's own pair
-  {
-    const float s = v0 + v1, d = v0 - v1;
-    v0 = s;
-    v1 = d;
-  }
-  // index bits 5 .. 0: lane l with lane l ^ span; the lane with the bit set
-  // holds the difference (partner - own), the other the sum
-#pragma unroll
-  for (int span = 32; span >= 1; span >>= 1) {
-    const float p0 = __shfl_xor(v0, span), p1 = __shfl_xor(v1, span);
-    const bool upper = (lane & span) != 0;
-    v0 = upper ? p0 - v0 : v0 + p0;
-    v1 = upper ? p1 - v1 : v1 + p1;
-  }
-  v0 *= kInvSqrt128;
-  v1 *= kInvSqrt128;
+  hadamard128_wave(v0, v1, lane);
   if constexpr (!PREPARE) {
     if (a.scale) {  // transform first, then scale
       v0 *= half_to_float(a.scale[c0]);

@@ -94,4 +94,29 @@ __device__ __forceinline__ uint32_t float_to_bf16(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// The orthonormal 128-point Hadamard transform H_128 / sqrt(128) (Sylvester's
+// natural order, entry (i, j) = (-1)^popcount(i & j)) of one block held by a
+// wave: lane l holds elements l (v0) and l + 64 (v1).  The butterfly over
+// index bit 6 pairs a lane's own two elements; those over bits 5 .. 0 pair
+// lane l with lane l ^ span, the lane with the bit set keeping the
+// difference.  Float32 throughout, times 2^-3.5 at the end; every caller
+// gets the same bits.
+__device__ __forceinline__ void hadamard128_wave(float &v0, float &v1, int lane) {
+  {
+    const float s = v0 + v1, d = v0 - v1;
+    v0 = s;
+    v1 = d;
+  }
+#pragma unroll
+  for (int span = 32; span >= 1; span >>= 1) {
+    const float p0 = __shfl_xor(v0, span), p1 = __shfl_xor(v1, span);
+    const bool upper = (lane & span) != 0;
+    v0 = upper ? p0 - v0 : v0 + p0;
+    v1 = upper ? p1 - v1 : v1 + p1;
+  }
+  constexpr float kInvSqrt128 = 0.08838834764831844055f;  // 2^-3.5
+  v0 *= kInvSqrt128;
+  v1 *= kInvSqrt128;
+}
+
 }  // namespace qmm

@@ -23,7 +23,8 @@ FORMATS = {"affine4_g64": AFFINE4_G64, "mxfp4": MXFP4, "nvfp4": NVFP4, "q6_k": Q
 ENTRY_POINTS = ("qdequant", "qgemv", "qgemv_workspace_size", "qgemm", "qgemm_workspace_size",
                 "qmoe_grouped", "qmoe_workspace_size", "qmoe_workspace_layout", "qmoe_router",
                 "qmoe_grouped_logits", "qmoe_grouped_noalloc", "qquant_mxfp4",
-                "qhadamard_prepare", "qhadamard_finish",
+                "qhadamard_prepare", "qhadamard_finish", "qgemv_hadamard_workspace_size",
+                "qgemv_hadamard",
                 "qgemm_w4a4_workspace_size", "qgemm_w4a4",
                 "qworkspace_init", "qbench_stream_read", "qbench_mfma_peak", "qstatus_string",
                 "qlast_hip_error")
@@ -73,6 +74,9 @@ def _lib():
         lib.qquant_mxfp4.argtypes = [VP, I32, I32, VP, VP, VP]
         lib.qhadamard_prepare.argtypes = [VP, I32, I32, VP, VP, VP]
         lib.qhadamard_finish.argtypes = [VP, I32, I32, VP, VP, I32, VP]
+        lib.qgemv_hadamard_workspace_size.argtypes = [P, I32, I32]
+        lib.qgemv_hadamard_workspace_size.restype = SZ
+        lib.qgemv_hadamard.argtypes = [P, VP, I32, VP, VP, VP, I32, VP, SZ, VP]
         lib.qgemm_w4a4_workspace_size.argtypes = [P, I32]
         lib.qgemm_w4a4_workspace_size.restype = SZ
         lib.qgemm_w4a4.argtypes = [P, VP, I32, VP, VP, VP, SZ, VP]
@@ -320,6 +324,28 @@ def hadamard_finish(y, out_scale=None, out=None, out_dtype=torch.float32, stream
     dt = F32 if out.dtype == torch.float32 else BF16
     _check(_lib().qhadamard_finish(_ptr(y), m, n, _ptr(out_scale), _ptr(out), dt,
                                    _stream(stream)), "qhadamard_finish")
+    return out
+
+
+def gemv_hadamard(w: Weight, x, in_scale=None, out_scale=None, y_dtype=torch.float32, out=None,
+                  workspace=None, stream=None):
+    """qgemv_hadamard: y = finish(W . prepare(x)), prepare fused into the GEMV,
+    x bf16 [m][k] raw activations, m in 1..4."""
+    dev, m = _check_gemv("qgemv_hadamard", w, x, None, out, workspace, _OUT)
+    if in_scale is not None:
+        _tensor("qgemv_hadamard", "in_scale", in_scale, (torch.float16,), (w.k,), dev)
+    if out_scale is not None:
+        _tensor("qgemv_hadamard", "out_scale", out_scale, (torch.float16,), (w.n,), dev)
+    if out is None:
+        out = torch.empty((m, w.n), dtype=y_dtype, device=dev)
+        _tensor("qgemv_hadamard", "out", out, _OUT)
+    dt = F32 if out.dtype == torch.float32 else BF16
+    need = int(_lib().qgemv_hadamard_workspace_size(w.c, m, dt))
+    if workspace is None and need:
+        workspace = new_workspace(need, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib().qgemv_hadamard(w.c, _ptr(x), m, _ptr(in_scale), _ptr(out_scale), _ptr(out), dt,
+                                 _ptr(workspace), ws_bytes, _stream(stream)), "qgemv_hadamard")
     return out
 
 

@@ -104,3 +104,76 @@ def test_hadamard_argument_errors():
     with pytest.raises(q.QmmError) as e:
         q.hadamard_finish(y, out=y)                                   # in place: alias
     assert e.value.status == -7
+
+
+# qgemv_hadamard: prepare fused into the GEMV's prologue, finish after it.
+# Bar: bitwise equal to qhadamard_prepare, qgemv and qhadamard_finish run in
+# sequence (the fused prologue runs the same transform routine and the same
+# block-sum arithmetic), for every format, 1-4 rows, with and without channel
+# scales, float32 and bf16 y.
+HAD_SHAPES = [(640, 1024), (384, 5120), (256, 17408)]
+
+
+def _had_weight(fmt, n, k, name):
+    return quant.synthetic_weight(fmt, n, k, outlier_rate=0.01, name=name)
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("shape", HAD_SHAPES)
+def test_gemv_hadamard_equals_the_staged_calls(fmt, m, shape):
+    q = _q()
+    n, k = shape
+    p = _had_weight(fmt, n, k, f"hg{fmt}{n}{k}")
+    w = q.Weight.from_host(p)
+    x = _dev_bf16(quant.synthetic_bf16(m, k, name=f"hgx{m}{k}"))
+    si = torch.from_numpy(_scales(k, f"hgsi{k}")).cuda()
+    so = torch.from_numpy(_scales(n, f"hgso{n}")).cuda()
+    for scaled in (False, True):
+        a, b = (si, so) if scaled else (None, None)
+        for dt in (torch.float32, torch.bfloat16):
+            fused = q.gemv_hadamard(w, x, a, b, y_dtype=dt)
+            staged = q.hadamard_finish(q.gemv(w, q.hadamard_prepare(x, a)), b, out_dtype=dt)
+            torch.cuda.synchronize()
+            assert torch.equal(fused.view(torch.int16), staged.view(torch.int16)), (scaled, dt)
+
+
+def test_gemv_hadamard_against_the_oracle_chain():
+    """The chain against the oracle's stages: the oracle's GEMV on the GPU's
+    prepared activations, then the oracle's finish; each output within
+    2e-3 |s_out| sum_i mag_i / sqrt(128) over its block (the GEMV's bound
+    carried through the orthonormal transform) plus 1e-6 of the finish's own
+    magnitude sum."""
+    q = _q()
+    n, k, m = 384, 5120, 3
+    p = _had_weight(4, n, k, "hgo")
+    w = q.Weight.from_host(p)
+    xb = quant.synthetic_bf16(m, k, name="hgox")
+    si, so = _scales(k, "hgosi"), _scales(n, "hgoso")
+    x = _dev_bf16(xb)
+    y = q.gemv_hadamard(w, x, torch.from_numpy(si).cuda(), torch.from_numpy(so).cuda())
+    y = y.cpu().numpy().astype(np.float64)
+    xp = q.hadamard_prepare(x, torch.from_numpy(si).cuda()).view(torch.int16).cpu().numpy().view(np.uint16)
+    ylin, mag = oracle.gemv(p, xp)
+    yref, fmag = oracle.hadamard_finish(ylin.astype(np.float32), so.view(np.uint16))
+    s_abs = np.abs(oracle.fp16(so.view(np.uint16)))
+    blk_mag = np.repeat(mag.reshape(m, n // 128, 128).sum(-1) / np.sqrt(128), 128, axis=-1).reshape(m, n)
+    bound = 2e-3 * s_abs * blk_mag + 1e-6 * fmag
+    ok = np.abs(y - yref) <= bound
+    assert ok.all(), f"{(~ok).sum()} outputs off"
+
+
+def test_gemv_hadamard_argument_errors():
+    q = _q()
+    p = _had_weight(1, 256, 192, "hge")           # k not a multiple of 128
+    w = q.Weight.from_host(p)
+    x = _dev_bf16(quant.synthetic_bf16(2, 192, name="hgex"))
+    with pytest.raises(q.QmmError) as e:
+        q.gemv_hadamard(w, x)
+    assert e.value.status == -3
+    p2 = _had_weight(1, 256, 256, "hge2")
+    w2 = q.Weight.from_host(p2)
+    x5 = _dev_bf16(quant.synthetic_bf16(5, 256, name="hgex5"))
+    with pytest.raises(q.QmmError) as e:
+        q.gemv_hadamard(w2, x5)
+    assert e.value.status == -5
