@@ -1,6 +1,6 @@
 """Benchmark of the dequantizing matmul hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu] [--sections decode,prefill,moe,fp4]
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--sections decode,prefill,mid,moe,fp4,hadamard]
     python bench.py --record-traffic FETCH.csv WRITE.csv   (no GPU work; see below)
 
 One step = one pass of the decode workload: every (format, shape, lanes)
@@ -32,6 +32,9 @@ own configurations and reported under "sections" (each with its own unit):
              (warm and cold) and 8192
     fp4      mxfp4 and nvfp4 matvecs (1% outliers at 8x), 5120 x 5120,
              5120 x 6144 and 248320 x 5120, M = 1..4 -> weight GB/s
+    hadamard qgemv_hadamard (prepare, GEMV, finish in one call) against
+             the three calls and the GEMV alone, 17408 x 5120 affine4_g64,
+             M = 1 and 4 -> us per call
 
 Prints one JSON line.  The oracle (CPU, float64) is timed on bounded samples
 of the decode, prefill and MoE workloads for the cpu_baseline field (all BLAS
@@ -48,6 +51,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import ctypes
 import hashlib
 import json
 import os
@@ -74,7 +78,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
-    ap.add_argument("--sections", default="decode,prefill,mid,moe,fp4")
+    ap.add_argument("--sections", default="decode,prefill,mid,moe,fp4,hadamard")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     return ap.parse_args()
 
@@ -541,6 +545,64 @@ def fp4_section(q, torch, dev):
     return {"unit": "GB/s", "cases": out}
 
 
+def hadamard_section(q, torch, dev):
+    """qgemv_hadamard (prepare, GEMV and finish in one call) against the
+    three calls (qhadamard_prepare, qgemv, qhadamard_finish) and the GEMV
+    alone, on the 17408 x 5120 affine matrix, cold weights, float32 y."""
+    from synth import formats as F
+    from synth import quant
+    out = []
+    n, k = 17408, 5120
+    p = quant.synthetic_weight(F.AFFINE4_G64, n, k, name="bench/had/w")
+    w0 = q.Weight.from_host(p, dev)
+    copies = max(2, int(np.ceil(800e6 / w0.nbytes())))
+    ws_ = [w0] + [q.Weight.from_host(p, dev) for _ in range(copies - 1)]
+    del p
+    g = torch.Generator().manual_seed(7)
+    si = (torch.rand(k, generator=g) * 4 - 2).to(torch.float16).to(dev)
+    so = (torch.rand(n, generator=g) * 4 - 2).to(torch.float16).to(dev)
+    for m in (1, 4):
+        x = dev_bf16(torch, quant.synthetic_bf16(m, k, name=f"bench/had/x{m}"), dev)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        xp = torch.empty_like(x)
+        ylin = torch.empty((m, n), dtype=torch.float32, device=dev)
+        it = iter(range(1 << 30))
+        # argument checks done once: plain C calls in the timed loops
+        q.gemv_hadamard(w0, x, si, so, out=y)
+        lib = q.lib_handle()
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        px, pxp, py, pyl, psi, pso = P(x), P(xp), P(y), P(ylin), P(si), P(so)
+        need = int(lib.qgemv_hadamard_workspace_size(w0.c, m, q.F32))
+        wsh = q.new_workspace(need, dev)
+        pws = P(wsh)
+
+        def fused():
+            rc = lib.qgemv_hadamard(ws_[next(it) % copies].c, px, m, psi, pso, py, q.F32, pws,
+                                    need, st)
+            assert rc == 0, rc
+
+        def plain():
+            rc = lib.qgemv(ws_[next(it) % copies].c, pxp, m, None, pyl, q.F32, None, 0, st)
+            assert rc == 0, rc
+
+        def staged():
+            rc = lib.qhadamard_prepare(px, m, k, psi, pxp, st)
+            rc |= lib.qgemv(ws_[next(it) % copies].c, pxp, m, None, pyl, q.F32, None, 0, st)
+            rc |= lib.qhadamard_finish(pyl, m, n, pso, py, q.F32, st)
+            assert rc == 0, rc
+
+        fm, _ = timed(torch, fused, 4 * copies)
+        sm, _ = timed(torch, staged, 4 * copies)
+        gm, _ = timed(torch, plain, 4 * copies)
+        out.append({"format": "affine4_g64", "shape": f"{n}x{k}", "m": m,
+                    "us_one_call": round(fm * 1e3, 2), "us_three_calls": round(sm * 1e3, 2),
+                    "us_gemv_alone": round(gm * 1e3, 2)})
+    del ws_, w0
+    torch.cuda.empty_cache()
+    return {"unit": "us per call", "cases": out}
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -644,6 +706,8 @@ def main():
         extra["moe"] = moe_section(q, torch, dev)
     if "fp4" in sections:
         extra["fp4"] = fp4_section(q, torch, dev)
+    if "hadamard" in sections:
+        extra["hadamard"] = hadamard_section(q, torch, dev)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,

@@ -243,10 +243,30 @@ int qhadamard_finish(const float *y, int32_t m, int32_t n, const void *out_scale
                                          (hipStream_t)stream));
 }
 
+namespace {
+
+// qgemv_hadamard's workspace: the prepared activations, the float32 product
+// when y is bf16, then qgemv's own split-K workspace
+struct HadWs {
+  size_t xp, ylin, gemv, total;
+};
+
+HadWs had_ws(const qmm_weight &w, int m, int y_dtype) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  HadWs h;
+  h.xp = up((size_t)m * w.k * 2);
+  h.ylin = y_dtype == QMM_BF16 ? up((size_t)m * w.n * 4) : 0;
+  h.gemv = qmm::plan_gemv(w.format, w.n, w.k, m).ws_bytes;
+  h.total = h.xp + h.ylin + h.gemv;
+  return h;
+}
+
+}  // namespace
+
 size_t qgemv_hadamard_workspace_size(const qmm_weight *w, int32_t m, int32_t y_dtype) {
   if (check_weight(w) || m < 1 || m > 4) return 0;
-  if (y_dtype != QMM_BF16) return 0;
-  return ((size_t)m * w->n * 4 + 255) / 256 * 256;
+  if (y_dtype != QMM_F32 && y_dtype != QMM_BF16) return 0;
+  return had_ws(*w, m, y_dtype).total;
 }
 
 int qgemv_hadamard(const qmm_weight *w, const void *x, int32_t m, const void *in_scale,
@@ -257,38 +277,36 @@ int qgemv_hadamard(const qmm_weight *w, const void *x, int32_t m, const void *in
   if (w->batch != 1) return QMM_ERR_SHAPE;
   if (m < 1 || m > 4) return QMM_ERR_M_RANGE;
   if (y_dtype != QMM_F32 && y_dtype != QMM_BF16) return QMM_ERR_DTYPE;
-  if (!x || !y) return QMM_ERR_NULL;
+  if (!x || !y || !workspace) return x && y ? QMM_ERR_WORKSPACE : QMM_ERR_NULL;
   if (w->k % 128 != 0 || w->n % 128 != 0) return QMM_ERR_SHAPE;
-  qmm::GemvPlan p;
-  if (!qmm::plan_gemv_rows(w->format, w->n, w->k, m, p)) return QMM_ERR_SHAPE;
   const size_t esz = y_dtype == QMM_F32 ? 4 : 2;
-  if (!aligned(x, 16) || !aligned(y, esz) || (in_scale && !aligned(in_scale, 2)) ||
+  if (!aligned(x, 2) || !aligned(y, esz) || (in_scale && !aligned(in_scale, 2)) ||
       (out_scale && !aligned(out_scale, 2)))
     return QMM_ERR_ALIGN;
-  const size_t ws = qgemv_hadamard_workspace_size(w, m, y_dtype);
-  if (ws) {
-    if (!workspace || workspace_bytes < ws) return QMM_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return QMM_ERR_ALIGN;
-  }
+  const HadWs h = had_ws(*w, m, y_dtype);
+  if (workspace_bytes < h.total) return QMM_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return QMM_ERR_ALIGN;
   const Range ry = range(y, (size_t)m * w->n * esz);
+  const Range rw = range(workspace, h.total);
   Range ins[10];
   int ni = weight_ranges(*w, ins);
   ins[ni++] = range(x, (size_t)m * w->k * 2);
   if (in_scale) ins[ni++] = range(in_scale, (size_t)w->k * 2);
   if (out_scale) ins[ni++] = range(out_scale, (size_t)w->n * 2);
+  if (overlap(ry, rw)) return QMM_ERR_ALIAS;
   for (int i = 0; i < ni; ++i)
-    if (overlap(ry, ins[i])) return QMM_ERR_ALIAS;
-  if (ws) {
-    const Range rw = range(workspace, ws);
-    if (overlap(rw, ry)) return QMM_ERR_ALIAS;
-    for (int i = 0; i < ni; ++i)
-      if (overlap(rw, ins[i])) return QMM_ERR_ALIAS;
-  }
+    if (overlap(ry, ins[i]) || overlap(rw, ins[i])) return QMM_ERR_ALIAS;
   hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  void *xp = ws;
   // the float32 product lands in y (finish then runs in place: each wave
-  // reads its block before writing it) or, for a bf16 y, in the workspace
-  void *ylin = ws ? workspace : y;
-  hipError_t e = qmm::launch_gemv_rows(*w, x, m, nullptr, ylin, QMM_F32, p, s, true, in_scale);
+  // reads its 128-block before writing it) or, for a bf16 y, in the workspace
+  void *ylin = h.ylin ? (void *)(ws + h.xp) : y;
+  void *gws = h.gemv ? (void *)(ws + h.xp + h.ylin) : nullptr;
+  hipError_t e = qmm::launch_hadamard(true, x, m, w->k, in_scale, xp, 1, s);
+  if (e != hipSuccess) return hip_status(e);
+  e = qmm::launch_gemv(*w, xp, m, nullptr, ylin, QMM_F32, gws,
+                       qmm::plan_gemv(w->format, w->n, w->k, m), s);
   if (e != hipSuccess) return hip_status(e);
   return hip_status(qmm::launch_hadamard(false, ylin, m, w->n, out_scale, y, y_dtype == QMM_BF16, s));
 }

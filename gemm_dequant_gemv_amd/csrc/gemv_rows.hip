@@ -137,10 +137,8 @@ struct RowsArgs {
   const uint16_t *x;
   const uint16_t *residual;
   void *y;
-  const uint16_t *had_scale;  // qgemv_hadamard: float16 input-channel scales, or null
   uint32_t codes_bytes, hi_bytes, scales_bytes, scales2_bytes, residual_bytes;
   int n, k, steps, y_bf16;
-  int hadamard;  // qgemv_hadamard: the prepare stage on the staged activations
 };
 
 // ---- the matrix-core form (2 to 8 activation rows)
@@ -486,56 +484,6 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
-  // qgemv_hadamard: the prepare stage of the EXL3 rotation ("TurboEXL3"
-  // section 3.1) on the staged activations, each 128-value block of each row
-  // scaled by the input-channel scales, transformed (hadamard128_wave, the
-  // routine of qhadamard_prepare) and rounded to bfloat16 in place; then the
-  // block sums are recomputed from the rounded values the way the staging
-  // computes them.  The GEMV then sees exactly qhadamard_prepare's output.
-  if (a.hadamard) {  // uniform
-    const int nblk = nch >> 2;
-    for (int u = wave; u < nblk * M; u += kWaves) {
-      const int blk = u / M, m = u - blk * M;
-      const int e = lane & 31, q = e >> 3, ee = e & 7;
-      const int pos = T::kPermute ? 2 * (ee & 3) + (ee >> 2) : ee;  // 16-bit slot in the piece
-      uint16_t *p0 = (uint16_t *)(xs + (4 * blk + (lane >> 5)) * XL::kStride + XL::piece(m, q)) + pos;
-      uint16_t *p1 = (uint16_t *)((char *)p0 + 2 * XL::kStride);
-      float v0 = bf_lo(*p0), v1 = bf_lo(*p1);
-      if (a.had_scale) {
-        v0 *= half_to_float(a.had_scale[blk * 128 + lane]);
-        v1 *= half_to_float(a.had_scale[blk * 128 + lane + 64]);
-      }
-      hadamard128_wave(v0, v1, lane);
-      *p0 = (uint16_t)float_to_bf16(v0);
-      *p1 = (uint16_t)float_to_bf16(v1);
-    }
-    if constexpr (kNS > 0) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int j = 0; j < kXPieces; ++j) {
-        if (j * kThreads >= pieces) break;  // uniform
-        const int i = j * kThreads + tid;
-        const bool ok = i < pieces;
-        const int ch = i / (4 * M), m = (i >> 2) % M, part_ = i & 3;
-        char *rec = xs + ch * XL::kStride;
-        const uint4 o = ok ? *(const uint4 *)(rec + XL::piece(m, part_)) : make_uint4(0u, 0u, 0u, 0u);
-        uint4 v = o;
-        if constexpr (T::kPermute) {  // back to value order
-          v.x = (o.x & 0xFFFFu) | (o.y << 16);
-          v.z = (o.x >> 16) | (o.y & 0xFFFF0000u);
-          v.y = (o.z & 0xFFFFu) | (o.w << 16);
-          v.w = (o.z >> 16) | (o.w & 0xFFFF0000u);
-        }
-        stage_sums(v, rec, m, part_, ok);
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  }
-
   const UnpackK K = unpack_consts();
   // gscale's load completed before the barrier above (loads complete in
   // order and x was loaded after it); the empty asm tells the compiler so,
@@ -759,11 +707,8 @@ bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p) {
 }
 
 hipError_t launch_gemv_rows(const qmm_weight &w, const void *x, int m, const void *residual,
-                            void *y, int y_dtype, const GemvPlan &p, hipStream_t s,
-                            bool hadamard, const void *had_scale) {
+                            void *y, int y_dtype, const GemvPlan &p, hipStream_t s) {
   RowsArgs a;
-  a.hadamard = hadamard ? 1 : 0;
-  a.had_scale = (const uint16_t *)had_scale;
   a.codes = (const uint8_t *)w.codes;
   a.codes_hi = (const uint8_t *)w.codes_hi;
   a.scales = (const uint8_t *)w.scales;

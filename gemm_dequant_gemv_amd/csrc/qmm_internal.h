@@ -79,11 +79,8 @@ int moe_tile_rows(const qmm_weight &gu, const qmm_weight &dn, int t, int topk, i
 MoeTables moe_tables(const MoeLayout &L, void *ws);
 
 hipError_t launch_dequant(const qmm_weight &w, int out_dtype, void *out, hipStream_t s);
-// hadamard: the prepare stage of the rotation (scale by had_scale, 128-block
-// Hadamard, bf16 rounding) on the staged activations first (qgemv_hadamard)
 hipError_t launch_gemv_rows(const qmm_weight &w, const void *x, int m, const void *residual,
-                            void *y, int y_dtype, const GemvPlan &p, hipStream_t s,
-                            bool hadamard = false, const void *had_scale = nullptr);
+                            void *y, int y_dtype, const GemvPlan &p, hipStream_t s);
 // qgemm's 5 to kRowsMaxM rows on the row-streaming kernel (weights read and
 // decoded once), bf16 y; false when the activations do not fit in LDS (the
 // call then takes the MFMA tiles)

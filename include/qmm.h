@@ -289,29 +289,29 @@ int qhadamard_finish(const float *y, int32_t m, int32_t n, const void *out_scale
                      int32_t out_dtype, void *stream);
 
 /*
- * qgemv_hadamard -- one EXL3-style projection at decode: prepare, the matrix-
- * vector product and finish in one call, the prepare stage fused into the
- * GEMV's prologue ("TurboEXL3", section 3.1: the prepare and finish stages
- * around the inner product; section 2.3: 128-block sign-randomized Hadamard
- * transforms and the two channel vectors):
+ * qgemv_hadamard -- one EXL3-style projection at decode in one call: the
+ * prepare stage, the matrix-vector product and the finish stage ("TurboEXL3",
+ * section 3.1: the prepare and finish stages around the inner product;
+ * section 2.3: 128-block sign-randomized Hadamard transforms and the two
+ * channel vectors):
  *
  *   y = finish( W . prepare(x) )      (prepare and finish as above)
  *
- * The GEMV kernel stages raw x in LDS, applies prepare there (the routine of
- * qhadamard_prepare, so the same bf16 values) and multiplies; finish follows
- * as a second launch on the stream.  The result is bitwise that of
- * qhadamard_prepare, qgemv and qhadamard_finish in sequence.
+ * Three launches on the stream, bitwise the result of qhadamard_prepare,
+ * qgemv and qhadamard_finish in sequence.  (Prepare was also built into the
+ * row-streaming GEMV's prologue, transforming the staged activations in LDS:
+ * every workgroup then repeats the whole transform of x, and it measured
+ * 0.7-25 us slower than the separate launch on the decode shapes, so the
+ * separate launch stays.)
  *
- * w          one matrix (batch 1) in any format; n and k multiples of 128; the
- *            activations of the call must fit the row-streaming kernel's LDS
- *            image (K up to 17408 at every m for the decode shapes;
- *            QMM_ERR_SHAPE otherwise)
+ * w          one matrix (batch 1) in any format; n and k multiples of 128
  * x          bf16 [m][k], m = 1..4 (raw activations: prepare is applied here)
  * in_scale, out_scale  float16 [k] / [n] or NULL (all ones)
  * y          [m][n] float32 (QMM_F32) or bf16 (QMM_BF16)
- * workspace  qgemv_hadamard_workspace_size bytes (the float32 product before
- *            finish when y is bf16; 0 for float32 y, where finish runs in
- *            place in y), 256-byte aligned; no zero-fill
+ * workspace  qgemv_hadamard_workspace_size bytes, 256-byte aligned, never
+ *            NULL: the prepared activations, the float32 product when y is
+ *            bf16 (a float32 y takes it, and finish runs in place), then
+ *            qgemv's split-K workspace if the call needs one; no zero-fill
  * Nothing may overlap y or the workspace (QMM_ERR_ALIAS).
  */
 size_t qgemv_hadamard_workspace_size(const qmm_weight *w, int32_t m, int32_t y_dtype);

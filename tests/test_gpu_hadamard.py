@@ -106,12 +106,12 @@ def test_hadamard_argument_errors():
     assert e.value.status == -7
 
 
-# qgemv_hadamard: prepare fused into the GEMV's prologue, finish after it.
-# Bar: bitwise equal to qhadamard_prepare, qgemv and qhadamard_finish run in
-# sequence (the fused prologue runs the same transform routine and the same
-# block-sum arithmetic), for every format, 1-4 rows, with and without channel
-# scales, float32 and bf16 y.
-HAD_SHAPES = [(640, 1024), (384, 5120), (256, 17408)]
+# qgemv_hadamard: prepare, the GEMV and finish in one call.  Bar: bitwise
+# equal to qhadamard_prepare, qgemv and qhadamard_finish run in sequence
+# (workspace carving, the in-place finish of a float32 y, the split-K GEMV at
+# K = 81920), for every format, 1-4 rows, with and without channel scales,
+# float32 and bf16 y.
+HAD_SHAPES = [(640, 1024), (384, 5120), (256, 17408), (128, 81920)]
 
 
 def _had_weight(fmt, n, k, name):
