@@ -17,7 +17,9 @@
 //     owns 256 weight rows x 32 TM activation rows; per 128-wide K slice the
 //     activation codes and scales go from memory straight into LDS (three
 //     slices in flight) and each wave loads its own 32 weight rows' codes and
-//     scales into registers (three slices ahead).  The codes are the MFMA
+//     scales into registers (three slices ahead, through the caches: the 32
+//     activation tiles of a weight tile read it again, and the non-temporal
+//     loads of the streaming GEMV measured 28-39% slower here).  The codes are the MFMA
 //     operands as they are: there is no decode step.  Inside a slice, lane
 //     half h multiplies K blocks 2h and 2h + 1 (k-steps 0 and 1) for both
 //     operands, so a lane reads 32 contiguous code bytes of its weight row.
@@ -35,7 +37,7 @@ typedef float f32x16_w __attribute__((ext_vector_type(16)));
 
 constexpr int kSliceK = 128;         // K values per slice: two k-steps of 64
 constexpr int kRowBytes = 64;        // code bytes of one row per slice
-constexpr int kW4Stages = 3;         // slices in flight
+constexpr int kW4Stages = 3;         // slices in flight (4 and 6 measured 2-6% slower)
 constexpr int kW4Waves = 8;
 constexpr int kW4BN = 32 * kW4Waves; // weight rows per workgroup
 
@@ -160,8 +162,8 @@ void gemm_w4a4_kernel(W4A4Args a) {
   };
   auto load_w = [&](int s) __attribute__((always_inline)) {
     WPiece p;
-    p.q0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rwc, v_wc, (uint32_t)s * kRowBytes, 2));
-    p.q1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rwc, v_wc, (uint32_t)s * kRowBytes + 16u, 2));
+    p.q0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rwc, v_wc, (uint32_t)s * kRowBytes, 0));
+    p.q1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rwc, v_wc, (uint32_t)s * kRowBytes + 16u, 0));
     p.s = __builtin_amdgcn_raw_buffer_load_b32(rws, v_ws, (uint32_t)s * 4u, 0);
     return p;
   };
@@ -206,18 +208,30 @@ void gemm_w4a4_kernel(W4A4Args a) {
       const int sa0 = (int)((wp.s >> sshift0) & 0xFFu), sa1 = (int)((wp.s >> sshift1) & 0xFFu);
       const v8i_t a0 = {(int)wp.q0.x, (int)wp.q0.y, (int)wp.q0.z, (int)wp.q0.w, 0, 0, 0, 0};
       const v8i_t a1 = {(int)wp.q1.x, (int)wp.q1.y, (int)wp.q1.z, (int)wp.q1.w, 0, 0, 0, 0};
+      // every activation operand and scale word of the slice first, so the
+      // products then issue back to back (reading each just before its
+      // product left the matrix cores waiting on one LDS round trip per
+      // product at two waves per SIMD)
+      u32x4_t b0[TM], b1[TM];
+      uint32_t xsc[TM];
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
         const uint8_t *row = stg + t * 32 * kRowBytes;
-        const u32x4_t b0 = *(const u32x4_t *)(row + xo[0]);
-        const u32x4_t b1 = *(const u32x4_t *)(row + xo[1]);
-        const uint32_t xsc = *(const uint32_t *)(stg + kCodeStage + (32 * t + lr) * 4);
-        const v8i_t bv0 = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
-        const v8i_t bv1 = {(int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w, 0, 0, 0, 0};
+        b0[t] = *(const u32x4_t *)(row + xo[0]);
+        b1[t] = *(const u32x4_t *)(row + xo[1]);
+        xsc[t] = *(const uint32_t *)(stg + kCodeStage + (32 * t + lr) * 4);
+      }
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const v8i_t bv0 = {(int)b0[t].x, (int)b0[t].y, (int)b0[t].z, (int)b0[t].w, 0, 0, 0, 0};
         acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            a0, bv0, acc[t], 4, 4, 0, sa0, 0, (int)((xsc >> sshift0) & 0xFFu));
+            a0, bv0, acc[t], 4, 4, 0, sa0, 0, (int)((xsc[t] >> sshift0) & 0xFFu));
+      }
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const v8i_t bv1 = {(int)b1[t].x, (int)b1[t].y, (int)b1[t].z, (int)b1[t].w, 0, 0, 0, 0};
         acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            a1, bv1, acc[t], 4, 4, 0, sa1, 0, (int)((xsc >> sshift1) & 0xFFu));
+            a1, bv1, acc[t], 4, 4, 0, sa1, 0, (int)((xsc[t] >> sshift1) & 0xFFu));
       }
     }
   }
