@@ -104,19 +104,27 @@ struct W4A4Args {
 // at one logical chunk land on 16 distinct bank groups.
 __device__ __forceinline__ int xchunk(int r, int c) { return c ^ ((r >> 2) & 3); }
 
-template <int TM>
+// The workgroup's 8 waves as kWN x kWM: wave w owns weight rows
+// 32 TN (w % kWN) .. (TN groups of 32) and activation rows 32 TM (w / kWN) ..
+// (TM groups of 32) of the 256 x 256 tile, so every activation operand read
+// from LDS feeds TN products and every weight operand TM.
+template <int TN, int TM>
 __global__ __launch_bounds__(64 * kW4Waves) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_w4a4_kernel(W4A4Args a) {
-  constexpr int BM = 32 * TM;
+  constexpr int kWN = kW4BN / (32 * TN);       // wave columns over the weight rows
+  constexpr int kWM = kW4Waves / kWN;          // wave rows over the activation rows
+  constexpr int BM = 32 * TM * kWM;
+  static_assert(kWN * 32 * TN == kW4BN && kWN * kWM == kW4Waves, "wave grid");
   constexpr int kCodeStage = BM * kRowBytes;  // activation codes of one slice
   constexpr int kStage = kCodeStage + BM * 4; // + their scales (4 per row)
   constexpr int XI = BM / 16 / kW4Waves;      // code-load instructions per wave and slice
   constexpr int SI = BM / 64;                 // scale-load instructions per slice
   static_assert(XI >= 1 && XI * 16 * kW4Waves == BM && SI >= 1 && SI <= kW4Waves, "tiles");
-  constexpr int kLoads = XI + 1 + 3;          // per wave and slice: X codes, X scales, W
+  constexpr int kLoads = XI + 1 + 3 * TN;     // per wave and slice: X codes, X scales, W
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % kWN, wm = wave / kWN;
   const int lr = lane & 31, h = lane >> 5;
   const int tiles_m = (a.m + BM - 1) / BM;
   const int m0 = ((int)blockIdx.x % tiles_m) * BM;
@@ -150,36 +158,48 @@ void gemm_w4a4_kernel(W4A4Args a) {
                                              v_xs, (uint32_t)s * 4u, 0, 0);
   };
 
-  // weights: lane (lr, h) holds weight row n0 + 32 wave + lr; per slice its
-  // code bytes 32 h .. 32 h + 31 (K blocks 2h, 2h + 1) and the row's 4 scales
+  // weights: lane (lr, h) holds weight rows n0 + 32 (TN wn + tn) + lr; per
+  // slice their code bytes 32 h .. 32 h + 31 (K blocks 2h, 2h + 1) and 4 scales
   const __amdgpu_buffer_rsrc_t rwc = make_rsrc(a.wcodes, (uint32_t)((size_t)a.n * kb));
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(a.wscales, (uint32_t)((size_t)a.n * kq));
-  const uint32_t wrow = (uint32_t)min(n0 + 32 * wave + lr, a.n - 1);
-  const uint32_t v_wc = wrow * kb + 32u * (uint32_t)h, v_ws = wrow * kq;
+  uint32_t v_wc[TN], v_ws[TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    const uint32_t wrow = (uint32_t)min(n0 + 32 * (TN * wn + tn) + lr, a.n - 1);
+    v_wc[tn] = wrow * kb + 32u * (uint32_t)h;
+    v_ws[tn] = wrow * kq;
+  }
   struct WPiece {
-    u32x4_t q0, q1;  // K blocks 2h, 2h + 1
-    uint32_t s;      // the row's 4 E8M0 scales of the slice
+    u32x4_t q0[TN], q1[TN];  // K blocks 2h, 2h + 1
+    uint32_t s[TN];          // each row's 4 E8M0 scales of the slice
   };
   auto load_w = [&](int s) __attribute__((always_inline)) {
     WPiece p;
-    p.q0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rwc, v_wc, (uint32_t)s * kRowBytes, 0));
-    p.q1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rwc, v_wc, (uint32_t)s * kRowBytes + 16u, 0));
-    p.s = __builtin_amdgcn_raw_buffer_load_b32(rws, v_ws, (uint32_t)s * 4u, 0);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      p.q0[tn] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rwc, v_wc[tn], (uint32_t)s * kRowBytes, 0));
+      p.q1[tn] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rwc, v_wc[tn], (uint32_t)s * kRowBytes + 16u, 0));
+      p.s[tn] = __builtin_amdgcn_raw_buffer_load_b32(rws, v_ws[tn], (uint32_t)s * 4u, 0);
+    }
     return p;
   };
   WPiece wr[kW4Stages];
 
-  f32x16_w acc[TM];
+  f32x16_w acc[TN][TM];
 #pragma unroll
-  for (int t = 0; t < TM; ++t)
+  for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[tn][t][e] = 0.f;
 
-  // this lane's activation operand reads: row 32 t + lr, logical chunk
-  // 2h + ks at its physical place ((32 t + lr) >> 2 & 3 = lr >> 2 & 3)
+  // this lane's activation operand reads: row 32 (TM wm + t) + lr, logical
+  // chunk 2h + ks at its physical place ((32 t' + lr) >> 2 & 3 = lr >> 2 & 3)
   uint32_t xo[2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) xo[ks] = (uint32_t)lr * kRowBytes + (uint32_t)xchunk(lr, 2 * h + ks) * 16u;
+  for (int ks = 0; ks < 2; ++ks)
+    xo[ks] = (uint32_t)(32 * TM * wm + lr) * kRowBytes + (uint32_t)xchunk(lr, 2 * h + ks) * 16u;
+  const uint32_t xso = (uint32_t)kCodeStage + (uint32_t)(32 * TM * wm + lr) * 4u;
   const int sshift0 = 8 * (2 * h), sshift1 = 8 * (2 * h + 1);
 
 #pragma unroll
@@ -205,13 +225,8 @@ void gemm_w4a4_kernel(W4A4Args a) {
 
       const uint8_t *stg = lds + (s % kW4Stages) * kStage;
       const WPiece &wp = wr[u];
-      const int sa0 = (int)((wp.s >> sshift0) & 0xFFu), sa1 = (int)((wp.s >> sshift1) & 0xFFu);
-      const v8i_t a0 = {(int)wp.q0.x, (int)wp.q0.y, (int)wp.q0.z, (int)wp.q0.w, 0, 0, 0, 0};
-      const v8i_t a1 = {(int)wp.q1.x, (int)wp.q1.y, (int)wp.q1.z, (int)wp.q1.w, 0, 0, 0, 0};
       // every activation operand and scale word of the slice first, so the
-      // products then issue back to back (reading each just before its
-      // product left the matrix cores waiting on one LDS round trip per
-      // product at two waves per SIMD)
+      // products then issue back to back
       u32x4_t b0[TM], b1[TM];
       uint32_t xsc[TM];
 #pragma unroll
@@ -219,19 +234,24 @@ void gemm_w4a4_kernel(W4A4Args a) {
         const uint8_t *row = stg + t * 32 * kRowBytes;
         b0[t] = *(const u32x4_t *)(row + xo[0]);
         b1[t] = *(const u32x4_t *)(row + xo[1]);
-        xsc[t] = *(const uint32_t *)(stg + kCodeStage + (32 * t + lr) * 4);
+        xsc[t] = *(const uint32_t *)(stg + xso + t * 32 * 4);
       }
 #pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        const v8i_t bv0 = {(int)b0[t].x, (int)b0[t].y, (int)b0[t].z, (int)b0[t].w, 0, 0, 0, 0};
-        acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            a0, bv0, acc[t], 4, 4, 0, sa0, 0, (int)((xsc[t] >> sshift0) & 0xFFu));
-      }
+      for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        const v8i_t bv1 = {(int)b1[t].x, (int)b1[t].y, (int)b1[t].z, (int)b1[t].w, 0, 0, 0, 0};
-        acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            a1, bv1, acc[t], 4, 4, 0, sa1, 0, (int)((xsc[t] >> sshift1) & 0xFFu));
+        for (int tn = 0; tn < TN; ++tn) {
+          const u32x4_t q = ks == 0 ? wp.q0[tn] : wp.q1[tn];
+          const v8i_t av = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+          const int sa = (int)((wp.s[tn] >> (ks == 0 ? sshift0 : sshift1)) & 0xFFu);
+#pragma unroll
+          for (int t = 0; t < TM; ++t) {
+            const u32x4_t b = ks == 0 ? b0[t] : b1[t];
+            const v8i_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+            acc[tn][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                av, bv, acc[tn][t], 4, 4, 0, sa, 0,
+                (int)((xsc[t] >> (ks == 0 ? sshift0 : sshift1)) & 0xFFu));
+          }
+        }
       }
     }
   }
@@ -240,32 +260,36 @@ void gemm_w4a4_kernel(W4A4Args a) {
   // value 4b + r: four consecutive weight rows per b
 #pragma unroll
   for (int t = 0; t < TM; ++t) {
-    const int ml = 32 * t + lr;
+    const int ml = 32 * (TM * wm + t) + lr;
     if (ml >= mrows) continue;
     const int m = m0 + ml;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int nb = n0 + 32 * wave + 8 * b + 4 * h;
-      float v[4] = {acc[t][4 * b], acc[t][4 * b + 1], acc[t][4 * b + 2], acc[t][4 * b + 3]};
-      const size_t base = (size_t)m * a.n + nb;
-      if (nb + 3 < a.n && (a.n & 3) == 0) {  // 8-byte aligned: 4 bf16 at once
-        if (a.residual) {
-          const uint2 r = *(const uint2 *)(a.residual + base);
-          v[0] += bf_lo(r.x);
-          v[1] += bf_hi(r.x);
-          v[2] += bf_lo(r.y);
-          v[3] += bf_hi(r.y);
-        }
-        *(uint2 *)(a.y + base) = make_uint2(float_to_bf16(v[0]) | (float_to_bf16(v[1]) << 16),
-                                            float_to_bf16(v[2]) | (float_to_bf16(v[3]) << 16));
-        continue;
-      }
+    for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (nb + r >= a.n) break;
-        float o = v[r];
-        if (a.residual) o += bf_lo(a.residual[base + r]);
-        a.y[base + r] = (uint16_t)float_to_bf16(o);
+      for (int b = 0; b < 4; ++b) {
+        const int nb = n0 + 32 * (TN * wn + tn) + 8 * b + 4 * h;
+        float v[4] = {acc[tn][t][4 * b], acc[tn][t][4 * b + 1], acc[tn][t][4 * b + 2],
+                      acc[tn][t][4 * b + 3]};
+        const size_t base = (size_t)m * a.n + nb;
+        if (nb + 3 < a.n && (a.n & 3) == 0) {  // 8-byte aligned: 4 bf16 at once
+          if (a.residual) {
+            const uint2 r = *(const uint2 *)(a.residual + base);
+            v[0] += bf_lo(r.x);
+            v[1] += bf_hi(r.x);
+            v[2] += bf_lo(r.y);
+            v[3] += bf_hi(r.y);
+          }
+          *(uint2 *)(a.y + base) = make_uint2(float_to_bf16(v[0]) | (float_to_bf16(v[1]) << 16),
+                                              float_to_bf16(v[2]) | (float_to_bf16(v[3]) << 16));
+          continue;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (nb + r >= a.n) break;
+          float o = v[r];
+          if (a.residual) o += bf_lo(a.residual[base + r]);
+          a.y[base + r] = (uint16_t)float_to_bf16(o);
+        }
       }
     }
   }
@@ -309,10 +333,14 @@ hipError_t launch_gemm_w4a4(const qmm_weight &w, const void *x, int m, const voi
   a.m = m;
   a.n = w.n;
   a.k = w.k;
-  constexpr int TM = 8;
-  constexpr size_t lds = (size_t)kW4Stages * (32 * TM * kRowBytes + 32 * TM * 4);
-  const unsigned grid = (unsigned)(((m + 32 * TM - 1) / (32 * TM)) * ((w.n + kW4BN - 1) / kW4BN));
-  hipLaunchKernelGGL((gemm_w4a4_kernel<TM>), dim3(grid), dim3(64 * kW4Waves), lds, s, a);
+  // one weight-row group per wave: 2 and 4 groups (activation operands
+  // shared by 2 or 4 products, but every weight row loaded by 2 or 4 waves)
+  // measured 17-24% and 46-50% slower on 17408 x 5120 at M = 512-8192
+  constexpr int TN = 1, TM = 8 / TN;
+  constexpr int BM = 256;
+  constexpr size_t lds = (size_t)kW4Stages * (BM * kRowBytes + BM * 4);
+  const unsigned grid = (unsigned)(((m + BM - 1) / BM) * ((w.n + kW4BN - 1) / kW4BN));
+  hipLaunchKernelGGL((gemm_w4a4_kernel<TN, TM>), dim3(grid), dim3(64 * kW4Waves), lds, s, a);
   return hipGetLastError();
 }
 
