@@ -5,9 +5,9 @@
 // Lane l holds the logits l, l + 64, l + 128, ... of the token as order keys
 // (a float32 mapped to a uint32 whose unsigned order is the float order, -0
 // taken as +0).  Each of the k rounds finds the largest key not yet taken:
-// every lane its own best (ascending index, so an equal key keeps the lower
-// index), then the maximum over (key, inverted index) across the wave (DPP
-// inside each row of 16 lanes, then the four rows), so equal logits go to the
+// every lane its own maximum, then the maximum across the wave (DPP inside
+// each row of 16 lanes, then the four rows); the lowest index holding it
+// (ballots over the lane's keys in index order), so equal logits go to the
 // lower expert id; the owner lane marks the winner taken.  Lane r keeps round
 // r's expert and logit (read back from its key), so the list comes out in
 // descending logit order.  The weights are the softmax of the k chosen logits
@@ -29,16 +29,11 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 // DPP controls: quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror
 constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 
-// (hi, lo) = the larger of itself and the pair DPP brings from another lane
-// of its row of 16
+// the larger of v and the value DPP brings from another lane of its row of 16
 template <int CTRL>
-__device__ __forceinline__ void dpp_max_u64(uint32_t &hi, uint32_t &lo) {
-  const uint32_t oh = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, 0xF, 0xF, false);
-  const uint32_t ol = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, 0xF, 0xF, false);
-  if (oh > hi || (oh == hi && ol > lo)) {
-    hi = oh;
-    lo = ol;
-  }
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return o > v ? o : v;
 }
 
 template <int CTRL>
@@ -59,37 +54,40 @@ __device__ __forceinline__ void topk_softmax_wave(const float *lg, int e, int k,
     const int i = lane + 64 * j;
     key[j] = i < e ? order_key(lg[i]) : 0u;  // 0: below every finite key
   }
-  uint64_t taken = 0;
+  // live keys: taken or absent ones are 0, below every finite key
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (lane + 64 * j >= e) key[j] = 0u;
   int my_id = 0;
   float my_logit = 0.0f;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;  // (key << 32) | (0xFFFFFFFF - index); 0: none
+    // the largest live key: each lane's, then inside each row of 16 (DPP),
+    // then over the four rows (uniform)
+    uint32_t mx = key[0];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = lane + 64 * j;
-      const uint64_t c = ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
-      if (i < e && !((taken >> j) & 1ull) && c > best) best = c;
-    }
-    // the maximum inside each row of 16 lanes (DPP), then over the four rows
-    // (one lane of each, uniform)
-    uint32_t bh = (uint32_t)(best >> 32), bl = (uint32_t)best;
-    dpp_max_u64<kDppQuadXor1>(bh, bl);
-    dpp_max_u64<kDppQuadXor2>(bh, bl);
-    dpp_max_u64<kDppHalfMirror>(bh, bl);
-    dpp_max_u64<kDppMirror>(bh, bl);
-    uint32_t kw = (uint32_t)__builtin_amdgcn_readlane((int)bh, 0);
-    uint32_t iw = (uint32_t)__builtin_amdgcn_readlane((int)bl, 0);
+    for (int j = 1; j < PER; ++j) mx = key[j] > mx ? key[j] : mx;
+    mx = dpp_max_u32<kDppQuadXor1>(mx);
+    mx = dpp_max_u32<kDppQuadXor2>(mx);
+    mx = dpp_max_u32<kDppHalfMirror>(mx);
+    mx = dpp_max_u32<kDppMirror>(mx);
+    uint32_t kw = (uint32_t)__builtin_amdgcn_readlane((int)mx, 0);
 #pragma unroll
     for (int row = 1; row < 4; ++row) {
-      const uint32_t h = (uint32_t)__builtin_amdgcn_readlane((int)bh, 16 * row);
-      const uint32_t l = (uint32_t)__builtin_amdgcn_readlane((int)bl, 16 * row);
-      if (h > kw || (h == kw && l > iw)) {
-        kw = h;
-        iw = l;
-      }
+      const uint32_t h = (uint32_t)__builtin_amdgcn_readlane((int)mx, 16 * row);
+      kw = h > kw ? h : kw;
     }
-    const int win = (int)(0xFFFFFFFFu - iw);
-    if ((win & 63) == lane) taken |= 1ull << (win >> 6);
+    // the lowest index holding it (index = lane + 64 j: the first j with a
+    // lane at kw, its lowest such lane), so equal logits go to the lower id
+    int win = 0;
+#pragma unroll
+    for (int j = PER - 1; j >= 0; --j) {
+      const uint64_t b = __ballot(key[j] == kw);
+      if (b != 0ull) win = 64 * j + (int)__builtin_ctzll(b);
+    }
+    const int wj = win >> 6, wl = win & 63;  // uniform
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (j == wj && lane == wl) key[j] = 0u;
     if (lane == r) {  // the logit back from its key: no reload from memory
       my_id = win;
       my_logit = __uint_as_float((kw & 0x80000000u) ? (kw & 0x7FFFFFFFu) : ~kw);
