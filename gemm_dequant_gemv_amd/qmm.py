@@ -331,11 +331,21 @@ def gemv_hadamard(w: Weight, x, in_scale=None, out_scale=None, y_dtype=torch.flo
                   workspace=None, stream=None):
     """qgemv_hadamard: y = finish(W . prepare(x)), prepare fused into the GEMV,
     x bf16 [m][k] raw activations, m in 1..4."""
-    dev, m = _check_gemv("qgemv_hadamard", w, x, None, out, workspace, _OUT)
+    where = "qgemv_hadamard"
+    dev = w.codes.device
+    _tensor(where, "x", x, _BF16, None, dev)
+    if x.dim() != 2 or x.shape[1] != w.k:
+        raise ValueError(f"{where}: x has shape {tuple(x.shape)}, expected (m, {w.k})")
+    m = x.shape[0]
     if in_scale is not None:
-        _tensor("qgemv_hadamard", "in_scale", in_scale, (torch.float16,), (w.k,), dev)
+        _tensor(where, "in_scale", in_scale, (torch.float16,), (w.k,), dev)
     if out_scale is not None:
-        _tensor("qgemv_hadamard", "out_scale", out_scale, (torch.float16,), (w.n,), dev)
+        _tensor(where, "out_scale", out_scale, (torch.float16,), (w.n,), dev)
+    if out is not None:
+        _tensor(where, "out", out, _OUT, (m, w.n), dev)
+    if workspace is not None:
+        _tensor(where, "workspace", workspace, _U8, None, dev)
+    _require_gpu(where, dev)
     if out is None:
         out = torch.empty((m, w.n), dtype=y_dtype, device=dev)
         _tensor("qgemv_hadamard", "out", out, _OUT)

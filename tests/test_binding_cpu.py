@@ -133,3 +133,23 @@ def test_host_planes_round_trip_dtypes():
                     (F.NVFP4, torch.uint8), (F.Q6_K, torch.int8)):
         w = _weight(fmt, 16, 256)
         assert w.scales.dtype == dt and w.codes.dtype == torch.uint8
+
+
+def test_gemv_hadamard_and_stage_argument_checks():
+    w = _weight()
+    x = _bf16(2, 256)
+    with pytest.raises(TypeError, match="in_scale has dtype"):
+        q.gemv_hadamard(w, x, in_scale=torch.zeros(256))
+    with pytest.raises(ValueError, match="in_scale has shape"):
+        q.gemv_hadamard(w, x, in_scale=torch.zeros(128, dtype=torch.float16))
+    with pytest.raises(ValueError, match="out_scale has shape"):
+        q.gemv_hadamard(w, x, out_scale=torch.zeros(256, dtype=torch.float16))
+    with pytest.raises(ValueError, match="x has shape"):
+        q.gemv_hadamard(w, _bf16(2, 128))
+    with pytest.raises(ValueError, match="must live on a GPU"):
+        q.gemv_hadamard(w, x, in_scale=torch.zeros(256, dtype=torch.float16),
+                        out_scale=torch.zeros(64, dtype=torch.float16))
+    with pytest.raises(TypeError, match="x has dtype"):
+        q.hadamard_prepare(torch.zeros((2, 256)))
+    with pytest.raises(TypeError, match="y has dtype"):
+        q.hadamard_finish(_bf16(2, 256))
