@@ -744,11 +744,12 @@ namespace qmm {
 // chunk of up to 8 rows): the row-streaming kernel, which reads and decodes
 // the weights once, with the exact weights (no bfloat16 rounding of the
 // weights, unlike the MFMA tiles) and a bfloat16 y.  Measured on 17408 x 5120
-// (cold weights, us, GEMV / MFMA tiles): affine 5 rows 23.9 / 38.0, 8 rows
-// 28.9 / 38.0; NVFP4 23.0 / 37.6, 27.1 / 38.2; Q6_K 31.6 / 55.6, 37.3 / 55.3;
-// MXFP4 21.8 / 37.2, 26.4 / 37.5.  Two chunks for 9 to 16 rows lost to the
-// MFMA tiles (affine 9 rows 42.2 / 38.2, 16 rows 56.7 / 40.3), so those rows
-// stay there.
+// (cold weights, us, GEMV with v_dot2 products / MFMA tiles): affine 5 rows
+// 23.9 / 38.0, 8 rows 28.9 / 38.0; NVFP4 23.0 / 37.6, 27.1 / 38.2; Q6_K
+// 31.6 / 55.6, 37.3 / 55.3; MXFP4 21.8 / 37.2, 26.4 / 37.5; with the
+// matrix-core products from 6 rows (5 for Q6_K), 8 rows take affine ~22,
+// NVFP4 ~20, Q6_K ~27 us.  Two chunks for 9 to 16 rows lost to the MFMA tiles
+// (affine 9 rows 42.2 / 38.2, 16 rows 56.7 / 40.3), so those rows stay there.
 bool gemm_rows_fits(const qmm_weight &w, int m) {
   if (m < 5 || m > kRowsMaxM || w.batch != 1) return false;
   GemvPlan p;
