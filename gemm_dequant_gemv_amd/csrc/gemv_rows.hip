@@ -9,11 +9,15 @@
 // chunk: its x in pair order, then its block sums), then its waves stream
 // weight rows:
 //   * rows go in pairs (2p, 2p+1), one per half-wave, dealt out in one of two
-//     ways: round-robin, where wave w of the grid owns pairs w, w + W, w + 2W,
-//     ... (W = waves in the grid), so at any moment the grid streams one
-//     contiguous band of rows; or balanced, where workgroup g owns the
-//     contiguous pairs [g P / G, (g+1) P / G) (P pairs, G workgroups) and
-//     splits their units (below), pair-major, evenly over its 16 waves;
+//     ways: round-robin, in rounds of W pairs (W = waves in the grid, 16 G
+//     for G workgroups): in round r wave w of workgroup g owns pair
+//     r W + 16 g + w, so that the grid streams one contiguous band of rows
+//     and a workgroup's waves neighbouring pairs, except in the last, partial
+//     round, where it owns pair r W + w G + g (wave-major: every workgroup
+//     gets its share of that round, give or take one pair); or balanced,
+//     where workgroup g owns the contiguous pairs [g P / G, (g+1) P / G) (P
+//     pairs) and splits their units (below), pair-major, evenly over its
+//     waves (the form for fewer pairs than waves and long rows);
 //   * a unit is one step of one pair: 1024 values (512 code bytes) of each
 //     row, one 16-byte load per lane (lane c of a half holds values 32c ..
 //     32c+31), so every load instruction reads whole 128-byte lines of two
@@ -34,13 +38,12 @@
 // Nothing crosses workgroups, so there is no split-K finish and no workspace,
 // and every sum has a fixed order: the result does not depend on timing.
 //
-// Round-robin pairs leave the waves uneven work: on 17408 rows an eighth of
-// the waves take half as many units again as the rest, on 5120 rows 40% of
-// the waves have none.  Where the per-unit vector work is heavy (Q6_K, and
-// the affine format at M >= 2) those waves set the kernel's time, and the
-// balanced form measured 4-15% faster; where it is light (the E2M1 formats,
-// affine at M = 1) the kernel waits on memory either way, and the balanced
-// form's final barrier and cut-pair finish made it 2-4% slower.
+// The waves of a workgroup need not end together: the compute unit's memory
+// throughput sets the pace, and a copy of the kernel that handed out units
+// to the waves at run time (chunks of 4 from an LDS counter, sums kept per
+// chunk and added in chunk order) so that they all ended within a chunk of
+// each other was 1-12% slower on every decode shape.  What matters is that
+// every workgroup gets the same work, which the wave-major last round gives.
 //
 // The activations must fit in LDS (K * M * 2 bytes plus block sums); the host
 // falls back to the split-K kernel otherwise.
@@ -119,10 +122,9 @@ struct XLayout {
   static_assert(MFL ? (kStride / 16) % 4 == 2 : (kStride / 16) % 2 == 1, "record stride");
 };
 
-// The balanced split where the per-unit vector work is heavy.
-constexpr bool use_balanced(int format, int m) {
-  return format == QMM_Q6_K || (format == QMM_AFFINE4_G64 && m >= 2) || m >= 5;
-}
+// How the waves share the rows (above): round-robin pairs, or each
+// workgroup's units split evenly over its waves.
+constexpr int kSplitRR = 0, kSplitBal = 1;
 
 constexpr int sums_per_chunk(int format) {
   return format == QMM_AFFINE4_G64 ? 1 : (format == QMM_Q6_K ? 2 : 0);
@@ -296,8 +298,9 @@ __device__ __forceinline__ float mf_finish(float (&acc)[MfShape<M>::kG][2], int 
   return out;
 }
 
-template <int FMT, int M, int U, bool BAL>
+template <int FMT, int M, int U, int SPLIT>
 __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsArgs a) {
+  constexpr bool BAL = SPLIT == kSplitBal;
   constexpr int kWaves = RowsShape<M>::kWaves;
   constexpr int kThreads = RowsShape<M>::kThreads;
   constexpr int kXPieces = RowsShape<M>::kXPieces;
@@ -317,10 +320,10 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = a.steps;
   const uint32_t k = (uint32_t)a.k;
-  // The wave walks pairs pbase + j * pstride from j = j0, step st0, for
-  // `units` units; (jl, sl) is its last unit, re-read by the loads past the end.
+  // The wave walks its pairs pair_of(j) from j = j0, step st0, for `units`
+  // units.
   const int npairs = (a.n + 1) / 2;
-  int pbase, pstride, units, j0 = 0, st0 = 0, jl, sl, L = 0;
+  int pbase, pstride, units, j0 = 0, st0 = 0, L = 0, rfull = 0, plast = 0;
   if constexpr (BAL) {
     // the workgroup's pairs [pbase, pbase + L / S) and their L units
     pbase = (int)((long long)blockIdx.x * npairs / gridDim.x);
@@ -330,17 +333,15 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
     units = (wave + 1) * L / kWaves - u0;
     j0 = u0 / S;
     st0 = u0 - j0 * S;
-    const int ulast = u0 + max(units, 1) - 1;
-    jl = ulast / S;
-    sl = ulast - jl * S;
   } else {
-    // pairs gw, gw + W, ... of the grid's W waves
+    // round r < rfull: pair r W + 16 g + w of the grid's W = 16 G waves; the
+    // last, partial round: pair rfull W + w G + g (wave-major), so that every
+    // workgroup gets the same number of pairs give or take one
     pbase = blockIdx.x * kWaves + wave;
     pstride = gridDim.x * kWaves;
-    const int mypairs = pbase < npairs ? (npairs - 1 - pbase) / pstride + 1 : 0;
-    units = mypairs * S;
-    jl = max(mypairs - 1, 0);
-    sl = S - 1;
+    rfull = npairs / pstride;
+    plast = rfull * pstride + wave * (int)gridDim.x + (int)blockIdx.x;
+    units = (rfull + (plast < npairs ? 1 : 0)) * S;
   }
   __shared__ float part[BAL ? kWaves : 1][2][kOut];  // sums of pairs cut by wave boundaries
 
@@ -394,9 +395,14 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
   //    there delayed each wave's exit by a memory round trip); the row past n
   //    of an odd n and lanes past K read whatever the buffer holds there, or
   //    zeros beyond its end, and their results are never used.
+  // the wave's j-th pair
+  auto pair_of = [&](int j) -> int {
+    if constexpr (BAL) return pbase + j;
+    return j < rfull ? pbase + j * pstride : plast;
+  };
   auto load_unit = [&](int t, int j, int s, RowData &rd, uint32_t &res) {
     const bool past = t >= units;  // uniform
-    const uint32_t row0 = 2u * (uint32_t)(pbase + j * pstride);
+    const uint32_t row0 = 2u * (uint32_t)pair_of(j);
     auto at = [past](uint32_t off, uint32_t bytes) { return past ? bytes : off; };
     rd.q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
         rc, v_code, at(row0 * (k / 2) + (uint32_t)s * (kStepK / 2), a.codes_bytes), 2));
@@ -509,6 +515,63 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
   const char *xb_lane = xs + cB * XL::kStride + XL::piece(mB, 0);
   const char *sb_lane = xs + cB * XL::kStride + XL::kSumOff + mB * 4 * (kNS > 0 ? kNS : 1);
 
+  // one unit's products into the lane's sums (step cs of the unit in b)
+  auto compute_unit = [&](const RowData &b, int cs) {
+    if constexpr (MF) {
+      // every lane takes part in the products; a lane whose chunk is past
+      // K multiplies zero activations and gets zero scale terms
+      RowData rd = b;
+      if (cs * kChunks + cA >= nch) {
+        rd.s = 0u;
+        rd.d = 0u;
+      }
+      uint32_t P[16];
+      unpack_pairs<FMT>(rd, P, K);
+      float t0s, t1s;
+      mf_scales<FMT>(rd, t0s, t1s);
+      const int off = cs * (kChunks * XL::kStride);
+      mf_unit<FMT, M, XL::kStride>(P, t0s, t1s, xb_lane + off, sb_lane + off, qi, accv);
+    } else if (cs * kChunks + c < nch) {
+      // this lane's record of step cs: lane base + a wave-uniform offset
+      const char *rec = xs_lane + cs * (kChunks * XL::kStride);
+      uint32_t X[M][16];
+      float Sx[M][2];
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = *(const uint4 *)(rec + XL::piece(m, q));
+          X[m][4 * q + 0] = v.x;
+          X[m][4 * q + 1] = v.y;
+          X[m][4 * q + 2] = v.z;
+          X[m][4 * q + 3] = v.w;
+        }
+        const float *sums = (const float *)(rec + XL::kSumOff);
+        Sx[m][0] = kNS > 0 ? sums[m * (kNS > 0 ? kNS : 1)] : 0.0f;
+        Sx[m][1] = kNS > 1 ? sums[m * 2 + 1] : 0.0f;
+      }
+      row_step<FMT, M>(b, X, Sx, acc, K);
+    }
+  };
+  // the pair's sums so far, reduced over the wave: lane 2m + h gets row 2p + h
+  // of activation row m (lanes < kOut); the lane sums restart from zero
+  auto take_sums = [&]() -> float {
+    float out = 0.0f;
+    if constexpr (MF) {
+      out = mf_finish<M>(accv, lane);
+    } else {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float s0, s1;
+        half_sums(acc[m], s0, s1);
+        acc[m] = 0.0f;
+        if (lane == 2 * m) out = s0;
+        if (lane == 2 * m + 1) out = s1;
+      }
+    }
+    return out;
+  };
+
   int cj = j0, cs = st0;  // unit being computed: pair index, step
   float fin_res = 0.0f;    // balanced: residual of the cut pair this wave finishes
   // Issue priority falls as the wave gets through its units.  The arbiter of
@@ -525,57 +588,11 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       if (t0 + j < units) {  // uniform
-        if constexpr (MF) {
-          // every lane takes part in the products; a lane whose chunk is past
-          // K multiplies zero activations and gets zero scale terms
-          RowData rd = buf[j];
-          if (cs * kChunks + cA >= nch) {
-            rd.s = 0u;
-            rd.d = 0u;
-          }
-          uint32_t P[16];
-          unpack_pairs<FMT>(rd, P, K);
-          float t0s, t1s;
-          mf_scales<FMT>(rd, t0s, t1s);
-          const int off = cs * (kChunks * XL::kStride);
-          mf_unit<FMT, M, XL::kStride>(P, t0s, t1s, xb_lane + off, sb_lane + off, qi, accv);
-        } else if (cs * kChunks + c < nch) {
-          // this lane's record of step cs: lane base + a wave-uniform offset
-          const char *rec = xs_lane + cs * (kChunks * XL::kStride);
-          uint32_t X[M][16];
-          float Sx[M][2];
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint4 v = *(const uint4 *)(rec + XL::piece(m, q));
-              X[m][4 * q + 0] = v.x;
-              X[m][4 * q + 1] = v.y;
-              X[m][4 * q + 2] = v.z;
-              X[m][4 * q + 3] = v.w;
-            }
-            const float *sums = (const float *)(rec + XL::kSumOff);
-            Sx[m][0] = kNS > 0 ? sums[m * (kNS > 0 ? kNS : 1)] : 0.0f;
-            Sx[m][1] = kNS > 1 ? sums[m * 2 + 1] : 0.0f;
-          }
-          row_step<FMT, M>(buf[j], X, Sx, acc, K);
-        }
+        compute_unit(buf[j], cs);
         if (cs == S - 1 || (BAL && t0 + j == units - 1)) {  // the wave is done with the pair
-          float out = 0.0f;
-          if constexpr (MF) {
-            out = mf_finish<M>(accv, lane);
-          } else {
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-              float s0, s1;
-              half_sums(acc[m], s0, s1);
-              acc[m] = 0.0f;
-              if (lane == 2 * m) out = s0;
-              if (lane == 2 * m + 1) out = s1;
-            }
-          }
+          const float out = take_sums();
           if (cs == S - 1 && (!BAL || cj != j0 || st0 == 0)) {  // the whole pair
-            const int row = 2 * (pbase + cj * pstride) + o_h;
+            const int row = 2 * pair_of(cj) + o_h;
             if (lane < kOut && row < a.n) store(row, out * gscale + bf_lo(res[j]));
           } else {  // a cut pair, the wave's first (slot 0) or last (slot 1)
             if (lane < kOut) part[BAL ? wave : 0][cj == j0 ? 0 : 1][lane] = out;
@@ -608,7 +625,7 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
   }
 }
 
-template <int FMT, int M, int U, bool BAL>
+template <int FMT, int M, int U, int SPLIT>
 hipError_t launch_rows_cfg(const RowsArgs &a, size_t lds, int grid, hipStream_t s) {
   constexpr int kThreads = RowsShape<M>::kThreads;
   // the dynamic LDS limit is raised once per device for each instantiation
@@ -618,26 +635,31 @@ hipError_t launch_rows_cfg(const RowsArgs &a, size_t lds, int grid, hipStream_t 
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(raised.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute((const void *)gemv_rows_kernel<FMT, M, U, BAL>,
+    e = hipFuncSetAttribute((const void *)gemv_rows_kernel<FMT, M, U, SPLIT>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     if (e != hipSuccess) return e;
     raised.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((gemv_rows_kernel<FMT, M, U, BAL>), dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((gemv_rows_kernel<FMT, M, U, SPLIT>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
 #ifdef QMM_TUNE
 #define QMM_ROWS_CONFIGS(X) X(1) X(2) X(3) X(4) X(6)
 #else
-#define QMM_ROWS_CONFIGS(X) X(2) X(3)
+#define QMM_ROWS_CONFIGS(X) X(2) X(3) X(4)
 #endif
 
 template <int FMT, int M>
 hipError_t launch_rows_fm(const RowsArgs &a, const GemvPlan &p, hipStream_t s) {
-  constexpr bool kBal = use_balanced(FMT, M);
-#define QMM_CASE(UU) \
-  if (p.depth == UU) return launch_rows_cfg<FMT, M, UU, kBal>(a, p.lds_bytes, p.tiles, s);
+  int split = p.balanced;
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_ROWS_SPLIT")) split = atoi(e);
+#endif
+#define QMM_CASE(UU)                                                                          \
+  if (p.depth == UU)                                                                          \
+    return split == kSplitBal ? launch_rows_cfg<FMT, M, UU, kSplitBal>(a, p.lds_bytes, p.tiles, s) \
+                              : launch_rows_cfg<FMT, M, UU, kSplitRR>(a, p.lds_bytes, p.tiles, s);
   QMM_ROWS_CONFIGS(QMM_CASE)
 #undef QMM_CASE
   return hipErrorInvalidConfiguration;
@@ -689,20 +711,38 @@ bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p) {
   if (cus <= 0) return false;
   p = GemvPlan{};
   p.kind = 1;
-  // units of loads in flight per wave
   p.rows_per_lane = 1;
-  // (5 to 8 rows: 3, measured 2-6% faster than 2 through qgemm on 17408 x 5120)
-  p.depth = m == 1 || m >= 5 ? 3 : 2;
-  p.balanced = use_balanced(format, m);
-#ifdef QMM_TUNE
-  if (const char *e = getenv("QMM_ROWS_U")) p.depth = atoi(e);
-#endif
   p.lanes_k = 32;
   p.steps = (k + kStepK - 1) / kStepK;
   p.tiles = cus;  // one workgroup per compute unit
   p.splits = 1;
   p.lds_bytes = lds;
-  (void)n;
+  // The split and the units of loads in flight per wave (cold weights, events
+  // around back-to-back launches, the settings interleaved in one process):
+  //   * balanced where the grid has more waves than pairs and the rows are
+  //     long: 5120 x 17408 3-9% faster than round-robin (Q6_K from 1 row,
+  //     affine from 2), which leaves 6 of 16 waves per compute unit idle
+  //     there; on 5120 x 5120 and 6144 x 5120 balanced is 14-18% slower (its
+  //     cut-pair finish and barrier cost more than the idle waves);
+  //   * round-robin elsewhere: on 17408 x 5120 8-14% faster than balanced and
+  //     14-19% faster than round-robin without the wave-major last round
+  //     (which gave an eighth of the workgroups half as many pairs again);
+  //   * 2 units in flight on the decode shapes (3 and 4 were 2-9% slower on
+  //     17408 x 5120), 4 on long streams of at least 8 rounds (the 248320 x
+  //     5120 projection 3-5% faster than with 2), 3 for 1 row balanced
+  //     (5120 x 17408) and for 5 to 8 rows.
+  const size_t waves = (size_t)cus * (m <= 4 ? RowsShape<4>::kWaves : RowsShape<8>::kWaves);
+  const size_t npairs = ((size_t)n + 1) / 2;
+  p.balanced = npairs < waves && p.steps >= 8 ? kSplitBal : kSplitRR;
+  if (m >= 5)
+    p.depth = 3;
+  else if (p.balanced == kSplitBal)
+    p.depth = m == 1 ? 3 : 2;
+  else
+    p.depth = npairs >= 8 * waves ? 4 : 2;
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_ROWS_U")) p.depth = atoi(e);
+#endif
   return true;
 }
 

@@ -24,7 +24,8 @@ struct GemvPlan {
   int rows_per_lane;  // R (row-streaming: rows per batch)
   int depth;          // D: steps (row-streaming: units) of weights in flight per lane
   int early;          // split-K: code loads issued before waiting for activations and scales
-  int balanced;       // row-streaming: pairs in per-workgroup blocks split evenly over the waves
+  int balanced;       // row-streaming split: 0 round-robin pairs, 1 each workgroup's units split
+                      // evenly over its waves
   int lanes_k;        // lanes sharing a row (each reads 16 bytes per step)
   int steps;      // steps per row
   int tiles;      // split-K: ceil(n / rows per workgroup); row-streaming: workgroups
