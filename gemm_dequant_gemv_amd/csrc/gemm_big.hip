@@ -32,6 +32,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdlib>
+#include <type_traits>
 
 #include "gemm_common.h"
 
@@ -196,68 +197,88 @@ void gemm_big_kernel(GemmArgs a) {
   // (the last slice again past the end, so that every wave issues the same
   // loads and the counts below hold)
   constexpr int kLoadsPerSlice = XI + w_loads_per_run<FMT>();
+  // The waits below count loads, so the loads must issue slice by slice: the
+  // scheduler is kept from regrouping them (left alone it can put every
+  // slice's weight loads ahead of the first slice's activations, which the
+  // first wait would then not cover).
 #pragma unroll
   for (int p = 0; p < kStages - 1; ++p) {
     const int sp = min(s_begin + p, s_end - 1);
     load_x(sp);
     wr[p] = load_run<FMT>(ws, sp);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  for (int s0 = s_begin; s0 < s_end; s0 += kStages) {
-#pragma unroll
-    for (int u = 0; u < kStages; ++u) {
-      const int s = s0 + u;
-      if (s >= s_end) break;  // uniform
-      // this wave's share of slice s is in LDS once at most the loads issued
-      // after it (kStages - 2 slices) are outstanding; the barrier then makes
-      // every wave's share visible and frees the stage read in iteration s - 1
-      // (whose operands are already in registers).  A bare s_barrier: the
-      // fence of __syncthreads would also wait for the slices still in flight.
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kLoadsPerSlice));
-      __builtin_amdgcn_s_barrier();
-      const int sn = min(s + kStages - 1, s_end - 1);
-      load_x(sn);
-      wr[(u + kStages - 1) % kStages] = load_run<FMT>(ws, sn);
+  // One slice: s is the slice, u its weight slot (s - s_begin) % kStages.
+  auto slice = [&](const int s, auto uc) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value;
+    // this wave's share of slice s is in LDS once at most the loads issued
+    // after it (kStages - 2 slices) are outstanding; the barrier then makes
+    // every wave's share visible and frees the stage read in iteration s - 1
+    // (whose operands are already in registers).  A bare s_barrier: the
+    // fence of __syncthreads would also wait for the slices still in flight.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kLoadsPerSlice));
+    __builtin_amdgcn_s_barrier();
+    const int sn = min(s + kStages - 1, s_end - 1);
+    load_x(sn);
+    wr[(u + kStages - 1) % kStages] = load_run<FMT>(ws, sn);
 
-      // the run's 32 weights: k-step st takes values 8 st .. 8 st + 7.  The
-      // decode of k-step st + 1's weights is interleaved with k-step st's
-      // MFMAs (each MFMA occupies the matrix core for many cycles, in which
-      // the wave issues independent vector instructions), so that only the
-      // first k-step's decode runs with the matrix core idle.
-      const PieceScale sc = piece_scale<FMT>(wr[u]);
-      uint32_t o[4];
-      decode_part<FMT>(wr[u], sc, 0, o);
-      bf16x8_t af = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
+    // the run's 32 weights: k-step st takes values 8 st .. 8 st + 7.  The
+    // decode of k-step st + 1's weights is interleaved with k-step st's
+    // MFMAs (each MFMA occupies the matrix core for many cycles, in which
+    // the wave issues independent vector instructions), so that only the
+    // first k-step's decode runs with the matrix core idle.
+    const PieceScale sc = piece_scale<FMT>(wr[u]);
+    uint32_t o[4];
+    decode_part<FMT>(wr[u], sc, 0, o);
+    bf16x8_t af = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
 
-      // Likewise the activation operands of k-step st + 1 are read from LDS
-      // during k-step st's MFMAs, so that no k-step but the first waits on LDS.
-      const uint8_t *stg = lds + (s % kStages) * kXStage;
-      bf16x8_t bfr[TM];
+    // Likewise the activation operands of k-step st + 1 are read from LDS
+    // during k-step st's MFMAs, so that no k-step but the first waits on LDS.
+    const uint8_t *stg = lds + (s % kStages) * kXStage;
+    bf16x8_t bfr[TM];
 #pragma unroll
-      for (int t = 0; t < TM; ++t) bfr[t] = *(const bf16x8_t *)(stg + t * 32 * kXRow + xo[0]);
+    for (int t = 0; t < TM; ++t) bfr[t] = *(const bf16x8_t *)(stg + t * 32 * kXRow + xo[0]);
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        // MFMA t, then one LDS read and part of the decode for k-step st + 1,
-        // in this order (the scheduler is kept from regrouping them)
-        __builtin_amdgcn_sched_barrier(0);
-        uint32_t on[4] = {0u, 0u, 0u, 0u};
-        bf16x8_t bfn[TM];
+    for (int st = 0; st < 4; ++st) {
+      // MFMA t, then one LDS read and part of the decode for k-step st + 1,
+      // in this order (the scheduler is kept from regrouping them)
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t on[4] = {0u, 0u, 0u, 0u};
+      bf16x8_t bfn[TM];
 #pragma unroll
-        for (int t = 0; t < TM; ++t) {
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[t], acc[t], 0, 0, 0);
-          if (st < 3) {
-            bfn[t] = *(const bf16x8_t *)(stg + t * 32 * kXRow + xo[st + 1]);
+      for (int t = 0; t < TM; ++t) {
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[t], acc[t], 0, 0, 0);
+        if (st < 3) {
+          bfn[t] = *(const bf16x8_t *)(stg + t * 32 * kXRow + xo[st + 1]);
 #pragma unroll
-            for (int i = t * 4 / TM; i < (t + 1) * 4 / TM; ++i) on[i] = decode_word<FMT>(wr[u], sc, st + 1, i);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+          for (int i = t * 4 / TM; i < (t + 1) * 4 / TM; ++i) on[i] = decode_word<FMT>(wr[u], sc, st + 1, i);
         }
-        af = __builtin_bit_cast(bf16x8_t, u32x4_t{on[0], on[1], on[2], on[3]});
-#pragma unroll
-        for (int t = 0; t < TM; ++t) bfr[t] = bfn[t];
+        __builtin_amdgcn_sched_barrier(0);
       }
+      af = __builtin_bit_cast(bf16x8_t, u32x4_t{on[0], on[1], on[2], on[3]});
+#pragma unroll
+      for (int t = 0; t < TM; ++t) bfr[t] = bfn[t];
     }
+  };
+  // Whole groups of kStages slices, then the rest: the loop body has no exit
+  // of its own, so that the compiler's wait analysis keeps track of the
+  // weight loads' age across the back edge.
+  static_assert(kStages == 3, "the slice loop is written out for three stages");
+  int s = s_begin;
+  for (; s + kStages <= s_end; s += kStages) {
+    slice(s, std::integral_constant<int, 0>{});
+    slice(s + 1, std::integral_constant<int, 1>{});
+    slice(s + 2, std::integral_constant<int, 2>{});
   }
+  if (s < s_end) slice(s, std::integral_constant<int, 0>{});
+  if (s + 1 < s_end) slice(s + 1, std::integral_constant<int, 1>{});
+
+  // The loads issued past the last slice (re-reads of it, so that the counts
+  // above hold) may still be in flight; a workgroup must not end with LDS
+  // writes pending, or they could land in the LDS of the next workgroup on
+  // the compute unit.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // epilogue: lane (lr, h) holds D[n = 8b + 4h + r][m = lr] of each tile as
   // value 4b + r: four consecutive W rows per b
