@@ -26,6 +26,8 @@
 //   The products of E2M1 values and powers of two are exact; only the float32
 //   sums round, in a fixed order (slices in order, the two lane halves inside
 //   the matrix core).
+#include <type_traits>
+
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
@@ -202,59 +204,75 @@ void gemm_w4a4_kernel(W4A4Args a) {
   const uint32_t xso = (uint32_t)kCodeStage + (uint32_t)(32 * TM * wm + lr) * 4u;
   const int sshift0 = 8 * (2 * h), sshift1 = 8 * (2 * h + 1);
 
+  // The waits below count loads, so the loads must issue slice by slice (the
+  // scheduler is kept from regrouping the first slices' loads).
 #pragma unroll
   for (int p = 0; p < kW4Stages - 1; ++p) {
     const int sp = min(p, slices - 1);
     load_x(sp);
     wr[p] = load_w(sp);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  for (int s0 = 0; s0 < slices; s0 += kW4Stages) {
-#pragma unroll
-    for (int u = 0; u < kW4Stages; ++u) {
-      const int s = s0 + u;
-      if (s >= slices) break;  // uniform
-      // slice s is in LDS (this wave's share) once at most the loads of the
-      // kW4Stages - 2 slices issued after it are outstanding; the barrier
-      // makes every wave's share visible and frees the stage of slice s - 1
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((kW4Stages - 2) * kLoads));
-      __builtin_amdgcn_s_barrier();
-      const int sn = min(s + kW4Stages - 1, slices - 1);
-      load_x(sn);
-      wr[(u + kW4Stages - 1) % kW4Stages] = load_w(sn);
+  // One slice: s is the slice, u its weight slot s % kW4Stages.
+  auto slice = [&](const int s, auto uc) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value;
+    // slice s is in LDS (this wave's share) once at most the loads of the
+    // kW4Stages - 2 slices issued after it are outstanding; the barrier
+    // makes every wave's share visible and frees the stage of slice s - 1
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kW4Stages - 2) * kLoads));
+    __builtin_amdgcn_s_barrier();
+    const int sn = min(s + kW4Stages - 1, slices - 1);
+    load_x(sn);
+    wr[(u + kW4Stages - 1) % kW4Stages] = load_w(sn);
 
-      const uint8_t *stg = lds + (s % kW4Stages) * kStage;
-      const WPiece &wp = wr[u];
-      // every activation operand and scale word of the slice first, so the
-      // products then issue back to back
-      u32x4_t b0[TM], b1[TM];
-      uint32_t xsc[TM];
+    const uint8_t *stg = lds + (s % kW4Stages) * kStage;
+    const WPiece &wp = wr[u];
+    // every activation operand and scale word of the slice first, so the
+    // products then issue back to back
+    u32x4_t b0[TM], b1[TM];
+    uint32_t xsc[TM];
 #pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        const uint8_t *row = stg + t * 32 * kRowBytes;
-        b0[t] = *(const u32x4_t *)(row + xo[0]);
-        b1[t] = *(const u32x4_t *)(row + xo[1]);
-        xsc[t] = *(const uint32_t *)(stg + xso + t * 32 * 4);
-      }
+    for (int t = 0; t < TM; ++t) {
+      const uint8_t *row = stg + t * 32 * kRowBytes;
+      b0[t] = *(const u32x4_t *)(row + xo[0]);
+      b1[t] = *(const u32x4_t *)(row + xo[1]);
+      xsc[t] = *(const uint32_t *)(stg + xso + t * 32 * 4);
+    }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const u32x4_t q = ks == 0 ? wp.q0[tn] : wp.q1[tn];
-          const v8i_t av = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-          const int sa = (int)((wp.s[tn] >> (ks == 0 ? sshift0 : sshift1)) & 0xFFu);
+      for (int tn = 0; tn < TN; ++tn) {
+        const u32x4_t q = ks == 0 ? wp.q0[tn] : wp.q1[tn];
+        const v8i_t av = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+        const int sa = (int)((wp.s[tn] >> (ks == 0 ? sshift0 : sshift1)) & 0xFFu);
 #pragma unroll
-          for (int t = 0; t < TM; ++t) {
-            const u32x4_t b = ks == 0 ? b0[t] : b1[t];
-            const v8i_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-            acc[tn][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                av, bv, acc[tn][t], 4, 4, 0, sa, 0,
-                (int)((xsc[t] >> (ks == 0 ? sshift0 : sshift1)) & 0xFFu));
-          }
+        for (int t = 0; t < TM; ++t) {
+          const u32x4_t b = ks == 0 ? b0[t] : b1[t];
+          const v8i_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+          acc[tn][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              av, bv, acc[tn][t], 4, 4, 0, sa, 0,
+              (int)((xsc[t] >> (ks == 0 ? sshift0 : sshift1)) & 0xFFu));
         }
       }
     }
+  };
+  // Whole groups of kW4Stages slices, then the rest: the loop body has no exit
+  // of its own, so that the compiler's wait analysis keeps track of the
+  // weight loads' age across the back edge (with an exit per slice it waited
+  // for the loads issued one slice earlier).
+  static_assert(kW4Stages == 3, "the slice loop is written out for three stages");
+  int s = 0;
+  for (; s + kW4Stages <= slices; s += kW4Stages) {
+    slice(s, std::integral_constant<int, 0>{});
+    slice(s + 1, std::integral_constant<int, 1>{});
+    slice(s + 2, std::integral_constant<int, 2>{});
   }
+  if (s < slices) slice(s, std::integral_constant<int, 0>{});
+  if (s + 1 < slices) slice(s + 1, std::integral_constant<int, 1>{});
+  // the re-reads issued past the last slice: no LDS write may be pending when
+  // the workgroup ends
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // epilogue: lane (lr, h) holds D[n = 8b + 4h + r][m = lr] of each tile as
   // value 4b + r: four consecutive weight rows per b
