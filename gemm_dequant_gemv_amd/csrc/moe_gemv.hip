@@ -113,9 +113,12 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
   const int items = (DOWN ? a.t : slots) * a.pairs;
   const int W = gridDim.x * WAVES;
   const int gw = blockIdx.x * WAVES + wave;
-  // the wave's jobs: gate/up items gw, gw + W, ...; down jobs [q0, q1) of the
-  // workgroup's items [ib0, ib1), item-major
-  int ib0 = 0, ib1 = 0, q0 = 0, myjobs;
+  // the wave's jobs: gate/up items gw, gw + W, ... for the rfull whole rounds
+  // of W items, then in the last, partial round item rfull W + w G + g
+  // (wave-major, so that every workgroup gets its share of that round: with
+  // gw there, half the workgroups took one item per wave more than the
+  // rest); down jobs [q0, q1) of the workgroup's items [ib0, ib1), item-major
+  int ib0 = 0, ib1 = 0, q0 = 0, myjobs, rfull = 0, ilast = 0;
   if constexpr (DOWN) {
     ib0 = (int)((long long)blockIdx.x * items / gridDim.x);
     ib1 = (int)((long long)(blockIdx.x + 1) * items / gridDim.x);
@@ -123,7 +126,9 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
     q0 = wave * nq / WAVES;
     myjobs = (wave + 1) * nq / WAVES - q0;
   } else {
-    myjobs = gw < items ? (items - 1 - gw) / W + 1 : 0;
+    rfull = items / W;
+    ilast = rfull * W + wave * (int)gridDim.x + (int)blockIdx.x;
+    myjobs = rfull + (ilast < items ? 1 : 0);
   }
   const int units = myjobs * S;
   // the wave's first and last job: (slot or token, pair or quad, term)
@@ -137,8 +142,8 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
       i1 = ib0 + qb / J;
       term_last = qb % J;
     } else {
-      i0 = gw;
-      i1 = myjobs > 0 ? gw + (myjobs - 1) * W : gw;
+      i0 = rfull > 0 ? gw : ilast;
+      i1 = myjobs > rfull ? ilast : (rfull > 0 ? gw + (rfull - 1) * W : ilast);
       term_first = term_last = 0;
     }
     s_first = i0 / a.pairs;
@@ -208,10 +213,15 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
   //    table afterwards, so that no later weight load waits for a scalar
   //    load of the routing ids.
   // Gate/up items advance by W: (slot, pair) moves by (W / pairs, W %
-  //    pairs), so the walk needs no division per unit; down items advance by
-  //    one (token, quad).
+  //    pairs), so the walk needs no division per unit, except into the last
+  //    round (job rfull); down items advance by one (token, quad).
   const int sW = DOWN ? 0 : W / a.pairs, pW = DOWN ? 1 : W - (W / a.pairs) * a.pairs;
-  auto advance = [&](int &s, int &p) {
+  auto advance = [&](int &s, int &p, int &jn) {
+    if (!DOWN && ++jn >= rfull) {
+      s = ilast / a.pairs;
+      p = ilast - s * a.pairs;
+      return;
+    }
     s += sW;
     p += pW;
     if (p >= a.pairs) { p -= a.pairs; ++s; }
@@ -271,17 +281,17 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
     }
   };
   RowData buf[U];
-  int ls = 0, lt = term_first, l_s = s_first, l_p = p_first;  // next unit to load
-  auto advance_unit = [&](int &st, int &term, int &s, int &p) {
+  int ls = 0, lt = term_first, l_s = s_first, l_p = p_first, l_j = 0;  // next unit to load
+  auto advance_unit = [&](int &st, int &term, int &s, int &p, int &jn) {
     if (++st == S) {
       st = 0;
-      if (++term == J) { term = 0; advance(s, p); }
+      if (++term == J) { term = 0; advance(s, p, jn); }
     }
   };
 #pragma unroll
   for (int j = 0; j < U; ++j) {
     load_unit(j, l_s, l_p, lt, ls, buf[j], false);
-    advance_unit(ls, lt, l_s, l_p);
+    advance_unit(ls, lt, l_s, l_p, l_j);
   }
   __builtin_amdgcn_sched_barrier(0);
   if (lane < slots) tab0 = table_entry(lane, gsc0);
@@ -355,7 +365,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
   // 2. the units: unit (item, term, step) of this wave
   const UnpackK K = unpack_consts();
   float acc[1] = {0.0f};
-  int cs = 0, ct = term_first, c_s = s_first, c_p = p_first;  // unit being computed
+  int cs = 0, ct = term_first, c_s = s_first, c_p = p_first, c_j = 0;  // unit being computed
   for (int t0 = 0; t0 < units; t0 += U) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
@@ -403,10 +413,10 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
           }
           acc[0] = 0.0f;
         }
-        advance_unit(cs, ct, c_s, c_p);
+        advance_unit(cs, ct, c_s, c_p, c_j);
       }
       load_unit(t0 + j + U, l_s, l_p, lt, ls, buf[j], true);
-      advance_unit(ls, lt, l_s, l_p);
+      advance_unit(ls, lt, l_s, l_p, l_j);
     }
   }
 
