@@ -426,6 +426,16 @@ __global__ __launch_bounds__(RowsShape<M>::kThreads) void gemv_rows_kernel(RowsA
     res = __builtin_amdgcn_raw_buffer_load_b16(rr, v_res, at(row0 * 2u, a.residual_bytes), 0);
   };
 
+  // Every wave of the workgroup has issued its activation loads before any
+  // issues a weight load: otherwise the activations of the waves dispatched
+  // last queue behind the first waves' weights (per-wave timestamps: the
+  // first waves had their x after 0.5 us, the median wave after ~2 us), and
+  // the staging barrier waits for the last of them.  An issue barrier only:
+  // nothing is waited for.  (Interleaved A/B on cold weights, two boxes: the
+  // FP4 5120- and 6144-row shapes 2-8% faster, the decode shapes from 1.5%
+  // slower to 7% faster, the mid band within 1.5%.)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   RowData buf[U];
   uint32_t res[U];
   int lj = j0, ls = st0;  // next unit to load: pair index, step
