@@ -105,7 +105,7 @@ void gemm_big_kernel(GemmArgs a) {
     tile = (int)blockIdx.x / a.splits;
     split = (int)blockIdx.x - tile * a.splits;
     m0 = (tile % tiles_m) * BM;
-    n0 = (tile / tiles_m) * kBN;
+    n0 = a.n_begin + (tile / tiles_m) * kBN;
     mrows = a.m - m0;
   } else {
     if (blockIdx.x >= *a.n_tiles) return;  // beyond this call's tiles (whole workgroup)
@@ -472,6 +472,10 @@ size_t split_counters_bytes(const qmm_weight &w, int m) {
   return (tiles * 4 + 255) / 256 * 256;
 }
 
+struct BigTail {
+  long tiles_m, tiles_n, tn_a;  // tiles of the first launch: tiles_m x tn_a
+};
+
 GemmArgs big_args(const qmm_weight &w) {
   GemmArgs a{};
   a.splits = 1;
@@ -485,6 +489,48 @@ GemmArgs big_args(const qmm_weight &w) {
   a.k = w.k;
   a.wrows = w.batch * w.n;
   return a;
+}
+
+// The big-tile configuration above 256 rows: 8 waves of 32 W rows x 256 X
+// rows (0) or x 192 rows (4), whichever leaves fewer idle compute units in
+// the last round of workgroups (one per compute unit).
+int big_cfg(const qmm_weight &w, int m) {
+  const long nt = (w.n + bn_of(8) - 1) / bn_of(8), cus = compute_units();
+  auto rounds = [&](int bm) { return ((m + bm - 1) / bm * nt + cus - 1) / cus; };
+  int cfg = 17 * rounds(192) < 20 * rounds(256) ? 4 : 0;
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_BIG_CFG")) cfg = atoi(e);
+#endif
+  return cfg;
+}
+
+// The last round of one-per-CU workgroups.  When it would hold at most three
+// fifths of the compute units, the big tiles cover whole rounds only (tn_a
+// of the tiles_n weight-row blocks) and a second launch takes the remaining
+// weight rows as 128 x 128 tiles, several to a compute unit.  M = 4096 at
+// 17408 rows: 1088 tiles of 256 x 256 are 4.25 rounds; 1024 of them, then
+// the last 1024 rows as 256 tiles of 128 x 128, measured 7% faster.  At
+// M = 8192 (8.5 rounds) the same split measured no faster, nor did the last
+// 128 big tiles with K split two or three ways (partials in a workspace):
+// 2-8% slower.  The matrix cores' clock, power-limited while every compute
+// unit runs, rises while the last half round runs alone.
+BigTail big_tail(const qmm_weight &w, int m, int cfg) {
+  BigTail t{};
+  const int bm = cfg == 0 ? 256 : 192;
+  t.tiles_m = (m + bm - 1) / bm;
+  t.tiles_n = (w.n + bn_of(8) - 1) / bn_of(8);
+  t.tn_a = t.tiles_n;
+  const long cus = compute_units();
+  const long full = t.tiles_m * t.tiles_n / cus;         // whole rounds
+  const long frac = t.tiles_m * t.tiles_n - full * cus;  // tiles of the last round
+  bool tail = full >= 4 && frac > 0 && 5 * frac <= 3 * cus;
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_BIG_TAIL")) tail = tail && atoi(e) != 0;
+#endif
+  if (!tail) return t;
+  const long tn_a = full * cus / t.tiles_m;  // weight-row blocks that fill whole rounds
+  if (tn_a > 0 && tn_a < t.tiles_n) t.tn_a = tn_a;
+  return t;
 }
 
 }  // namespace
@@ -535,17 +581,19 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
   // faster; M = 300 and 512 1.2x, M >= 3072 no gain.  Up to 256 rows of X: 4 waves of 32 x 128, whose 128-row W tiles
   // give a 128-row call 136 workgroups (1.9x faster than 128 x 128 tiles
   // staged through LDS at M = 128, 1.4x at M = 256).
-  int cfg = 1;
-  if (m > 256) {
-    const long nt = (w.n + bn_of(8) - 1) / bn_of(8), cus = compute_units();
-    auto rounds = [&](int bm) { return ((m + bm - 1) / bm * nt + cus - 1) / cus; };
-    cfg = 17 * rounds(192) < 20 * rounds(256) ? 4 : 0;
+  const int cfg = m > 256 ? big_cfg(w, m) : 1;
+  if (cfg == 0 || cfg == 4) {
+    const BigTail t = big_tail(w, m, cfg);
+    const dim3 ga((unsigned)(t.tiles_m * t.tn_a));
+    const hipError_t e = cfg == 0 ? launch_big_mode<8, 8, kDense>(w.format, a, ga, s)
+                                  : launch_big_mode<6, 8, kDense>(w.format, a, ga, s);
+    if (e != hipSuccess || t.tn_a == t.tiles_n) return e;
+    // the remaining weight rows as 128 x 128 tiles, several to a compute unit
+    a.n_begin = (int)(t.tn_a * bn_of(8));
+    const int rest = w.n - a.n_begin;
+    const dim3 gb((unsigned)(((m + 127) / 128) * ((rest + bn_of(4) - 1) / bn_of(4))));
+    return launch_big_mode<4, 4, kDense>(w.format, a, gb, s);
   }
-#ifdef QMM_TUNE
-  if (const char *e = getenv("QMM_BIG_CFG")) cfg = atoi(e);
-#endif
-  if (cfg == 0) return launch_big_mode<8, 8, kDense>(w.format, a, grid(256, bn_of(8)), s);
-  if (cfg == 4) return launch_big_mode<6, 8, kDense>(w.format, a, grid(192, bn_of(8)), s);
   // up to 256 rows: split K when the caller's workspace holds the partials
   const int sk = small_m_splits(w, m);
   if (sk > 1 && workspace && workspace_bytes >= gemm_big_workspace(w, m)) {

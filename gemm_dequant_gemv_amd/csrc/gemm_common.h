@@ -37,6 +37,7 @@ struct GemmArgs {
   // dense split-K: workgroup (tile, split) sums slices [split * sps, ...) and
   // leaves float32 partials; the last of a tile's splits adds them in order
   int splits, sps;
+  int n_begin;         // dense: first weight row (output column) of the launch's tiles
   float *partials;     // [splits][m][n]
   uint32_t *counters;  // [tiles], cleared ahead of each split launch
   int wrows;                     // rows of the weight planes (all experts)
