@@ -510,10 +510,11 @@ int big_cfg(const qmm_weight &w, int m) {
 // weight rows as 128 x 128 tiles, several to a compute unit.  M = 4096 at
 // 17408 rows: 1088 tiles of 256 x 256 are 4.25 rounds; 1024 of them, then
 // the last 1024 rows as 256 tiles of 128 x 128, measured 7% faster.  At
-// M = 8192 (8.5 rounds) the same split measured no faster, nor did the last
-// 128 big tiles with K split two or three ways (partials in a workspace):
-// 2-8% slower.  The matrix cores' clock, power-limited while every compute
-// unit runs, rises while the last half round runs alone.
+// M = 8192 (8.5 rounds: 2048 big tiles, then 512 small ones) it measured
+// within 1%, and the last 128 big tiles with K split two or three ways
+// (partials in a workspace) 2-8% slower: the matrix cores' clock,
+// power-limited while every compute unit runs, rises while the last half
+// round runs alone.
 BigTail big_tail(const qmm_weight &w, int m, int cfg) {
   BigTail t{};
   const int bm = cfg == 0 ? 256 : 192;
