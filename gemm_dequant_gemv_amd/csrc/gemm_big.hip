@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "gemm_common.h"
+#include "swiglu_device.h"
 
 namespace qmm {
 namespace {
@@ -367,8 +368,8 @@ void gemm_big_kernel(GemmArgs a) {
         // in float32: h = silu(g) * u, silu(g) = g / (1 + e^-g)
         const int col = n0 / 2 + nl / 2;  // even, and I is even
         if (col < a.inter) {
-          const float h0 = v[0] / (1.0f + expf(-v[0])) * v[1];
-          const float h1 = v[2] / (1.0f + expf(-v[2])) * v[3];
+          const float h0 = silu_f32(v[0]) * v[1];
+          const float h1 = silu_f32(v[2]) * v[3];
           *(uint32_t *)(a.h + (size_t)m * a.inter + col) = pack_bf16(h0, h1);
         }
         continue;

@@ -34,6 +34,7 @@
 
 #include "gemv_step.h"
 #include "router_device.h"
+#include "swiglu_device.h"
 
 namespace qmm {
 namespace {
@@ -398,7 +399,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemv_kernel(MoeGemvArgs a) {
             half_sums(acc[0], s0, s1);
             if (valid && lane == 0) {
               const float gv = s0 * g, uv = s1 * g;
-              const float hv = gv / (1.0f + expf(-gv)) * uv;
+              const float hv = silu_f32(gv) * uv;
               a.h[(size_t)s * a.pairs + p] = (uint16_t)float_to_bf16(hv);
             }
           } else {
