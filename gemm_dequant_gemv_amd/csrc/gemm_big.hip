@@ -110,16 +110,20 @@ void gemm_big_kernel(GemmArgs a) {
     mrows = a.m - m0;
   } else {
     // workgroup -> (routing tile, column block).  Workgroups go to the 8
-    // XCDs in turn (workgroup w to XCD w % 8), so workgroup 8 (q ncb + c) +
-    // x takes column block c of tile 8 q + x: a tile's column blocks run
-    // back to back on one XCD and share its activation slices in that
-    // XCD's L2.  (With tiles fastest in a 2-D grid they ran on different
-    // XCDs about two rounds apart, and the tile was gathered from memory
-    // once per column block: 1.10 -> 1.02 ms per layer at T = 8192,
-    // 2-4% at T = 100-2048, bit-identical.)  Any other XCD count only
-    // changes which workgroups share an L2.
+    // XCDs in turn (workgroup w to XCD w % 8); the consecutive workgroups
+    // of XCD x take the tile pair 2 (8 q + x), 2 (8 q + x) + 1 column block
+    // by column block, so the pair's gathered activation slices (and the
+    // weight rows of an expert with two tiles) are shared in that XCD's L2.
+    // Measured (interleaved A/B, bit-identical): one tile per XCD run
+    // against tiles fastest in a 2-D grid (a tile's column blocks on
+    // different XCDs about two rounds apart, each gathering the tile again)
+    // T = 8192 1.097 -> 1.019 ms per layer, T = 100-2048 2-4% faster; pairs
+    // against single tiles T = 2048 7%, T = 512 4%, T = 8192 1% faster;
+    // groups of 4 or 8 tiles 1-7% slower than pairs.  Any other XCD count
+    // only changes which workgroups share an L2.
     const int ncb = (a.n + kBN - 1) / kBN, j = (int)blockIdx.x >> 3;
-    const int tl = (j / ncb) * 8 + ((int)blockIdx.x & 7), cb = j % ncb;
+    const int q = j / (2 * ncb), r = j - q * 2 * ncb;
+    const int tl = (q * 8 + ((int)blockIdx.x & 7)) * 2 + (r & 1), cb = r >> 1;
     if (tl >= *a.n_tiles) return;  // beyond this call's tiles (whole workgroup)
     const uint32_t *t = a.tiles + 3 * tl;
     expert = (int)t[0];
@@ -629,10 +633,10 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
 }
 
 // the grouped launches' 1-D grid: routing tiles (rounded up to a multiple
-// of 8) x column blocks of bn weight rows
+// of 16: 8 XCDs x tile pairs) x column blocks of bn weight rows
 static dim3 moe_grid(int max_tiles, int n, int bn) {
   const unsigned ncb = (unsigned)((n + bn - 1) / bn);
-  return dim3((unsigned)((max_tiles + 7) / 8 * 8) * ncb);
+  return dim3((unsigned)((max_tiles + 15) / 16 * 16) * ncb);
 }
 
 hipError_t launch_moe_big_gate_up(const qmm_weight &gu, const void *x, const MoeTables &t,
