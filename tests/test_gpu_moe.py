@@ -191,6 +191,25 @@ def test_moe_parity_small(T, fmts):
     check_y(gu, dn, x, ids, w, c["E"], c["S"], yh, hd, tokens)
 
 
+@pytest.mark.parametrize("T,rows", [(17, 32), (200, 64), (300, 128), (600, 192), (800, 256)])
+def test_moe_every_tile_height(T, rows):
+    """The grouped form at each routing tile height (32 to 256 rows; the
+    height follows the mean rows per routed expert), so that every tile
+    configuration of the gate/up and down GEMMs, and their mapping of
+    workgroups to (tile, column block), meets the oracle stage by stage."""
+    q = _q()
+    c = SMALL
+    gu, dn, x, ids, w = make_case(F.NVFP4, F.AFFINE4_G64, c["E"], c["S"], c["H"], c["I"], T,
+                                  c["topk"], f"moeth{T}")
+    yh, r = run_gpu(q, gu, dn, x, ids, w, c["E"], c["S"])
+    assert not r["slot_rows"] and r["tile_rows"] == rows
+    check_grouping(r, ids, c["E"], c["S"])
+    tokens = list(range(0, T, 5)) + [T - 1]
+    hd = gpu_h_dict(r, T, c["topk"], c["S"], tokens)
+    check_h(gu, x, ids, c["E"], c["S"], hd, tokens)
+    check_y(gu, dn, x, ids, w, c["E"], c["S"], yh, hd, tokens)
+
+
 def test_moe_no_shared_weighted_shared_and_bf16_out():
     q = _q()
     E, H, I, T, topk = 8, 256, 128, 50, 2
