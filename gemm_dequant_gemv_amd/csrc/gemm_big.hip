@@ -507,30 +507,21 @@ GemmArgs big_args(const qmm_weight &w) {
   return a;
 }
 
-// The big-tile configuration above 256 rows: 8 waves of 32 W rows x 256 X
-// rows (0) or x 192 rows (4), whichever leaves fewer idle compute units in
-// the last round of workgroups (one per compute unit).
-int big_cfg(const qmm_weight &w, int m) {
-  const long nt = (w.n + bn_of(8) - 1) / bn_of(8), cus = compute_units();
-  auto rounds = [&](int bm) { return ((m + bm - 1) / bm * nt + cus - 1) / cus; };
-  int cfg = 17 * rounds(192) < 20 * rounds(256) ? 4 : 0;
-#ifdef QMM_TUNE
-  if (const char *e = getenv("QMM_BIG_CFG")) cfg = atoi(e);
-#endif
-  return cfg;
-}
+// The last round of one-per-CU workgroups.  When at least one whole round
+// is followed by a last round that holds at most a quarter of the compute
+// units, the big tiles cover the whole rounds only (tn_a of the tiles_n
+// weight-row blocks) and a second launch takes the remaining weight rows as
+// 128 x 128 tiles, several to a compute unit.  Measured on 17408 x 5120
+// (interleaved A/B, bit-identical: each output's sum over K runs in the same
+// order in either tile): M = 4096 (1024 + 256 small tiles) 7-8% faster,
+// M = 3072 9%, M = 1024 7-9% (against 192-row tiles), M = 2048 and 8192
+// within 1%; a last round of 3/5 of the compute units (M = 1536) 4% slower,
+// and K split two or three ways over the last 128 big tiles of M = 8192
+// (partials in a workspace) 2-8% slower: while only part of the chip runs,
+// the matrix cores' power-limited clock rises, so a short last round costs
+// less than its share of tiles.
+bool big_tail_fits(long full, long frac, long cus) { return full >= 1 && frac > 0 && 4 * frac <= cus; }
 
-// The last round of one-per-CU workgroups.  When it would hold at most three
-// fifths of the compute units, the big tiles cover whole rounds only (tn_a
-// of the tiles_n weight-row blocks) and a second launch takes the remaining
-// weight rows as 128 x 128 tiles, several to a compute unit.  M = 4096 at
-// 17408 rows: 1088 tiles of 256 x 256 are 4.25 rounds; 1024 of them, then
-// the last 1024 rows as 256 tiles of 128 x 128, measured 7% faster.  At
-// M = 8192 (8.5 rounds: 2048 big tiles, then 512 small ones) it measured
-// within 1%, and the last 128 big tiles with K split two or three ways
-// (partials in a workspace) 2-8% slower: the matrix cores' clock,
-// power-limited while every compute unit runs, rises while the last half
-// round runs alone.
 BigTail big_tail(const qmm_weight &w, int m, int cfg) {
   BigTail t{};
   const int bm = cfg == 0 ? 256 : 192;
@@ -540,7 +531,7 @@ BigTail big_tail(const qmm_weight &w, int m, int cfg) {
   const long cus = compute_units();
   const long full = t.tiles_m * t.tiles_n / cus;         // whole rounds
   const long frac = t.tiles_m * t.tiles_n - full * cus;  // tiles of the last round
-  bool tail = full >= 4 && frac > 0 && 5 * frac <= 3 * cus;
+  bool tail = big_tail_fits(full, frac, cus);
 #ifdef QMM_TUNE
   if (const char *e = getenv("QMM_BIG_TAIL")) tail = tail && atoi(e) != 0;
 #endif
@@ -548,6 +539,25 @@ BigTail big_tail(const qmm_weight &w, int m, int cfg) {
   const long tn_a = full * cus / t.tiles_m;  // weight-row blocks that fill whole rounds
   if (tn_a > 0 && tn_a < t.tiles_n) t.tn_a = tn_a;
   return t;
+}
+
+// The big-tile configuration above 256 rows: 8 waves of 32 W rows x 256 X
+// rows (0) or x 192 rows (4), whichever takes fewer rounds of workgroups (one
+// per compute unit; a 192-row round takes about 0.85 of a 256-row one, and
+// a 256-row last round short enough for the small-tile tail counts as twice
+// its share of a round).
+int big_cfg(const qmm_weight &w, int m) {
+  const long nt = (w.n + bn_of(8) - 1) / bn_of(8), cus = compute_units();
+  const long t0 = (m + 255) / 256 * nt, t4 = (m + 191) / 192 * nt;
+  const long full0 = t0 / cus, frac0 = t0 - full0 * cus;
+  const double r0 = big_tail_fits(full0, frac0, cus) ? full0 + 2.0 * frac0 / cus
+                                                      : (double)((t0 + cus - 1) / cus);
+  const double r4 = 0.85 * (double)((t4 + cus - 1) / cus);
+  int cfg = r4 < r0 ? 4 : 0;
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_BIG_CFG")) cfg = atoi(e);
+#endif
+  return cfg;
 }
 
 }  // namespace
@@ -591,13 +601,13 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
   };
   // 8 waves of 32 W rows x 256 X rows: each decoded weight feeds twice the
   // MFMAs of the 4-wave 64 x 128 form (measured 1.3x faster from M = 512 on);
-  // or 8 waves of 32 x 192 where that leaves fewer idle compute units in the
-  // last round of workgroups (one workgroup per compute unit; a 192-row round
-  // takes about 0.85 of a 256-row one): M = 2048 at 17408 rows is 544
-  // workgroups of 256 (2.1 rounds) or 748 of 192 (2.9 rounds), measured 1.14x
-  // faster; M = 300 and 512 1.2x, M >= 3072 no gain.  Up to 256 rows of X: 4 waves of 32 x 128, whose 128-row W tiles
-  // give a 128-row call 136 workgroups (1.9x faster than 128 x 128 tiles
-  // staged through LDS at M = 128, 1.4x at M = 256).
+  // or 8 waves of 32 x 192 where that takes fewer rounds of workgroups
+  // (big_cfg; 192-row tiles measured 1.2x faster at M = 300 and 512 on 17408
+  // rows, and 1.14x at M = 2048 before the tail launch below existed, which
+  // now gives 256-row tiles the same time there).  Up to 256 rows of X: 4
+  // waves of 32 x 128, whose 128-row W tiles give a 128-row call 136
+  // workgroups (1.9x faster than 128 x 128 tiles staged through LDS at
+  // M = 128, 1.4x at M = 256).
   const int cfg = m > 256 ? big_cfg(w, m) : 1;
   if (cfg == 0 || cfg == 4) {
     const BigTail t = big_tail(w, m, cfg);

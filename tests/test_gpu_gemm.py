@@ -119,9 +119,9 @@ def test_gemm_rejects():
 
 
 # The prefill workload's own sizes, in the tile configurations the library
-# picks for them (256-row activation tiles at M = 8192, 192-row at 2048, at
-# 4096 256-row tiles for whole rounds of workgroups and 128 x 128 tiles for
-# the last 1024 weight rows, and
+# picks for them (256-row activation tiles at M = 8192; at 1024, 2048, 3072
+# and 4096 256-row tiles for whole rounds of workgroups and 128 x 128 tiles
+# for the last 1024 weight rows; 192-row at 512, and
 # the mid band's tiles: 32 rows with 4 K splits at M = 8, 64 rows at 48, 128
 # rows at 96): the GPU computes
 # the whole product; the oracle checks sampled activation rows (every output
@@ -142,7 +142,7 @@ def full_weights():
 
 @pytest.mark.parametrize("fmt,m", [(F.AFFINE4_G64, 128), (F.AFFINE4_G64, 512),
                                    (F.AFFINE4_G64, 2048), (F.AFFINE4_G64, 8192),
-                                   (F.AFFINE4_G64, 4096),
+                                   (F.AFFINE4_G64, 4096), (F.AFFINE4_G64, 3072), (F.NVFP4, 1024),
                                    (F.NVFP4, 128), (F.NVFP4, 512), (F.NVFP4, 2048),
                                    (F.NVFP4, 4096), (F.NVFP4, 8192), (F.AFFINE4_G64, 8), (F.NVFP4, 16),
                                    (F.Q6_K, 5), (F.NVFP4, 48), (F.Q6_K, 96)])
