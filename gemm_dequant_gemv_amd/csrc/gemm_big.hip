@@ -446,19 +446,6 @@ hipError_t launch_big_mode(int format, const GemmArgs &a, dim3 grid, hipStream_t
 // workgroups' rows of W for a configuration of `waves` waves
 constexpr int bn_of(int waves) { return 32 * waves; }
 
-// compute units of the current device (cached per device)
-long compute_units() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  int v = cached[dev & 63].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-    return 256;
-  cached[dev & 63].store(v, std::memory_order_relaxed);
-  return v;
-}
-
 // Small calls (m <= 256 rows): the activation tile height and the number of
 // K splits, from a sweep on 17408 x 5120 (MI355X, kernel trace, medians of 24
 // cold-weight launches; unsplit 128-row tiles take ~55 us for any m, a
@@ -561,6 +548,18 @@ int big_cfg(const qmm_weight &w, int m) {
 }
 
 }  // namespace
+
+long compute_units() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  int v = cached[dev & 63].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    return 256;
+  cached[dev & 63].store(v, std::memory_order_relaxed);
+  return v;
+}
 
 size_t gemm_big_workspace(const qmm_weight &w, int m) {
   const int sk = small_m_splits(w, m);

@@ -95,6 +95,8 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
                            void *y, void *workspace, size_t workspace_bytes, hipStream_t s);
 // workspace that lets a dense call of m rows split K (0: it never splits)
 size_t gemm_big_workspace(const qmm_weight &w, int m);
+// compute units of the current device (cached per device; 256 if the query fails)
+long compute_units();
 // the 256-row-tile kernels (gemm_big.hip) address X (x_rows rows) and the
 // weight planes with 32-bit offsets
 bool gemm_big_fits(const qmm_weight &w, size_t x_rows);

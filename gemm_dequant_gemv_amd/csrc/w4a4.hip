@@ -26,6 +26,8 @@
 //   The products of E2M1 values and powers of two are exact; only the float32
 //   sums round, in a fixed order (slices in order, the two lane halves inside
 //   the matrix core).
+#include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "qmm_device.h"
@@ -99,6 +101,7 @@ struct W4A4Args {
   const uint16_t *residual;         // bf16 [m][n] or null
   uint16_t *y;                      // bf16 [m][n]
   int m, n, k;
+  int n_begin;                      // first weight row of the launch's tiles
 };
 
 // Physical 16-byte chunk of logical chunk c of activation row r in a slice's
@@ -130,7 +133,7 @@ void gemm_w4a4_kernel(W4A4Args a) {
   const int lr = lane & 31, h = lane >> 5;
   const int tiles_m = (a.m + BM - 1) / BM;
   const int m0 = ((int)blockIdx.x % tiles_m) * BM;
-  const int n0 = ((int)blockIdx.x / tiles_m) * kW4BN;
+  const int n0 = a.n_begin + ((int)blockIdx.x / tiles_m) * kW4BN;
   const int mrows = a.m - m0;
   const int slices = a.k / kSliceK;
   const uint32_t kb = (uint32_t)a.k / 2, kq = (uint32_t)a.k / 32;
@@ -371,8 +374,29 @@ hipError_t launch_gemm_w4a4(const qmm_weight &w, const void *x, int m, const voi
   constexpr int TN = 1, TM = 8 / TN;
   constexpr int BM = 256;
   constexpr size_t lds = (size_t)kW4Stages * (BM * kRowBytes + BM * 4);
-  const unsigned grid = (unsigned)(((m + BM - 1) / BM) * ((w.n + kW4BN - 1) / kW4BN));
-  hipLaunchKernelGGL((gemm_w4a4_kernel<TN, TM>), dim3(grid), dim3(64 * kW4Waves), lds, s, a);
+  a.n_begin = 0;
+  // The last round of one-per-CU workgroups: after at least one whole round,
+  // a last round of at most a quarter of the compute units runs as a second
+  // launch over the remaining weight rows with 128 activation rows per tile
+  // (twice as many workgroups, each half the work)
+  const long tiles_m = (m + BM - 1) / BM, tiles_n = (w.n + kW4BN - 1) / kW4BN;
+  const long cus = compute_units(), full = tiles_m * tiles_n / cus;
+  const long frac = tiles_m * tiles_n - full * cus;
+  long tn_a = tiles_n;
+  if (full >= 1 && frac > 0 && 4 * frac <= cus) tn_a = std::min(tiles_n, std::max(1L, full * cus / tiles_m));
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_W4_TAIL"); e && !atoi(e)) tn_a = tiles_n;
+#endif
+  hipLaunchKernelGGL((gemm_w4a4_kernel<TN, TM>), dim3((unsigned)(tiles_m * tn_a)), dim3(64 * kW4Waves),
+                     lds, s, a);
+  if (tn_a == tiles_n) return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int BMT = 128;
+  constexpr size_t lds_t = (size_t)kW4Stages * (BMT * kRowBytes + BMT * 4);
+  a.n_begin = (int)(tn_a * kW4BN);
+  const unsigned grid_t = (unsigned)(((m + BMT - 1) / BMT) * (tiles_n - tn_a));
+  hipLaunchKernelGGL((gemm_w4a4_kernel<1, 4>), dim3(grid_t), dim3(64 * kW4Waves), lds_t, s, a);
   return hipGetLastError();
 }
 

@@ -145,9 +145,11 @@ def test_gemm_w4a4_rejects():
 
 
 # The prefill workload's weight, 17408 x 5120 MXFP4, at the sizes the
-# benchmark times: the GPU computes every output, the oracle checks sampled
-# activation rows (every output column of each), tile edges included.
-@pytest.mark.parametrize("m", [128, 2048, 8192])
+# benchmark times (and M = 1024, whose last round of 256 x 256 tiles runs as
+# 128-row tiles, as at 2048): the GPU computes every output, the oracle
+# checks sampled activation rows (every output column of each), tile edges
+# included.
+@pytest.mark.parametrize("m", [128, 1024, 2048, 8192])
 def test_gemm_w4a4_full_size_sampled(m):
     q = _q()
     n, k = 17408, 5120
