@@ -511,7 +511,7 @@ bool big_tail_fits(long full, long frac, long cus) { return full >= 1 && frac > 
 
 BigTail big_tail(const qmm_weight &w, int m, int cfg) {
   BigTail t{};
-  const int bm = cfg == 0 ? 256 : 192;
+  const int bm = cfg == 0 ? 256 : cfg == 10 ? 320 : 192;
   t.tiles_m = (m + bm - 1) / bm;
   t.tiles_n = (w.n + bn_of(8) - 1) / bn_of(8);
   t.tn_a = t.tiles_n;
@@ -529,18 +529,29 @@ BigTail big_tail(const qmm_weight &w, int m, int cfg) {
 }
 
 // The big-tile configuration above 256 rows: 8 waves of 32 W rows x 256 X
-// rows (0) or x 192 rows (4), whichever takes fewer rounds of workgroups (one
-// per compute unit; a 192-row round takes about 0.85 of a 256-row one, and
-// a 256-row last round short enough for the small-tile tail counts as twice
-// its share of a round).
+// rows (0), x 192 rows (4) or x 320 rows (10), whichever takes the least
+// time counted in rounds of 256-row workgroups (one per compute unit): a
+// 192-row round takes about 0.85 of a 256-row one, a 320-row round 1.25, and
+// a small-tile tail about 0.33 per round of 128 x 128 tiles (each of them
+// runs the whole K loop, so a short tail still takes that long: 192-row
+// tiles plus a tail at M = 768 measured 20% slower than one round of
+// 256-row tiles).  (320-row tiles, 244 registers a lane, measured as their
+// round count predicts: 2-3% faster at M = 8192 on 17408 rows, 1768 tiles
+// in 6.9 rounds against 2176 in 8.5; equal at 16384, 6% slower at 4096.)
 int big_cfg(const qmm_weight &w, int m) {
   const long nt = (w.n + bn_of(8) - 1) / bn_of(8), cus = compute_units();
-  const long t0 = (m + 255) / 256 * nt, t4 = (m + 191) / 192 * nt;
-  const long full0 = t0 / cus, frac0 = t0 - full0 * cus;
-  const double r0 = big_tail_fits(full0, frac0, cus) ? full0 + 2.0 * frac0 / cus
-                                                      : (double)((t0 + cus - 1) / cus);
-  const double r4 = 0.85 * (double)((t4 + cus - 1) / cus);
+  auto cost = [&](int bm, double per_round) {
+    const long tm = (m + bm - 1) / bm, tl = tm * nt, full = tl / cus, frac = tl - full * cus;
+    if (big_tail_fits(full, frac, cus)) {
+      const long tn_a = std::min(nt, std::max(1L, full * cus / tm));
+      const long small = (m + 127) / 128 * ((w.n - tn_a * bn_of(8) + bn_of(4) - 1) / bn_of(4));
+      return per_round * (double)((tm * tn_a + cus - 1) / cus) + 0.33 * (double)((small + cus - 1) / cus);
+    }
+    return per_round * (double)((tl + cus - 1) / cus);
+  };
+  const double r0 = cost(256, 1.0), r4 = cost(192, 0.85), r10 = cost(320, 1.25);
   int cfg = r4 < r0 ? 4 : 0;
+  if (r10 < std::min(r0, r4)) cfg = 10;
 #ifdef QMM_TUNE
   if (const char *e = getenv("QMM_BIG_CFG")) cfg = atoi(e);
 #endif
@@ -608,11 +619,12 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
   // workgroups (1.9x faster than 128 x 128 tiles staged through LDS at
   // M = 128, 1.4x at M = 256).
   const int cfg = m > 256 ? big_cfg(w, m) : 1;
-  if (cfg == 0 || cfg == 4) {
+  if (cfg == 0 || cfg == 4 || cfg == 10) {
     const BigTail t = big_tail(w, m, cfg);
     const dim3 ga((unsigned)(t.tiles_m * t.tn_a));
-    const hipError_t e = cfg == 0 ? launch_big_mode<8, 8, kDense>(w.format, a, ga, s)
-                                  : launch_big_mode<6, 8, kDense>(w.format, a, ga, s);
+    const hipError_t e = cfg == 0  ? launch_big_mode<8, 8, kDense>(w.format, a, ga, s)
+                         : cfg == 4 ? launch_big_mode<6, 8, kDense>(w.format, a, ga, s)
+                                    : launch_big_mode<10, 8, kDense>(w.format, a, ga, s);
     if (e != hipSuccess || t.tn_a == t.tiles_n) return e;
     // the remaining weight rows as 128 x 128 tiles, several to a compute unit
     a.n_begin = (int)(t.tn_a * bn_of(8));

@@ -119,7 +119,7 @@ def test_gemm_rejects():
 
 
 # The prefill workload's own sizes, in the tile configurations the library
-# picks for them (256-row activation tiles at M = 8192; at 1024, 2048, 3072
+# picks for them (320-row activation tiles at M = 8192; at 1024, 2048, 3072
 # and 4096 256-row tiles for whole rounds of workgroups and 128 x 128 tiles
 # for the last 1024 weight rows; 192-row at 512, and
 # the mid band's tiles: 32 rows with 4 K splits at M = 8, 64 rows at 48, 128
@@ -152,7 +152,8 @@ def test_gemm_prefill_full_size_sampled(full_weights, fmt, m):
     x = quant.synthetic_bf16(m, FULL_K, name=f"gfullx{m}")
     w = q.Weight.from_host(p)
     y = _host_f64(q.gemm(w, _dev_bf16(x)))
-    edges = [0, 1, 31, 32, 63, 64, 127, 128, 191, 192, 255, 256, m // 2, m - 2, m - 1]
+    edges = [0, 1, 31, 32, 63, 64, 127, 128, 191, 192, 255, 256, 319, 320, 639, 640, m // 2, m - 2,
+             m - 1]
     rows = np.unique(np.concatenate([edges, rng.randint_bytes(71, f"gfr{m}", 21, 0, 256).astype(np.int64) * (m // 256)]))
     rows = rows[rows < m]
     yref, mag = oracle.gemm(p, x[rows])
