@@ -383,7 +383,10 @@ hipError_t launch_gemm_w4a4(const qmm_weight &w, const void *x, int m, const voi
   const long cus = compute_units(), full = tiles_m * tiles_n / cus;
   const long frac = tiles_m * tiles_n - full * cus;
   long tn_a = tiles_n;
-  if (full >= 1 && frac > 0 && 4 * frac <= cus) tn_a = std::min(tiles_n, std::max(1L, full * cus / tiles_m));
+  if (full >= 1 && frac > 0 && 4 * frac <= cus) {
+    const long ta = full * cus / tiles_m;  // weight-row blocks that fill whole rounds
+    if (ta >= 1 && ta < tiles_n) tn_a = ta;
+  }
 #ifdef QMM_TUNE
   if (const char *e = getenv("QMM_W4_TAIL"); e && !atoi(e)) tn_a = tiles_n;
 #endif
