@@ -738,16 +738,17 @@ bool plan_gemv_rows(int format, int n, int k, int m, GemvPlan &p) {
   //     14-19% faster than round-robin without the wave-major last round
   //     (which gave an eighth of the workgroups half as many pairs again);
   //   * 2 units in flight on the decode shapes (3 and 4 were 2-9% slower on
-  //     17408 x 5120), 4 on long streams of at least 8 rounds (the 248320 x
-  //     5120 projection 3-5% faster than with 2), 3 for 1 row balanced
-  //     (5120 x 17408) and for 5 to 8 rows.
+  //     17408 x 5120; on 5120 x 17408 at 1 row 3 was faster until the x loads
+  //     were issued ahead of every weight load, and is now 3% slower), 4 on
+  //     long streams of at least 8 rounds (the 248320 x 5120 projection 3-5%
+  //     faster than with 2), 3 for 5 to 8 rows.
   const size_t waves = (size_t)cus * (m <= 4 ? RowsShape<4>::kWaves : RowsShape<8>::kWaves);
   const size_t npairs = ((size_t)n + 1) / 2;
   p.balanced = npairs < waves && p.steps >= 8 ? kSplitBal : kSplitRR;
   if (m >= 5)
     p.depth = 3;
   else if (p.balanced == kSplitBal)
-    p.depth = m == 1 ? 3 : 2;
+    p.depth = 2;
   else
     p.depth = npairs >= 8 * waves ? 4 : 2;
 #ifdef QMM_TUNE
