@@ -14,19 +14,22 @@
 //     sign in bit 3, a value that rounds to zero coded 0.
 //   gemm_w4a4_kernel: the product of the MXFP4 weights and the quantized
 //     activations, float32 sums, bf16 y (+ residual).  A workgroup of 8 waves
-//     owns 256 weight rows x 32 TM activation rows; per 128-wide K slice the
+//     owns 256 weight rows x 32 TM activation rows; per 256-wide K slice the
 //     activation codes and scales go from memory straight into LDS (three
 //     slices in flight) and each wave loads its own 32 weight rows' codes and
 //     scales into registers (three slices ahead, through the caches: the 32
 //     activation tiles of a weight tile read it again, and the non-temporal
-//     loads of the streaming GEMV measured 28-39% slower here).  The codes are the MFMA
-//     operands as they are: there is no decode step.  Inside a slice, lane
-//     half h multiplies K blocks 2h and 2h + 1 (k-steps 0 and 1) for both
-//     operands, so a lane reads 32 contiguous code bytes of its weight row.
+//     loads of the streaming GEMV measured 28-39% slower here).  The codes are
+//     the MFMA operands as they are: there is no decode step.  Inside a slice,
+//     lane half h multiplies K blocks 4h .. 4h + 3 (k-steps 0 .. 3) for both
+//     operands, so a lane reads 64 contiguous code bytes of its weight row.
+//     (128-wide slices, one barrier per two k-steps instead of four, were
+//     7-12% slower.)
 //   The products of E2M1 values and powers of two are exact; only the float32
-//   sums round, in a fixed order (slices in order, the two lane halves inside
-//   the matrix core).
+//   sums round, in a fixed order (slices in order, k-steps in order, the two
+//   lane halves inside the matrix core).
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <type_traits>
 
@@ -39,9 +42,7 @@ namespace {
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_w __attribute__((ext_vector_type(16)));
 
-constexpr int kSliceK = 128;         // K values per slice: two k-steps of 64
-constexpr int kRowBytes = 64;        // code bytes of one row per slice
-constexpr int kW4Stages = 3;         // slices in flight (4 and 6 measured 2-6% slower)
+constexpr int kW4Stages = 3;         // slices in flight (128-wide: 4 and 6 measured 2-6% slower)
 constexpr int kW4Waves = 8;
 constexpr int kW4BN = 32 * kW4Waves; // weight rows per workgroup
 
@@ -104,28 +105,44 @@ struct W4A4Args {
   int n_begin;                      // first weight row of the launch's tiles
 };
 
-// Physical 16-byte chunk of logical chunk c of activation row r in a slice's
-// LDS image (64 bytes per row): the 16 rows one ds_read_b128 lane group reads
-// at one logical chunk land on 16 distinct bank groups.
-__device__ __forceinline__ int xchunk(int r, int c) { return c ^ ((r >> 2) & 3); }
+// Slices of KS k-steps of 64 values (KS = 4 where K is a multiple of 256,
+// else 2): per row KS * 32 code bytes in 2 KS chunks of 16, and KS / 2 words
+// of four E8M0 scales.
+template <int KS>
+struct W4Slice {
+  static constexpr int kK = 64 * KS;          // K values per slice
+  static constexpr int kRowBytes = 32 * KS;   // code bytes of one row per slice
+  static constexpr int kChunks = 2 * KS;      // 16-byte chunks of one row
+  static constexpr int kScaleWords = KS / 2;  // E8M0 words of one row per slice
+  // Physical 16-byte chunk of logical chunk c of activation row r in a
+  // slice's LDS image: the 16 rows one ds_read_b128 lane group reads at one
+  // logical chunk land on 16 distinct bank groups (16 / kChunks rows share
+  // a 256-byte bank row; the row's next bits pick the XOR).
+  static __device__ __forceinline__ int xchunk(int r, int c) {
+    return c ^ ((r / (16 / kChunks)) & (kChunks - 1));
+  }
+};
 
 // The workgroup's 8 waves as kWN x kWM: wave w owns weight rows
 // 32 TN (w % kWN) .. (TN groups of 32) and activation rows 32 TM (w / kWN) ..
 // (TM groups of 32) of the 256 x 256 tile, so every activation operand read
 // from LDS feeds TN products and every weight operand TM.
-template <int TN, int TM>
+template <int TN, int TM, int KS>
 __global__ __launch_bounds__(64 * kW4Waves) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_w4a4_kernel(W4A4Args a) {
+  using SL = W4Slice<KS>;
+  constexpr int kSliceK = SL::kK, kRowBytes = SL::kRowBytes, kKSteps = KS;
+  constexpr int kScaleWords = SL::kScaleWords;
   constexpr int kWN = kW4BN / (32 * TN);       // wave columns over the weight rows
   constexpr int kWM = kW4Waves / kWN;          // wave rows over the activation rows
   constexpr int BM = 32 * TM * kWM;
   static_assert(kWN * 32 * TN == kW4BN && kWN * kWM == kW4Waves, "wave grid");
   constexpr int kCodeStage = BM * kRowBytes;  // activation codes of one slice
-  constexpr int kStage = kCodeStage + BM * 4; // + their scales (4 per row)
-  constexpr int XI = BM / 16 / kW4Waves;      // code-load instructions per wave and slice
-  constexpr int SI = BM / 64;                 // scale-load instructions per slice
-  static_assert(XI >= 1 && XI * 16 * kW4Waves == BM && SI >= 1 && SI <= kW4Waves, "tiles");
-  constexpr int kLoads = XI + 1 + 3 * TN;     // per wave and slice: X codes, X scales, W
+  constexpr int kStage = kCodeStage + BM * 4 * kScaleWords; // + their scales
+  constexpr int XI = BM * kRowBytes / 1024 / kW4Waves;  // code-load instructions per wave and slice
+  constexpr int SI = BM * kScaleWords / 64;             // scale-load instructions per slice
+  static_assert(XI >= 1 && XI * 1024 * kW4Waves == BM * kRowBytes && SI >= 1 && SI <= kW4Waves, "tiles");
+  constexpr int kLoads = XI + 1 + (kKSteps + 1) * TN;  // X codes, X scales, W codes + scales
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -139,52 +156,63 @@ void gemm_w4a4_kernel(W4A4Args a) {
   const uint32_t kb = (uint32_t)a.k / 2, kq = (uint32_t)a.k / 32;
 
   // activation codes: lane L of this wave's instruction i writes LDS piece
-  // P = (wave + 8 i) 64 + L of the stage, i.e. row P / 4, physical chunk
-  // P % 4, which holds the row's logical chunk xchunk(row, P % 4)
+  // P = (wave + 8 i) 64 + L of the stage, i.e. row P / 2KS, physical chunk
+  // P % 2KS, which holds the row's logical chunk xchunk(row, P % 2KS)
   const __amdgpu_buffer_rsrc_t rxc = make_rsrc(a.xcodes, (uint32_t)((size_t)a.m * kb));
   const __amdgpu_buffer_rsrc_t rxs = make_rsrc(a.xscales, (uint32_t)((size_t)a.m * kq));
   uint32_t v_x[XI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
     const int P = (wave + kW4Waves * i) * 64 + lane;
-    const int r = P >> 2;
-    v_x[i] = (uint32_t)(m0 + min(r, mrows - 1)) * kb + (uint32_t)xchunk(r, P & 3) * 16u;
+    const int r = P / SL::kChunks;
+    v_x[i] = (uint32_t)(m0 + min(r, mrows - 1)) * kb + (uint32_t)SL::xchunk(r, P % SL::kChunks) * 16u;
   }
   // activation scales: instruction wave % SI covers rows 64 (wave % SI) ..;
   // waves past SI repeat one (the same bytes to the same place)
   const int si = wave % SI;
-  const uint32_t v_xs = (uint32_t)(m0 + min(si * 64 + lane, mrows - 1)) * kq;
+  const int srow = (si * 64 + lane) / kScaleWords, sword = (si * 64 + lane) % kScaleWords;
+  const uint32_t v_xs = (uint32_t)(m0 + min(srow, mrows - 1)) * kq + (uint32_t)sword * 4u;
   auto load_x = [&](int s) __attribute__((always_inline)) {
     uint8_t *st = lds + (s % kW4Stages) * kStage;
 #pragma unroll
     for (int i = 0; i < XI; ++i)
       buffer_load_lds16(rxc, st + (wave + kW4Waves * i) * 1024, v_x[i], (uint32_t)s * kRowBytes);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, (lds_void_t *)(st + kCodeStage + si * 256), 4,
-                                             v_xs, (uint32_t)s * 4u, 0, 0);
+                                             v_xs, (uint32_t)s * (kSliceK / 32), 0, 0);
   };
 
   // weights: lane (lr, h) holds weight rows n0 + 32 (TN wn + tn) + lr; per
-  // slice their code bytes 32 h .. 32 h + 31 (K blocks 2h, 2h + 1) and 4 scales
+  // slice their code bytes 16 KS h .. (K blocks KS h .. KS h + KS - 1) and the
+  // row's 2 KS scales of the slice
   const __amdgpu_buffer_rsrc_t rwc = make_rsrc(a.wcodes, (uint32_t)((size_t)a.n * kb));
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(a.wscales, (uint32_t)((size_t)a.n * kq));
   uint32_t v_wc[TN], v_ws[TN];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
     const uint32_t wrow = (uint32_t)min(n0 + 32 * (TN * wn + tn) + lr, a.n - 1);
-    v_wc[tn] = wrow * kb + 32u * (uint32_t)h;
+    v_wc[tn] = wrow * kb + 16u * KS * (uint32_t)h;
     v_ws[tn] = wrow * kq;
   }
   struct WPiece {
-    u32x4_t q0[TN], q1[TN];  // K blocks 2h, 2h + 1
-    uint32_t s[TN];          // each row's 4 E8M0 scales of the slice
+    u32x4_t q[kKSteps][TN];       // K blocks KS h + ks
+    uint32_t s[TN][kScaleWords];  // each row's 2 KS E8M0 scales of the slice
   };
   auto load_w = [&](int s) __attribute__((always_inline)) {
     WPiece p;
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
-      p.q0[tn] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rwc, v_wc[tn], (uint32_t)s * kRowBytes, 0));
-      p.q1[tn] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rwc, v_wc[tn], (uint32_t)s * kRowBytes + 16u, 0));
-      p.s[tn] = __builtin_amdgcn_raw_buffer_load_b32(rws, v_ws[tn], (uint32_t)s * 4u, 0);
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks)
+        p.q[ks][tn] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+            rwc, v_wc[tn], (uint32_t)s * kRowBytes + 16u * ks, 0));
+      if constexpr (kScaleWords == 2) {
+        const uint2 w2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+            rws, v_ws[tn], (uint32_t)s * (kSliceK / 32), 0));
+        p.s[tn][0] = w2.x;
+        p.s[tn][kScaleWords - 1] = w2.y;
+      } else {
+        p.s[tn][0] = __builtin_amdgcn_raw_buffer_load_b32(rws, v_ws[tn], (uint32_t)s * (kSliceK / 32), 0);
+      }
     }
     return p;
   };
@@ -199,13 +227,17 @@ void gemm_w4a4_kernel(W4A4Args a) {
       for (int e = 0; e < 16; ++e) acc[tn][t][e] = 0.f;
 
   // this lane's activation operand reads: row 32 (TM wm + t) + lr, logical
-  // chunk 2h + ks at its physical place ((32 t' + lr) >> 2 & 3 = lr >> 2 & 3)
-  uint32_t xo[2];
+  // chunk KS h + ks at its physical place (the XOR takes row bits below 32,
+  // so it is that of lr)
+  uint32_t xo[kKSteps];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-    xo[ks] = (uint32_t)(32 * TM * wm + lr) * kRowBytes + (uint32_t)xchunk(lr, 2 * h + ks) * 16u;
-  const uint32_t xso = (uint32_t)kCodeStage + (uint32_t)(32 * TM * wm + lr) * 4u;
-  const int sshift0 = 8 * (2 * h), sshift1 = 8 * (2 * h + 1);
+  for (int ks = 0; ks < kKSteps; ++ks)
+    xo[ks] = (uint32_t)(32 * TM * wm + lr) * kRowBytes + (uint32_t)SL::xchunk(lr, KS * h + ks) * 16u;
+  // the lane's scale bytes KS h .. KS h + KS - 1 of the row: word (KS h) / 4
+  // from byte (KS h) % 4 on
+  const uint32_t xso = (uint32_t)kCodeStage + (uint32_t)(32 * TM * wm + lr) * 4u * kScaleWords +
+                       (uint32_t)(KS * h / 4) * 4u;
+  const int sbyte0 = (KS * h) % 4;
 
   // The waits below count loads, so the loads must issue slice by slice (the
   // scheduler is kept from regrouping the first slices' loads).
@@ -231,46 +263,38 @@ void gemm_w4a4_kernel(W4A4Args a) {
 
     const uint8_t *stg = lds + (s % kW4Stages) * kStage;
     const WPiece &wp = wr[u];
-    // k-step 0's activation operands and the scale words first; k-step 1's
-    // operands are read from LDS during k-step 0's MFMAs (one read after
-    // each of the last TM MFMAs, the order pinned), so that only k-step 0
-    // waits on LDS (left to itself the scheduler issued each read one or two
-    // MFMAs ahead of its use: 1-3% slower)
-    u32x4_t b0[TM], b1[TM];
+    // k-step 0's activation operands and the scale words first; k-step
+    // ks + 1's operands are read from LDS during k-step ks's MFMAs (one read
+    // after each of the last TM MFMAs, the order pinned)
+    u32x4_t bk[2][TM];
     uint32_t xsc[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       const uint8_t *row = stg + t * 32 * kRowBytes;
-      b0[t] = *(const u32x4_t *)(row + xo[0]);
-      xsc[t] = *(const uint32_t *)(stg + xso + t * 32 * 4);
+      bk[0][t] = *(const u32x4_t *)(row + xo[0]);
+      xsc[t] = *(const uint32_t *)(stg + xso + t * 32 * 4 * kScaleWords);
     }
+    uint32_t wsc[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) wsc[tn] = h ? wp.s[tn][kScaleWords - 1] : wp.s[tn][0];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      const u32x4_t q = wp.q0[tn];
-      const v8i_t av = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-      const int sa = (int)((wp.s[tn] >> sshift0) & 0xFFu);
+    for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        const u32x4_t b = b0[t];
-        const v8i_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-        acc[tn][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            av, bv, acc[tn][t], 4, 4, 0, sa, 0, (int)((xsc[t] >> sshift0) & 0xFFu));
-        if (tn == TN - 1) b1[t] = *(const u32x4_t *)(stg + t * 32 * kRowBytes + xo[1]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+      for (int tn = 0; tn < TN; ++tn) {
+        const u32x4_t q = wp.q[ks][tn];
+        const v8i_t av = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+        const int sa = (int)((wsc[tn] >> (8 * (sbyte0 + ks))) & 0xFFu);
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      const u32x4_t q = wp.q1[tn];
-      const v8i_t av = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-      const int sa = (int)((wp.s[tn] >> sshift1) & 0xFFu);
-#pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        const u32x4_t b = b1[t];
-        const v8i_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-        acc[tn][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            av, bv, acc[tn][t], 4, 4, 0, sa, 0, (int)((xsc[t] >> sshift1) & 0xFFu));
+        for (int t = 0; t < TM; ++t) {
+          const u32x4_t b = bk[ks & 1][t];
+          const v8i_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+          acc[tn][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              av, bv, acc[tn][t], 4, 4, 0, sa, 0, (int)((xsc[t] >> (8 * (sbyte0 + ks))) & 0xFFu));
+          if (tn == TN - 1 && ks + 1 < kKSteps)
+            bk[(ks + 1) & 1][t] = *(const u32x4_t *)(stg + t * 32 * kRowBytes + xo[ks + 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   };
@@ -352,6 +376,49 @@ hipError_t launch_quant_mxfp4(const void *x, int m, int k, void *codes, void *sc
   return hipGetLastError();
 }
 
+namespace {
+
+// Dynamic LDS above the default 64 KB: raised once per device and kernel.
+template <int TN, int TM, int KS>
+hipError_t allow_w4_lds(size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  static std::atomic<uint64_t> raised{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (raised.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute((const void *)gemm_w4a4_kernel<TN, TM, KS>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) raised.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
+// The GEMM launches: tiles_m x tn_a tiles of 256 x 256, then (tn_a <
+// tiles_n) the remaining weight rows as 128-row activation tiles.
+template <int KS>
+hipError_t launch_w4_tiles(W4A4Args a, int m, long tiles_m, long tn_a, long tiles_n, hipStream_t s) {
+  using SL = W4Slice<KS>;
+  constexpr int BM = 256, BMT = 128;
+  constexpr size_t lds = (size_t)kW4Stages * (BM * SL::kRowBytes + BM * 4 * SL::kScaleWords);
+  constexpr size_t lds_t = (size_t)kW4Stages * (BMT * SL::kRowBytes + BMT * 4 * SL::kScaleWords);
+  hipError_t e = allow_w4_lds<1, 8, KS>(lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemm_w4a4_kernel<1, 8, KS>), dim3((unsigned)(tiles_m * tn_a)), dim3(64 * kW4Waves),
+                     lds, s, a);
+  if (tn_a == tiles_n) return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = allow_w4_lds<1, 4, KS>(lds_t);
+  if (e != hipSuccess) return e;
+  a.n_begin = (int)(tn_a * kW4BN);
+  const unsigned grid_t = (unsigned)(((m + BMT - 1) / BMT) * (tiles_n - tn_a));
+  hipLaunchKernelGGL((gemm_w4a4_kernel<1, 4, KS>), dim3(grid_t), dim3(64 * kW4Waves), lds_t, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_gemm_w4a4(const qmm_weight &w, const void *x, int m, const void *residual,
                             void *y, void *workspace, hipStream_t s) {
   uint8_t *xc = (uint8_t *)workspace;
@@ -371,9 +438,7 @@ hipError_t launch_gemm_w4a4(const qmm_weight &w, const void *x, int m, const voi
   // one weight-row group per wave: 2 and 4 groups (activation operands
   // shared by 2 or 4 products, but every weight row loaded by 2 or 4 waves)
   // measured 17-24% and 46-50% slower on 17408 x 5120 at M = 512-8192
-  constexpr int TN = 1, TM = 8 / TN;
   constexpr int BM = 256;
-  constexpr size_t lds = (size_t)kW4Stages * (BM * kRowBytes + BM * 4);
   a.n_begin = 0;
   // The last round of one-per-CU workgroups: after at least one whole round,
   // a last round of at most a quarter of the compute units runs as a second
@@ -390,17 +455,9 @@ hipError_t launch_gemm_w4a4(const qmm_weight &w, const void *x, int m, const voi
 #ifdef QMM_TUNE
   if (const char *e = getenv("QMM_W4_TAIL"); e && !atoi(e)) tn_a = tiles_n;
 #endif
-  hipLaunchKernelGGL((gemm_w4a4_kernel<TN, TM>), dim3((unsigned)(tiles_m * tn_a)), dim3(64 * kW4Waves),
-                     lds, s, a);
-  if (tn_a == tiles_n) return hipGetLastError();
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  constexpr int BMT = 128;
-  constexpr size_t lds_t = (size_t)kW4Stages * (BMT * kRowBytes + BMT * 4);
-  a.n_begin = (int)(tn_a * kW4BN);
-  const unsigned grid_t = (unsigned)(((m + BMT - 1) / BMT) * (tiles_n - tn_a));
-  hipLaunchKernelGGL((gemm_w4a4_kernel<1, 4>), dim3(grid_t), dim3(64 * kW4Waves), lds_t, s, a);
-  return hipGetLastError();
+  // 256-wide K slices where K allows (a multiple of 256), else 128-wide
+  return w.k % 256 == 0 ? launch_w4_tiles<4>(a, m, tiles_m, tn_a, tiles_n, s)
+                        : launch_w4_tiles<2>(a, m, tiles_m, tn_a, tiles_n, s);
 }
 
 }  // namespace qmm

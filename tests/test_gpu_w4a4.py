@@ -87,7 +87,9 @@ def test_quant_mxfp4_argument_errors():
 
 
 # several 256 x 256 tiles with ragged m and n, residual on even m
-SHAPES = [(1, 64, 256), (130, 300, 768), (257, 515, 1024), (256, 256, 512), (77, 1000, 2304)]
+# K a multiple of 256 takes 256-wide K slices, the others (384, 1408) 128-wide ones
+SHAPES = [(1, 64, 256), (130, 300, 768), (257, 515, 1024), (256, 256, 512), (77, 1000, 2304),
+          (33, 200, 384), (300, 520, 1408)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
