@@ -39,21 +39,30 @@ struct RouteArgs {
 };
 
 // Block-wide exclusive scan of one value per thread (1024 threads); returns the
-// prefix and writes the total to *total.
+// prefix and writes the total to *total.  Each wave scans its 64 values in
+// registers (six shuffle steps), then every thread adds the totals of the
+// waves before its own from LDS: two barriers in all.
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *buf, uint32_t *total) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kRouteThreads; off <<= 1) {
-    const uint32_t add = tid >= off ? buf[tid - off] : 0u;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+  constexpr int kWaves = kRouteThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
   }
-  const uint32_t incl = buf[tid];
-  if (tid == kRouteThreads - 1) *total = incl;
+  if (lane == 63) buf[wave] = incl;
   __syncthreads();
-  return incl - v;
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t s = buf[w];
+    before += w < wave ? s : 0u;
+    all += s;
+  }
+  if (tid == 0) *total = all;
+  __syncthreads();
+  return before + incl - v;
 }
 
 // Steps 2 to 4 of the route, given each expert's row count in s_count:
@@ -247,20 +256,26 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_scan_kernel(RouteParA
   const int tid = threadIdx.x;
   const int ne = a.num_routed + a.num_shared;
   const int groups = a.tb.route_groups;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.tb.wg_counts, (uint32_t)groups * (uint32_t)ne * 4u);
   // each expert's total, and each workgroup's first position in its group
   for (int e = tid; e < ne; e += kRouteThreads) {
     if (e < a.num_routed) {
-      // batches of 16 loads before their stores: one wait on memory per batch
+      const uint32_t col = (uint32_t)e * 4u;
+      // batches of 64 loads before their stores: one wait on memory per batch
+      // (one batch up to 64 route workgroups); buffer loads and stores at the
+      // column's lane offset plus a uniform row offset, so the batch holds no
+      // addresses in registers
       uint32_t run = 0;
-      for (int g0 = 0; g0 < groups; g0 += 16) {
-        uint32_t v[16];
+      for (int g0 = 0; g0 < groups; g0 += 64) {
+        uint32_t v[64];
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          v[j] = g0 + j < groups ? a.tb.wg_counts[(size_t)(g0 + j) * ne + e] : 0u;
+        for (int j = 0; j < 64; ++j)
+          v[j] = g0 + j < groups ? __builtin_amdgcn_raw_buffer_load_b32(rw, col, (g0 + j) * ne * 4, 0)
+                                 : 0u;
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
+        for (int j = 0; j < 64; ++j)
           if (g0 + j < groups) {
-            a.tb.wg_counts[(size_t)(g0 + j) * ne + e] = run;
+            __builtin_amdgcn_raw_buffer_store_b32(run, rw, col, (g0 + j) * ne * 4, 0);
             run += v[j];
           }
       }

@@ -268,11 +268,12 @@ def test_moe_invalid_expert_ids_contribute_nothing(T):
     check_y(gu, dn, x, ids2, w2, E, 1, yh, hd, tokens)
 
 
-@pytest.mark.parametrize("T", [1638, 1700, 4000])
+@pytest.mark.parametrize("T", [1638, 1700, 4000, 14000])
 def test_moe_many_slots_route(T):
     """Calls with more than 16384 routed slots group them over many workgroups
     (per-workgroup counts, one scan, placement); 1638 x 10 slots is the largest
-    call of the one-workgroup route.  Dropped ids sit in the first, a middle
+    call of the one-workgroup route, and 14000 x 10 slots take 69 workgroups
+    (the scan reads their counts in two batches of up to 64).  Dropped ids sit in the first, a middle
     and the last (ragged) chunk; the tables must still match the oracle's."""
     q = _q()
     E, S, H, I, topk = 64, 1, 256, 128, 10
