@@ -528,6 +528,18 @@ BigTail big_tail(const qmm_weight &w, int m, int cfg) {
   return t;
 }
 
+// Activation rows of the tail's tiles, in blocks of 32: 128, halved while the
+// halved tiles still fit one round of workgroups (nb blocks of 128 weight
+// rows).
+int tail_tm(long m, long nb, long cus) {
+  int tm = 4;
+  while (tm > 1 && (m + 16 * tm - 1) / (16 * tm) * nb <= cus) tm /= 2;
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_TAIL_TM")) tm = atoi(e);
+#endif
+  return tm;
+}
+
 // The big-tile configuration above 256 rows: 8 waves of 32 W rows x 256 X
 // rows (0), x 192 rows (4) or x 320 rows (10), whichever takes the least
 // time counted in rounds of 256-row workgroups (one per compute unit): a
@@ -626,10 +638,14 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
                          : cfg == 4 ? launch_big_mode<6, 8, kDense>(w.format, a, ga, s)
                                     : launch_big_mode<10, 8, kDense>(w.format, a, ga, s);
     if (e != hipSuccess || t.tn_a == t.tiles_n) return e;
-    // the remaining weight rows as 128 x 128 tiles, several to a compute unit
+    // the remaining weight rows as tiles of 128 weight rows
     a.n_begin = (int)(t.tn_a * bn_of(8));
     const int rest = w.n - a.n_begin;
-    const dim3 gb((unsigned)(((m + 127) / 128) * ((rest + bn_of(4) - 1) / bn_of(4))));
+    const int nb = (rest + bn_of(4) - 1) / bn_of(4);
+    const int tm = tail_tm(m, nb, compute_units());
+    const dim3 gb((unsigned)(((m + 32 * tm - 1) / (32 * tm)) * nb));
+    if (tm == 1) return launch_big_mode<1, 4, kDense>(w.format, a, gb, s);
+    if (tm == 2) return launch_big_mode<2, 4, kDense>(w.format, a, gb, s);
     return launch_big_mode<4, 4, kDense>(w.format, a, gb, s);
   }
   // up to 256 rows: split K when the caller's workspace holds the partials

@@ -120,8 +120,9 @@ def test_gemm_rejects():
 
 # The prefill workload's own sizes, in the tile configurations the library
 # picks for them (320-row activation tiles at M = 8192; at 1024, 2048, 3072
-# and 4096 256-row tiles for whole rounds of workgroups and 128 x 128 tiles
-# for the last 1024 weight rows; 192-row at 512, and
+# and 4096 256-row tiles for whole rounds of workgroups and tiles of 128
+# weight rows for the last 1024, by 32 activation rows at M = 1024, 64 at
+# 2048 and 128 at 3072 and 4096; 192-row at 512, and
 # the mid band's tiles: 32 rows with 4 K splits at M = 8, 64 rows at 48, 128
 # rows at 96): the GPU computes
 # the whole product; the oracle checks sampled activation rows (every output
