@@ -395,13 +395,13 @@ hipError_t allow_w4_lds(size_t lds) {
 }
 
 // The GEMM launches: tiles_m x tn_a tiles of 256 x 256, then (tn_a <
-// tiles_n) the remaining weight rows as 128-row activation tiles.
+// tiles_n) the remaining weight rows as tiles of 128 activation rows, or of
+// 64 with 256-wide slices where those still fit one round of workgroups.
 template <int KS>
 hipError_t launch_w4_tiles(W4A4Args a, int m, long tiles_m, long tn_a, long tiles_n, hipStream_t s) {
   using SL = W4Slice<KS>;
-  constexpr int BM = 256, BMT = 128;
+  constexpr int BM = 256;
   constexpr size_t lds = (size_t)kW4Stages * (BM * SL::kRowBytes + BM * 4 * SL::kScaleWords);
-  constexpr size_t lds_t = (size_t)kW4Stages * (BMT * SL::kRowBytes + BMT * 4 * SL::kScaleWords);
   hipError_t e = allow_w4_lds<1, 8, KS>(lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((gemm_w4a4_kernel<1, 8, KS>), dim3((unsigned)(tiles_m * tn_a)), dim3(64 * kW4Waves),
@@ -409,12 +409,24 @@ hipError_t launch_w4_tiles(W4A4Args a, int m, long tiles_m, long tn_a, long tile
   if (tn_a == tiles_n) return hipGetLastError();
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = allow_w4_lds<1, 4, KS>(lds_t);
-  if (e != hipSuccess) return e;
   a.n_begin = (int)(tn_a * kW4BN);
-  const unsigned grid_t = (unsigned)(((m + BMT - 1) / BMT) * (tiles_n - tn_a));
-  hipLaunchKernelGGL((gemm_w4a4_kernel<1, 4, KS>), dim3(grid_t), dim3(64 * kW4Waves), lds_t, s, a);
-  return hipGetLastError();
+  auto tail = [&](auto tm_c) {
+    constexpr int TM = decltype(tm_c)::value, BMT = 32 * TM;
+    constexpr size_t lds_t = (size_t)kW4Stages * (BMT * SL::kRowBytes + BMT * 4 * SL::kScaleWords);
+    hipError_t e2 = allow_w4_lds<1, TM, KS>(lds_t);
+    if (e2 != hipSuccess) return e2;
+    const unsigned grid_t = (unsigned)(((m + BMT - 1) / BMT) * (tiles_n - tn_a));
+    hipLaunchKernelGGL((gemm_w4a4_kernel<1, TM, KS>), dim3(grid_t), dim3(64 * kW4Waves), lds_t, s, a);
+    return hipGetLastError();
+  };
+  if constexpr (KS == 4) {
+    bool half = (m + 63) / 64 * (tiles_n - tn_a) <= compute_units();
+#ifdef QMM_TUNE
+    if (const char *v = getenv("QMM_W4_TAIL_TM")) half = atoi(v) == 2;
+#endif
+    if (half) return tail(std::integral_constant<int, 2>());
+  }
+  return tail(std::integral_constant<int, 4>());
 }
 
 }  // namespace

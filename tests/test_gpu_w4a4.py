@@ -147,11 +147,11 @@ def test_gemm_w4a4_rejects():
 
 
 # The prefill workload's weight, 17408 x 5120 MXFP4, at the sizes the
-# benchmark times (and M = 1024, whose last round of 256 x 256 tiles runs as
-# 128-row tiles, as at 2048): the GPU computes every output, the oracle
-# checks sampled activation rows (every output column of each), tile edges
-# included.
-@pytest.mark.parametrize("m", [128, 1024, 2048, 8192])
+# benchmark times (and M = 1024 and 1000, whose last round of 256 x 256 tiles
+# runs as 64-row tiles, as at 2048; 1000 leaves the last of them ragged): the
+# GPU computes every output, the oracle checks sampled activation rows (every
+# output column of each), tile edges included.
+@pytest.mark.parametrize("m", [128, 1000, 1024, 2048, 8192])
 def test_gemm_w4a4_full_size_sampled(m):
     q = _q()
     n, k = 17408, 5120
@@ -159,7 +159,7 @@ def test_gemm_w4a4_full_size_sampled(m):
     x = quant.synthetic_bf16(m, k, name=f"w4fullx{m}")
     w = q.Weight.from_host(p)
     y = _host_f64(q.gemm_w4a4(w, _dev_bf16(x)))
-    edges = [0, 1, 31, 32, 127, 128, 255, 256, m // 2, m - 2, m - 1]
+    edges = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 959, 960, m // 2, m - 2, m - 1]
     rows = np.unique(np.concatenate([edges, rng.randint_bytes(73, f"w4fr{m}", 13, 0, 256)
                                      .astype(np.int64) * (m // 256)]))
     rows = rows[rows < m]
