@@ -456,7 +456,27 @@ constexpr int bn_of(int waves) { return 32 * waves; }
 //   else:    128-row tiles, unsplit  (57 us at m = 128; 2 splits 75 us)
 // A split writes and reads back m x n float32 partials, so it pays only while
 // m is small.
-int small_m_tile(int m) { return m <= 32 ? 1 : (m <= 64 ? 2 : 4); }
+// Activation rows per tile (in blocks of 32) up to 256 rows: the fewest
+// blocks that cover M up to 64 rows (those calls may split K); above, the
+// height whose tiles take the least time counted in rounds of workgroups (one
+// per compute unit), a 64-row tile taking ~0.8 and a 32-row one ~0.72 of a
+// 128-row one (each runs the whole K loop).  Interleaved A/B, NVFP4 and
+// affine, bit-identical: 17408 x 5120 at M = 192 89 -> 72 us (64-row tiles
+// in 2 rounds against 128-row tiles in 2); 5120 x 17408 (40 blocks of weight
+// rows) at M = 96-192 129-134 -> 98-105 us (32-row), at 256 135 -> 114 us
+// (64-row); 17408 x 5120 at M = 96, 128 and 256 keeps 128-row tiles.
+int small_m_tile(const qmm_weight &w, int m) {
+  if (m <= 64) return m <= 32 ? 1 : 2;
+  const long nb = (w.n + 127) / 128, cus = compute_units();
+  int best = 4;
+  double best_cost = 0.0;
+  for (int tm : {4, 2, 1}) {
+    const long tiles = (m + 32 * tm - 1) / (32 * tm) * nb;
+    const double cost = (double)((tiles + cus - 1) / cus) * (tm == 4 ? 1.0 : tm == 2 ? 0.8 : 0.72);
+    if (tm == 4 || cost < best_cost) best = tm, best_cost = cost;
+  }
+  return best;
+}
 
 int small_m_splits(const qmm_weight &w, int m) {
   if (m > 256 || w.n % 4 != 0) return 1;
@@ -660,7 +680,7 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
     const hipError_t e = launch_zero(workspace, split_counters_bytes(w, m), s);
     if (e != hipSuccess) return e;
   }
-  int tm = small_m_tile(m);
+  int tm = small_m_tile(w, m);
 #ifdef QMM_TUNE
   if (const char *e = getenv("QMM_SMALL_TM")) tm = atoi(e);
 #endif

@@ -124,7 +124,7 @@ def test_gemm_rejects():
 # weight rows for the last 1024, by 32 activation rows at M = 1024, 64 at
 # 2048 and 128 at 3072 and 4096; 192-row at 512, and
 # the mid band's tiles: 32 rows with 4 K splits at M = 8, 64 rows at 48, 128
-# rows at 96): the GPU computes
+# rows at 96, 64 rows at 192): the GPU computes
 # the whole product; the oracle checks sampled activation rows (every output
 # column of each), including both edges of the tiles.
 FULL_N, FULL_K = 17408, 5120
@@ -146,7 +146,7 @@ def full_weights():
                                    (F.AFFINE4_G64, 4096), (F.AFFINE4_G64, 3072), (F.NVFP4, 1024),
                                    (F.NVFP4, 128), (F.NVFP4, 512), (F.NVFP4, 2048),
                                    (F.NVFP4, 4096), (F.NVFP4, 8192), (F.AFFINE4_G64, 8), (F.NVFP4, 16),
-                                   (F.Q6_K, 5), (F.NVFP4, 48), (F.Q6_K, 96)])
+                                   (F.Q6_K, 5), (F.NVFP4, 48), (F.Q6_K, 96), (F.NVFP4, 192)])
 def test_gemm_prefill_full_size_sampled(full_weights, fmt, m):
     q = _q()
     p = full_weights(fmt)
