@@ -456,39 +456,57 @@ constexpr int bn_of(int waves) { return 32 * waves; }
 //   else:    128-row tiles, unsplit  (57 us at m = 128; 2 splits 75 us)
 // A split writes and reads back m x n float32 partials, so it pays only while
 // m is small.
-// Activation rows per tile (in blocks of 32) up to 256 rows: the fewest
-// blocks that cover M up to 64 rows (those calls may split K); above, the
-// height whose tiles take the least time counted in rounds of workgroups (one
-// per compute unit), a 64-row tile taking ~0.8 and a 32-row one ~0.72 of a
-// 128-row one (each runs the whole K loop).  Interleaved A/B, NVFP4 and
-// affine, bit-identical: 17408 x 5120 at M = 192 89 -> 72 us (64-row tiles
-// in 2 rounds against 128-row tiles in 2); 5120 x 17408 (40 blocks of weight
-// rows) at M = 96-192 129-134 -> 98-105 us (32-row), at 256 135 -> 114 us
-// (64-row); 17408 x 5120 at M = 96, 128 and 256 keeps 128-row tiles.
-int small_m_tile(const qmm_weight &w, int m) {
-  if (m <= 64) return m <= 32 ? 1 : 2;
-  const long nb = (w.n + 127) / 128, cus = compute_units();
-  int best = 4;
-  double best_cost = 0.0;
-  for (int tm : {4, 2, 1}) {
-    const long tiles = (m + 32 * tm - 1) / (32 * tm) * nb;
-    const double cost = (double)((tiles + cus - 1) / cus) * (tm == 4 ? 1.0 : tm == 2 ? 0.8 : 0.72);
-    if (tm == 4 || cost < best_cost) best = tm, best_cost = cost;
+// Up to 256 activation rows: the tile height (tm blocks of 32 rows) and the
+// K split (sk ways, float32 partials in the caller's workspace).  Up to 64
+// rows: the fewest blocks that cover M, split 4 ways up to 16 rows and 2 up
+// to 32.  Above: the (tm, sk) whose workgroups take the least time counted
+// in rounds of one workgroup per compute unit, a workgroup costing its slices
+// (64 K values) weighted by tile height (1, 0.8 and 0.72 for 128, 64 and 32
+// rows: each tile runs its whole K range) plus ~20 slices for a split's
+// partials, finish and counter clearing.  Interleaved A/B, NVFP4 (bits equal
+// where nothing splits): 17408 x 5120 at M = 160-192 89 -> 72 us (64-row
+// tiles), 96, 128 and 256 unchanged (no split pays with 80 slices); 5120 x
+// 17408 (40 blocks of weight rows, 272 slices) at M = 96-128 97-99 -> 52-56
+// us (128-row tiles split 4 ways), 192 105 -> 72 us (64-row, 2 ways), 256
+// 110 -> 87 us (128-row, 2 ways).  `split` false: the caller's workspace
+// cannot hold partials.
+struct SmallPlan {
+  int tm, sk;
+};
+
+SmallPlan small_m_plan(const qmm_weight &w, int m, bool split) {
+  const int slices = w.k / kBK;
+  // partial offsets stay 32-bit; each split keeps the three-stage pipeline busy
+  auto split_ok = [&](int sk) {
+    return split && w.n % 4 == 0 && (slices + sk - 1) / sk >= 4 &&
+           (double)sk * m * w.n * 4 < 4294967296.0;
+  };
+  SmallPlan p{4, 1};
+  if (m <= 64) {
+    p.tm = m <= 32 ? 1 : 2;
+    p.sk = m <= 16 ? 4 : (m <= 32 ? 2 : 1);
+    while (p.sk > 1 && !split_ok(p.sk)) p.sk /= 2;
+  } else {
+    const long nb = (w.n + 127) / 128, cus = compute_units();
+    double best = 0.0;
+    for (int tm : {4, 2, 1})
+      for (int sk : {1, 2, 4}) {
+        if (sk > 1 && !split_ok(sk)) continue;
+        const long wgs = (m + 32 * tm - 1) / (32 * tm) * nb * sk;
+        const double per = (tm == 4 ? 1.0 : tm == 2 ? 0.8 : 0.72) * ((slices + sk - 1) / sk) +
+                           (sk > 1 ? 20.0 : 0.0);
+        const double cost = (double)((wgs + cus - 1) / cus) * per;
+        if ((tm == 4 && sk == 1) || cost < best) p = {tm, sk}, best = cost;
+      }
   }
-  return best;
+#ifdef QMM_TUNE
+  if (const char *e = getenv("QMM_GEMM_SPLITS")) p.sk = split ? std::max(1, atoi(e)) : 1;
+  if (const char *e = getenv("QMM_SMALL_TM")) p.tm = atoi(e);
+#endif
+  return p;
 }
 
-int small_m_splits(const qmm_weight &w, int m) {
-  if (m > 256 || w.n % 4 != 0) return 1;
-#ifdef QMM_TUNE
-  if (const char *e = getenv("QMM_GEMM_SPLITS")) return std::max(1, atoi(e));
-#endif
-  int sk = m <= 16 ? 4 : (m <= 32 ? 2 : 1);
-  const int slices = w.k / kBK;
-  while (sk > 1 && ((slices + sk - 1) / sk < 4 || (double)sk * m * w.n * 4 >= 4294967296.0))
-    sk /= 2;  // keep the three-stage pipeline busy; 32-bit partial offsets
-  return sk;
-}
+int small_m_splits(const qmm_weight &w, int m) { return m > 256 ? 1 : small_m_plan(w, m, true).sk; }
 
 size_t split_counters_bytes(const qmm_weight &w, int m) {
   const size_t tiles = (size_t)((m + 31) / 32) * ((w.n + 127) / 128);  // 32-row tiles at most
@@ -669,10 +687,12 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
     return launch_big_mode<4, 4, kDense>(w.format, a, gb, s);
   }
   // up to 256 rows: split K when the caller's workspace holds the partials
-  const int sk = small_m_splits(w, m);
-  if (sk > 1 && workspace && workspace_bytes >= gemm_big_workspace(w, m)) {
-    a.splits = sk;
-    a.sps = (w.k / kBK + sk - 1) / sk;
+  SmallPlan p = small_m_plan(w, m, true);
+  if (p.sk > 1 && !(workspace && workspace_bytes >= gemm_big_workspace(w, m)))
+    p = small_m_plan(w, m, false);
+  if (p.sk > 1) {
+    a.splits = p.sk;
+    a.sps = (w.k / kBK + p.sk - 1) / p.sk;
     a.counters = (uint32_t *)workspace;
     a.partials = (float *)((char *)workspace + split_counters_bytes(w, m));
     // the workspace may hold anything: the tile counters start from zero,
@@ -680,10 +700,7 @@ hipError_t launch_gemm_big(const qmm_weight &w, const void *x, int m, const void
     const hipError_t e = launch_zero(workspace, split_counters_bytes(w, m), s);
     if (e != hipSuccess) return e;
   }
-  int tm = small_m_tile(w, m);
-#ifdef QMM_TUNE
-  if (const char *e = getenv("QMM_SMALL_TM")) tm = atoi(e);
-#endif
+  const int tm = p.tm;
   if (tm == 1) return launch_big_mode<1, 4, kDense>(w.format, a, grid(32, bn_of(4)), s);
   if (tm == 2) return launch_big_mode<2, 4, kDense>(w.format, a, grid(64, bn_of(4)), s);
   return launch_big_mode<4, 4, kDense>(w.format, a, grid(128, bn_of(4)), s);

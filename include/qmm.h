@@ -206,14 +206,15 @@ int qbench_mfma_peak(int32_t iters, int32_t blocks, void *sink, double *flops, v
  * residual  bf16 [m][n] or NULL
  * y         bf16 [m][n], rounded to nearest even
  * x, y and residual must be 16-byte aligned.
- * workspace  optional.  For calls of up to 32 rows, qgemm_workspace_size
- *            returns the bytes (256-byte aligned, any contents) with which
- *            the call splits K over several workgroups: each writes float32
- *            partial sums and the last of a tile's workgroups adds them in
- *            split order (a fixed order, so results are the same on every
- *            run; they differ from an unsplit call's only in summation
- *            order).  With a NULL or smaller workspace the call runs
- *            unsplit.  Above 32 rows it returns 0.
+ * workspace  optional.  For calls of up to 32 rows, and of 65 to 256 rows
+ *            where the weight has few row blocks and a long K (e.g. 5120 x
+ *            17408), qgemm_workspace_size returns the bytes (256-byte
+ *            aligned, any contents) with which the call splits K over several
+ *            workgroups: each writes float32 partial sums and the last of a
+ *            tile's workgroups adds them in split order (a fixed order, so
+ *            results are the same on every run; they differ from an unsplit
+ *            call's only in summation order).  With a NULL or smaller
+ *            workspace the call runs unsplit.  Otherwise it returns 0.
  */
 size_t qgemm_workspace_size(const qmm_weight *w, int32_t m);
 int qgemm(const qmm_weight *w, const void *x, int32_t m, const void *residual, void *y,

@@ -161,6 +161,31 @@ def test_gemm_prefill_full_size_sampled(full_weights, fmt, m):
     _check(y[rows], yref, mag)
 
 
+# The prefill workload's down-projection shape, 5120 x 17408 (40 blocks of
+# 128 weight rows, 272 K slices), at 65 to 256 rows: K split 4 ways over
+# 128-row tiles at 96 and 128 rows, 2 ways over 64-row tiles at 192 and over
+# 128-row tiles at 256 (float32 partials in the workspace the binding
+# allocates), and unsplit when the caller's workspace is too small.
+@pytest.mark.parametrize("fmt,m", [(F.NVFP4, 96), (F.AFFINE4_G64, 128), (F.NVFP4, 192),
+                                   (F.AFFINE4_G64, 256)])
+def test_gemm_down_shape_split_sampled(fmt, m):
+    q = _q()
+    n, k = 5120, 17408
+    p = quant.synthetic_weight(fmt, n, k, name=f"gdown{fmt}")
+    x = quant.synthetic_bf16(m, k, name=f"gdownx{m}")
+    w = q.Weight.from_host(p)
+    xd = _dev_bf16(x)
+    y = _host_f64(q.gemm(w, xd))
+    rows = np.array([0, 1, 31, 32, 63, 64, 95, 127, 128, 191, m // 2, m - 1])
+    rows = np.unique(rows[rows < m])
+    yref, mag = oracle.gemm(p, x[rows])
+    _check(y[rows], yref, mag)
+    # a workspace too small for the partials: the same call unsplit
+    small = torch.empty(256, dtype=torch.uint8, device="cuda")
+    y2 = _host_f64(q.gemm(w, xd, workspace=small))
+    _check(y2[rows], yref, mag)
+
+
 # The mid band: 5 to 8 rows whose activations fit in LDS take the
 # row-streaming GEMV (no workspace), 9 and more the MFMA tiles (split K up to
 # 32 rows); ragged n and a residual on even m; bf16 y within the product bound.
