@@ -457,10 +457,10 @@ constexpr int bn_of(int waves) { return 32 * waves; }
 // A split writes and reads back m x n float32 partials, so it pays only while
 // m is small.
 // Up to 256 activation rows: the tile height (tm blocks of 32 rows) and the
-// K split (sk ways, float32 partials in the caller's workspace).  Up to 64
-// rows: the fewest blocks that cover M, split 4 ways up to 16 rows and 2 up
-// to 32.  Above: the (tm, sk) whose workgroups take the least time counted
-// in rounds of one workgroup per compute unit, a workgroup costing its slices
+// K split (sk ways, float32 partials in the caller's workspace).  From the
+// fewest blocks that cover M (split 4 ways up to 16 rows and 2 up to 32),
+// lower tiles or more splits where they take less time counted in rounds of
+// one workgroup per compute unit, a workgroup costing its slices
 // (64 K values) weighted by tile height (1, 0.8 and 0.72 for 128, 64 and 32
 // rows: each tile runs its whole K range) plus ~20 slices for a split's
 // partials, finish and counter clearing.  Interleaved A/B, NVFP4 (bits equal
@@ -468,8 +468,9 @@ constexpr int bn_of(int waves) { return 32 * waves; }
 // tiles), 96, 128 and 256 unchanged (no split pays with 80 slices); 5120 x
 // 17408 (40 blocks of weight rows, 272 slices) at M = 96-128 97-99 -> 52-56
 // us (128-row tiles split 4 ways), 192 105 -> 72 us (64-row, 2 ways), 256
-// 110 -> 87 us (128-row, 2 ways).  `split` false: the caller's workspace
-// cannot hold partials.
+// 110 -> 87 us (128-row, 2 ways), 40-64 102-106 -> 38-42 us (64-row, 4
+// ways), 24 52 -> 32 us (32-row, 4 ways).  `split` false: the caller's
+// workspace cannot hold partials.
 struct SmallPlan {
   int tm, sk;
 };
@@ -481,24 +482,27 @@ SmallPlan small_m_plan(const qmm_weight &w, int m, bool split) {
     return split && w.n % 4 == 0 && (slices + sk - 1) / sk >= 4 &&
            (double)sk * m * w.n * 4 < 4294967296.0;
   };
-  SmallPlan p{4, 1};
-  if (m <= 64) {
-    p.tm = m <= 32 ? 1 : 2;
-    p.sk = m <= 16 ? 4 : (m <= 32 ? 2 : 1);
-    while (p.sk > 1 && !split_ok(p.sk)) p.sk /= 2;
-  } else {
-    const long nb = (w.n + 127) / 128, cus = compute_units();
-    double best = 0.0;
-    for (int tm : {4, 2, 1})
-      for (int sk : {1, 2, 4}) {
-        if (sk > 1 && !split_ok(sk)) continue;
-        const long wgs = (m + 32 * tm - 1) / (32 * tm) * nb * sk;
-        const double per = (tm == 4 ? 1.0 : tm == 2 ? 0.8 : 0.72) * ((slices + sk - 1) / sk) +
-                           (sk > 1 ? 20.0 : 0.0);
-        const double cost = (double)((wgs + cus - 1) / cus) * per;
-        if ((tm == 4 && sk == 1) || cost < best) p = {tm, sk}, best = cost;
-      }
-  }
+  // the base plan: the fewest blocks that cover M, and (up to 32 rows) the
+  // split measured best on the mid band's 17408 x 5120 calls
+  const int tm0 = m <= 32 ? 1 : m <= 64 ? 2 : 4;
+  int sk0 = m <= 16 ? 4 : (m <= 32 ? 2 : 1);
+  while (sk0 > 1 && !split_ok(sk0)) sk0 /= 2;
+  const long nb = (w.n + 127) / 128, cus = compute_units();
+  auto cost = [&](int tm, int sk) {
+    const long wgs = (m + 32 * tm - 1) / (32 * tm) * nb * sk;
+    const double per = (tm == 4 ? 1.0 : tm == 2 ? 0.8 : 0.72) * ((slices + sk - 1) / sk) +
+                       (sk > 1 ? 20.0 : 0.0);
+    return (double)((wgs + cus - 1) / cus) * per;
+  };
+  // lower tiles or more splits where the round count says so
+  SmallPlan p{tm0, sk0};
+  double best = cost(tm0, sk0);
+  for (int tm : {4, 2, 1})
+    for (int sk : {1, 2, 4}) {
+      if (tm > tm0 || sk < sk0 || (sk > 1 && !split_ok(sk))) continue;
+      const double c = cost(tm, sk);
+      if (c < best) p = {tm, sk}, best = c;
+    }
 #ifdef QMM_TUNE
   if (const char *e = getenv("QMM_GEMM_SPLITS")) p.sk = split ? std::max(1, atoi(e)) : 1;
   if (const char *e = getenv("QMM_SMALL_TM")) p.tm = atoi(e);

@@ -206,7 +206,7 @@ int qbench_mfma_peak(int32_t iters, int32_t blocks, void *sink, double *flops, v
  * residual  bf16 [m][n] or NULL
  * y         bf16 [m][n], rounded to nearest even
  * x, y and residual must be 16-byte aligned.
- * workspace  optional.  For calls of up to 32 rows, and of 65 to 256 rows
+ * workspace  optional.  For calls of up to 32 rows, and of up to 256 rows
  *            where the weight has few row blocks and a long K (e.g. 5120 x
  *            17408), qgemm_workspace_size returns the bytes (256-byte
  *            aligned, any contents) with which the call splits K over several

@@ -162,12 +162,13 @@ def test_gemm_prefill_full_size_sampled(full_weights, fmt, m):
 
 
 # The prefill workload's down-projection shape, 5120 x 17408 (40 blocks of
-# 128 weight rows, 272 K slices), at 65 to 256 rows: K split 4 ways over
-# 128-row tiles at 96 and 128 rows, 2 ways over 64-row tiles at 192 and over
-# 128-row tiles at 256 (float32 partials in the workspace the binding
-# allocates), and unsplit when the caller's workspace is too small.
-@pytest.mark.parametrize("fmt,m", [(F.NVFP4, 96), (F.AFFINE4_G64, 128), (F.NVFP4, 192),
-                                   (F.AFFINE4_G64, 256)])
+# 128 weight rows, 272 K slices), at 17 to 256 rows: K split 4 ways over
+# 32-row tiles at 24 rows, over 64-row tiles at 48 and over 128-row tiles at
+# 96 and 128, 2 ways over 64-row tiles at 192 and over 128-row tiles at 256
+# (float32 partials in the workspace the binding allocates), and unsplit
+# when the caller's workspace is too small.
+@pytest.mark.parametrize("fmt,m", [(F.AFFINE4_G64, 24), (F.NVFP4, 48), (F.NVFP4, 96),
+                                   (F.AFFINE4_G64, 128), (F.NVFP4, 192), (F.AFFINE4_G64, 256)])
 def test_gemm_down_shape_split_sampled(fmt, m):
     q = _q()
     n, k = 5120, 17408
